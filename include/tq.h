@@ -1,0 +1,171 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) TurboQuant hot path.
+ *
+ * The method (cited by page title and section):
+ *   [P5] "谷歌TurboQuant如何绕过内存墙？重新审视它的技术突破", section
+ *        "2.TurboQuant到底做了什么？": 第一阶段 (random rotation, then an
+ *        MSE-optimal Lloyd-Max scalar quantiser for the known Beta-shaped law
+ *        of a rotated coordinate, no per-block scale or zero point) and
+ *        第二阶段 (b-1 MSE bits plus a 1-bit QJL transform of the residual,
+ *        which makes the inner-product estimate unbiased).
+ *   [P3] "TurboQuant 与 AI 效率革命：当旧数学遇到新智能", section 三
+ *        (非对称估计器: sqrt(pi/2)/m * ||k|| * <S q, sign(S k)>; 零开销的秘密:
+ *        m sign bits plus one 32-bit norm) and section 四 (三段论: rotation P,
+ *        JL projection S in R^{m x d}, sign(S * residual)).
+ *
+ * Conventions for every entry point:
+ *   - Return value is a tq_status; TQ_OK (0) on success.  Nothing throws
+ *     across the ABI.  tq_last_error() gives a human-readable reason for the
+ *     last failure on the calling thread.
+ *   - Device pointers are caller-owned HIP device memory on the current
+ *     device; host pointers are ordinary host memory.  Each argument below
+ *     says which.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device entry points only enqueue kernels on it and return; asynchronous
+ *     faults surface at the caller's next synchronisation.
+ *   - The library allocates device memory only for its per-(parameters,
+ *     device) cache of the rotation, the JL matrix and the codebook, built on
+ *     the first call that needs them and freed by tq_release_cache().  The
+ *     hot-path calls allocate nothing; scratch comes in through `workspace`.
+ *   - Sizes: d and m must be multiples of 128 in [128, 1024]; the device
+ *     kernels of this version support d == m == 128 (other shapes return
+ *     TQ_ERR_UNSUPPORTED).  b in [1, 5] (prod) or [1, 4] (mse) with the
+ *     number of Lloyd-Max bits B <= 4.  n == 0 (or seq == 0) is a no-op.
+ *   - Device pointers must be 16-byte aligned (TQ_ERR_ALIGNMENT otherwise).
+ *   - Inputs must be finite (precondition, not checked).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_LAYOUT_VERSION 1
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad enum        */
+  TQ_ERR_UNSUPPORTED = 2,  /* valid for the method, not built for (d, m, b) */
+  TQ_ERR_ALIGNMENT = 3,    /* device pointer not 16-byte aligned            */
+  TQ_ERR_HIP = 4,          /* HIP runtime error or no usable device         */
+  TQ_ERR_NO_MEMORY = 5,    /* cache allocation failed / workspace too small */
+} tq_status;
+
+/* prod: B = b-1 Lloyd-Max bits + m QJL sign bits (unbiased inner products);
+ * mse : B = b Lloyd-Max bits only (reconstruction, used for values).       */
+typedef enum { TQ_MODE_PROD = 0, TQ_MODE_MSE = 1 } tq_mode;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+/* The problem statement: dimension d, total bits per coordinate b, number of
+ * JL rows m, mode, and the seeds of the rotation Pi and of S.  Pi is the Q
+ * factor (with positive diag(R)) of a d x d Gaussian drawn from seed_pi; S is
+ * an m x d N(0,1) matrix drawn from seed_s.  Both Gaussians come from
+ * SplitMix64 words (element (i, j) of an R x C matrix is counter i*C + j,
+ * Box-Muller on counter pairs); see DESIGN notes in the repository.       */
+typedef struct {
+  int32_t d;
+  int32_t b;
+  int32_t m;
+  int32_t mode;     /* tq_mode */
+  uint64_t seed_pi;
+  uint64_t seed_s;
+} tq_params;
+
+/* Packed codes of n vectors, structure of arrays, all device memory owned by
+ * the caller (sizes from tq_codes_bytes):
+ *   idx   uint32 [n][d/32][B]  word w of plane j holds bit j of the indices
+ *                              of 32 coordinates: coordinate
+ *                              c = 128 q + 16 t + 4 k + i (t<8, k<4, i<4)
+ *                              sits in word 4 q + k at bit 4 t + i.
+ *                              NULL when B == 0.
+ *   sgn   uint32 [n][m/32]     QJL sign bits, same word/bit map over the m
+ *                              rows; bit set <=> (S r)_row >= 0.  prod only.
+ *   knorm float  [n]           ||x||
+ *   rnorm float  [n]           ||r||, r = x - ||x|| Pi^T c[idx].  prod only.
+ * Vector v of a KV cache with n_kv heads and seq positions is
+ * (batch * n_kv + head) * seq + pos.                                      */
+typedef struct {
+  uint32_t *idx;
+  uint32_t *sgn;
+  float *knorm;
+  float *rnorm;
+} tq_codes;
+
+const char *tq_status_string(tq_status s);
+const char *tq_last_error(void);
+int32_t tq_layout_version(void);
+
+/* Lloyd-Max codebook for the law of one coordinate of a randomly rotated
+ * unit vector in R^d, density proportional to (1-x^2)^((d-3)/2) on [-1, 1]
+ * ([P5] 第一阶段: "the Beta law, solved once by Lloyd-Max, stored forever").
+ * Host only, pure.  centroids: host float[2^B] ascending; boundaries: host
+ * float[2^B - 1], boundaries[j] = fp32((c_j + c_{j+1}) / 2) with the middle
+ * one exactly 0.  B = b-1 (prod) or b (mse); B == 0 writes nothing.  d >= 3. */
+tq_status tq_make_codebook(int32_t d, int32_t b, int32_t mode, float *centroids,
+                           float *boundaries);
+
+/* Byte sizes of the four code arrays for n vectors: out[0] idx, out[1] sgn,
+ * out[2] knorm, out[3] rnorm (0 for an absent array).  Host only.          */
+tq_status tq_codes_bytes(const tq_params *p, int64_t n, size_t out[4]);
+
+/* The seeded matrices in float64-accurate form rounded to float32, for tests:
+ * pi: host float[d*d] row-major (y = Pi x), s: host float[m*d] row-major.
+ * Either pointer may be NULL.  Host only.                                  */
+tq_status tq_export_matrices(const tq_params *p, float *pi, float *s);
+
+/* Online encode of n vectors ([P5] 第一阶段 + 第二阶段; [P3] 四):
+ *   nu = ||x||, u = Pi x / nu, idx_i = #{j : u_i >= boundary_j},
+ *   prod: r = x - nu Pi^T c[idx], sign bits of S r, rnorm = ||r||.
+ * x: device, row-major [n][d], dtype TQ_F32 or TQ_BF16.  codes: device
+ * arrays sized by tq_codes_bytes.  A zero vector encodes as idx = 2^(B-1),
+ * all sign bits 1, both norms 0.                                           */
+tq_status tq_encode(const tq_params *p, const void *x, int32_t dtype, int64_t n,
+                    tq_codes codes, void *stream);
+
+/* Workspace bytes tq_score needs for n_kv*g queries.  Host only.           */
+tq_status tq_score_workspace_bytes(const tq_params *p, int64_t n_kv, int64_t g,
+                                   size_t *bytes);
+
+/* Decode-time attention logits straight from the packed codes ([P3]
+ * 非对称估计器 applied to the residual, plus the MSE part):
+ *   logit[h][n] = knorm_n * <Pi q_h, c[idx_n]>
+ *               + sqrt(pi/2)/m * rnorm_n * <S q_h, s_n>,  s = +-1,
+ * query head h reads KV head h / g (grouped-query attention).
+ * q: device float [n_kv*g][d]; codes: device, n_kv*seq vectors, KV head k
+ * owning vectors k*seq .. k*seq+seq-1; logits: device float [n_kv*g][seq]
+ * (unscaled).  workspace: device, >= tq_score_workspace_bytes.             */
+tq_status tq_score(const tq_params *p, const float *q, int64_t n_kv, int64_t g,
+                   tq_codes codes, int64_t seq, float *logits, void *workspace,
+                   size_t ws_bytes, void *stream);
+
+/* Workspace bytes tq_attend needs.  Host only.                             */
+tq_status tq_attend_workspace_bytes(const tq_params *kp, const tq_params *vp,
+                                    int64_t batch, int64_t n_kv, int64_t g,
+                                    int64_t seq, size_t *bytes);
+
+/* One decode step of attention over a compressed KV cache:
+ *   p = softmax(scale * logits) over all seq positions (logits as tq_score),
+ *   out[b][h] = sum_n p_n * ||v_n|| * Pi_V^T c_V[idx_n].
+ * kp: prod-mode parameters of the keys; vp: mse-mode parameters of the
+ * values (same d).  q: device float [batch][n_kv*g][d]; kcodes / vcodes:
+ * device, batch*n_kv*seq vectors each; out: device float [batch][n_kv*g][d].
+ * scale <= 0 selects 1/sqrt(d).  workspace: device, >= the size above.     */
+tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
+                    int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
+                    tq_codes vcodes, int64_t seq, float scale, float *out,
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/* Frees every cached matrix/codebook on every device.  Not thread-safe with
+ * concurrent calls into the library.                                       */
+tq_status tq_release_cache(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,666 @@
+// Host side of libtq: argument checking, the seeded matrices (Pi, S, S'),
+// the Lloyd-Max codebook, the per-(parameters, device) cache and the C ABI
+// entry points declared in include/tq.h.
+//
+// The pages describe the method; this file supplies the one-off set-up it
+// needs:
+//   * "谷歌TurboQuant如何绕过内存墙？重新审视它的技术突破", 第一阶段: a random
+//     rotation makes every coordinate follow one known Beta-shaped law, so a
+//     Lloyd-Max codebook for that law is computed once and reused.
+//   * "TurboQuant 与 AI 效率革命：当旧数学遇到新智能", section 四: a random
+//     rotation P (generated once and reused), a JL projection S in R^{m x d}.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <tuple>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+// --------------------------------------------------------------------------
+// errors
+// --------------------------------------------------------------------------
+static thread_local std::string g_last_error;
+
+void set_error(const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+#define TQ_HIP_CHECK(expr)                                                  \
+  do {                                                                      \
+    hipError_t e_ = (expr);                                                 \
+    if (e_ != hipSuccess) {                                                 \
+      set_error("%s failed: %s", #expr, hipGetErrorString(e_));            \
+      return TQ_ERR_HIP;                                                    \
+    }                                                                       \
+  } while (0)
+
+// --------------------------------------------------------------------------
+// SplitMix64 (Steele, Lea & Flood 2014): word k of the stream seeded with
+// `seed` is mix(seed + (k + 1) * golden_gamma).  Gaussians by Box-Muller on
+// word pairs (2p, 2p + 1) for counter pair p; even counter -> cosine branch.
+// --------------------------------------------------------------------------
+static inline uint64_t sm64(uint64_t seed, uint64_t k) {
+  uint64_t z = seed + (k + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+static void seeded_gaussian(uint64_t seed, int64_t rows, int64_t cols,
+                            std::vector<double> &out) {
+  const int64_t n = rows * cols;
+  out.assign(n, 0.0);
+  const double two53 = 1.0 / 9007199254740992.0;
+  for (int64_t c = 0; c < n; c += 2) {
+    const uint64_t pair = (uint64_t)c / 2;
+    const double u1 = ((double)(sm64(seed, 2 * pair) >> 11) + 1.0) * two53;
+    const double u2 = (double)(sm64(seed, 2 * pair + 1) >> 11) * two53;
+    const double rad = std::sqrt(-2.0 * std::log(u1));
+    const double ang = 2.0 * M_PI * u2;
+    out[c] = rad * std::cos(ang);
+    if (c + 1 < n) out[c + 1] = rad * std::sin(ang);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Pi: Q of G = QR with diag(R) > 0, by Householder reflections.
+// G row-major d x d in, Pi row-major d x d out (y = Pi x).
+// --------------------------------------------------------------------------
+static void rotation_from_gaussian(int d, const std::vector<double> &g,
+                                   std::vector<double> &pi) {
+  // column-major working copy: a[j*d + i] = G[i][j]
+  std::vector<double> a((size_t)d * d), vs((size_t)d * d, 0.0), rdiag(d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) a[(size_t)j * d + i] = g[(size_t)i * d + j];
+  for (int k = 0; k < d; ++k) {
+    double *col = &a[(size_t)k * d];
+    double nrm = 0.0;
+    for (int i = k; i < d; ++i) nrm += col[i] * col[i];
+    nrm = std::sqrt(nrm);
+    const double alpha = col[k] > 0 ? -nrm : nrm;  // reflect away from x0
+    double *v = &vs[(size_t)k * d];
+    for (int i = k; i < d; ++i) v[i] = col[i];
+    v[k] -= alpha;
+    double vn = 0.0;
+    for (int i = k; i < d; ++i) vn += v[i] * v[i];
+    vn = std::sqrt(vn);
+    if (vn > 0)
+      for (int i = k; i < d; ++i) v[i] /= vn;
+    rdiag[k] = alpha;
+    // A[k:, j] -= 2 v (v . A[k:, j]) for j >= k
+    for (int j = k; j < d; ++j) {
+      double *cj = &a[(size_t)j * d];
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += v[i] * cj[i];
+      dot *= 2.0;
+      for (int i = k; i < d; ++i) cj[i] -= dot * v[i];
+    }
+  }
+  // Q = H_0 H_1 ... H_{d-1} I, accumulated backwards; column-major q.
+  std::vector<double> q((size_t)d * d, 0.0);
+  for (int i = 0; i < d; ++i) q[(size_t)i * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k) {
+    const double *v = &vs[(size_t)k * d];
+    for (int j = k; j < d; ++j) {
+      double *cj = &q[(size_t)j * d];
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += v[i] * cj[i];
+      dot *= 2.0;
+      for (int i = k; i < d; ++i) cj[i] -= dot * v[i];
+    }
+  }
+  // positive diagonal: G = (Q D)(D R) with D = sign(diag R)
+  pi.assign((size_t)d * d, 0.0);
+  for (int j = 0; j < d; ++j) {
+    const double s = rdiag[j] < 0 ? -1.0 : 1.0;
+    for (int i = 0; i < d; ++i) pi[(size_t)i * d + j] = s * q[(size_t)j * d + i];
+  }
+}
+
+// --------------------------------------------------------------------------
+// Lloyd-Max codebook for f_d(x) ∝ (1-x^2)^((d-3)/2).  Cell masses come from
+// the regularised incomplete beta function ((X+1)/2 ~ Beta(a, a),
+// a = (d-1)/2), evaluated by its continued fraction (DLMF 8.17.22) with the
+// modified Lentz method; cell first moments from the antiderivative
+// -C (1-x^2)^((d-1)/2) / (d-1).
+// --------------------------------------------------------------------------
+typedef long double ld;
+
+static ld ibeta_cf(ld a, ld b, ld y) {
+  const ld tiny = 1e-300L, eps = 1e-19L;
+  ld f = 1.0L, c = 1.0L, dd = 0.0L;
+  for (int i = 0; i <= 4000; ++i) {
+    const int m = i / 2;
+    ld num;
+    if (i == 0) {
+      num = 1.0L;
+    } else if (i % 2 == 0) {
+      num = (m * (b - m) * y) / ((a + 2 * m - 1) * (a + 2 * m));
+    } else {
+      num = -((a + m) * (a + b + m) * y) / ((a + 2 * m) * (a + 2 * m + 1));
+    }
+    dd = 1.0L + num * dd;
+    if (std::fabs(dd) < tiny) dd = tiny;
+    dd = 1.0L / dd;
+    c = 1.0L + num / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    const ld cd = c * dd;
+    f *= cd;
+    if (std::fabs(1.0L - cd) < eps) break;
+  }
+  return f - 1.0L;
+}
+
+// upper tail P(X >= x) for 0 <= x <= 1 = I_{(1-x)/2}(a, a)
+static ld coord_tail(int d, ld x) {
+  const ld a = (d - 1) / 2.0L;
+  const ld y = (1.0L - x) / 2.0L;
+  if (y <= 0) return 0.0L;
+  const ld lbeta = std::lgamma(a) + std::lgamma(a) - std::lgamma(2 * a);
+  const ld front = std::exp(a * std::log(y) + a * std::log1p(-y) - lbeta) / a;
+  return front * ibeta_cf(a, a, y);
+}
+
+static ld coord_moment_antider(int d, ld x) {
+  const ld logc = std::lgamma(d / 2.0L) - 0.5L * std::log((ld)M_PI) -
+                  std::lgamma((d - 1) / 2.0L);
+  const ld w = 1.0L - x * x;
+  if (w <= 0) return 0.0L;
+  return -std::exp(logc + ((d - 1) / 2.0L) * std::log(w)) / (d - 1);
+}
+
+static void lloyd_max_codebook(int d, int nbits, std::vector<double> &cent) {
+  const int L = 1 << nbits, half = L / 2;
+  std::vector<ld> c(half), nc(half), e(half + 1);
+  const ld span = std::min<ld>(3.0L / std::sqrt((ld)d), 1.0L);
+  for (int j = 0; j < half; ++j) c[j] = (j + 0.5L) * span / half;
+  ld prev = 1.0L;
+  for (int it = 0; it < 100000; ++it) {
+    e[0] = 0.0L;
+    e[half] = 1.0L;
+    for (int j = 1; j < half; ++j) e[j] = 0.5L * (c[j - 1] + c[j]);
+    ld delta = 0.0L;
+    for (int j = 0; j < half; ++j) {
+      const ld mass = coord_tail(d, e[j]) - coord_tail(d, e[j + 1]);
+      const ld mom = coord_moment_antider(d, e[j + 1]) - coord_moment_antider(d, e[j]);
+      nc[j] = mom / mass;
+      delta = std::max(delta, std::fabs(nc[j] - c[j]));
+    }
+    c.swap(nc);
+    // converged, or stalled at the rounding floor of long double
+    if (delta <= 1e-17L * c[half - 1]) break;
+    if (delta < 1e-15L * c[half - 1] && delta >= prev) break;
+    prev = delta;
+  }
+  cent.resize(L);
+  for (int j = 0; j < half; ++j) {
+    cent[half + j] = (double)c[j];
+    cent[half - 1 - j] = -(double)c[j];
+  }
+}
+
+static void build_codebook(int d, int nbits, Codebook &cb) {
+  std::memset(&cb, 0, sizeof(cb));
+  cb.nbits = nbits;
+  if (nbits == 0) return;
+  std::vector<double> cent;
+  lloyd_max_codebook(d, nbits, cent);
+  const int L = 1 << nbits;
+  for (int j = 0; j < L; ++j) cb.c[j] = (float)cent[j];
+  for (int j = 0; j + 1 < L; ++j)
+    cb.t[j] = (float)(0.5 * ((double)cb.c[j] + (double)cb.c[j + 1]));
+  cb.t[L / 2 - 1] = 0.0f;
+  // c[idx] = sum over odd subsets S of the planes of coef_S * prod_{k in S} sigma_k,
+  // sigma_k = 2 bit_k(idx) - 1 (the even subsets vanish because c is odd).
+  int np = 0;
+  for (int size = 1; size <= nbits; size += 2)
+    for (uint32_t mask = 1; mask < (1u << nbits); ++mask)
+      if (__builtin_popcount(mask) == size) cb.part_mask[np++] = mask;
+  cb.nparts = np;
+  for (int s = 0; s < np; ++s) {
+    double acc = 0.0;
+    for (int idx = 0; idx < L; ++idx) {
+      int sign = 1;
+      for (int k = 0; k < nbits; ++k)
+        if (cb.part_mask[s] >> k & 1) sign *= ((idx >> k) & 1) ? 1 : -1;
+      acc += sign * (double)cb.c[idx];
+    }
+    cb.coef[s] = acc / L;
+  }
+}
+
+// --------------------------------------------------------------------------
+// argument checks
+// --------------------------------------------------------------------------
+static int mse_bits(const tq_params *p) { return p->mode == TQ_MODE_PROD ? p->b - 1 : p->b; }
+
+static tq_status check_params(const tq_params *p) {
+  if (!p) {
+    set_error("params is NULL");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (p->mode != TQ_MODE_PROD && p->mode != TQ_MODE_MSE) {
+    set_error("mode %d is neither TQ_MODE_PROD nor TQ_MODE_MSE", p->mode);
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (p->d < 128 || p->d > 1024 || p->d % 128) {
+    set_error("d = %d: must be a multiple of 128 in [128, 1024]", p->d);
+    return p->d > 0 ? TQ_ERR_UNSUPPORTED : TQ_ERR_INVALID_ARG;
+  }
+  if (p->mode == TQ_MODE_PROD && (p->m < 128 || p->m > 1024 || p->m % 128)) {
+    set_error("m = %d: must be a multiple of 128 in [128, 1024]", p->m);
+    return p->m > 0 ? TQ_ERR_UNSUPPORTED : TQ_ERR_INVALID_ARG;
+  }
+  const int B = mse_bits(p);
+  if (p->b < 1 || B > 4) {
+    set_error("b = %d out of range for mode %d", p->b, p->mode);
+    return p->b < 1 ? TQ_ERR_INVALID_ARG : TQ_ERR_UNSUPPORTED;
+  }
+  return TQ_OK;
+}
+
+static bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// --------------------------------------------------------------------------
+// host matrices and device cache
+// --------------------------------------------------------------------------
+static void host_matrices(const tq_params *p, std::vector<double> *pi,
+                          std::vector<double> *s) {
+  if (pi) {
+    std::vector<double> g;
+    seeded_gaussian(p->seed_pi, p->d, p->d, g);
+    rotation_from_gaussian(p->d, g, *pi);
+  }
+  if (s) seeded_gaussian(p->seed_s, p->m, p->d, *s);
+}
+
+static uint16_t bf16_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;  // round to nearest even
+  return (uint16_t)(u >> 16);
+}
+
+static double bf16_value(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// Split a 128 x 128 row-major double matrix into hi/lo bf16 fragments.
+// col_of(kt, lanegroup, e) gives the matrix column that element e of a lane
+// in lane group `lanegroup` holds within column block kt.
+template <typename ColOf>
+static void make_fragments(const std::vector<double> &mat, ColOf col_of,
+                           std::vector<uint16_t> &hi, std::vector<uint16_t> &lo) {
+  hi.assign(kFragElems, 0);
+  lo.assign(kFragElems, 0);
+  size_t o = 0;
+  for (int nt = 0; nt < 8; ++nt)
+    for (int kt = 0; kt < 4; ++kt)
+      for (int l = 0; l < 64; ++l)
+        for (int e = 0; e < 8; ++e, ++o) {
+          const int row = 16 * nt + (l & 15);
+          const int col = col_of(kt, l >> 4, e);
+          const double v = mat[(size_t)row * 128 + col];
+          const uint16_t h = bf16_bits((float)v);
+          hi[o] = h;
+          lo[o] = bf16_bits((float)(v - bf16_value(h)));
+        }
+}
+
+template <typename T>
+static tq_status upload(T **dst, const std::vector<T> &src) {
+  TQ_HIP_CHECK(hipMalloc((void **)dst, src.size() * sizeof(T)));
+  TQ_HIP_CHECK(hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice));
+  return TQ_OK;
+}
+
+static tq_status build_derived(const tq_params *p, int dev, Derived *D) {
+  D->p = *p;
+  D->device = dev;
+  D->B = mse_bits(p);
+  build_codebook(p->d, D->B, D->cb);
+  const bool prod = p->mode == TQ_MODE_PROD;
+  std::vector<double> pi, s;
+  host_matrices(p, &pi, prod ? &s : nullptr);
+  std::vector<float> f(pi.begin(), pi.end());
+  tq_status st = upload(&D->pi32, f);
+  if (st) return st;
+  if (prod) {
+    f.assign(s.begin(), s.end());
+    if ((st = upload(&D->s32, f))) return st;
+  }
+  if (p->d == 128 && (!prod || p->m == 128)) {
+    std::vector<uint16_t> hi, lo;
+    // GEMM 1 (Pi x): element e of lane group g in block kt is column 32 kt + 8 g + e
+    make_fragments(pi, [](int kt, int g, int e) { return 32 * kt + 8 * g + e; }, hi, lo);
+    if ((st = upload(&D->pi_hi, hi)) || (st = upload(&D->pi_lo, lo))) return st;
+    if (prod) {
+      // S' = S Pi^T, consumed against the residual held in the layout of the
+      // first GEMM's output: element e of lane group g in block kt is
+      // coordinate 32 kt + 16 (e / 4) + 4 g + e % 4.
+      std::vector<double> sp((size_t)128 * 128, 0.0);
+      for (int r = 0; r < 128; ++r)
+        for (int c = 0; c < 128; ++c) {
+          double acc = 0.0;
+          for (int j = 0; j < 128; ++j) acc += s[(size_t)r * 128 + j] * pi[(size_t)c * 128 + j];
+          sp[(size_t)r * 128 + c] = acc;
+        }
+      make_fragments(sp, [](int kt, int g, int e) { return 32 * kt + 16 * (e / 4) + 4 * g + e % 4; },
+                     hi, lo);
+      if ((st = upload(&D->sp_hi, hi)) || (st = upload(&D->sp_lo, lo))) return st;
+    }
+  }
+  return TQ_OK;
+}
+
+static void free_derived(Derived *D) {
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  (void)hipSetDevice(D->device);
+  (void)hipFree(D->pi32);
+  (void)hipFree(D->s32);
+  (void)hipFree(D->pi_hi);
+  (void)hipFree(D->pi_lo);
+  (void)hipFree(D->sp_hi);
+  (void)hipFree(D->sp_lo);
+  (void)hipSetDevice(cur);
+  delete D;
+}
+
+typedef std::tuple<int, int, int, int, uint64_t, uint64_t, int> CacheKey;
+static std::mutex g_cache_mu;
+static std::map<CacheKey, Derived *> g_cache;
+
+tq_status get_derived(const tq_params *p, const Derived **out) {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    set_error("no HIP device available");
+    return TQ_ERR_HIP;
+  }
+  int dev = 0;
+  TQ_HIP_CHECK(hipGetDevice(&dev));
+  const int m = p->mode == TQ_MODE_PROD ? p->m : 0;
+  const uint64_t ss = p->mode == TQ_MODE_PROD ? p->seed_s : 0;
+  CacheKey key(p->d, p->b, m, p->mode, p->seed_pi, ss, dev);
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  auto it = g_cache.find(key);
+  if (it != g_cache.end()) {
+    *out = it->second;
+    return TQ_OK;
+  }
+  Derived *D = new Derived();
+  tq_status st = build_derived(p, dev, D);
+  if (st != TQ_OK) {
+    free_derived(D);
+    return st;
+  }
+  g_cache[key] = D;
+  *out = D;
+  return TQ_OK;
+}
+
+static bool kernels_support(const tq_params *p) {
+  return p->d == 128 && (p->mode == TQ_MODE_MSE || p->m == 128);
+}
+
+}  // namespace tq
+
+// ============================================================================
+// C ABI
+// ============================================================================
+using namespace tq;
+
+extern "C" {
+
+const char *tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_ALIGNMENT: return "TQ_ERR_ALIGNMENT";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    case TQ_ERR_NO_MEMORY: return "TQ_ERR_NO_MEMORY";
+  }
+  return "TQ_ERR_UNKNOWN";
+}
+
+const char *tq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t tq_layout_version(void) { return TQ_LAYOUT_VERSION; }
+
+tq_status tq_make_codebook(int32_t d, int32_t b, int32_t mode, float *centroids,
+                           float *boundaries) {
+  if (mode != TQ_MODE_PROD && mode != TQ_MODE_MSE) {
+    set_error("bad mode %d", mode);
+    return TQ_ERR_INVALID_ARG;
+  }
+  const int B = mode == TQ_MODE_PROD ? b - 1 : b;
+  if (d < 3 || b < 1 || B > 4) {
+    set_error("tq_make_codebook: d = %d, b = %d out of range", d, b);
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (B == 0) return TQ_OK;
+  if (!centroids || !boundaries) {
+    set_error("tq_make_codebook: NULL output");
+    return TQ_ERR_INVALID_ARG;
+  }
+  Codebook cb;
+  build_codebook(d, B, cb);
+  std::memcpy(centroids, cb.c, sizeof(float) * (1 << B));
+  std::memcpy(boundaries, cb.t, sizeof(float) * ((1 << B) - 1));
+  return TQ_OK;
+}
+
+tq_status tq_codes_bytes(const tq_params *p, int64_t n, size_t out[4]) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (n < 0 || !out) {
+    set_error("tq_codes_bytes: n < 0 or NULL output");
+    return TQ_ERR_INVALID_ARG;
+  }
+  const int B = mse_bits(p);
+  const bool prod = p->mode == TQ_MODE_PROD;
+  out[0] = (size_t)n * (p->d / 32) * B * 4;
+  out[1] = prod ? (size_t)n * (p->m / 32) * 4 : 0;
+  out[2] = (size_t)n * 4;
+  out[3] = prod ? (size_t)n * 4 : 0;
+  return TQ_OK;
+}
+
+tq_status tq_export_matrices(const tq_params *p, float *pi, float *s) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  std::vector<double> vpi, vs;
+  const bool prod = p->mode == TQ_MODE_PROD;
+  host_matrices(p, pi ? &vpi : nullptr, (s && prod) ? &vs : nullptr);
+  if (pi)
+    for (size_t i = 0; i < vpi.size(); ++i) pi[i] = (float)vpi[i];
+  if (s && prod)
+    for (size_t i = 0; i < vs.size(); ++i) s[i] = (float)vs[i];
+  return TQ_OK;
+}
+
+static tq_status check_codes(const tq_params *p, const tq_codes &c) {
+  const bool prod = p->mode == TQ_MODE_PROD;
+  const int B = p->mode == TQ_MODE_PROD ? p->b - 1 : p->b;
+  if ((B > 0 && !c.idx) || !c.knorm || (prod && (!c.sgn || !c.rnorm))) {
+    set_error("code array missing");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if ((B > 0 && !aligned16(c.idx)) || !aligned16(c.knorm) ||
+      (prod && (!aligned16(c.sgn) || !aligned16(c.rnorm)))) {
+    set_error("code arrays must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  return TQ_OK;
+}
+
+tq_status tq_encode(const tq_params *p, const void *x, int32_t dtype, int64_t n,
+                    tq_codes codes, void *stream) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (n < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) {
+    set_error("tq_encode: n < 0 or bad dtype");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (n == 0) return TQ_OK;
+  if (!x) {
+    set_error("tq_encode: x is NULL");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if ((st = check_codes(p, codes))) return st;
+  if (!aligned16(x)) {
+    set_error("tq_encode: x must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (!kernels_support(p)) {
+    set_error("tq_encode: device kernels are built for d = m = 128 only");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const Derived *D = nullptr;
+  if ((st = get_derived(p, &D))) return st;
+  return launch_encode(*D, x, dtype, n, codes, (hipStream_t)stream);
+}
+
+tq_status tq_score_workspace_bytes(const tq_params *p, int64_t n_kv, int64_t g,
+                                   size_t *bytes) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (n_kv < 0 || g < 1 || !bytes) {
+    set_error("tq_score_workspace_bytes: bad n_kv/g/bytes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  Derived D;
+  D.p = *p;
+  D.B = mse_bits(p);
+  D.cb.nparts = D.B == 0 ? 0 : (D.B == 1 ? 1 : D.B == 2 ? 2 : D.B == 3 ? 4 : 8);
+  *bytes = score_workspace_bytes(D, n_kv, g);
+  return TQ_OK;
+}
+
+tq_status tq_score(const tq_params *p, const float *q, int64_t n_kv, int64_t g,
+                   tq_codes codes, int64_t seq, float *logits, void *workspace,
+                   size_t ws_bytes, void *stream) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (n_kv < 0 || g < 1 || seq < 0) {
+    set_error("tq_score: bad n_kv/g/seq");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (n_kv == 0 || seq == 0) return TQ_OK;
+  if (!q || !logits || !workspace) {
+    set_error("tq_score: NULL q/logits/workspace");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if ((st = check_codes(p, codes))) return st;
+  if (!aligned16(q) || !aligned16(logits) || !aligned16(workspace)) {
+    set_error("tq_score: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (!kernels_support(p)) {
+    set_error("tq_score: device kernels are built for d = m = 128 only");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const Derived *D = nullptr;
+  if ((st = get_derived(p, &D))) return st;
+  if (ws_bytes < score_workspace_bytes(*D, n_kv, g)) {
+    set_error("tq_score: workspace too small (%zu < %zu)", ws_bytes,
+              score_workspace_bytes(*D, n_kv, g));
+    return TQ_ERR_NO_MEMORY;
+  }
+  return launch_score(*D, q, n_kv, g, codes, seq, logits, workspace, (hipStream_t)stream);
+}
+
+tq_status tq_attend_workspace_bytes(const tq_params *kp, const tq_params *vp,
+                                    int64_t batch, int64_t n_kv, int64_t g,
+                                    int64_t seq, size_t *bytes) {
+  tq_status st = check_params(kp);
+  if (st) return st;
+  if ((st = check_params(vp))) return st;
+  if (batch < 0 || n_kv < 0 || g < 1 || seq < 0 || !bytes) {
+    set_error("tq_attend_workspace_bytes: bad sizes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  Derived K, V;
+  K.p = *kp;
+  K.B = mse_bits(kp);
+  K.cb.nparts = K.B == 0 ? 0 : (K.B == 1 ? 1 : K.B == 2 ? 2 : K.B == 3 ? 4 : 8);
+  V.p = *vp;
+  V.B = mse_bits(vp);
+  V.cb.nparts = V.B == 0 ? 0 : (V.B == 1 ? 1 : V.B == 2 ? 2 : V.B == 3 ? 4 : 8);
+  *bytes = attend_workspace_bytes(K, V, batch, n_kv, g, seq);
+  return TQ_OK;
+}
+
+tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
+                    int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
+                    tq_codes vcodes, int64_t seq, float scale, float *out,
+                    void *workspace, size_t ws_bytes, void *stream) {
+  tq_status st = check_params(kp);
+  if (st) return st;
+  if ((st = check_params(vp))) return st;
+  if (kp->mode != TQ_MODE_PROD || vp->mode != TQ_MODE_MSE || kp->d != vp->d) {
+    set_error("tq_attend: keys must be prod mode, values mse mode, same d");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (batch < 0 || n_kv < 0 || g < 1 || seq < 0) {
+    set_error("tq_attend: bad sizes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (batch == 0 || n_kv == 0) return TQ_OK;
+  if (seq == 0) {
+    set_error("tq_attend: softmax over an empty sequence");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (!q || !out || !workspace) {
+    set_error("tq_attend: NULL q/out/workspace");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if ((st = check_codes(kp, kcodes)) || (st = check_codes(vp, vcodes))) return st;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) {
+    set_error("tq_attend: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (!kernels_support(kp) || !kernels_support(vp)) {
+    set_error("tq_attend: device kernels are built for d = m = 128 only");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const Derived *K = nullptr, *V = nullptr;
+  if ((st = get_derived(kp, &K)) || (st = get_derived(vp, &V))) return st;
+  if (ws_bytes < attend_workspace_bytes(*K, *V, batch, n_kv, g, seq)) {
+    set_error("tq_attend: workspace too small");
+    return TQ_ERR_NO_MEMORY;
+  }
+  if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)kp->d);
+  return launch_attend(*K, *V, q, batch, n_kv, g, kcodes, vcodes, seq, scale, out,
+                       workspace, (hipStream_t)stream);
+}
+
+tq_status tq_release_cache(void) {
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  for (auto &kv : g_cache) free_derived(kv.second);
+  g_cache.clear();
+  return TQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal declarations shared by the host side (tq_host.cpp) and the device
+// side (tq_kernels.hip) of libtq.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxLevels = 16;  // 2^B with B <= 4
+constexpr int kMaxParts = 8;    // odd subsets of B <= 4 bit planes
+
+// Codebook in the form the kernels consume.  Passed by value as a kernel
+// argument.
+struct Codebook {
+  int32_t nbits;                // B
+  int32_t nparts;               // number of odd subsets of the B planes
+  float c[kMaxLevels];          // fp32 centroids, ascending
+  float t[kMaxLevels - 1];      // fp32 boundaries
+  uint32_t part_mask[kMaxParts];  // planes XORed into each part
+  double coef[kMaxParts];       // c[idx] = sum_S coef_S * prod_{k in S} (2 b_k - 1)
+};
+
+// Everything derived from one tq_params on one device.
+struct Derived {
+  tq_params p;
+  int device;
+  int B;  // Lloyd-Max bits
+  Codebook cb;
+  // device buffers
+  float *pi32 = nullptr;       // [d][d]   Pi, row-major (y = Pi x)
+  float *s32 = nullptr;        // [m][d]   S
+  uint16_t *pi_hi = nullptr;   // bf16 fragments of Pi for the encode GEMM
+  uint16_t *pi_lo = nullptr;
+  uint16_t *sp_hi = nullptr;   // bf16 fragments of S' = S Pi^T
+  uint16_t *sp_lo = nullptr;
+};
+
+// Returns the cache entry for (p, current device), building it on first use.
+tq_status get_derived(const tq_params *p, const Derived **out);
+
+void set_error(const char *fmt, ...);
+
+// Launchers (tq_kernels.hip).  Shapes are validated by the caller.
+tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n,
+                        tq_codes codes, hipStream_t stream);
+size_t score_workspace_bytes(const Derived &D, int64_t n_kv, int64_t g);
+tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g,
+                       tq_codes codes, int64_t seq, float *logits, void *ws,
+                       hipStream_t stream);
+size_t attend_workspace_bytes(const Derived &K, const Derived &V, int64_t batch,
+                              int64_t n_kv, int64_t g, int64_t seq);
+tq_status launch_attend(const Derived &K, const Derived &V, const float *q,
+                        int64_t batch, int64_t n_kv, int64_t g, tq_codes k,
+                        tq_codes v, int64_t seq, float scale, float *out,
+                        void *ws, hipStream_t stream);
+
+// Fragment geometry of the d = m = 128 encode kernel: a 128 x 128 matrix is
+// stored as [16-row tile nt][32-column block kt][lane][8] bf16 values; lane l
+// covers row 16 nt + l % 16 and lane group l / 16.
+constexpr int kFragElems = 128 * 128;
+
+}  // namespace tq

@@ -1,0 +1,201 @@
+"""Thin Python binding of libtq (include/tq.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels
+of libtq.so.  PyTorch supplies device memory and the current stream.  The
+binding raises if the library is missing or a call fails; there is no other
+code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+MODE_PROD = 0
+MODE_MSE = 1
+F32 = 0
+BF16 = 1
+
+_STATUS = {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNSUPPORTED",
+           3: "TQ_ERR_ALIGNMENT", 4: "TQ_ERR_HIP", 5: "TQ_ERR_NO_MEMORY"}
+
+
+class TQError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("b", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("seed_pi", ctypes.c_uint64), ("seed_s", ctypes.c_uint64)]
+
+
+class _Codes(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("sgn", ctypes.c_void_p),
+                ("knorm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p)]
+
+
+EXPORTS = ["tq_status_string", "tq_last_error", "tq_layout_version", "tq_make_codebook",
+           "tq_codes_bytes", "tq_export_matrices", "tq_encode", "tq_score_workspace_bytes",
+           "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_release_cache"]
+
+_lib = None
+
+
+def lib():
+    """Load libtq.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, C, vp, i64 = ctypes.POINTER(_Params), _Codes, ctypes.c_void_p, ctypes.c_int64
+        sz = ctypes.c_size_t
+        sig = {
+            "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "tq_last_error": (ctypes.c_char_p, []),
+            "tq_layout_version": (ctypes.c_int32, []),
+            "tq_make_codebook": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]),
+            "tq_codes_bytes": (ctypes.c_int, [P, i64, ctypes.POINTER(sz)]),
+            "tq_export_matrices": (ctypes.c_int, [P, vp, vp]),
+            "tq_encode": (ctypes.c_int, [P, vp, ctypes.c_int32, i64, C, vp]),
+            "tq_score_workspace_bytes": (ctypes.c_int, [P, i64, i64, ctypes.POINTER(sz)]),
+            "tq_score": (ctypes.c_int, [P, vp, i64, i64, C, i64, vp, vp, sz, vp]),
+            "tq_attend_workspace_bytes": (ctypes.c_int, [P, P, i64, i64, i64, i64, ctypes.POINTER(sz)]),
+            "tq_attend": (ctypes.c_int, [P, P, vp, i64, i64, i64, C, C, i64, ctypes.c_float, vp, vp, sz, vp]),
+            "tq_release_cache": (ctypes.c_int, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise TQError(fn, status, lib().tq_last_error().decode())
+
+
+@dataclass(frozen=True)
+class Params:
+    """The problem statement: d, total bits b, JL rows m, mode, seeds of Pi and S."""
+    d: int
+    b: int
+    m: int = 128
+    mode: int = MODE_PROD
+    seed_pi: int = 2
+    seed_s: int = 3
+
+    @property
+    def B(self) -> int:
+        return self.b - 1 if self.mode == MODE_PROD else self.b
+
+    @property
+    def prod(self) -> bool:
+        return self.mode == MODE_PROD
+
+    def c(self) -> _Params:
+        return _Params(self.d, self.b, self.m, self.mode, self.seed_pi, self.seed_s)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------- host calls
+def make_codebook(d: int, b: int, mode: int = MODE_PROD):
+    B = b - 1 if mode == MODE_PROD else b
+    c = np.zeros(max(1, 1 << B), dtype=np.float32)
+    t = np.zeros(max(1, (1 << B) - 1), dtype=np.float32)
+    _check("tq_make_codebook", lib().tq_make_codebook(d, b, mode, c.ctypes.data, t.ctypes.data))
+    return c[: (1 << B) if B else 0], t[: (1 << B) - 1 if B else 0]
+
+
+def codes_bytes(p: Params, n: int):
+    out = (ctypes.c_size_t * 4)()
+    _check("tq_codes_bytes", lib().tq_codes_bytes(ctypes.byref(p.c()), n, out))
+    return list(out)
+
+
+def export_matrices(p: Params):
+    pi = np.zeros((p.d, p.d), dtype=np.float32)
+    s = np.zeros((p.m, p.d), dtype=np.float32) if p.prod else None
+    _check("tq_export_matrices", lib().tq_export_matrices(
+        ctypes.byref(p.c()), pi.ctypes.data, None if s is None else s.ctypes.data))
+    return pi, s
+
+
+def score_workspace_bytes(p: Params, n_kv: int, g: int) -> int:
+    out = ctypes.c_size_t()
+    _check("tq_score_workspace_bytes", lib().tq_score_workspace_bytes(ctypes.byref(p.c()), n_kv, g, ctypes.byref(out)))
+    return out.value
+
+
+def attend_workspace_bytes(kp: Params, vp: Params, batch, n_kv, g, seq) -> int:
+    out = ctypes.c_size_t()
+    _check("tq_attend_workspace_bytes", lib().tq_attend_workspace_bytes(
+        ctypes.byref(kp.c()), ctypes.byref(vp.c()), batch, n_kv, g, seq, ctypes.byref(out)))
+    return out.value
+
+
+def release_cache():
+    _check("tq_release_cache", lib().tq_release_cache())
+
+
+# ----------------------------------------------------------------- device memory
+def alloc_codes(p: Params, n: int, device="cuda"):
+    """Caller-owned code arrays (torch tensors) for n vectors."""
+    import torch
+    B = p.B
+    return {
+        "idx": torch.empty((n, p.d // 32, B), dtype=torch.int32, device=device) if B else None,
+        "sgn": torch.empty((n, p.m // 32), dtype=torch.int32, device=device) if p.prod else None,
+        "knorm": torch.empty((n,), dtype=torch.float32, device=device),
+        "rnorm": torch.empty((n,), dtype=torch.float32, device=device) if p.prod else None,
+    }
+
+
+def _codes(c: dict) -> _Codes:
+    return _Codes(*(None if c.get(k) is None else c[k].data_ptr() for k in ("idx", "sgn", "knorm", "rnorm")))
+
+
+# ----------------------------------------------------------------- device calls
+def encode(p: Params, x, codes: dict, stream=None):
+    """x: cuda tensor [n, d] float32 or bfloat16, contiguous."""
+    import torch
+    assert x.is_contiguous() and x.dim() == 2 and x.shape[1] == p.d
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    _check("tq_encode", lib().tq_encode(ctypes.byref(p.c()), _ptr(x), dt, x.shape[0],
+                                        _codes(codes), _stream(stream)))
+
+
+def score(p: Params, q, codes: dict, n_kv: int, g: int, seq: int, logits, workspace, stream=None):
+    """q: [n_kv*g, d] float32; logits: [n_kv*g, seq] float32 (written)."""
+    assert q.is_contiguous() and logits.is_contiguous()
+    _check("tq_score", lib().tq_score(ctypes.byref(p.c()), _ptr(q), n_kv, g, _codes(codes), seq,
+                                      _ptr(logits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+
+
+def attend(kp: Params, vp: Params, q, batch, n_kv, g, kcodes, vcodes, seq, out, workspace,
+           scale: float = 0.0, stream=None):
+    """q: [batch, n_kv*g, d] float32; out: [batch, n_kv*g, d] float32 (written)."""
+    assert q.is_contiguous() and out.is_contiguous()
+    _check("tq_attend", lib().tq_attend(ctypes.byref(kp.c()), ctypes.byref(vp.c()), _ptr(q), batch, n_kv, g,
+                                        _codes(kcodes), _codes(vcodes), seq, scale, _ptr(out),
+                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))
