@@ -1,0 +1,204 @@
+"""Benchmark of the TurboQuant hot path on one MI355X.
+
+One step = the whole hot path on the Llama-3.1-8B-shaped decode layer:
+  tq_encode of all 8 KV heads x 32768 positions x d 128 bf16 keys (b = 3:
+  2-bit Lloyd-Max + 1-bit QJL, m = 128), then tq_score of one decode step
+  (32 query heads, grouped 4:1) from the packed codes.
+Inputs are resident in HBM before the timed region; the timed region is
+bracketed by torch.cuda.synchronize().
+
+Reported on one JSON line:
+  value        keys encoded + scored per second through the whole step (Mvectors/s)
+  encode_*     the encode kernel alone (HIP events around its launch)
+  score_*      the score launch alone on the same layer (codes 14.7 MB: they sit
+               in the 256 MB last-level cache) and, separately timed, the score
+               kernel streaming 32 such layers' codes (470 MB) from HBM
+  roofline     the dominant kernel (encode, a bf16 MFMA contraction)
+  roofline_score  the score kernel on the 32-layer stream (HBM-bound)
+  cpu_baseline the CPU oracle (numpy float64) on a bounded sample of the step
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+N_KV, SEQ, D, M, G = 8, 32768, 128, 128, 4
+LAYERS = 32
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--b", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-score", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=8)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for scaling PMC byte counters)")
+    return ap.parse_args()
+
+
+def cpu_baseline(b, heads):
+    """The oracle as it stands on `heads` KV heads of the same layer recipe."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from kv_cache_compression_04_amd import synth
+    from oracle import tq_oracle as o
+
+    p = o.Params(D, b, M, o.MODE_PROD, 2, 3)
+    _ = p.pi, p.s, p.codebook          # set-up outside the timed region
+    x = synth.llama_keys(heads=heads, seq=SEQ, seed=1).double().numpy()
+    q = synth.queries(heads * G, seed=5).double().numpy()
+    t0 = time.perf_counter()
+    codes = o.encode(x, p)
+    o.pack(codes, p)
+    o.score(q, codes, p, heads, G, SEQ)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    n = heads * SEQ
+    return {"value": round(n / dt / 1e6, 4), "unit": "Mvectors/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of {N_KV} KV heads x {SEQ} positions (encode + pack + score of "
+                      f"{heads * G} query heads), float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the hot path is per-GPU and needs no collectives)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from kv_cache_compression_04_amd import synth, tq
+
+    if args.copy_calibration:
+        # a plain copy: 512 MiB read + 512 MiB written per launch
+        nbytes = 512 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                          "launches": 5}), flush=True)
+        return
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    p = tq.Params(D, args.b, M, tq.MODE_PROD, 2, 3)
+    n = N_KV * SEQ
+    x = synth.llama_keys(heads=N_KV, seq=SEQ, seed=1, device=dev)
+    q = synth.queries(N_KV * G, seed=5, device=dev)
+    codes = tq.alloc_codes(p, n, dev)
+    logits = torch.empty((N_KV * G, SEQ), device=dev)
+    ws = torch.empty(tq.score_workspace_bytes(p, N_KV, G), dtype=torch.uint8, device=dev)
+    code_bytes = sum(tq.codes_bytes(p, 1))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tq.encode(p, x, codes)
+        if ev is not None:
+            ev[1].record(stream)
+        tq.score(p, q, codes, N_KV, G, SEQ, logits, ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    enc_flops = (2 * D * D + 2 * D * M) * n
+    enc_tflops = enc_flops / (enc_ms * 1e-3) / 1e12
+    score_bytes_layer = code_bytes * n + 4 * N_KV * G * SEQ
+    out = {
+        "metric": "tq_score packed-KV GB/s (% of HBM peak) + tq_encode Mvectors/s, d=128 b=3",
+        "value": round(n / (ms_step * 1e-3) / 1e6, 3),
+        "unit": "Mvectors/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 MFMA (hi/lo split, fp32 accumulate) + int8 MFMA (int32 accumulate)",
+        "data": "synthetic (seeded Llama-3.1-8B-shaped keys: N(0,1) x per-channel log-normal, 2% outlier channels x20)",
+        "config": {"workload": f"Llama-3.1-8B-shaped decode layer: {N_KV} KV heads x seq {SEQ} x d {D} bf16 keys, "
+                               f"{N_KV * G} query heads (GQA {G}:1), b={args.b}, m={M}; encode all keys + score one decode step",
+                   "b": args.b, "d": D, "m": M, "n_keys": n, "query_heads": N_KV * G},
+        "encode_ms": round(enc_ms, 5),
+        "encode_mvectors_per_s": round(n / (enc_ms * 1e-3) / 1e6, 2),
+        "score_ms_one_layer": round(sc_ms, 5),
+        "score_gbps_one_layer_cache_resident": round(score_bytes_layer / (sc_ms * 1e-3) / 1e9, 1),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "mfma", "achieved": round(enc_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(enc_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "encode128_kernel", "algorithmic_per_launch": f"{enc_flops} flop "
+                     "((2 d^2 + 2 d m) per key; the hi/lo split executes 5 bf16 passes of the two GEMMs)"},
+    }
+
+    if not args.no_hbm_score:
+        # 32 layers' codes of the same shape streamed by one launch (n_kv = 256)
+        nL = N_KV * LAYERS
+        big = tq.alloc_codes(p, nL * SEQ, dev)
+        for layer in range(LAYERS):
+            sl = slice(layer * n, (layer + 1) * n)
+            xl = synth.llama_keys(heads=N_KV, seq=SEQ, seed=100 + layer, device=dev)
+            tq.encode(p, xl, {k: (v[sl] if v is not None else None) for k, v in big.items()})
+        del xl
+        qb = synth.queries(nL * G, seed=6, device=dev)
+        lb = torch.empty((nL * G, SEQ), device=dev)
+        wsb = torch.empty(tq.score_workspace_bytes(p, nL, G), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            tq.score(p, qb, big, nL, G, SEQ, lb, wsb)
+        torch.cuda.synchronize()
+        reps = max(5, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            tq.score(p, qb, big, nL, G, SEQ, lb, wsb)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        bytes_ = code_bytes * nL * SEQ + 4 * nL * G * SEQ
+        gbps = bytes_ / (ms * 1e-3) / 1e9
+        out["score_hbm"] = {"workload": f"{LAYERS} layers x {N_KV} KV heads x {SEQ} positions, one launch",
+                            "ms": round(ms, 4), "GBps": round(gbps, 1),
+                            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                            "bytes_per_launch": bytes_}
+        out["roofline_score"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                                 "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                                 "kernel": "score128_kernel (+ qprep128_kernel)",
+                                 "algorithmic_per_launch": f"{bytes_} B ({code_bytes} B of codes per key + 4 B per logit)"}
+        del big, lb
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.b, args.cpu_sample_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

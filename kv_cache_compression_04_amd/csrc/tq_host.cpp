@@ -345,9 +345,11 @@ static tq_status build_derived(const tq_params *p, int dev, Derived *D) {
   std::vector<float> f(pi.begin(), pi.end());
   tq_status st = upload(&D->pi32, f);
   if (st) return st;
+  if ((st = upload(&D->pi64, pi))) return st;
   if (prod) {
     f.assign(s.begin(), s.end());
     if ((st = upload(&D->s32, f))) return st;
+    if ((st = upload(&D->s64, s))) return st;
   }
   if (p->d == 128 && (!prod || p->m == 128)) {
     std::vector<uint16_t> hi, lo;
@@ -379,6 +381,8 @@ static void free_derived(Derived *D) {
   (void)hipSetDevice(D->device);
   (void)hipFree(D->pi32);
   (void)hipFree(D->s32);
+  (void)hipFree(D->pi64);
+  (void)hipFree(D->s64);
   (void)hipFree(D->pi_hi);
   (void)hipFree(D->pi_lo);
   (void)hipFree(D->sp_hi);

@@ -33,6 +33,8 @@ struct Derived {
   // device buffers
   float *pi32 = nullptr;       // [d][d]   Pi, row-major (y = Pi x)
   float *s32 = nullptr;        // [m][d]   S
+  double *pi64 = nullptr;      // the same in float64 (query preparation)
+  double *s64 = nullptr;
   uint16_t *pi_hi = nullptr;   // bf16 fragments of Pi for the encode GEMM
   uint16_t *pi_lo = nullptr;
   uint16_t *sp_hi = nullptr;   // bf16 fragments of S' = S Pi^T

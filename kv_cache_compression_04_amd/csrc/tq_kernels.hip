@@ -53,14 +53,22 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// float -> bf16 bits, round to nearest even (finite inputs)
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// (a, b) -> packed hi = bf16(a) | bf16(b) << 16 and lo = bf16 of the remainders
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 h = {(__bf16)a, (__bf16)b};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const bf16x2 l = {(__bf16)(a - __uint_as_float(hb << 16)), (__bf16)(b - __uint_as_float(hb & 0xFFFF0000u))};
+  hi = hb;
+  lo = __builtin_bit_cast(uint32_t, l);
+}
 
 // ===========================================================================
 // Encode, d = m = 128
@@ -91,15 +99,13 @@ __device__ __forceinline__ void load_x_frag(const void *__restrict__ x, int64_t 
     float4 a = valid ? p[0] : make_float4(0, 0, 0, 0);
     float4 b = valid ? p[1] : make_float4(0, 0, 0, 0);
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t h[8], l[8];
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sumsq += v[i] * v[i];
-      h[i] = bf16_rne(v[i]);
-      l[i] = bf16_rne(v[i] - bf16_to_f32(h[i]));
-    }
-    hi = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
-    lo = make_uint4(l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16);
+    for (int i = 0; i < 8; ++i) sumsq += v[i] * v[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
   }
 }
 
@@ -220,13 +226,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
           // element e of the GEMM-2 operand for block kt2 is coordinate
           // 32 kt2 + 16 (e / 4) + 4 g + e % 4, i.e. e = 4 h + i
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t h0 = bf16_rne(rho[2 * hh]), h1 = bf16_rne(rho[2 * hh + 1]);
-            const uint32_t l0 = bf16_rne(rho[2 * hh] - bf16_to_f32(h0));
-            const uint32_t l1 = bf16_rne(rho[2 * hh + 1] - bf16_to_f32(h1));
-            rh[ct][2 * h + hh] = h0 | h1 << 16;
-            rl[ct][2 * h + hh] = l0 | l1 << 16;
-          }
+          for (int hh = 0; hh < 2; ++hh) split2(rho[2 * hh], rho[2 * hh + 1], rh[ct][2 * h + hh], rl[ct][2 * h + hh]);
         }
       }
       if (PROD) {
@@ -345,24 +345,86 @@ __host__ __device__ constexpr int score_mfmas(int nparts, bool prod) {
   return 2 * nparts + (prod ? 2 : 0);
 }
 
-struct QConst {  // per query
-  float idx_scale;  // 2^-E of the index part
-  float idx_bias;   // sum_S coef_S * sum_c qt_c
-  float sgn_scale;  // sqrt(pi/2)/m * 2^-E'
-  float sgn_bias;   // sqrt(pi/2)/m * sum_r qs_r
+struct QConst {  // per query, float64 so that logits keep ~1e-8 relative accuracy
+  double idx_scale;  // 2^-E of the index part
+  double idx_bias;   // sum_S coef_S * sum_c qt_c
+  double sgn_scale;  // sqrt(pi/2)/m * 2^-E'
+  double sgn_bias;   // sqrt(pi/2)/m * sum_r qs_r
 };
 
-// one workgroup per (KV head, query group)
+// The 8 bit slices of a packed word as int8 MFMA operands: slice s keeps bit s
+// of every byte.  Words are pre-shifted by s & ~1, so a set bit weighs
+// 2^(s & 1) (1 or 2) and the query side loses at most one bit to the weight.
+__device__ __forceinline__ void bit_slices(uint32_t w, i32x4 &lo4, i32x4 &hi4) {
+  const uint32_t w2 = w >> 2, w4 = w >> 4, w6 = w >> 6;
+  lo4 = i32x4{(int)(w & 0x01010101u), (int)(w & 0x02020202u), (int)(w2 & 0x01010101u),
+              (int)(w2 & 0x02020202u)};
+  hi4 = i32x4{(int)(w4 & 0x01010101u), (int)(w4 & 0x02020202u), (int)(w6 & 0x01010101u),
+              (int)(w6 & 0x02020202u)};
+}
+
+// Logit of (query kg, key kc) for one 16-key tile: lane (kc, kg) of a wave,
+// planes = the key's index words of lane group kg, sw = its sign word.
+template <int B, bool PROD, int NP>
+__device__ __forceinline__ double tile_logit(const i32x4 *A, const uint32_t *planes, uint32_t sw,
+                                             float kn, float rn, const QConst &cst,
+                                             const Codebook &cb) {
+  i32x4 ai = {0, 0, 0, 0}, as = {0, 0, 0, 0};
+#pragma unroll
+  for (int sp = 0; sp < NP; ++sp) {
+    uint32_t part = 0;
+#pragma unroll
+    for (int p = 0; p < B; ++p)
+      if (cb.part_mask[sp] >> p & 1) part ^= planes[p];
+    i32x4 lo4, hi4;
+    bit_slices(part, lo4, hi4);
+    ai = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * sp], lo4, ai, 0, 0, 0);
+    ai = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * sp + 1], hi4, ai, 0, 0, 0);
+  }
+  if (PROD) {
+    i32x4 lo4, hi4;
+    bit_slices(sw, lo4, hi4);
+    as = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NP], lo4, as, 0, 0, 0);
+    as = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NP + 1], hi4, as, 0, 0, 0);
+  }
+  // rows 4 kg + t of column kc: limb t of query kg; combine exactly in float64
+  double l = 0.0;
+  if (NP > 0) {
+    const double vi = (double)ai[0] + 128.0 * (double)ai[1] + 16384.0 * (double)ai[2] +
+                      2097152.0 * (double)ai[3];
+    l += (double)kn * (vi * cst.idx_scale - cst.idx_bias);
+  }
+  if (PROD) {
+    const double vs = (double)as[0] + 128.0 * (double)as[1] + 16384.0 * (double)as[2] +
+                      2097152.0 * (double)as[3];
+    l += (double)rn * (vs * cst.sgn_scale - cst.sgn_bias);
+  }
+  return l;
+}
+
+// Balanced base-128 digit t (t = 0..3) of an integer |Q| < 2^26.
+__device__ __forceinline__ int limb_of(int Q, int t) {
+  int digit = 0;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    if (tt > t) break;
+    digit = ((Q + 64) & 127) - 64;
+    Q = (Q - digit) >> 7;  // exact: Q - digit is a multiple of 128
+  }
+  return digit;
+}
+
+// Query preparation for one (KV head, group of 4 queries): qt = Pi q and
+// qs = S q in float32, then the int8 operands of the score MFMAs.
+// One workgroup of 256 threads per group.
 template <bool PROD>
 __global__ __launch_bounds__(256) void qprep128_kernel(const float *__restrict__ q, int64_t g,
-                                                       int ngroups, const float *__restrict__ pi,
-                                                       const float *__restrict__ s, Codebook cb,
+                                                       int ngroups, const double *__restrict__ pi,
+                                                       const double *__restrict__ s, Codebook cb,
                                                        int m, i32x4 *__restrict__ aops,
                                                        QConst *__restrict__ qc) {
-  __shared__ float qin[4][128];
-  __shared__ float qt[4][128];
-  __shared__ float qs[4][128];
-  __shared__ double red[4][4];
+  __shared__ double qin[4][128];
+  __shared__ double qv[2][4][128];  // [0] = Pi q, [1] = S q
   __shared__ int expo[4][2];
   const int hg = blockIdx.x;
   const int h = hg / ngroups, grp = hg % ngroups;
@@ -370,50 +432,71 @@ __global__ __launch_bounds__(256) void qprep128_kernel(const float *__restrict__
   for (int i = tid; i < 512; i += 256) {
     const int jq = i >> 7, c = i & 127;
     const int64_t qh = (int64_t)grp * 4 + jq;
-    qin[jq][c] = qh < g ? q[((int64_t)h * g + qh) * 128 + c] : 0.f;
+    qin[jq][c] = qh < g ? (double)q[((int64_t)h * g + qh) * 128 + c] : 0.0;
   }
   __syncthreads();
-  for (int i = tid; i < 512; i += 256) {
-    const int jq = i >> 7, c = i & 127;
-    float a = 0.f, b = 0.f;
-    for (int j = 0; j < 128; ++j) {
-      a = fmaf(pi[c * 128 + j], qin[jq][j], a);
-      if (PROD) b = fmaf(s[c * 128 + j], qin[jq][j], b);
+  {
+    // thread -> one row of Pi (tid < 128) or of S (tid >= 128), all 4 queries
+    const int which = tid >> 7, r = tid & 127;
+    if (which == 0 || PROD) {
+      const double2 *row = reinterpret_cast<const double2 *>((which ? s : pi) + r * 128);
+      double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+#pragma unroll 16
+      for (int j2 = 0; j2 < 64; ++j2) {
+        const double2 w = row[j2];
+        const double wv[2] = {w.x, w.y};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = 2 * j2 + e;
+          a0 = fma(wv[e], qin[0][j], a0);
+          a1 = fma(wv[e], qin[1][j], a1);
+          a2 = fma(wv[e], qin[2][j], a2);
+          a3 = fma(wv[e], qin[3][j], a3);
+        }
+      }
+      qv[which][0][r] = a0;
+      qv[which][1][r] = a1;
+      qv[which][2][r] = a2;
+      qv[which][3][r] = a3;
     }
-    qt[jq][c] = a;
-    qs[jq][c] = b;
   }
   __syncthreads();
   const int NP = cb.nparts;
-  if (tid < 4) {
-    const int jq = tid;
-    double mq = 0, ms = 0, sq = 0, ssum = 0, acoef = 0, amax = 0;
-    for (int c = 0; c < 128; ++c) {
-      mq = fmax(mq, fabs((double)qt[jq][c]));
-      ms = fmax(ms, fabs((double)qs[jq][c]));
-      sq += qt[jq][c];
-      ssum += qs[jq][c];
+  {
+    // wave w reduces query w: max |qt|, max |qs|, sum qt, sum qs
+    const int jq = tid >> 6, lane = tid & 63;
+    double mq = fmax(fabs(qv[0][jq][lane]), fabs(qv[0][jq][lane + 64]));
+    double ms = PROD ? fmax(fabs(qv[1][jq][lane]), fabs(qv[1][jq][lane + 64])) : 0.0;
+    double sq = qv[0][jq][lane] + qv[0][jq][lane + 64];
+    double ss = PROD ? qv[1][jq][lane] + qv[1][jq][lane + 64] : 0.0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mq = fmax(mq, __shfl_xor(mq, off));
+      ms = fmax(ms, __shfl_xor(ms, off));
+      sq += __shfl_xor(sq, off);
+      ss += __shfl_xor(ss, off);
     }
-    for (int p = 0; p < NP; ++p) {
-      acoef += cb.coef[p];
-      amax = fmax(amax, fabs(cb.coef[p]));
+    if (lane == 0) {
+      double acoef = 0, amax = 0;
+      for (int p = 0; p < NP; ++p) {
+        acoef += cb.coef[p];
+        amax = fmax(amax, fabs(cb.coef[p]));
+      }
+      // scale the largest operand magnitude below 2^26
+      int e1 = 0, e2 = 0, k;
+      const double A1 = 2.0 * amax * mq, A2 = 2.0 * ms;
+      if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
+      if (A2 > 0) { frexp(A2, &k); e2 = 26 - k; }
+      expo[jq][0] = e1;
+      expo[jq][1] = e2;
+      const double cq = sqrt(M_PI / 2.0) / m;
+      QConst o;
+      o.idx_scale = ldexp(1.0, -e1);
+      o.idx_bias = acoef * sq;
+      o.sgn_scale = cq * ldexp(1.0, -e2);
+      o.sgn_bias = cq * ss;
+      qc[(int64_t)hg * 4 + jq] = o;
     }
-    // largest operand magnitude below 2^26 after scaling by 2^E
-    int e1 = 0, e2 = 0;
-    const double A1 = 2.0 * amax * mq, A2 = 2.0 * ms;
-    int k;
-    if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
-    if (A2 > 0) { frexp(A2, &k); e2 = 26 - k; }
-    expo[jq][0] = e1;
-    expo[jq][1] = e2;
-    const double cq = sqrt(M_PI / 2.0) / m;
-    QConst o;
-    o.idx_scale = (float)ldexp(1.0, -e1);
-    o.idx_bias = (float)(acoef * sq);
-    o.sgn_scale = (float)(cq * ldexp(1.0, -e2));
-    o.sgn_bias = (float)(cq * ssum);
-    qc[(int64_t)hg * 4 + jq] = o;
-    (void)red;
   }
   __syncthreads();
   const int NMF = score_mfmas(NP, PROD);
@@ -425,28 +508,25 @@ __global__ __launch_bounds__(256) void qprep128_kernel(const float *__restrict__
     const int h2 = j & 1;
     const double coef = sgnpart ? 2.0 : 2.0 * cb.coef[j >> 1];
     const int E = expo[jq][sgnpart ? 1 : 0];
+    const double *src = qv[sgnpart ? 1 : 0][jq];
     int out[4];
+#pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t packed = 0;
       const int sl = 4 * h2 + w;
+#pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = 32 * e + 16 * (sl >> 2) + 4 * kg + (sl & 3);
-        const double v = coef * (double)(sgnpart ? qs[jq][c] : qt[jq][c]);
-        long long Q = llrint(ldexp(v, E - sl));
-        if (sl == 7) Q = -Q;
-        // balanced base-128 digits, limb t
-        long long digit = 0;
-        for (int tt = 0; tt <= t; ++tt) {
-          digit = ((Q + 64) & 127) - 64;
-          Q = (Q - digit) / 128;
-        }
-        packed |= (uint32_t)(uint8_t)(int8_t)digit << (8 * e);
+        const int Q = (int)llrint(ldexp(coef * src[c], E - (sl & 1)));
+        packed |= (uint32_t)(uint8_t)(int8_t)limb_of(Q, t) << (8 * e);
       }
       out[w] = (int)packed;
     }
     aops[((int64_t)hg * NMF + j) * 64 + l] = i32x4{out[0], out[1], out[2], out[3]};
   }
 }
+
+constexpr int kScoreU = 4;  // tiles whose loads are issued together
 
 template <int B, bool PROD>
 __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
@@ -456,6 +536,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
     int ngroups, int tiles_per_wave, Codebook cb, float *__restrict__ logits) {
   constexpr int NP = B == 0 ? 0 : (B == 1 ? 1 : B == 2 ? 2 : B == 3 ? 4 : 8);
   constexpr int NMF = score_mfmas(NP, PROD);
+  constexpr int BB = B > 0 ? B : 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hg = blockIdx.y;
   const int h = hg / ngroups, grp = hg % ngroups;
@@ -467,59 +548,46 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
   const int64_t qh = (int64_t)grp * 4 + kg;  // this lane's output query within the head
   const bool qvalid = qh < g;
   float *out = logits + ((int64_t)h * g + qh) * seq;
+  const uint32_t *idx_h = idx + (int64_t)h * seq * 4 * BB;
+  const uint32_t *sgn_h = sgn + (int64_t)h * seq * 4;
+  const float *kn_h = knorm + (int64_t)h * seq;
+  const float *rn_h = rnorm + (int64_t)h * seq;
 
   const int64_t tiles = (seq + 15) / 16;
   const int64_t t0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
   const int64_t t1 = t0 + tiles_per_wave < tiles ? t0 + tiles_per_wave : tiles;
-  for (int64_t tile = t0; tile < t1; ++tile) {
-    const int64_t pos = tile * 16 + kc;
-    const bool valid = pos < seq;
-    const int64_t vid = (int64_t)h * seq + (valid ? pos : 0);
-    uint32_t pl[B > 0 ? B : 1];
+  for (int64_t tb = t0; tb < t1; tb += kScoreU) {
+    // loads are unconditional (positions clamped into the sequence) so the
+    // compiler can issue them back to back; out-of-range results are not stored
+    uint32_t pl[kScoreU][BB], sw[kScoreU];
+    float kn[kScoreU], rn[kScoreU];
+    bool valid[kScoreU];
 #pragma unroll
-    for (int p = 0; p < B; ++p) pl[p] = valid ? idx[(vid * 4 + kg) * B + p] : 0u;
-    const uint32_t sw = PROD && valid ? sgn[vid * 4 + kg] : 0u;
-    const float kn = valid ? knorm[vid] : 0.f;
-    const float rn = PROD && valid ? rnorm[vid] : 0.f;
-    i32x4 ai = {0, 0, 0, 0}, as = {0, 0, 0, 0};
-#pragma unroll
-    for (int sp = 0; sp < NP; ++sp) {
-      uint32_t part = 0;
-#pragma unroll
-      for (int p = 0; p < B; ++p)
-        if (cb.part_mask[sp] >> p & 1) part ^= pl[p];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const i32x4 bw = {(int)(part & (0x01010101u << (4 * h2 + 0))),
-                          (int)(part & (0x01010101u << (4 * h2 + 1))),
-                          (int)(part & (0x01010101u << (4 * h2 + 2))),
-                          (int)(part & (0x01010101u << (4 * h2 + 3)))};
-        ai = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * sp + h2], bw, ai, 0, 0, 0);
+    for (int u = 0; u < kScoreU; ++u) {
+      const int64_t pos = (tb + u) * 16 + kc;
+      valid[u] = (tb + u) < t1 && pos < seq;
+      const uint32_t vp = (uint32_t)(pos < seq ? pos : seq - 1);
+      const uint32_t *ip = idx_h + (vp * 4u + kg) * BB;
+      if constexpr (B == 1) {
+        pl[u][0] = ip[0];
+      } else if constexpr (B == 2) {
+        const uint2 t = *reinterpret_cast<const uint2 *>(ip);
+        pl[u][0] = t.x; pl[u][1] = t.y;
+      } else if constexpr (B == 3) {
+        pl[u][0] = ip[0]; pl[u][1] = ip[1]; pl[u][2] = ip[2];
+      } else if constexpr (B == 4) {
+        const uint4 t = *reinterpret_cast<const uint4 *>(ip);
+        pl[u][0] = t.x; pl[u][1] = t.y; pl[u][2] = t.z; pl[u][3] = t.w;
       }
+      sw[u] = PROD ? sgn_h[vp * 4u + kg] : 0u;
+      kn[u] = kn_h[vp];
+      rn[u] = PROD ? rn_h[vp] : 0.f;
     }
-    if (PROD) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const i32x4 bw = {(int)(sw & (0x01010101u << (4 * h2 + 0))),
-                          (int)(sw & (0x01010101u << (4 * h2 + 1))),
-                          (int)(sw & (0x01010101u << (4 * h2 + 2))),
-                          (int)(sw & (0x01010101u << (4 * h2 + 3)))};
-        as = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NP + h2], bw, as, 0, 0, 0);
-      }
+    for (int u = 0; u < kScoreU; ++u) {
+      const double l = tile_logit<B, PROD, NP>(A, pl[u], sw[u], kn[u], rn[u], cst, cb);
+      if (valid[u] && qvalid) out[(tb + u) * 16 + kc] = (float)l;
     }
-    // lane (kc, kg) holds rows 4 kg + t (query kg, limb t) of column kc (this key)
-    float li = 0.f, ls = 0.f;
-    if (NP > 0) {
-      const float vi = (float)ai[0] + 128.f * (float)ai[1] + 16384.f * (float)ai[2] +
-                       2097152.f * (float)ai[3];
-      li = kn * (vi * cst.idx_scale - cst.idx_bias);
-    }
-    if (PROD) {
-      const float vs = (float)as[0] + 128.f * (float)as[1] + 16384.f * (float)as[2] +
-                       2097152.f * (float)as[3];
-      ls = rn * (vs * cst.sgn_scale - cst.sgn_bias);
-    }
-    if (valid && qvalid) out[pos] = li + ls;
   }
 }
 
@@ -539,9 +607,13 @@ static void launch_score_t(const Derived &D, const float *q, int64_t n_kv, int64
   i32x4 *aops = (i32x4 *)ws;
   QConst *qc = (QConst *)((char *)ws + (size_t)n_kv * ngroups * NMF * 64 * sizeof(i32x4));
   qprep128_kernel<PROD><<<dim3((unsigned)(n_kv * ngroups)), dim3(256), 0, s>>>(
-      q, g, ngroups, D.pi32, D.s32, D.cb, D.p.m, aops, qc);
+      q, g, ngroups, D.pi64, D.s64, D.cb, D.p.m, aops, qc);
+  // tiles per wave: a multiple of the prefetch depth, aiming at >= 8 waves per SIMD
   const int64_t tiles = (seq + 15) / 16;
-  const int tpw = 8;
+  const int64_t total = tiles * n_kv * ngroups;
+  const int64_t want_waves = 8LL * 4 * num_cus(D.device);
+  int tpw = (int)std::min<int64_t>(32, std::max<int64_t>(kScoreU, total / std::max<int64_t>(1, want_waves)));
+  tpw = (tpw + kScoreU - 1) / kScoreU * kScoreU;
   const int64_t chunks = (tiles + (int64_t)tpw * kScoreWaves - 1) / ((int64_t)tpw * kScoreWaves);
   score128_kernel<B, PROD><<<dim3((unsigned)chunks, (unsigned)(n_kv * ngroups)),
                              dim3(kScoreWaves * 64), 0, s>>>(aops, qc, c.idx, c.sgn, c.knorm,
@@ -575,21 +647,325 @@ tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g
 }
 
 // ===========================================================================
-// Attend (not yet built on the device)
+// Attend, d = m = 128: flash-decoding split over the sequence
 // ===========================================================================
+// Each wave owns kAttKPW consecutive positions of one (batch, KV head, query
+// group) and produces, per query, the running max m, the sum l of
+// exp(logit - m) and the un-normalised rotated-domain output
+//   o_rot[c] = sum_n exp(logit_n - m) ||v_n|| c_V[idx_n][c].
+// Phase 1 computes the logits of its positions with the score MFMAs and keeps
+// them in LDS.  Phase 2 turns them into weights w = exp(scale*logit - m) * ||v||
+// and quantises them to four balanced int8 limbs with one power-of-two scale
+// per query.  Phase 3 is the weighted sum over positions as int8 MFMAs: the
+// value codebook is expanded like the key's (odd subsets of bit planes), the
+// K dimension of the MFMA runs over positions, and the B operand for
+// coordinate c is bit c of 4 consecutive positions per dword, obtained with a
+// byte transpose (v_perm) of their index words followed by one AND per slice.
+// A merge kernel combines the splits and applies Pi_V^T once per query head.
+constexpr int kAttKPW = 512;   // positions per wave
+constexpr int kAttWaves = 4;
+
+struct AttPartial {  // per (group, split, query): m, l, o_rot[128]
+  float m, l, o[128];
+};
+
+template <int BK, int BV>
+__global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
+    const i32x4 *__restrict__ aops, const QConst *__restrict__ qc,
+    const uint32_t *__restrict__ kidx, const uint32_t *__restrict__ ksgn,
+    const float *__restrict__ knorm, const float *__restrict__ rnorm,
+    const uint32_t *__restrict__ vidx, const float *__restrict__ vnorm, int64_t seq, int64_t g,
+    int ngroups, int nsplit, float scale, Codebook kcb, Codebook vcb,
+    AttPartial *__restrict__ part) {
+  constexpr int NPK = BK == 0 ? 0 : (BK == 1 ? 1 : BK == 2 ? 2 : BK == 3 ? 4 : 8);
+  constexpr int NPV = BV == 1 ? 1 : BV == 2 ? 2 : BV == 3 ? 4 : 8;
+  constexpr int NMF = score_mfmas(NPK, true);
+  constexpr int BKK = BK > 0 ? BK : 1;
+  __shared__ float lg[kAttWaves][4][kAttKPW];              // logits, then weights
+  __shared__ uint32_t limbs[kAttWaves][4][4][kAttKPW / 4];   // [query][limb][positions / 4]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hg = blockIdx.y;  // (batch * n_kv + head) * ngroups + group
+  const int hb = hg / ngroups;
+  const int split = blockIdx.x * kAttWaves + wave;
+  const int c16 = lane & 15, kg = lane >> 4;
+  const int64_t p0 = (int64_t)split * kAttKPW;
+  if (split >= nsplit) return;  // whole wave leaves together; no block barrier below
+  const int npos = (int)(seq - p0 < kAttKPW ? seq - p0 : kAttKPW);
+
+  // ---------------- phase 1: logits of this wave's positions
+  {
+    i32x4 A[NMF];
+#pragma unroll
+    for (int j = 0; j < NMF; ++j) A[j] = aops[((int64_t)hg * NMF + j) * 64 + lane];
+    const QConst cst = qc[(int64_t)hg * 4 + kg];
+    const uint32_t *ki = kidx + ((int64_t)hb * seq) * 4 * BKK;
+    const uint32_t *ks = ksgn + (int64_t)hb * seq * 4;
+    const float *kn = knorm + (int64_t)hb * seq;
+    const float *rn = rnorm + (int64_t)hb * seq;
+    float mx = -INFINITY;
+#pragma unroll 2
+    for (int t = 0; t < kAttKPW / 16; ++t) {
+      const int pl = t * 16 + c16;
+      const bool valid = pl < npos;
+      const uint32_t vp = (uint32_t)(p0 + (valid ? pl : 0));
+      uint32_t planes[BKK];
+#pragma unroll
+      for (int p = 0; p < BK; ++p) planes[p] = ki[(vp * 4u + kg) * BKK + p];
+      const uint32_t sw = ks[vp * 4u + kg];
+      const float kv = kn[vp], rv = rn[vp];
+      const double lt = tile_logit<BK, true, NPK>(A, planes, sw, kv, rv, cst, kcb);
+      const float logit = valid ? (float)(lt * (double)scale) : -INFINITY;
+      lg[wave][kg][pl] = logit;
+      mx = fmaxf(mx, logit);
+    }
+    // max over the 16 lanes of this query (one DPP row)
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    // lanes 16 kg .. 16 kg + 15 now agree on query kg's max.  The weights below
+    // are read by other lanes of this wave: order the LDS accesses.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // ---------------- phase 2: weights, quantised to int8 limbs
+    // lane (c16, kg) handles query kg, positions 4 c16 + 64 r + {0..3}
+    const float m = mx;
+    const float *vn = vnorm + (int64_t)hb * seq;
+    float lsum = 0.f, wmax = 0.f;
+    float wv[kAttKPW / 64][4];
+#pragma unroll
+    for (int r = 0; r < kAttKPW / 64; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pl = 64 * r + 4 * c16 + e;
+        const float lgt = lg[wave][kg][pl];
+        const float pexp = pl < npos ? __expf(lgt - m) : 0.f;
+        lsum += pexp;
+        const float w = pexp * vn[(uint32_t)(p0 + (pl < npos ? pl : 0))];
+        wv[r][e] = w;
+        wmax = fmaxf(wmax, w);
+      }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      lsum += __shfl_xor(lsum, off);
+      wmax = fmaxf(wmax, __shfl_xor(wmax, off));
+    }
+    int E = 0, k;
+    if (wmax > 0.f) { frexpf(wmax, &k); E = 26 - k; }
+    double qsum = 0.0;  // exact: integers below 2^53
+#pragma unroll
+    for (int r = 0; r < kAttKPW / 64; ++r) {
+      uint32_t lw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int Q = (int)rintf(ldexpf(wv[r][e], E));
+        qsum += (double)Q;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) lw[t] |= (uint32_t)(uint8_t)(int8_t)limb_of(Q, t) << (8 * e);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) limbs[wave][kg][t][16 * r + c16] = lw[t];
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) qsum += __shfl_xor(qsum, off);
+    // per-query scalars for the epilogue (the logits are no longer needed)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (c16 == 0) {
+      lg[wave][kg][0] = m;
+      lg[wave][kg][1] = lsum;
+      lg[wave][kg][2] = (float)(qsum * (double)ldexpf(1.0f, -E));  // sum of the quantised weights
+      lg[wave][kg][3] = __int_as_float(E);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+
+  // ---------------- phase 3: o_rot = sum_n w_n c_V[idx_n] as int8 MFMAs
+  // B lane (c16 = (w, beta), kg) covers positions 16 kg + 4 gi + e of each
+  // 64-position block: dword gi byte e of D_beta is byte beta of dword w of
+  // position 4 gi + e.  Slice s (bit s of every byte) is coordinate
+  // 32 beta + 16 (s / 4) + 4 w + s % 4.
+  const int w = c16 >> 2, beta = c16 & 3;
+  i32x4 acc[NPV][8];
+#pragma unroll
+  for (int sp = 0; sp < NPV; ++sp)
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) acc[sp][sl] = i32x4{0, 0, 0, 0};
+  const uint32_t *vi = vidx + (int64_t)hb * seq * 4 * BV;
+  // v_perm selectors picking byte beta of each source dword: perm(a, b, sel)
+  // selects from bytes {b0..b3 = b, b4..b7 = a}
+  const uint32_t sel_lo = (uint32_t)(beta | (beta + 4) << 8 | 0x0C0C0000u);  // [b.byte beta, a.byte beta, 0, 0]
+  for (int blk = 0; blk < kAttKPW / 64; ++blk) {
+    const i32x4 Aw = *reinterpret_cast<const i32x4 *>(
+        reinterpret_cast<const uint8_t *>(&limbs[wave][0][0][0]) +
+        ((size_t)((c16 >> 2) * 4 + (c16 & 3)) * (kAttKPW / 4) * 4) + blk * 64 + 16 * kg);
+    uint32_t D[NPV][4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      uint32_t x[4][BV];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pl = blk * 64 + 16 * kg + 4 * gi + e;
+        const uint32_t vp = (uint32_t)(p0 + (pl < npos ? pl : 0));
+        const uint32_t *src = vi + (vp * 4u + w) * BV;
+        if constexpr (BV == 2) {
+          const uint2 t2 = *reinterpret_cast<const uint2 *>(src);
+          x[e][0] = t2.x; x[e][1] = t2.y;
+        } else if constexpr (BV == 4) {
+          const uint4 t4 = *reinterpret_cast<const uint4 *>(src);
+          x[e][0] = t4.x; x[e][1] = t4.y; x[e][2] = t4.z; x[e][3] = t4.w;
+        } else {
+#pragma unroll
+          for (int p = 0; p < BV; ++p) x[e][p] = src[p];
+        }
+      }
+      uint32_t pd[BV];
+#pragma unroll
+      for (int p = 0; p < BV; ++p) {
+        const uint32_t lo = __builtin_amdgcn_perm(x[1][p], x[0][p], sel_lo);
+        const uint32_t hi = __builtin_amdgcn_perm(x[3][p], x[2][p], sel_lo);
+        pd[p] = lo | hi << 16;
+      }
+#pragma unroll
+      for (int sp = 0; sp < NPV; ++sp) {
+        uint32_t pt = 0;
+#pragma unroll
+        for (int p = 0; p < BV; ++p)
+          if (vcb.part_mask[sp] >> p & 1) pt ^= pd[p];
+        D[sp][gi] = pt;
+      }
+    }
+#pragma unroll
+    for (int sp = 0; sp < NPV; ++sp)
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const uint32_t mk = 0x01010101u << sl;
+        const i32x4 bw = {(int)(D[sp][0] & mk), (int)(D[sp][1] & mk), (int)(D[sp][2] & mk), (int)(D[sp][3] & mk)};
+        acc[sp][sl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aw, bw, acc[sp][sl], 0, 0, 0);
+      }
+  }
+
+  // ---------------- epilogue: lane (c16, kg) holds query kg, limbs t = 0..3 of
+  // the 8 coordinates 32 beta + 16 (s / 4) + 4 w + s % 4
+  const float m = lg[wave][kg][0];
+  const float lsum = lg[wave][kg][1];
+  const float wsum = lg[wave][kg][2];
+  const int E = __float_as_int(lg[wave][kg][3]);
+  const int64_t qh = (int64_t)(hg % ngroups) * 4 + kg;
+  double csum = 0.0;
+#pragma unroll
+  for (int sp = 0; sp < NPV; ++sp) csum += vcb.coef[sp];
+  AttPartial *dst = part + ((int64_t)hg * nsplit + split) * 4 + kg;
+  if (qh < g) {
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const float sc = ldexpf(sl == 7 ? -2.0f : 2.0f, -E - sl);  // 2 * 2^-E * weight of slice
+      float o = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < NPV; ++sp) {
+        const i32x4 a = acc[sp][sl];
+        const float v = (float)a[0] + 128.f * (float)a[1] + 16384.f * (float)a[2] + 2097152.f * (float)a[3];
+        o += (float)vcb.coef[sp] * v;
+      }
+      const int c = 32 * beta + 16 * (sl >> 2) + 4 * w + (sl & 3);
+      dst->o[c] = o * sc - (float)(csum * (double)wsum);
+    }
+    if (c16 == 0) {
+      dst->m = m;
+      dst->l = lsum;
+    }
+  }
+}
+
+// Combine the splits of one query head and rotate back: out = Pi_V^T o_rot / L.
+__global__ __launch_bounds__(128) void attend_merge_kernel(const AttPartial *__restrict__ part,
+                                                           int nsplit, int ngroups, int64_t g,
+                                                           const float *__restrict__ piv,
+                                                           float *__restrict__ out) {
+  __shared__ float orot[128];
+  const int hq = blockIdx.x;        // (batch * n_kv + head) * g + j
+  const int64_t hb = hq / g, j = hq % g;
+  const int64_t hg = hb * ngroups + j / 4;
+  const int jq = (int)(j % 4);
+  const int tid = threadIdx.x;
+  const AttPartial *p = part + (int64_t)hg * nsplit * 4 + jq;
+  float M = -INFINITY;
+  for (int sidx = 0; sidx < nsplit; ++sidx) M = fmaxf(M, p[(int64_t)sidx * 4].m);
+  float L = 0.f;
+  for (int sidx = 0; sidx < nsplit; ++sidx) L += p[(int64_t)sidx * 4].l * __expf(p[(int64_t)sidx * 4].m - M);
+  float acc = 0.f;
+  for (int sidx = 0; sidx < nsplit; ++sidx) {
+    const float wgt = __expf(p[(int64_t)sidx * 4].m - M);
+    acc += wgt * p[(int64_t)sidx * 4].o[tid];
+  }
+  orot[tid] = acc / L;
+  __syncthreads();
+  float o = 0.f;
+  for (int c = 0; c < 128; ++c) o = fmaf(piv[c * 128 + tid], orot[c], o);
+  out[(int64_t)hq * 128 + tid] = o;
+}
+
+static int nparts_of_(int B) { return B == 0 ? 0 : (B == 1 ? 1 : B == 2 ? 2 : B == 3 ? 4 : 8); }
+
 size_t attend_workspace_bytes(const Derived &K, const Derived &V, int64_t batch, int64_t n_kv,
                               int64_t g, int64_t seq) {
-  (void)K; (void)V; (void)batch; (void)n_kv; (void)g; (void)seq;
-  return 16;
+  (void)V;
+  const int64_t ngroups = (g + 3) / 4;
+  const int64_t nhg = batch * n_kv * ngroups;
+  const int64_t nsplit = (seq + kAttKPW - 1) / kAttKPW;
+  const int NMF = score_mfmas(nparts_of_(K.B), true);
+  return (size_t)nhg * ((size_t)NMF * 64 * sizeof(i32x4) + 4 * sizeof(QConst)) +
+         (size_t)nhg * nsplit * 4 * sizeof(AttPartial) + 256;
+}
+
+template <int BK, int BV>
+static void launch_attend_t(const Derived &K, const Derived &V, const float *q, int64_t batch,
+                            int64_t n_kv, int64_t g, tq_codes k, tq_codes v, int64_t seq,
+                            float scale, float *out, void *ws, hipStream_t s) {
+  const int ngroups = (int)((g + 3) / 4);
+  const int64_t nhg = batch * n_kv * ngroups;
+  const int nsplit = (int)((seq + kAttKPW - 1) / kAttKPW);
+  const int NMF = score_mfmas(nparts_of_(BK), true);
+  i32x4 *aops = (i32x4 *)ws;
+  QConst *qc = (QConst *)((char *)ws + (size_t)nhg * NMF * 64 * sizeof(i32x4));
+  uintptr_t pp = (uintptr_t)((char *)qc + (size_t)nhg * 4 * sizeof(QConst));
+  pp = (pp + 255) & ~(uintptr_t)255;
+  AttPartial *part = (AttPartial *)pp;
+  qprep128_kernel<true><<<dim3((unsigned)nhg), dim3(256), 0, s>>>(q, g, ngroups, K.pi64, K.s64, K.cb,
+                                                                  K.p.m, aops, qc);
+  attend128_kernel<BK, BV><<<dim3((unsigned)((nsplit + kAttWaves - 1) / kAttWaves), (unsigned)nhg),
+                             dim3(kAttWaves * 64), 0, s>>>(aops, qc, k.idx, k.sgn, k.knorm, k.rnorm,
+                                                           v.idx, v.knorm, seq, g, ngroups, nsplit,
+                                                           scale, K.cb, V.cb, part);
+  attend_merge_kernel<<<dim3((unsigned)(batch * n_kv * g)), dim3(128), 0, s>>>(part, nsplit, ngroups, g,
+                                                                               V.pi32, out);
 }
 
 tq_status launch_attend(const Derived &K, const Derived &V, const float *q, int64_t batch,
                         int64_t n_kv, int64_t g, tq_codes k, tq_codes v, int64_t seq, float scale,
                         float *out, void *ws, hipStream_t s) {
-  (void)K; (void)V; (void)q; (void)batch; (void)n_kv; (void)g; (void)k; (void)v; (void)seq;
-  (void)scale; (void)out; (void)ws; (void)s;
-  set_error("tq_attend: not built yet");
-  return TQ_ERR_UNSUPPORTED;
+  if ((uint64_t)batch * n_kv * ((g + 3) / 4) > 65535u || seq >= (1LL << 28)) {
+    set_error("tq_attend: batch * n_kv * ceil(g/4) must be <= 65535 and seq < 2^28");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  if (V.B < 1) {
+    set_error("tq_attend: values need at least one Lloyd-Max bit");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  switch (K.B * 8 + V.B) {
+#define TQ_ATT_CASE(bk, bv) \
+    case bk * 8 + bv: launch_attend_t<bk, bv>(K, V, q, batch, n_kv, g, k, v, seq, scale, out, ws, s); break;
+    TQ_ATT_CASE(0, 1) TQ_ATT_CASE(0, 2) TQ_ATT_CASE(0, 3) TQ_ATT_CASE(0, 4)
+    TQ_ATT_CASE(1, 1) TQ_ATT_CASE(1, 2) TQ_ATT_CASE(1, 3) TQ_ATT_CASE(1, 4)
+    TQ_ATT_CASE(2, 1) TQ_ATT_CASE(2, 2) TQ_ATT_CASE(2, 3) TQ_ATT_CASE(2, 4)
+    TQ_ATT_CASE(3, 1) TQ_ATT_CASE(3, 2) TQ_ATT_CASE(3, 3) TQ_ATT_CASE(3, 4)
+    TQ_ATT_CASE(4, 1) TQ_ATT_CASE(4, 2) TQ_ATT_CASE(4, 3) TQ_ATT_CASE(4, 4)
+#undef TQ_ATT_CASE
+    default:
+      set_error("tq_attend: unsupported bit widths");
+      return TQ_ERR_UNSUPPORTED;
+  }
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
 }
 
 }  // namespace tq

@@ -178,3 +178,80 @@ def test_llama_layer_full_size(b):
     torch.cuda.synchronize()
     worst = check_logits(logits.cpu().numpy(), ref, q, ref_codes["knorm"], n_kv, g, seq, 128)
     print(f"[parity] llama layer b={b} score: worst/tol={worst:.4f}", flush=True)
+
+
+# ------------------------------------------------------------------ attend
+def check_attend(got, ref):
+    """max_i |o_gpu - o_ref| <= 1e-4 * max_i |o_ref| for every query head."""
+    got = np.asarray(got, np.float64).reshape(-1, ref.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    err = np.max(np.abs(got - ref), axis=1)
+    scale = np.max(np.abs(ref), axis=1)
+    worst = float(np.max(err / (1e-4 * scale)))
+    assert np.all(err <= 1e-4 * scale), f"attend error up to {worst:.3f} x tolerance"
+    return worst
+
+
+def _attend_case(kp, vp, batch, n_kv, g, seq, seed=0):
+    okp, ovp = _oparams(kp), _oparams(vp)
+    k = synth.llama_keys(heads=n_kv, seq=seq, seed=seed + 1, dtype=torch.float32, batch=batch).double().numpy()
+    v = synth.llama_keys(heads=n_kv, seq=seq, seed=seed + 2, dtype=torch.float32, batch=batch).double().numpy()
+    q = synth.queries(batch * n_kv * g, seed=seed + 5).numpy().astype(np.float64)
+    kc, vc = o.encode(k, okp), o.encode(v, ovp)
+    ref = o.attend(q, kc, vc, okp, ovp, batch, n_kv, g, seq)
+    out = torch.full((batch, n_kv * g, kp.d), float("nan"), device=DEV)
+    ws = torch.empty(tq.attend_workspace_bytes(kp, vp, batch, n_kv, g, seq), dtype=torch.uint8, device=DEV)
+    tq.attend(kp, vp, torch.from_numpy(q.astype(np.float32)).to(DEV).reshape(batch, n_kv * g, kp.d),
+              batch, n_kv, g, _upload(o.pack(kc, okp)), _upload(o.pack(vc, ovp)), seq, out, ws)
+    torch.cuda.synchronize()
+    worst = check_attend(out.cpu().numpy(), ref)
+    print(f"[parity] attend kb={kp.b} vb={vp.b} batch={batch} n_kv={n_kv} g={g} seq={seq}: worst/tol={worst:.4f}",
+          flush=True)
+
+
+KP = tq.Params(128, 3, 128, tq.MODE_PROD, 2, 3)
+VP = tq.Params(128, 3, 128, tq.MODE_MSE, 4, 0)
+
+
+@pytest.mark.parametrize("batch,n_kv,g,seq", [(2, 2, 4, 1000), (1, 1, 1, 1), (1, 3, 2, 513), (1, 1, 5, 64),
+                                              (1, 1, 4, 512), (1, 2, 4, 4096)])
+def test_attend_shapes(batch, n_kv, g, seq):
+    _attend_case(KP, VP, batch, n_kv, g, seq)
+
+
+@pytest.mark.parametrize("kb,vb", [(1, 3), (2, 1), (4, 2), (5, 4), (3, 4), (4, 3)])
+def test_attend_bit_widths(kb, vb):
+    _attend_case(tq.Params(128, kb, 128, tq.MODE_PROD, 7, 8), tq.Params(128, vb, 128, tq.MODE_MSE, 9, 0),
+                 1, 2, 4, 700, seed=kb * 10 + vb)
+
+
+def test_attend_long_context_full_size():
+    """batch 4 x 8 KV heads x 131072 positions, d 128, 32 query heads: K prod
+    b=3, V mse b=3.  Every (batch, head) is encoded on the GPU; two sampled
+    (batch, head) slices are overwritten with the oracle's codes and their
+    outputs checked against the oracle."""
+    batch, n_kv, g, seq = 4, 8, 4, 131072
+    k = synth.llama_keys(heads=n_kv, seq=seq, seed=1, device=DEV, batch=batch)
+    v = synth.llama_keys(heads=n_kv, seq=seq, seed=2, device=DEV, batch=batch)
+    kc, vc = _gpu_encode(KP, k), _gpu_encode(VP, v)
+    q = synth.queries(batch * n_kv * g, seed=5, device=DEV).reshape(batch, n_kv * g, 128)
+    okp, ovp = _oparams(KP), _oparams(VP)
+    refs = {}
+    for (b, h) in [(0, 3), (3, 7)]:
+        hb = b * n_kv + h
+        sl = slice(hb * seq, (hb + 1) * seq)
+        okc = o.encode(k[sl].double().cpu().numpy(), okp)
+        ovc = o.encode(v[sl].double().cpu().numpy(), ovp)
+        for dst, pk in ((kc, o.pack(okc, okp)), (vc, o.pack(ovc, ovp))):
+            for name, arr in _upload(pk).items():
+                if arr is not None:
+                    dst[name][sl] = arr
+        qs = q[b, h * g:(h + 1) * g].double().cpu().numpy().astype(np.float32).astype(np.float64)
+        refs[(b, h)] = o.attend(qs, okc, ovc, okp, ovp, 1, 1, g, seq)[0]
+    out = torch.empty((batch, n_kv * g, 128), device=DEV)
+    ws = torch.empty(tq.attend_workspace_bytes(KP, VP, batch, n_kv, g, seq), dtype=torch.uint8, device=DEV)
+    tq.attend(KP, VP, q.contiguous(), batch, n_kv, g, kc, vc, seq, out, ws)
+    torch.cuda.synchronize()
+    for (b, h), ref in refs.items():
+        worst = check_attend(out[b, h * g:(h + 1) * g].cpu().numpy(), ref)
+        print(f"[parity] attend long context (b={b}, h={h}): worst/tol={worst:.4f}", flush=True)
