@@ -41,6 +41,7 @@ def _parse():
     ap.add_argument("--b", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-score", action="store_true")
+    ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling PMC byte counters)")
@@ -194,6 +195,43 @@ def main():
                                  "kernel": "score128_kernel (+ qprep128_kernel)",
                                  "algorithmic_per_launch": f"{bytes_} B ({code_bytes} B of codes per key + 4 B per logit)"}
         del big, lb
+
+    if not args.no_attend:
+        # long-context decode attention: batch 4 x 8 KV heads x 131072 positions, d 128,
+        # keys prod b=3 (m=128), values mse b=3; 32 query heads
+        ab, akv, aseq = 4, 8, 131072
+        kp = tq.Params(D, 3, M, tq.MODE_PROD, 2, 3)
+        vp = tq.Params(D, 3, M, tq.MODE_MSE, 4, 0)
+        kc = tq.alloc_codes(kp, ab * akv * aseq, dev)
+        vc = tq.alloc_codes(vp, ab * akv * aseq, dev)
+        for b in range(ab):
+            sl = slice(b * akv * aseq, (b + 1) * akv * aseq)
+            kx = synth.llama_keys(heads=akv, seq=aseq, seed=200 + b, device=dev)
+            tq.encode(kp, kx, {k: (v[sl] if v is not None else None) for k, v in kc.items()})
+            vx = synth.llama_keys(heads=akv, seq=aseq, seed=300 + b, device=dev)
+            tq.encode(vp, vx, {k: (v[sl] if v is not None else None) for k, v in vc.items()})
+        del kx, vx
+        aq = synth.queries(ab * akv * G, seed=7, device=dev).reshape(ab, akv * G, D)
+        aout = torch.empty((ab, akv * G, D), device=dev)
+        aws = torch.empty(tq.attend_workspace_bytes(kp, vp, ab, akv, G, aseq), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            tq.attend(kp, vp, aq, ab, akv, G, kc, vc, aseq, aout, aws)
+        torch.cuda.synchronize()
+        reps = max(5, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            tq.attend(kp, vp, aq, ab, akv, G, kc, vc, aseq, aout, aws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nb = (sum(tq.codes_bytes(kp, 1)) + sum(tq.codes_bytes(vp, 1))) * ab * akv * aseq
+        gbps = nb / (ms * 1e-3) / 1e9
+        out["attend_hbm"] = {"workload": f"batch {ab} x {akv} KV heads x {aseq} positions x d {D}, "
+                                         f"{akv * G} query heads; K prod b=3 m={M}, V mse b=3",
+                             "ms": round(ms, 4), "GBps": round(gbps, 1),
+                             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_call": nb}
+        del kc, vc
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.b, args.cpu_sample_heads)

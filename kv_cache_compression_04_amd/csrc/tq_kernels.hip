@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
        batch += (int64_t)gridDim.x * kEncWaves) {
     const int64_t v0 = batch * kEncBatch;
     uint4 xh[kEncCT][4], xl[kEncCT][4];
-    float nu[kEncCT], inv[kEncCT];
+    float nu[kEncCT], inv[kEncCT], zmask[kEncCT];
 #pragma unroll
     for (int ct = 0; ct < kEncCT; ++ct) {
       const int64_t row = v0 + 16 * ct + vcol;
@@ -152,6 +152,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
       ss += __shfl_xor(ss, 32);
       nu[ct] = sqrtf(ss);
       inv[ct] = nu[ct] > 0.f ? 1.0f / nu[ct] : 0.f;
+      zmask[ct] = nu[ct] > 0.f ? 1.f : 0.f;  // a zero vector has a zero residual
     }
 
     // Coordinates are processed in 4 blocks of 32 (kt2).  For each block:
@@ -206,21 +207,27 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
             const float u = acc[h][ct][i] * inv[ct];
             float r = u;
             if (B > 0) {
-              int idx = 0;
+              // thermometer code g_j = [u >= t_j]; bit k of the index is the
+              // parity of g_{m 2^k - 1}, m = 1, 2, ...; bits are shifted in
+              // (w = 2 w + bit), so the word comes out bit-reversed
+              bool gj[(1 << B) > 1 ? (1 << B) - 1 : 1];
               float c = cb.c[0];
 #pragma unroll
               for (int j = 0; j < (1 << B) - 1; ++j) {
-                const bool ge = u >= cb.t[j];
-                idx += ge ? 1 : 0;
-                c = ge ? cb.c[j + 1] : c;
+                gj[j] = u >= cb.t[j];
+                c = gj[j] ? cb.c[j + 1] : c;
               }
-              const int bit = 4 * (2 * kt2 + h) + i;
 #pragma unroll
-              for (int p = 0; p < B; ++p) planes[ct][p] |= (uint32_t)((idx >> p) & 1) << bit;
+              for (int p = 0; p < B; ++p) {
+                bool bit = false;
+#pragma unroll
+                for (int j = (1 << p) - 1; j < (1 << B) - 1; j += (1 << p)) bit ^= gj[j];
+                planes[ct][p] = planes[ct][p] + planes[ct][p] + (bit ? 1u : 0u);
+              }
               r = u - c;
             }
-            r = nu[ct] > 0.f ? r : 0.f;
-            rsq[ct] += r * r;
+            r = r * zmask[ct];
+            rsq[ct] = fmaf(r, r, rsq[ct]);
             rho[i] = r;
           }
           // element e of the GEMM-2 operand for block kt2 is coordinate
@@ -245,19 +252,25 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
         }
       }
     }
-    // sign bits: acc2[nt][ct][i] = z[row 16 nt + 4 g + i][vector 16 ct + vcol]
+    // sign bits: acc2[nt][ct][i] = z[row 16 nt + 4 g + i][vector 16 ct + vcol],
+    // shifted in from the highest row down so that row 4 nt + i lands at bit 4 nt + i
     uint32_t sbits[kEncCT];
 #pragma unroll
     for (int ct = 0; ct < kEncCT; ++ct) {
       uint32_t w = 0;
       if (PROD) {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int nt = 7; nt >= 0; --nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w |= (acc2[nt][ct][i] >= 0.f ? 1u : 0u) << (4 * nt + i);
+          for (int i = 3; i >= 0; --i) w = w + w + (acc2[nt][ct][i] >= 0.f ? 1u : 0u);
       }
       sbits[ct] = w;
     }
+    // index planes were shifted in from the lowest coordinate up: reverse them
+#pragma unroll
+    for (int ct = 0; ct < kEncCT; ++ct)
+#pragma unroll
+      for (int p = 0; p < (B > 0 ? B : 1); ++p) planes[ct][p] = __builtin_bitreverse32(planes[ct][p]);
 
     // ---- store
 #pragma unroll
@@ -417,52 +430,65 @@ __device__ __forceinline__ int limb_of(int Q, int t) {
 // Query preparation for one (KV head, group of 4 queries): qt = Pi q and
 // qs = S q in float32, then the int8 operands of the score MFMAs.
 // One workgroup of 256 threads per group.
+constexpr int kQprepThreads = 512;
+
 template <bool PROD>
-__global__ __launch_bounds__(256) void qprep128_kernel(const float *__restrict__ q, int64_t g,
-                                                       int ngroups, const double *__restrict__ pi,
-                                                       const double *__restrict__ s, Codebook cb,
-                                                       int m, i32x4 *__restrict__ aops,
-                                                       QConst *__restrict__ qc) {
+__global__ __launch_bounds__(kQprepThreads) void qprep128_kernel(
+    const float *__restrict__ q, int64_t g, int ngroups, const float *__restrict__ pi,
+    const float *__restrict__ s, Codebook cb, int m, i32x4 *__restrict__ aops,
+    QConst *__restrict__ qc) {
+  __shared__ float mat[256][129];   // rows of Pi (0..127) and S (128..255), padded
   __shared__ double qin[4][128];
   __shared__ double qv[2][4][128];  // [0] = Pi q, [1] = S q
   __shared__ int expo[4][2];
   const int hg = blockIdx.x;
   const int h = hg / ngroups, grp = hg % ngroups;
   const int tid = threadIdx.x;
-  for (int i = tid; i < 512; i += 256) {
+  {
+    // 64 KB (Pi) + 64 KB (S): 16 float4 per thread, all issued before any use
+    constexpr int kRows = PROD ? 256 : 128;
+    constexpr int kPer = kRows * 32 / kQprepThreads;
+    float4 buf[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int f = tid + i * kQprepThreads;  // float4 index over the rows
+      const int r = f >> 5, c4 = f & 31;
+      buf[i] = reinterpret_cast<const float4 *>(r < 128 ? pi + r * 128 : s + (r - 128) * 128)[c4];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int f = tid + i * kQprepThreads;
+      const int r = f >> 5, c4 = f & 31;
+      mat[r][4 * c4 + 0] = buf[i].x;
+      mat[r][4 * c4 + 1] = buf[i].y;
+      mat[r][4 * c4 + 2] = buf[i].z;
+      mat[r][4 * c4 + 3] = buf[i].w;
+    }
+  }
+  for (int i = tid; i < 512; i += kQprepThreads) {
     const int jq = i >> 7, c = i & 127;
     const int64_t qh = (int64_t)grp * 4 + jq;
     qin[jq][c] = qh < g ? (double)q[((int64_t)h * g + qh) * 128 + c] : 0.0;
   }
   __syncthreads();
   {
-    // thread -> one row of Pi (tid < 128) or of S (tid >= 128), all 4 queries
-    const int which = tid >> 7, r = tid & 127;
-    if (which == 0 || PROD) {
-      const double2 *row = reinterpret_cast<const double2 *>((which ? s : pi) + r * 128);
-      double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-#pragma unroll 16
-      for (int j2 = 0; j2 < 64; ++j2) {
-        const double2 w = row[j2];
-        const double wv[2] = {w.x, w.y};
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = 2 * j2 + e;
-          a0 = fma(wv[e], qin[0][j], a0);
-          a1 = fma(wv[e], qin[1][j], a1);
-          a2 = fma(wv[e], qin[2][j], a2);
-          a3 = fma(wv[e], qin[3][j], a3);
-        }
+    // thread -> one row (Pi rows 0..127, S rows 128..255) and two queries, float64 sums
+    const int r = tid & 255, jp = tid >> 8;  // queries 2 jp, 2 jp + 1
+    if (r < 128 || PROD) {
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll 8
+      for (int j = 0; j < 128; ++j) {
+        const double w = (double)mat[r][j];
+        a0 = fma(w, qin[2 * jp][j], a0);
+        a1 = fma(w, qin[2 * jp + 1][j], a1);
       }
-      qv[which][0][r] = a0;
-      qv[which][1][r] = a1;
-      qv[which][2][r] = a2;
-      qv[which][3][r] = a3;
+      qv[r >> 7][2 * jp][r & 127] = a0;
+      qv[r >> 7][2 * jp + 1][r & 127] = a1;
     }
   }
   __syncthreads();
   const int NP = cb.nparts;
-  {
+  if (tid < 256) {
     // wave w reduces query w: max |qt|, max |qs|, sum qt, sum qs
     const int jq = tid >> 6, lane = tid & 63;
     double mq = fmax(fabs(qv[0][jq][lane]), fabs(qv[0][jq][lane + 64]));
@@ -500,7 +526,7 @@ __global__ __launch_bounds__(256) void qprep128_kernel(const float *__restrict__
   }
   __syncthreads();
   const int NMF = score_mfmas(NP, PROD);
-  for (int i = tid; i < NMF * 64; i += 256) {
+  for (int i = tid; i < NMF * 64; i += kQprepThreads) {
     const int j = i >> 6, l = i & 63;
     const int row = l & 15, kg = l >> 4;
     const int jq = row >> 2, t = row & 3;
@@ -526,7 +552,7 @@ __global__ __launch_bounds__(256) void qprep128_kernel(const float *__restrict__
   }
 }
 
-constexpr int kScoreU = 4;  // tiles whose loads are issued together
+constexpr int kScoreU = 8;  // tiles whose loads are issued together
 
 template <int B, bool PROD>
 __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
@@ -556,16 +582,15 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
   const int64_t tiles = (seq + 15) / 16;
   const int64_t t0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
   const int64_t t1 = t0 + tiles_per_wave < tiles ? t0 + tiles_per_wave : tiles;
+  // Positions are clamped into the sequence so every load is in bounds and the
+  // loads of a group of kScoreU tiles issue back to back; results of
+  // out-of-range tiles are not stored.
   for (int64_t tb = t0; tb < t1; tb += kScoreU) {
-    // loads are unconditional (positions clamped into the sequence) so the
-    // compiler can issue them back to back; out-of-range results are not stored
     uint32_t pl[kScoreU][BB], sw[kScoreU];
     float kn[kScoreU], rn[kScoreU];
-    bool valid[kScoreU];
 #pragma unroll
     for (int u = 0; u < kScoreU; ++u) {
       const int64_t pos = (tb + u) * 16 + kc;
-      valid[u] = (tb + u) < t1 && pos < seq;
       const uint32_t vp = (uint32_t)(pos < seq ? pos : seq - 1);
       const uint32_t *ip = idx_h + (vp * 4u + kg) * BB;
       if constexpr (B == 1) {
@@ -586,7 +611,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
 #pragma unroll
     for (int u = 0; u < kScoreU; ++u) {
       const double l = tile_logit<B, PROD, NP>(A, pl[u], sw[u], kn[u], rn[u], cst, cb);
-      if (valid[u] && qvalid) out[(tb + u) * 16 + kc] = (float)l;
+      const int64_t pos = (tb + u) * 16 + kc;
+      if ((tb + u) < t1 && pos < seq && qvalid) out[pos] = (float)l;
     }
   }
 }
@@ -606,8 +632,8 @@ static void launch_score_t(const Derived &D, const float *q, int64_t n_kv, int64
   const int NMF = score_mfmas(nparts_of(B), PROD);
   i32x4 *aops = (i32x4 *)ws;
   QConst *qc = (QConst *)((char *)ws + (size_t)n_kv * ngroups * NMF * 64 * sizeof(i32x4));
-  qprep128_kernel<PROD><<<dim3((unsigned)(n_kv * ngroups)), dim3(256), 0, s>>>(
-      q, g, ngroups, D.pi64, D.s64, D.cb, D.p.m, aops, qc);
+  qprep128_kernel<PROD><<<dim3((unsigned)(n_kv * ngroups)), dim3(kQprepThreads), 0, s>>>(
+      q, g, ngroups, D.pi32, D.s32, D.cb, D.p.m, aops, qc);
   // tiles per wave: a multiple of the prefetch depth, aiming at >= 8 waves per SIMD
   const int64_t tiles = (seq + 15) / 16;
   const int64_t total = tiles * n_kv * ngroups;
@@ -654,16 +680,19 @@ tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g
 // exp(logit - m) and the un-normalised rotated-domain output
 //   o_rot[c] = sum_n exp(logit_n - m) ||v_n|| c_V[idx_n][c].
 // Phase 1 computes the logits of its positions with the score MFMAs and keeps
-// them in LDS.  Phase 2 turns them into weights w = exp(scale*logit - m) * ||v||
-// and quantises them to four balanced int8 limbs with one power-of-two scale
-// per query.  Phase 3 is the weighted sum over positions as int8 MFMAs: the
-// value codebook is expanded like the key's (odd subsets of bit planes), the
-// K dimension of the MFMA runs over positions, and the B operand for
-// coordinate c is bit c of 4 consecutive positions per dword, obtained with a
-// byte transpose (v_perm) of their index words followed by one AND per slice.
-// A merge kernel combines the splits and applies Pi_V^T once per query head.
+// them in LDS.  Phase 2 turns them into weights w = exp(logit - m) ||v||.
+// Phase 3 walks 64-position blocks: the value codebook is the odd multilinear
+// expansion c_V[idx] = sum_S a_S sigma_S of the bit planes, so
+//   o_rot[c] = sum_S sum_n (2 a_S w_n) bit_S,n,c - sum_S a_S sum_n w_n,
+// an int8 MFMA with K running over positions: A = 2 a_S w_n quantised to four
+// balanced int8 limbs (one power-of-two scale per query, one operand per part
+// S, all parts into one accumulator), B = bit c of 4 consecutive positions
+// per dword (a byte transpose of their index words with v_perm, then one AND
+// per bit slice).  A merge kernel combines the splits and applies Pi_V^T once
+// per query head.
 constexpr int kAttKPW = 512;   // positions per wave
 constexpr int kAttWaves = 4;
+constexpr int kAttU = 8;       // key tiles whose loads are issued together
 
 struct AttPartial {  // per (group, split, query): m, l, o_rot[128]
   float m, l, o[128];
@@ -681,18 +710,21 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
   constexpr int NPV = BV == 1 ? 1 : BV == 2 ? 2 : BV == 3 ? 4 : 8;
   constexpr int NMF = score_mfmas(NPK, true);
   constexpr int BKK = BK > 0 ? BK : 1;
-  __shared__ float lg[kAttWaves][4][kAttKPW];              // logits, then weights
-  __shared__ uint32_t limbs[kAttWaves][4][4][kAttKPW / 4];   // [query][limb][positions / 4]
+  __shared__ __attribute__((aligned(16))) float lg[kAttWaves][4][kAttKPW];  // logits, then weights
+  // one block of quantised weights: [part][query][limb][positions / 4]
+  __shared__ __attribute__((aligned(16))) uint32_t limbs[kAttWaves][NPV][4][4][64 / 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hg = blockIdx.y;  // (batch * n_kv + head) * ngroups + group
   const int hb = hg / ngroups;
   const int split = blockIdx.x * kAttWaves + wave;
   const int c16 = lane & 15, kg = lane >> 4;
   const int64_t p0 = (int64_t)split * kAttKPW;
-  if (split >= nsplit) return;  // whole wave leaves together; no block barrier below
+  if (split >= nsplit) return;  // the whole wave leaves; no workgroup barrier follows
   const int npos = (int)(seq - p0 < kAttKPW ? seq - p0 : kAttKPW);
+  const uint32_t last = (uint32_t)(seq - 1);
 
   // ---------------- phase 1: logits of this wave's positions
+  float m;
   {
     i32x4 A[NMF];
 #pragma unroll
@@ -703,126 +735,143 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
     const float *kn = knorm + (int64_t)hb * seq;
     const float *rn = rnorm + (int64_t)hb * seq;
     float mx = -INFINITY;
-#pragma unroll 2
-    for (int t = 0; t < kAttKPW / 16; ++t) {
-      const int pl = t * 16 + c16;
-      const bool valid = pl < npos;
-      const uint32_t vp = (uint32_t)(p0 + (valid ? pl : 0));
-      uint32_t planes[BKK];
+    for (int t0 = 0; t0 < kAttKPW / 16; t0 += kAttU) {
+      uint32_t planes[kAttU][BKK], sw[kAttU];
+      float kv[kAttU], rv[kAttU];
 #pragma unroll
-      for (int p = 0; p < BK; ++p) planes[p] = ki[(vp * 4u + kg) * BKK + p];
-      const uint32_t sw = ks[vp * 4u + kg];
-      const float kv = kn[vp], rv = rn[vp];
-      const double lt = tile_logit<BK, true, NPK>(A, planes, sw, kv, rv, cst, kcb);
-      const float logit = valid ? (float)(lt * (double)scale) : -INFINITY;
-      lg[wave][kg][pl] = logit;
-      mx = fmaxf(mx, logit);
+      for (int u = 0; u < kAttU; ++u) {
+        const uint32_t pos = (uint32_t)(p0 + (t0 + u) * 16 + c16);
+        const uint32_t vp = pos < (uint32_t)seq ? pos : last;
+#pragma unroll
+        for (int p = 0; p < BK; ++p) planes[u][p] = ki[(vp * 4u + kg) * BKK + p];
+        sw[u] = ks[vp * 4u + kg];
+        kv[u] = kn[vp];
+        rv[u] = rn[vp];
+      }
+#pragma unroll
+      for (int u = 0; u < kAttU; ++u) {
+        const int pl = (t0 + u) * 16 + c16;
+        const double lt = tile_logit<BK, true, NPK>(A, planes[u], sw[u], kv[u], rv[u], cst, kcb);
+        const float logit = pl < npos ? (float)(lt * (double)scale) : -INFINITY;
+        lg[wave][kg][pl] = logit;
+        mx = fmaxf(mx, logit);
+      }
     }
-    // max over the 16 lanes of this query (one DPP row)
+    // max over the 16 lanes of this query (lanes 16 kg .. 16 kg + 15)
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    // lanes 16 kg .. 16 kg + 15 now agree on query kg's max.  The weights below
-    // are read by other lanes of this wave: order the LDS accesses.
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // ---------------- phase 2: weights, quantised to int8 limbs
-    // lane (c16, kg) handles query kg, positions 4 c16 + 64 r + {0..3}
-    const float m = mx;
+    m = mx;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+
+  // ---------------- phase 2: weights w = exp(logit - m) * ||v||, in place
+  // lane (c16, kg): query kg, positions 4 c16 + 64 r + {0..3}
+  float lsum = 0.f, wmax = 0.f;
+  {
     const float *vn = vnorm + (int64_t)hb * seq;
-    float lsum = 0.f, wmax = 0.f;
-    float wv[kAttKPW / 64][4];
 #pragma unroll
-    for (int r = 0; r < kAttKPW / 64; ++r)
+    for (int r = 0; r < kAttKPW / 64; ++r) {
+      const int pl0 = 64 * r + 4 * c16;
+      const float4 lv = *reinterpret_cast<const float4 *>(&lg[wave][kg][pl0]);
+      const float lvv[4] = {lv.x, lv.y, lv.z, lv.w};
+      float wv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int pl = 64 * r + 4 * c16 + e;
-        const float lgt = lg[wave][kg][pl];
-        const float pexp = pl < npos ? __expf(lgt - m) : 0.f;
-        lsum += pexp;
-        const float w = pexp * vn[(uint32_t)(p0 + (pl < npos ? pl : 0))];
-        wv[r][e] = w;
-        wmax = fmaxf(wmax, w);
+        const int pl = pl0 + e;
+        const uint32_t pos = (uint32_t)(p0 + pl);
+        const float pe = pl < npos ? __expf(lvv[e] - m) : 0.f;
+        lsum += pe;
+        wv[e] = pe * vn[pos < (uint32_t)seq ? pos : last];
+        wmax = fmaxf(wmax, wv[e]);
       }
+      *reinterpret_cast<float4 *>(&lg[wave][kg][pl0]) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+    }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) {
       lsum += __shfl_xor(lsum, off);
       wmax = fmaxf(wmax, __shfl_xor(wmax, off));
     }
-    int E = 0, k;
-    if (wmax > 0.f) { frexpf(wmax, &k); E = 26 - k; }
-    double qsum = 0.0;  // exact: integers below 2^53
+  }
+  // one power-of-two scale per query covering every part: |2 a_S w| 2^E < 2^26
+  double amax = 0.0;
 #pragma unroll
-    for (int r = 0; r < kAttKPW / 64; ++r) {
-      uint32_t lw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int Q = (int)rintf(ldexpf(wv[r][e], E));
-        qsum += (double)Q;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) lw[t] |= (uint32_t)(uint8_t)(int8_t)limb_of(Q, t) << (8 * e);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) limbs[wave][kg][t][16 * r + c16] = lw[t];
-    }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) qsum += __shfl_xor(qsum, off);
-    // per-query scalars for the epilogue (the logits are no longer needed)
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (c16 == 0) {
-      lg[wave][kg][0] = m;
-      lg[wave][kg][1] = lsum;
-      lg[wave][kg][2] = (float)(qsum * (double)ldexpf(1.0f, -E));  // sum of the quantised weights
-      lg[wave][kg][3] = __int_as_float(E);
-    }
+  for (int sp = 0; sp < NPV; ++sp) amax = fmax(amax, fabs(vcb.coef[sp]));
+  int E = 0;
+  {
+    int k;
+    const double A1 = 2.0 * amax * (double)wmax;
+    if (A1 > 0) { frexp(A1, &k); E = 26 - k; }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 
   // ---------------- phase 3: o_rot = sum_n w_n c_V[idx_n] as int8 MFMAs
   // B lane (c16 = (w, beta), kg) covers positions 16 kg + 4 gi + e of each
-  // 64-position block: dword gi byte e of D_beta is byte beta of dword w of
-  // position 4 gi + e.  Slice s (bit s of every byte) is coordinate
-  // 32 beta + 16 (s / 4) + 4 w + s % 4.
+  // block: byte e of dword gi of D_beta is byte beta of index word w of
+  // position 4 gi + e.  Slice s (bit s of every byte, pre-shifted so a bit
+  // weighs 2^(s & 1)) is coordinate 32 beta + 16 (s / 4) + 4 w + s % 4.
   const int w = c16 >> 2, beta = c16 & 3;
-  i32x4 acc[NPV][8];
+  const uint32_t sel_lo = (uint32_t)(beta | (beta + 4) << 8 | 0x0C0C0000u);
+  i32x4 acc[8];
 #pragma unroll
-  for (int sp = 0; sp < NPV; ++sp)
-#pragma unroll
-    for (int sl = 0; sl < 8; ++sl) acc[sp][sl] = i32x4{0, 0, 0, 0};
+  for (int sl = 0; sl < 8; ++sl) acc[sl] = i32x4{0, 0, 0, 0};
+  double qsum = 0.0;  // sum of Q / 2 * 2^-E over this lane's quantisation tasks
   const uint32_t *vi = vidx + (int64_t)hb * seq * 4 * BV;
-  // v_perm selectors picking byte beta of each source dword: perm(a, b, sel)
-  // selects from bytes {b0..b3 = b, b4..b7 = a}
-  const uint32_t sel_lo = (uint32_t)(beta | (beta + 4) << 8 | 0x0C0C0000u);  // [b.byte beta, a.byte beta, 0, 0]
+  // quantisation of one block: lane (c16, kg) takes query kg, positions
+  // 4 c16 .. 4 c16 + 3 of the block, every part
   for (int blk = 0; blk < kAttKPW / 64; ++blk) {
-    const i32x4 Aw = *reinterpret_cast<const i32x4 *>(
-        reinterpret_cast<const uint8_t *>(&limbs[wave][0][0][0]) +
-        ((size_t)((c16 >> 2) * 4 + (c16 & 3)) * (kAttKPW / 4) * 4) + blk * 64 + 16 * kg);
+    // V index words of this lane's 16 positions (issued first)
+    uint32_t x[4][4][BV];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pos = (uint32_t)(p0 + blk * 64 + 16 * kg + 4 * gi + e);
+        const uint32_t *src = vi + ((pos < (uint32_t)seq ? pos : last) * 4u + w) * BV;
+        if constexpr (BV == 2) {
+          const uint2 t2 = *reinterpret_cast<const uint2 *>(src);
+          x[gi][e][0] = t2.x; x[gi][e][1] = t2.y;
+        } else if constexpr (BV == 4) {
+          const uint4 t4 = *reinterpret_cast<const uint4 *>(src);
+          x[gi][e][0] = t4.x; x[gi][e][1] = t4.y; x[gi][e][2] = t4.z; x[gi][e][3] = t4.w;
+        } else {
+#pragma unroll
+          for (int p = 0; p < BV; ++p) x[gi][e][p] = src[p];
+        }
+      }
+    // quantise 2 a_S w_n of this block into limb dwords
+    {
+      const float4 wv4 = *reinterpret_cast<const float4 *>(&lg[wave][kg][blk * 64 + 4 * c16]);
+      const float wv[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
+#pragma unroll
+      for (int sp = 0; sp < NPV; ++sp) {
+        const double cf = 2.0 * vcb.coef[sp];
+        uint32_t lw[4] = {0u, 0u, 0u, 0u};
+        int qs = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int Q = (int)llrint(ldexp(cf * (double)wv[e], E));
+          qs += Q;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) lw[t] |= (uint32_t)(uint8_t)(int8_t)limb_of(Q, t) << (8 * e);
+        }
+        qsum += ldexp(0.5 * (double)qs, -E);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) limbs[wave][sp][kg][t][c16] = lw[t];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // transpose: D[S][gi] = parity part S of the byte-beta transposes
     uint32_t D[NPV][4];
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      uint32_t x[4][BV];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pl = blk * 64 + 16 * kg + 4 * gi + e;
-        const uint32_t vp = (uint32_t)(p0 + (pl < npos ? pl : 0));
-        const uint32_t *src = vi + (vp * 4u + w) * BV;
-        if constexpr (BV == 2) {
-          const uint2 t2 = *reinterpret_cast<const uint2 *>(src);
-          x[e][0] = t2.x; x[e][1] = t2.y;
-        } else if constexpr (BV == 4) {
-          const uint4 t4 = *reinterpret_cast<const uint4 *>(src);
-          x[e][0] = t4.x; x[e][1] = t4.y; x[e][2] = t4.z; x[e][3] = t4.w;
-        } else {
-#pragma unroll
-          for (int p = 0; p < BV; ++p) x[e][p] = src[p];
-        }
-      }
       uint32_t pd[BV];
 #pragma unroll
       for (int p = 0; p < BV; ++p) {
-        const uint32_t lo = __builtin_amdgcn_perm(x[1][p], x[0][p], sel_lo);
-        const uint32_t hi = __builtin_amdgcn_perm(x[3][p], x[2][p], sel_lo);
+        const uint32_t lo = __builtin_amdgcn_perm(x[gi][1][p], x[gi][0][p], sel_lo);
+        const uint32_t hi = __builtin_amdgcn_perm(x[gi][3][p], x[gi][2][p], sel_lo);
         pd[p] = lo | hi << 16;
       }
 #pragma unroll
@@ -835,39 +884,43 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
       }
     }
 #pragma unroll
-    for (int sp = 0; sp < NPV; ++sp)
+    for (int sp = 0; sp < NPV; ++sp) {
+      // A: rows (query c16 / 4, limb c16 % 4), positions 16 kg .. 16 kg + 15
+      const i32x4 Aw = *reinterpret_cast<const i32x4 *>(&limbs[wave][sp][c16 >> 2][c16 & 3][4 * kg]);
+      i32x4 lo4[4], hi4[4];
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const uint32_t mk = 0x01010101u << sl;
-        const i32x4 bw = {(int)(D[sp][0] & mk), (int)(D[sp][1] & mk), (int)(D[sp][2] & mk), (int)(D[sp][3] & mk)};
-        acc[sp][sl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aw, bw, acc[sp][sl], 0, 0, 0);
+      for (int gi = 0; gi < 4; ++gi) {
+        i32x4 a4, b4;
+        bit_slices(D[sp][gi], a4, b4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          lo4[k][gi] = a4[k];
+          hi4[k][gi] = b4[k];
+        }
       }
-  }
-
-  // ---------------- epilogue: lane (c16, kg) holds query kg, limbs t = 0..3 of
-  // the 8 coordinates 32 beta + 16 (s / 4) + 4 w + s % 4
-  const float m = lg[wave][kg][0];
-  const float lsum = lg[wave][kg][1];
-  const float wsum = lg[wave][kg][2];
-  const int E = __float_as_int(lg[wave][kg][3]);
-  const int64_t qh = (int64_t)(hg % ngroups) * 4 + kg;
-  double csum = 0.0;
 #pragma unroll
-  for (int sp = 0; sp < NPV; ++sp) csum += vcb.coef[sp];
+      for (int k = 0; k < 4; ++k) {
+        acc[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aw, lo4[k], acc[k], 0, 0, 0);
+        acc[4 + k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aw, hi4[k], acc[4 + k], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  // sum over the 16 lanes of query kg: sum_S sum_n Q_S,n / 2 * 2^-E
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) qsum += __shfl_xor(qsum, off);
+  // ---------------- epilogue: lane (c16, kg) holds query kg, limbs t = 0..3
+  const int64_t qh = (int64_t)(hg % ngroups) * 4 + kg;
   AttPartial *dst = part + ((int64_t)hg * nsplit + split) * 4 + kg;
   if (qh < g) {
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      const float sc = ldexpf(sl == 7 ? -2.0f : 2.0f, -E - sl);  // 2 * 2^-E * weight of slice
-      float o = 0.f;
-#pragma unroll
-      for (int sp = 0; sp < NPV; ++sp) {
-        const i32x4 a = acc[sp][sl];
-        const float v = (float)a[0] + 128.f * (float)a[1] + 16384.f * (float)a[2] + 2097152.f * (float)a[3];
-        o += (float)vcb.coef[sp] * v;
-      }
+      const i32x4 a = acc[sl];
+      const double v = (double)a[0] + 128.0 * (double)a[1] + 16384.0 * (double)a[2] +
+                       2097152.0 * (double)a[3];
       const int c = 32 * beta + 16 * (sl >> 2) + 4 * w + (sl & 3);
-      dst->o[c] = o * sc - (float)(csum * (double)wsum);
+      dst->o[c] = (float)(ldexp(v, -E - (sl & 1)) - qsum);
     }
     if (c16 == 0) {
       dst->m = m;
@@ -877,31 +930,55 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
 }
 
 // Combine the splits of one query head and rotate back: out = Pi_V^T o_rot / L.
-__global__ __launch_bounds__(128) void attend_merge_kernel(const AttPartial *__restrict__ part,
-                                                           int nsplit, int ngroups, int64_t g,
-                                                           const float *__restrict__ piv,
-                                                           float *__restrict__ out) {
-  __shared__ float orot[128];
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(
+    const AttPartial *__restrict__ part, int nsplit, int ngroups, int64_t g,
+    const float *__restrict__ piv, float *__restrict__ out) {
+  __shared__ float wsp[1024];      // exp(m_s - M) per split (nsplit <= 1024 here; larger loops)
+  __shared__ float red[kMergeThreads / 64][2];
+  __shared__ float orot[2][128];
   const int hq = blockIdx.x;        // (batch * n_kv + head) * g + j
   const int64_t hb = hq / g, j = hq % g;
   const int64_t hg = hb * ngroups + j / 4;
   const int jq = (int)(j % 4);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const AttPartial *p = part + (int64_t)hg * nsplit * 4 + jq;
   float M = -INFINITY;
-  for (int sidx = 0; sidx < nsplit; ++sidx) M = fmaxf(M, p[(int64_t)sidx * 4].m);
-  float L = 0.f;
-  for (int sidx = 0; sidx < nsplit; ++sidx) L += p[(int64_t)sidx * 4].l * __expf(p[(int64_t)sidx * 4].m - M);
-  float acc = 0.f;
-  for (int sidx = 0; sidx < nsplit; ++sidx) {
-    const float wgt = __expf(p[(int64_t)sidx * 4].m - M);
-    acc += wgt * p[(int64_t)sidx * 4].o[tid];
-  }
-  orot[tid] = acc / L;
+  for (int sidx = tid; sidx < nsplit; sidx += kMergeThreads) M = fmaxf(M, p[(int64_t)sidx * 4].m);
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red[wv][0] = M;
   __syncthreads();
-  float o = 0.f;
-  for (int c = 0; c < 128; ++c) o = fmaf(piv[c * 128 + tid], orot[c], o);
-  out[(int64_t)hq * 128 + tid] = o;
+  M = red[0][0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w][0]);
+  float L = 0.f;
+  for (int sidx = tid; sidx < nsplit; sidx += kMergeThreads) {
+    const float e = __expf(p[(int64_t)sidx * 4].m - M);
+    if (sidx < 1024) wsp[sidx] = e;
+    L += p[(int64_t)sidx * 4].l * e;
+  }
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+  __syncthreads();
+  if (lane == 0) red[wv][1] = L;
+  __syncthreads();
+  L = 0.f;
+  for (int w = 0; w < kMergeThreads / 64; ++w) L += red[w][1];
+  // o_rot[c]: two halves of the splits per coordinate
+  const int c = tid & 127, half = tid >> 7;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int sidx = half; sidx < nsplit; sidx += 2) {
+    const float e = sidx < 1024 ? wsp[sidx] : __expf(p[(int64_t)sidx * 4].m - M);
+    acc = fmaf(e, p[(int64_t)sidx * 4].o[c], acc);
+  }
+  orot[half][c] = acc;
+  __syncthreads();
+  if (tid < 128) {
+    float o = 0.f;
+    const float inv = 1.0f / L;
+#pragma unroll 8
+    for (int cc = 0; cc < 128; ++cc) o = fmaf(piv[cc * 128 + tid], (orot[0][cc] + orot[1][cc]) * inv, o);
+    out[(int64_t)hq * 128 + tid] = o;
+  }
 }
 
 static int nparts_of_(int B) { return B == 0 ? 0 : (B == 1 ? 1 : B == 2 ? 2 : B == 3 ? 4 : 8); }
@@ -930,13 +1007,13 @@ static void launch_attend_t(const Derived &K, const Derived &V, const float *q, 
   uintptr_t pp = (uintptr_t)((char *)qc + (size_t)nhg * 4 * sizeof(QConst));
   pp = (pp + 255) & ~(uintptr_t)255;
   AttPartial *part = (AttPartial *)pp;
-  qprep128_kernel<true><<<dim3((unsigned)nhg), dim3(256), 0, s>>>(q, g, ngroups, K.pi64, K.s64, K.cb,
+  qprep128_kernel<true><<<dim3((unsigned)nhg), dim3(kQprepThreads), 0, s>>>(q, g, ngroups, K.pi32, K.s32, K.cb,
                                                                   K.p.m, aops, qc);
   attend128_kernel<BK, BV><<<dim3((unsigned)((nsplit + kAttWaves - 1) / kAttWaves), (unsigned)nhg),
                              dim3(kAttWaves * 64), 0, s>>>(aops, qc, k.idx, k.sgn, k.knorm, k.rnorm,
                                                            v.idx, v.knorm, seq, g, ngroups, nsplit,
                                                            scale, K.cb, V.cb, part);
-  attend_merge_kernel<<<dim3((unsigned)(batch * n_kv * g)), dim3(128), 0, s>>>(part, nsplit, ngroups, g,
+  attend_merge_kernel<<<dim3((unsigned)(batch * n_kv * g)), dim3(kMergeThreads), 0, s>>>(part, nsplit, ngroups, g,
                                                                                V.pi32, out);
 }
 
