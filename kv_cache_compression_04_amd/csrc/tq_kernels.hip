@@ -73,8 +73,8 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
 // ===========================================================================
 // Encode, d = m = 128
 // ===========================================================================
-constexpr int kEncWaves = 8;          // waves per workgroup
-constexpr int kEncCT = 2;             // 16-vector column tiles per wave batch
+constexpr int kEncWaves = 16;         // waves per workgroup
+constexpr int kEncCT = 1;             // 16-vector column tiles per wave batch
 constexpr int kEncBatch = 16 * kEncCT;  // vectors per wave batch
 constexpr int kFragU4 = kFragElems / 8;  // uint4 per fragment matrix (2048)
 
@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
        batch += (int64_t)gridDim.x * kEncWaves) {
     const int64_t v0 = batch * kEncBatch;
     uint4 xh[kEncCT][4], xl[kEncCT][4];
-    float nu[kEncCT], inv[kEncCT], zmask[kEncCT];
+    float nu[kEncCT];
+    float cs[kEncCT][1 << B], ts[kEncCT][(1 << B) > 1 ? (1 << B) - 1 : 1];
 #pragma unroll
     for (int ct = 0; ct < kEncCT; ++ct) {
       const int64_t row = v0 + 16 * ct + vcol;
@@ -151,8 +152,14 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
       nu[ct] = sqrtf(ss);
-      inv[ct] = nu[ct] > 0.f ? 1.0f / nu[ct] : 0.f;
-      zmask[ct] = nu[ct] > 0.f ? 1.f : 0.f;  // a zero vector has a zero residual
+      // the codebook scaled by ||x||: y = Pi x is compared with t_j ||x|| and the
+      // residual is formed as y - c ||x|| = ||x|| (u - c), so no division is
+      // needed; a zero vector gets y = 0 and a zero residual
+#pragma unroll
+      for (int j = 0; j < (1 << B); ++j) cs[ct][j] = cb.c[j] * nu[ct];
+      // (for a zero vector the unscaled boundaries reproduce the u = 0 decisions)
+#pragma unroll
+      for (int j = 0; j + 1 < (1 << B); ++j) ts[ct][j] = nu[ct] > 0.f ? cb.t[j] * nu[ct] : cb.t[j];
     }
 
     // Coordinates are processed in 4 blocks of 32 (kt2).  For each block:
@@ -204,18 +211,18 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
           float rho[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float u = acc[h][ct][i] * inv[ct];
-            float r = u;
+            const float y = acc[h][ct][i];  // ||x|| u
+            float r = y;
             if (B > 0) {
               // thermometer code g_j = [u >= t_j]; bit k of the index is the
               // parity of g_{m 2^k - 1}, m = 1, 2, ...; bits are shifted in
               // (w = 2 w + bit), so the word comes out bit-reversed
               bool gj[(1 << B) > 1 ? (1 << B) - 1 : 1];
-              float c = cb.c[0];
+              float c = cs[ct][0];
 #pragma unroll
               for (int j = 0; j < (1 << B) - 1; ++j) {
-                gj[j] = u >= cb.t[j];
-                c = gj[j] ? cb.c[j + 1] : c;
+                gj[j] = y >= ts[ct][j];
+                c = gj[j] ? cs[ct][j + 1] : c;
               }
 #pragma unroll
               for (int p = 0; p < B; ++p) {
@@ -224,9 +231,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
                 for (int j = (1 << p) - 1; j < (1 << B) - 1; j += (1 << p)) bit ^= gj[j];
                 planes[ct][p] = planes[ct][p] + planes[ct][p] + (bit ? 1u : 0u);
               }
-              r = u - c;
+              r = y - c;
             }
-            r = r * zmask[ct];
             rsq[ct] = fmaf(r, r, rsq[ct]);
             rho[i] = r;
           }
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
         if (PROD) sgn_out[row * 4 + g] = sbits[ct];
         if (g == 0) {
           knorm_out[row] = nu[ct];
-          if (PROD) rnorm_out[row] = nu[ct] * sqrtf(r2);
+          if (PROD) rnorm_out[row] = sqrtf(r2);
         }
       }
     }
@@ -323,7 +329,9 @@ tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n, t
                         hipStream_t s) {
   const int64_t nbatch = (n + kEncBatch - 1) / kEncBatch;
   const int64_t need = (nbatch + kEncWaves - 1) / kEncWaves;
-  const int grid = (int)std::min<int64_t>(need, num_cus(D.device));
+  // one workgroup per CU holds the 128 KB of prod-mode fragments; mse mode (64 KB) fits two
+  const int per_cu = D.p.mode == TQ_MODE_PROD ? 1 : 2;
+  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * per_cu);
   const bool prod = D.p.mode == TQ_MODE_PROD;
   switch (D.B * 2 + (prod ? 1 : 0)) {
     case 0 * 2 + 1: launch_encode_t<0, true>(D, x, dtype, n, c, s, grid); break;
