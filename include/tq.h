@@ -65,8 +65,10 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
  * JL rows m, mode, and the seeds of the rotation Pi and of S.  Pi is the Q
  * factor (with positive diag(R)) of a d x d Gaussian drawn from seed_pi; S is
  * an m x d N(0,1) matrix drawn from seed_s.  Both Gaussians come from
- * SplitMix64 words (element (i, j) of an R x C matrix is counter i*C + j,
- * Box-Muller on counter pairs); see DESIGN notes in the repository.       */
+ * SplitMix64 words: word k = mix(seed + (k+1) * 0x9E3779B97F4A7C15);
+ * element (i, j) of an R x C matrix is counter c = i*C + j; counter pair
+ * p = c/2 takes u1 = (w_2p >> 11 + 1) 2^-53 and u2 = (w_2p+1 >> 11) 2^-53,
+ * even c -> sqrt(-2 ln u1) cos(2 pi u2), odd c -> the sine branch.        */
 typedef struct {
   int32_t d;
   int32_t b;
@@ -102,7 +104,7 @@ int32_t tq_layout_version(void);
 
 /* Lloyd-Max codebook for the law of one coordinate of a randomly rotated
  * unit vector in R^d, density proportional to (1-x^2)^((d-3)/2) on [-1, 1]
- * ([P5] 第一阶段: "the Beta law, solved once by Lloyd-Max, stored forever").
+ * ([P5] 第一阶段: the law is known, so the codebook is computed once).
  * Host only, pure.  centroids: host float[2^B] ascending; boundaries: host
  * float[2^B - 1], boundaries[j] = fp32((c_j + c_{j+1}) / 2) with the middle
  * one exactly 0.  B = b-1 (prod) or b (mse); B == 0 writes nothing.  d >= 3. */
@@ -158,6 +160,28 @@ tq_status tq_attend_workspace_bytes(const tq_params *kp, const tq_params *vp,
 tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
                     int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
                     tq_codes vcodes, int64_t seq, float scale, float *out,
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/* MSE reconstruction of n vectors, x~ = ||x|| Pi^T c[idx] ([P5] 第一阶段: the
+ * reconstruction whose squared error the Lloyd-Max codebook minimises).
+ * Prod-mode codes decode their B = b-1 bit MSE part (the QJL bits carry no
+ * reconstruction).  codes: device, n vectors; out: device float [n][d].    */
+tq_status tq_decode(const tq_params *p, tq_codes codes, int64_t n, float *out,
+                    void *stream);
+
+/* Workspace bytes tq_search needs.  Host only.                             */
+tq_status tq_search_workspace_bytes(const tq_params *p, int64_t nq, int64_t n,
+                                    int32_t k, size_t *bytes);
+
+/* Top-k search over compressed vectors (vector search with the same
+ * estimator as tq_score): for each of nq queries, the k database vectors of
+ * largest logit, in descending order, ties broken by the lower index.
+ * q: device float [nq][d]; codes: device, n vectors; out_idx: device int64
+ * [nq][k]; out_val: device float [nq][k] (may be NULL).  1 <= k <= 32 and
+ * k <= n.  workspace: device, >= tq_search_workspace_bytes (it holds the
+ * nq x n logits).                                                          */
+tq_status tq_search(const tq_params *p, const float *q, int64_t nq, tq_codes codes,
+                    int64_t n, int32_t k, int64_t *out_idx, float *out_val,
                     void *workspace, size_t ws_bytes, void *stream);
 
 /* Frees every cached matrix/codebook on every device.  Not thread-safe with

@@ -660,6 +660,82 @@ tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
                        workspace, (hipStream_t)stream);
 }
 
+tq_status tq_decode(const tq_params *p, tq_codes codes, int64_t n, float *out, void *stream) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (n < 0) {
+    set_error("tq_decode: n < 0");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (n == 0) return TQ_OK;
+  if (!out) {
+    set_error("tq_decode: out is NULL");
+    return TQ_ERR_INVALID_ARG;
+  }
+  const int B = mse_bits(p);
+  if ((B > 0 && !codes.idx) || !codes.knorm) {
+    set_error("tq_decode: idx/knorm missing");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if ((B > 0 && !aligned16(codes.idx)) || !aligned16(codes.knorm) || !aligned16(out)) {
+    set_error("tq_decode: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (p->d != 128) {
+    set_error("tq_decode: device kernels are built for d = 128 only");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const Derived *D = nullptr;
+  if ((st = get_derived(p, &D))) return st;
+  return launch_decode(*D, codes, n, out, (hipStream_t)stream);
+}
+
+tq_status tq_search_workspace_bytes(const tq_params *p, int64_t nq, int64_t n, int32_t k,
+                                    size_t *bytes) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (nq < 0 || n < 0 || k < 1 || k > 32 || !bytes) {
+    set_error("tq_search_workspace_bytes: bad nq/n/k");
+    return TQ_ERR_INVALID_ARG;
+  }
+  size_t sb = 0;
+  if ((st = tq_score_workspace_bytes(p, 1, nq > 0 ? nq : 1, &sb))) return st;
+  *bytes = ((sb + 255) & ~(size_t)255) + (size_t)nq * n * sizeof(float);
+  return TQ_OK;
+}
+
+tq_status tq_search(const tq_params *p, const float *q, int64_t nq, tq_codes codes, int64_t n,
+                    int32_t k, int64_t *out_idx, float *out_val, void *workspace,
+                    size_t ws_bytes, void *stream) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (nq < 0 || n < 0 || k < 1 || k > 32 || (nq > 0 && k > n)) {
+    set_error("tq_search: need nq >= 0, 1 <= k <= 32, k <= n");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (nq == 0) return TQ_OK;
+  if (!q || !out_idx || !workspace) {
+    set_error("tq_search: NULL q/out_idx/workspace");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (!aligned16(out_idx) || (out_val && !aligned16(out_val))) {
+    set_error("tq_search: outputs must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  size_t need = 0;
+  if ((st = tq_search_workspace_bytes(p, nq, n, k, &need))) return st;
+  if (ws_bytes < need) {
+    set_error("tq_search: workspace too small (%zu < %zu)", ws_bytes, need);
+    return TQ_ERR_NO_MEMORY;
+  }
+  size_t sb = 0;
+  if ((st = tq_score_workspace_bytes(p, 1, nq, &sb))) return st;
+  const size_t off = (sb + 255) & ~(size_t)255;
+  float *logits = (float *)((char *)workspace + off);
+  if ((st = tq_score(p, q, 1, nq, codes, n, logits, workspace, sb, stream))) return st;
+  return launch_topk(logits, nq, n, k, out_idx, out_val, (hipStream_t)stream);
+}
+
 tq_status tq_release_cache(void) {
   std::lock_guard<std::mutex> lock(g_cache_mu);
   for (auto &kv : g_cache) free_derived(kv.second);

@@ -60,6 +60,11 @@ tq_status launch_attend(const Derived &K, const Derived &V, const float *q,
                         tq_codes v, int64_t seq, float scale, float *out,
                         void *ws, hipStream_t stream);
 
+tq_status launch_decode(const Derived &D, tq_codes codes, int64_t n, float *out,
+                        hipStream_t stream);
+tq_status launch_topk(const float *logits, int64_t nq, int64_t n, int k, int64_t *out_idx,
+                      float *out_val, hipStream_t stream);
+
 // Fragment geometry of the d = m = 128 encode kernel: a 128 x 128 matrix is
 // stored as [16-row tile nt][32-column block kt][lane][8] bf16 values; lane l
 // covers row 16 nt + l % 16 and lane group l / 16.

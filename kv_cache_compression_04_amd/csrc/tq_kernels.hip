@@ -1053,4 +1053,172 @@ tq_status launch_attend(const Derived &K, const Derived &V, const float *q, int6
   return TQ_OK;
 }
 
+// ===========================================================================
+// Decode (MSE reconstruction), d = 128: x~ = ||x|| Pi^T c[idx]
+// ===========================================================================
+// 256 threads per workgroup, Pi (float32, 64 KB) in LDS; two vectors per
+// round, one output coordinate per thread: x~_j = nu sum_c Pi[c][j] c[idx_c].
+template <int B>
+__global__ __launch_bounds__(256) void decode128_kernel(const uint32_t *__restrict__ idx,
+                                                        const float *__restrict__ knorm,
+                                                        int64_t n, const float *__restrict__ pi,
+                                                        Codebook cb, float *__restrict__ out) {
+  __shared__ float P[128][128];
+  __shared__ float cv[2][128];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 128 * 32; i += 256)
+    reinterpret_cast<float4 *>(&P[0][0])[i] = reinterpret_cast<const float4 *>(pi)[i];
+  const int half = tid >> 7, j = tid & 127;
+  for (int64_t v0 = (int64_t)blockIdx.x * 2; v0 < n; v0 += (int64_t)gridDim.x * 2) {
+    const int64_t v = v0 + half;
+    __syncthreads();  // P ready (first round) / cv consumed (later rounds)
+    if (v < n) {
+      // centroid of coordinate j: word 4 (j / 128) + (j / 4) % 4, bit 4 ((j % 128) / 16) + j % 4
+      const int w = (j >> 2) & 3, bit = 4 * (j >> 4) + (j & 3);
+      int id = 0;
+#pragma unroll
+      for (int p = 0; p < B; ++p) id |= (int)((idx[(v * 4 + w) * B + p] >> bit) & 1u) << p;
+      cv[half][j] = cb.c[id];
+    }
+    __syncthreads();
+    if (v < n) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < 128; ++c) acc = fmaf(P[c][j], cv[half][c], acc);
+      out[v * 128 + j] = knorm[v] * acc;
+    }
+  }
+}
+
+__global__ void fill_zero_kernel(float *__restrict__ out, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = 0.f;
+}
+
+tq_status launch_decode(const Derived &D, tq_codes codes, int64_t n, float *out, hipStream_t s) {
+  const int grid = (int)std::min<int64_t>((n + 1) / 2, 4LL * num_cus(D.device));
+  switch (D.B) {
+    case 0:
+      // no Lloyd-Max bits (prod mode with b = 1): the reconstruction is zero
+      // (a fill kernel rather than a memset, so the call stays capturable)
+      fill_zero_kernel<<<grid, 256, 0, s>>>(out, n * 128);
+      break;
+    case 1: decode128_kernel<1><<<grid, 256, 0, s>>>(codes.idx, codes.knorm, n, D.pi32, D.cb, out); break;
+    case 2: decode128_kernel<2><<<grid, 256, 0, s>>>(codes.idx, codes.knorm, n, D.pi32, D.cb, out); break;
+    case 3: decode128_kernel<3><<<grid, 256, 0, s>>>(codes.idx, codes.knorm, n, D.pi32, D.cb, out); break;
+    case 4: decode128_kernel<4><<<grid, 256, 0, s>>>(codes.idx, codes.knorm, n, D.pi32, D.cb, out); break;
+    default:
+      set_error("tq_decode: unsupported B = %d", D.B);
+      return TQ_ERR_UNSUPPORTED;
+  }
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+// ===========================================================================
+// Top-k over rows of logits (vector search), k <= 32
+// ===========================================================================
+// One workgroup of 256 threads per query row.  Each thread keeps a sorted
+// list of its K best (value desc, index asc) over indices t, t + 256, ...;
+// waves merge their 64 lists by K rounds of arg-max extraction, then wave 0
+// merges the 4 wave lists the same way.
+template <int K>
+__device__ __forceinline__ bool better(float va, int64_t ia, float vb, int64_t ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+template <int K>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int64_t n,
+                                                   int k, int64_t *__restrict__ out_idx,
+                                                   float *__restrict__ out_val) {
+  __shared__ float sv[4][K];
+  __shared__ int64_t si[4][K];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const float *x = logits + row * n;
+  float v[K];
+  int64_t id[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) { v[i] = -INFINITY; id[i] = INT64_MAX; }
+  for (int64_t j = tid; j < n; j += 256) {
+    const float xv = x[j];
+    if (better<K>(xv, j, v[K - 1], id[K - 1])) {
+      // insert: shift down everything worse than (xv, j)
+      float cv = xv;
+      int64_t ci = j;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        if (better<K>(cv, ci, v[i], id[i])) {
+          const float tv = v[i];
+          const int64_t ti = id[i];
+          v[i] = cv; id[i] = ci;
+          cv = tv; ci = ti;
+        }
+      }
+    }
+  }
+  // wave merge: K rounds, the best head among 64 lanes is popped
+  int head = 0;
+  for (int r = 0; r < k; ++r) {
+    float hv = -INFINITY;
+    int64_t hi = INT64_MAX;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (i == head) { hv = v[i]; hi = id[i]; }
+    float bv = hv;
+    int64_t bi = hi;
+    int bl = lane;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int64_t oi = __shfl_xor(bi, off);
+      const int ol = __shfl_xor(bl, off);
+      if (better<K>(ov, oi, bv, bi)) { bv = ov; bi = oi; bl = ol; }
+    }
+    if (lane == bl) ++head;
+    if (lane == 0) { sv[wave][r] = bv; si[wave][r] = bi; }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lanes 0..3 walk the four wave lists
+    int pos = 0;
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int64_t bi = INT64_MAX;
+      if (lane < 4 && pos < k) { bv = sv[lane][pos]; bi = si[lane][pos]; }
+      int bl = lane;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int64_t oi = __shfl_xor(bi, off);
+        const int ol = __shfl_xor(bl, off);
+        if (better<K>(ov, oi, bv, bi)) { bv = ov; bi = oi; bl = ol; }
+      }
+      if (lane == bl) ++pos;
+      if (lane == 0) {
+        out_idx[row * k + r] = bi;
+        if (out_val) out_val[row * k + r] = bv;
+      }
+    }
+  }
+}
+
+tq_status launch_topk(const float *logits, int64_t nq, int64_t n, int k, int64_t *out_idx,
+                      float *out_val, hipStream_t s) {
+  if (nq > 0x7fffffffLL) {
+    set_error("tq_search: too many queries");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const dim3 grid((unsigned)nq), blk(256);
+  if (k <= 8)
+    topk_kernel<8><<<grid, blk, 0, s>>>(logits, n, k, out_idx, out_val);
+  else if (k <= 16)
+    topk_kernel<16><<<grid, blk, 0, s>>>(logits, n, k, out_idx, out_val);
+  else
+    topk_kernel<32><<<grid, blk, 0, s>>>(logits, n, k, out_idx, out_val);
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
 }  // namespace tq

@@ -43,7 +43,8 @@ class _Codes(ctypes.Structure):
 
 EXPORTS = ["tq_status_string", "tq_last_error", "tq_layout_version", "tq_make_codebook",
            "tq_codes_bytes", "tq_export_matrices", "tq_encode", "tq_score_workspace_bytes",
-           "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_release_cache"]
+           "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_decode",
+           "tq_search_workspace_bytes", "tq_search", "tq_release_cache"]
 
 _lib = None
 
@@ -70,6 +71,9 @@ def lib():
             "tq_score": (ctypes.c_int, [P, vp, i64, i64, C, i64, vp, vp, sz, vp]),
             "tq_attend_workspace_bytes": (ctypes.c_int, [P, P, i64, i64, i64, i64, ctypes.POINTER(sz)]),
             "tq_attend": (ctypes.c_int, [P, P, vp, i64, i64, i64, C, C, i64, ctypes.c_float, vp, vp, sz, vp]),
+            "tq_decode": (ctypes.c_int, [P, C, i64, vp, vp]),
+            "tq_search_workspace_bytes": (ctypes.c_int, [P, i64, i64, ctypes.c_int32, ctypes.POINTER(sz)]),
+            "tq_search": (ctypes.c_int, [P, vp, i64, C, i64, ctypes.c_int32, vp, vp, vp, sz, vp]),
             "tq_release_cache": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -152,6 +156,12 @@ def attend_workspace_bytes(kp: Params, vp: Params, batch, n_kv, g, seq) -> int:
     return out.value
 
 
+def search_workspace_bytes(p: Params, nq: int, n: int, k: int) -> int:
+    out = ctypes.c_size_t()
+    _check("tq_search_workspace_bytes", lib().tq_search_workspace_bytes(ctypes.byref(p.c()), nq, n, k, ctypes.byref(out)))
+    return out.value
+
+
 def release_cache():
     _check("tq_release_cache", lib().tq_release_cache())
 
@@ -199,3 +209,17 @@ def attend(kp: Params, vp: Params, q, batch, n_kv, g, kcodes, vcodes, seq, out, 
                                         _codes(kcodes), _codes(vcodes), seq, scale, _ptr(out),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
+
+
+def decode(p: Params, codes: dict, n: int, out, stream=None):
+    """out: [n, d] float32 (written) = ||x|| Pi^T c[idx]."""
+    assert out.is_contiguous()
+    _check("tq_decode", lib().tq_decode(ctypes.byref(p.c()), _codes(codes), n, _ptr(out), _stream(stream)))
+
+
+def search(p: Params, q, codes: dict, n: int, k: int, out_idx, out_val, workspace, stream=None):
+    """q: [nq, d] float32; out_idx: [nq, k] int64; out_val: [nq, k] float32 or None."""
+    assert q.is_contiguous() and out_idx.is_contiguous()
+    _check("tq_search", lib().tq_search(ctypes.byref(p.c()), _ptr(q), q.shape[0], _codes(codes), n, k,
+                                        _ptr(out_idx), _ptr(out_val), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -255,3 +255,92 @@ def test_attend_long_context_full_size():
     for (b, h), ref in refs.items():
         worst = check_attend(out[b, h * g:(h + 1) * g].cpu().numpy(), ref)
         print(f"[parity] attend long context (b={b}, h={h}): worst/tol={worst:.4f}", flush=True)
+
+
+# ------------------------------------------------------------------ decode (MSE reconstruction)
+@pytest.mark.parametrize("b,mode", [(3, tq.MODE_PROD), (1, tq.MODE_PROD), (5, tq.MODE_PROD),
+                                    (2, tq.MODE_MSE), (4, tq.MODE_MSE)])
+def test_decode(b, mode):
+    p = tq.Params(128, b, 128, mode, 31, 32)
+    op = _oparams(p)
+    x = synth.llama_keys(heads=1, seq=1037, seed=b, dtype=torch.float32).double().numpy()
+    codes = o.encode(x, op)
+    out = torch.full((x.shape[0], 128), float("nan"), device=DEV)
+    tq.decode(p, _upload(o.pack(codes, op)), x.shape[0], out)
+    torch.cuda.synchronize()
+    ref = o.dequantize(codes, op)
+    err = np.abs(out.cpu().numpy() - ref)
+    # float32 Pi and float32 sums of 128 terms: |error| <= 1e-5 ||x||
+    assert np.all(err <= 1e-5 * codes["knorm"].astype(np.float64)[:, None] + 1e-30)
+
+
+# ------------------------------------------------------------------ search (many-query score + top-k)
+def check_search(idx, val, ref, q, knorm, k, d=128):
+    """Returned sets equal the oracle's up to swaps among logits within tolerance."""
+    qn = np.linalg.norm(q, axis=1)
+    for r in range(ref.shape[0]):
+        row = ref[r]
+        tol = 1e-4 * np.maximum(np.abs(row), qn[r] * knorm / math.sqrt(d))
+        got = idx[r]
+        assert len(set(got.tolist())) == k and got.min() >= 0 and got.max() < row.size
+        order = np.argsort(-row, kind="stable")
+        kth = row[order[k - 1]]
+        tk = tol[order[k - 1]]
+        assert np.all(row[got] >= kth - tol[got] - tk), f"row {r}: returned a non-top-{k} key"
+        must = np.nonzero(row > kth + tol + tk)[0]
+        assert set(must.tolist()) <= set(got.tolist()), f"row {r}: missed a clear top-{k} key"
+        if val is not None:
+            assert np.all(np.abs(val[r] - row[got]) <= tol[got])
+            assert np.all(np.diff(val[r]) <= 0)
+
+
+@pytest.mark.parametrize("nq,n,k,b", [(16, 4096, 10, 3), (37, 1000, 1, 3), (4, 300, 32, 4), (5, 17, 17, 2)])
+def test_search(nq, n, k, b):
+    p = tq.Params(128, b, 128, tq.MODE_PROD, 41, 42)
+    op = _oparams(p)
+    x = synth.sweep_keys(n=n, seed=nq).double().numpy()
+    q = synth.queries(nq, seed=n).numpy().astype(np.float64)
+    codes = o.encode(x, op)
+    ref = o.score(q, codes, op, 1, nq, n)
+    out_idx = torch.empty((nq, k), dtype=torch.int64, device=DEV)
+    out_val = torch.empty((nq, k), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.search_workspace_bytes(p, nq, n, k), dtype=torch.uint8, device=DEV)
+    tq.search(p, torch.from_numpy(q.astype(np.float32)).to(DEV), _upload(o.pack(codes, op)), n, k,
+              out_idx, out_val, ws)
+    torch.cuda.synchronize()
+    check_search(out_idx.cpu().numpy(), out_val.cpu().numpy(), ref, q, codes["knorm"].astype(np.float64), k)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_bit_width_sweep_config(b):
+    """65536 unit-direction x log-normal-norm vectors, d 128, 1024 queries: GPU
+    encode (checked on 2048 sampled rows), many-query score of all 1024 x 65536
+    logits from the oracle's codes (checked on 64 query rows) and top-10."""
+    n, nq = 65536, 1024
+    p = tq.Params(128, b, 128)
+    op = _oparams(p)
+    x = synth.sweep_keys(n=n, seed=1, device=DEV)
+    codes = _gpu_encode(p, x)
+    rows = np.sort(np.random.default_rng(b).choice(n, 2048, replace=False))
+    rep = {}
+    check_encode(x[torch.from_numpy(rows).to(DEV)].double().cpu().numpy(),
+                 {k: v[rows] for k, v in to_numpy_codes(codes).items()}, op, rep)
+    _report(f"sweep b={b} encode sample", rep)
+    xs = x.double().cpu().numpy()
+    oc = o.encode(xs, op)
+    q = synth.queries(nq, seed=5).numpy().astype(np.float64)
+    dq = torch.from_numpy(q.astype(np.float32)).to(DEV)
+    dcodes = _upload(o.pack(oc, op))
+    logits = torch.empty((nq, n), device=DEV)
+    ws = torch.empty(tq.score_workspace_bytes(p, 1, nq), dtype=torch.uint8, device=DEV)
+    tq.score(p, dq, dcodes, 1, nq, n, logits, ws)
+    out_idx = torch.empty((nq, 10), dtype=torch.int64, device=DEV)
+    sws = torch.empty(tq.search_workspace_bytes(p, nq, n, 10), dtype=torch.uint8, device=DEV)
+    tq.search(p, dq, dcodes, n, 10, out_idx, None, sws)
+    torch.cuda.synchronize()
+    qrows = np.arange(0, nq, nq // 64)
+    ref = o.score(q[qrows], oc, op, 1, len(qrows), n)
+    worst = check_logits(logits[torch.from_numpy(qrows).to(DEV)].cpu().numpy(), ref, q[qrows],
+                         oc["knorm"], 1, len(qrows), n, 128)
+    check_search(out_idx.cpu().numpy()[qrows], None, ref, q[qrows], oc["knorm"].astype(np.float64), 10)
+    print(f"[parity] sweep b={b}: score worst/tol={worst:.4f}, top-10 ok on {len(qrows)} queries", flush=True)

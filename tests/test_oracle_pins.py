@@ -71,7 +71,7 @@ def test_rotation_is_the_unique_positive_qr_factor(d):
 
 
 def test_rotation_preserves_norms_and_inner_products():
-    # "应用随机旋转矩阵 P（保持内积）" -- section 四 of "TurboQuant 与 AI 效率革命"
+    # The preconditioning rotation keeps inner products: "TurboQuant 与 AI 效率革命：当旧数学遇到新智能", section 四.
     pi = o.rotation(128, 2)
     rng = np.random.default_rng(0)
     x, y = rng.standard_normal((2, 50, 128))
@@ -92,8 +92,9 @@ def _coord_cdf(d, x):
 
 
 def test_rotated_coordinates_follow_the_beta_law():
-    # "一个单位向量经过随机旋转后，其每个坐标分量的数值都会收敛到一个已知的概率分布——Beta分布"
-    # ("谷歌TurboQuant如何绕过内存墙", 第一阶段).  Fixed x with heavy outliers, many seeds.
+    # After a random rotation each coordinate of a unit vector follows a fixed
+    # Beta law: "谷歌TurboQuant如何绕过内存墙？重新审视它的技术突破", 第一阶段.
+    # Fixed x with heavy outliers, many seeds.
     d = 32
     x = np.ones(d)
     x[:3] = 40.0
@@ -241,7 +242,8 @@ def test_measured_distortion_matches_analytic(b):
 
 
 def test_one_bit_inner_product_bias():
-    # "在1bit量化时，MSE最优量化器会给内积引入2/π≈0.637的乘性偏差" ("谷歌TurboQuant如何绕过内存墙", 第二阶段).
+    # A 1-bit MSE-optimal quantiser shrinks inner products by about 2/pi:
+    # "谷歌TurboQuant如何绕过内存墙？重新审视它的技术突破", 第二阶段.
     # With q = x, E<q, x~>/<q, x> = d c^2 exactly for the 1-bit codebook; -> 2/pi as d grows.
     d = 128
     p = _params(d=d, b=1, mode=o.MODE_MSE)
@@ -257,7 +259,8 @@ def test_one_bit_inner_product_bias():
 
 
 def test_qjl_estimator_is_unbiased_over_draws_of_S():
-    # "这个估计器是无偏的：E[Prod_QJL] = ⟨q, k⟩" ("TurboQuant 与 AI 效率革命", 三·非对称估计器)
+    # The asymmetric QJL estimator is unbiased: "TurboQuant 与 AI 效率革命：当旧数学遇到新智能",
+    # section 三, 非对称估计器.
     d = m = 32
     rng = np.random.default_rng(3)
     x = rng.standard_normal((1, d)) * 3
