@@ -43,6 +43,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-score", action="store_true")
     ap.add_argument("--no-attend", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling PMC byte counters)")
@@ -258,6 +259,53 @@ def main():
                              "ms": round(ms, 4), "GBps": round(gbps, 1),
                              "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_call": nb}
         del kc, vc
+
+    if not args.no_sweep:
+        # bit-width sweep: 65536 unit-direction x log-normal-norm float32 vectors, 1024 queries
+        sn, snq = 65536, 1024
+        sx = synth.sweep_keys(n=sn, seed=1, device=dev)
+        sq = synth.queries(snq, seed=5, device=dev)
+        true_ip = sq @ sx.T
+        qn = torch.linalg.vector_norm(sq, dim=1, keepdim=True)
+        xn = torch.linalg.vector_norm(sx, dim=1, keepdim=True).T
+        rows = []
+        for b in (1, 2, 3, 4):
+            pp = tq.Params(D, b, M, tq.MODE_PROD, 2, 3)
+            pm = tq.Params(D, b, M, tq.MODE_MSE, 2, 3)
+            cp = tq.alloc_codes(pp, sn, dev)
+            cm = tq.alloc_codes(pm, sn, dev)
+            lg = torch.empty((snq, sn), device=dev)
+            sws = torch.empty(tq.score_workspace_bytes(pp, 1, snq), dtype=torch.uint8, device=dev)
+            xr = torch.empty_like(sx)
+            tq.encode(pp, sx, cp)
+            tq.score(pp, sq, cp, 1, snq, sn, lg, sws)
+            torch.cuda.synchronize()
+            reps = 5
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            for _ in range(reps):
+                tq.encode(pp, sx, cp)
+            e[1].record(stream)
+            for _ in range(reps):
+                tq.score(pp, sq, cp, 1, snq, sn, lg, sws)
+            e[2].record(stream)
+            tq.encode(pm, sx, cm)
+            tq.decode(pm, cm, sn, xr)
+            torch.cuda.synchronize()
+            enc_ms = e[0].elapsed_time(e[1]) / reps
+            sc_ms = e[1].elapsed_time(e[2]) / reps
+            dist = (torch.sum((sx - xr) ** 2, dim=1) / torch.sum(sx * sx, dim=1)).mean().item()
+            err = (lg - true_ip) / (qn * xn)
+            rows.append({"b": b, "encode_ms": round(enc_ms, 4),
+                         "encode_mvectors_per_s": round(sn / (enc_ms * 1e-3) / 1e6, 1),
+                         "score_ms_1024q": round(sc_ms, 4),
+                         "score_glogits_per_s": round(snq * sn / (sc_ms * 1e-3) / 1e9, 1),
+                         "mse_distortion_mse_mode": round(dist, 6),
+                         "ip_bias_prod": round(err.mean().item(), 7),
+                         "ip_rmse_prod": round(err.pow(2).mean().sqrt().item(), 6)})
+            del cp, cm, lg, sws, xr
+        out["bit_width_sweep"] = {"workload": f"{sn} x d {D} float32 (unit direction x log-normal norm), "
+                                              f"{snq} N(0,1) queries, m={M}", "rows": rows}
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.b, args.cpu_sample_heads)
