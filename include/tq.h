@@ -27,10 +27,11 @@
  *     device) cache of the rotation, the JL matrix and the codebook, built on
  *     the first call that needs them and freed by tq_release_cache().  The
  *     hot-path calls allocate nothing; scratch comes in through `workspace`.
- *   - Sizes: d and m must be multiples of 128 in [128, 1024]; the device
- *     kernels of this version support d == m == 128 (other shapes return
- *     TQ_ERR_UNSUPPORTED).  b in [1, 5] (prod) or [1, 4] (mse) with the
- *     number of Lloyd-Max bits B <= 4.  n == 0 (or seq == 0) is a no-op.
+ *   - Sizes: d and m must be multiples of 128 in [128, 1024].  tq_encode,
+ *     tq_score and tq_search take every such shape; tq_attend and tq_decode
+ *     are built for d == 128 (and m == 128 for prod-mode keys) and return
+ *     TQ_ERR_UNSUPPORTED otherwise.  b in [1, 5] (prod) or [1, 4] (mse) with
+ *     the number of Lloyd-Max bits B <= 4.  n == 0 (or seq == 0) is a no-op.
  *   - Device pointers must be 16-byte aligned (TQ_ERR_ALIGNMENT otherwise).
  *   - Inputs must be finite (precondition, not checked).
  */
@@ -120,14 +121,22 @@ tq_status tq_codes_bytes(const tq_params *p, int64_t n, size_t out[4]);
  * Either pointer may be NULL.  Host only.                                  */
 tq_status tq_export_matrices(const tq_params *p, float *pi, float *s);
 
+/* Workspace bytes tq_encode needs for n vectors: 0 in mse mode and for
+ * d == m == 128; otherwise it holds the residual of up to 32768 vectors at a
+ * time, min(n rounded up to 128, 32768) * (4 d + 4 d / 128) bytes.
+ * Host only.                                                               */
+tq_status tq_encode_workspace_bytes(const tq_params *p, int64_t n, size_t *bytes);
+
 /* Online encode of n vectors ([P5] 第一阶段 + 第二阶段; [P3] 四):
  *   nu = ||x||, u = Pi x / nu, idx_i = #{j : u_i >= boundary_j},
  *   prod: r = x - nu Pi^T c[idx], sign bits of S r, rnorm = ||r||.
  * x: device, row-major [n][d], dtype TQ_F32 or TQ_BF16.  codes: device
- * arrays sized by tq_codes_bytes.  A zero vector encodes as idx = 2^(B-1),
- * all sign bits 1, both norms 0.                                           */
+ * arrays sized by tq_codes_bytes.  workspace: device, at least
+ * tq_encode_workspace_bytes(p, n) bytes (may be NULL when that is 0); its
+ * contents are scratch, nothing needs clearing.  A zero vector encodes as
+ * idx = 2^(B-1), all sign bits 1, both norms 0.                            */
 tq_status tq_encode(const tq_params *p, const void *x, int32_t dtype, int64_t n,
-                    tq_codes codes, void *stream);
+                    tq_codes codes, void *workspace, size_t ws_bytes, void *stream);
 
 /* Workspace bytes tq_score needs for n_kv*g queries.  Host only.           */
 tq_status tq_score_workspace_bytes(const tq_params *p, int64_t n_kv, int64_t g,

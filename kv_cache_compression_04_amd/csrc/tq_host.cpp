@@ -327,6 +327,32 @@ static void make_fragments(const std::vector<double> &mat, ColOf col_of,
         }
 }
 
+// Split an R x K row-major double matrix into the general-shape GEMM
+// fragments: uint4 [K/32 block kt][R/16 tile nt][hi, lo][lane], element e of
+// lane l = mat[16 nt + l % 16][col_of(kt, l / 16, e)].
+template <typename ColOf>
+static void make_gemm_fragments(const std::vector<double> &mat, int R, int K, ColOf col_of,
+                                std::vector<uint4> &out) {
+  const int NT = R / 16, KT = K / 32;
+  out.assign((size_t)KT * NT * 2 * 64, make_uint4(0, 0, 0, 0));
+  for (int kt = 0; kt < KT; ++kt)
+    for (int nt = 0; nt < NT; ++nt)
+      for (int l = 0; l < 64; ++l) {
+        uint16_t h[8], lo[8];
+        for (int e = 0; e < 8; ++e) {
+          const double v = mat[(size_t)(16 * nt + (l & 15)) * K + col_of(kt, l >> 4, e)];
+          h[e] = bf16_bits((float)v);
+          lo[e] = bf16_bits((float)(v - bf16_value(h[e])));
+        }
+        uint4 vh, vl;
+        std::memcpy(&vh, h, 16);
+        std::memcpy(&vl, lo, 16);
+        const size_t o = (((size_t)kt * NT + nt) * 2) * 64 + l;
+        out[o] = vh;
+        out[o + 64] = vl;
+      }
+}
+
 template <typename T>
 static tq_status upload(T **dst, const std::vector<T> &src) {
   TQ_HIP_CHECK(hipMalloc((void **)dst, src.size() * sizeof(T)));
@@ -351,25 +377,41 @@ static tq_status build_derived(const tq_params *p, int dev, Derived *D) {
     if ((st = upload(&D->s32, f))) return st;
     if ((st = upload(&D->s64, s))) return st;
   }
-  if (p->d == 128 && (!prod || p->m == 128)) {
+  // S' = S Pi^T (m x d): the second projection acts on the residual in the
+  // rotated domain, S r = S Pi^T (Pi r)
+  std::vector<double> sp;
+  if (prod) {
+    const int d = p->d, m = p->m;
+    sp.assign((size_t)m * d, 0.0);
+    for (int r = 0; r < m; ++r)
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < d; ++j) acc += s[(size_t)r * d + j] * pi[(size_t)c * d + j];
+        sp[(size_t)r * d + c] = acc;
+      }
+  }
+  if (is_d128(*p)) {
     std::vector<uint16_t> hi, lo;
     // GEMM 1 (Pi x): element e of lane group g in block kt is column 32 kt + 8 g + e
     make_fragments(pi, [](int kt, int g, int e) { return 32 * kt + 8 * g + e; }, hi, lo);
     if ((st = upload(&D->pi_hi, hi)) || (st = upload(&D->pi_lo, lo))) return st;
     if (prod) {
-      // S' = S Pi^T, consumed against the residual held in the layout of the
-      // first GEMM's output: element e of lane group g in block kt is
-      // coordinate 32 kt + 16 (e / 4) + 4 g + e % 4.
-      std::vector<double> sp((size_t)128 * 128, 0.0);
-      for (int r = 0; r < 128; ++r)
-        for (int c = 0; c < 128; ++c) {
-          double acc = 0.0;
-          for (int j = 0; j < 128; ++j) acc += s[(size_t)r * 128 + j] * pi[(size_t)c * 128 + j];
-          sp[(size_t)r * 128 + c] = acc;
-        }
+      // S' is consumed against the residual held in the layout of the first
+      // GEMM's output: element e of lane group g in block kt is coordinate
+      // 32 kt + 16 (e / 4) + 4 g + e % 4.
       make_fragments(sp, [](int kt, int g, int e) { return 32 * kt + 16 * (e / 4) + 4 * g + e % 4; },
                      hi, lo);
       if ((st = upload(&D->sp_hi, hi)) || (st = upload(&D->sp_lo, lo))) return st;
+    }
+  } else {
+    // same column maps, general shapes, K-block-major fragments
+    std::vector<uint4> fr;
+    make_gemm_fragments(pi, p->d, p->d, [](int kt, int g, int e) { return 32 * kt + 8 * g + e; }, fr);
+    if ((st = upload(&D->pi_frag, fr))) return st;
+    if (prod) {
+      make_gemm_fragments(sp, p->m, p->d,
+                          [](int kt, int g, int e) { return 32 * kt + 16 * (e / 4) + 4 * g + e % 4; }, fr);
+      if ((st = upload(&D->sp_frag, fr))) return st;
     }
   }
   return TQ_OK;
@@ -387,6 +429,8 @@ static void free_derived(Derived *D) {
   (void)hipFree(D->pi_lo);
   (void)hipFree(D->sp_hi);
   (void)hipFree(D->sp_lo);
+  (void)hipFree(D->pi_frag);
+  (void)hipFree(D->sp_frag);
   (void)hipSetDevice(cur);
   delete D;
 }
@@ -423,9 +467,6 @@ tq_status get_derived(const tq_params *p, const Derived **out) {
   return TQ_OK;
 }
 
-static bool kernels_support(const tq_params *p) {
-  return p->d == 128 && (p->mode == TQ_MODE_MSE || p->m == 128);
-}
 
 }  // namespace tq
 
@@ -519,8 +560,19 @@ static tq_status check_codes(const tq_params *p, const tq_codes &c) {
   return TQ_OK;
 }
 
+tq_status tq_encode_workspace_bytes(const tq_params *p, int64_t n, size_t *bytes) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (n < 0 || !bytes) {
+    set_error("tq_encode_workspace_bytes: n < 0 or NULL output");
+    return TQ_ERR_INVALID_ARG;
+  }
+  *bytes = encode_workspace_bytes(*p, n);
+  return TQ_OK;
+}
+
 tq_status tq_encode(const tq_params *p, const void *x, int32_t dtype, int64_t n,
-                    tq_codes codes, void *stream) {
+                    tq_codes codes, void *workspace, size_t ws_bytes, void *stream) {
   tq_status st = check_params(p);
   if (st) return st;
   if (n < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) {
@@ -533,17 +585,18 @@ tq_status tq_encode(const tq_params *p, const void *x, int32_t dtype, int64_t n,
     return TQ_ERR_INVALID_ARG;
   }
   if ((st = check_codes(p, codes))) return st;
-  if (!aligned16(x)) {
-    set_error("tq_encode: x must be 16-byte aligned");
+  if (!aligned16(x) || (workspace && !aligned16(workspace))) {
+    set_error("tq_encode: x and workspace must be 16-byte aligned");
     return TQ_ERR_ALIGNMENT;
   }
-  if (!kernels_support(p)) {
-    set_error("tq_encode: device kernels are built for d = m = 128 only");
-    return TQ_ERR_UNSUPPORTED;
+  const size_t need = encode_workspace_bytes(*p, n);
+  if (need > 0 && (!workspace || ws_bytes < need)) {
+    set_error("tq_encode: workspace too small (%zu < %zu)", workspace ? ws_bytes : (size_t)0, need);
+    return TQ_ERR_NO_MEMORY;
   }
   const Derived *D = nullptr;
   if ((st = get_derived(p, &D))) return st;
-  return launch_encode(*D, x, dtype, n, codes, (hipStream_t)stream);
+  return launch_encode(*D, x, dtype, n, codes, workspace, ws_bytes, (hipStream_t)stream);
 }
 
 tq_status tq_score_workspace_bytes(const tq_params *p, int64_t n_kv, int64_t g,
@@ -554,11 +607,7 @@ tq_status tq_score_workspace_bytes(const tq_params *p, int64_t n_kv, int64_t g,
     set_error("tq_score_workspace_bytes: bad n_kv/g/bytes");
     return TQ_ERR_INVALID_ARG;
   }
-  Derived D;
-  D.p = *p;
-  D.B = mse_bits(p);
-  D.cb.nparts = D.B == 0 ? 0 : (D.B == 1 ? 1 : D.B == 2 ? 2 : D.B == 3 ? 4 : 8);
-  *bytes = score_workspace_bytes(D, n_kv, g);
+  *bytes = score_workspace_bytes(*p, n_kv, g);
   return TQ_OK;
 }
 
@@ -581,17 +630,13 @@ tq_status tq_score(const tq_params *p, const float *q, int64_t n_kv, int64_t g,
     set_error("tq_score: pointers must be 16-byte aligned");
     return TQ_ERR_ALIGNMENT;
   }
-  if (!kernels_support(p)) {
-    set_error("tq_score: device kernels are built for d = m = 128 only");
-    return TQ_ERR_UNSUPPORTED;
+  if (ws_bytes < score_workspace_bytes(*p, n_kv, g)) {
+    set_error("tq_score: workspace too small (%zu < %zu)", ws_bytes,
+              score_workspace_bytes(*p, n_kv, g));
+    return TQ_ERR_NO_MEMORY;
   }
   const Derived *D = nullptr;
   if ((st = get_derived(p, &D))) return st;
-  if (ws_bytes < score_workspace_bytes(*D, n_kv, g)) {
-    set_error("tq_score: workspace too small (%zu < %zu)", ws_bytes,
-              score_workspace_bytes(*D, n_kv, g));
-    return TQ_ERR_NO_MEMORY;
-  }
   return launch_score(*D, q, n_kv, g, codes, seq, logits, workspace, (hipStream_t)stream);
 }
 
@@ -645,7 +690,7 @@ tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
     set_error("tq_attend: pointers must be 16-byte aligned");
     return TQ_ERR_ALIGNMENT;
   }
-  if (!kernels_support(kp) || !kernels_support(vp)) {
+  if (!is_d128(*kp) || !is_d128(*vp)) {
     set_error("tq_attend: device kernels are built for d = m = 128 only");
     return TQ_ERR_UNSUPPORTED;
   }

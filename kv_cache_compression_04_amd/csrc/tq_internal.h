@@ -39,7 +39,16 @@ struct Derived {
   uint16_t *pi_lo = nullptr;
   uint16_t *sp_hi = nullptr;   // bf16 fragments of S' = S Pi^T
   uint16_t *sp_lo = nullptr;
+  // General shapes (d, m multiples of 128 other than d = m = 128): GEMM
+  // fragments [K/32 block kt][16-row tile nt][hi, lo][lane] of uint4 (8 bf16).
+  uint4 *pi_frag = nullptr;    // Pi,  d x d
+  uint4 *sp_frag = nullptr;    // S',  m x d
 };
+
+// True when the d = m = 128 kernels serve these parameters.
+inline bool is_d128(const tq_params &p) {
+  return p.d == 128 && (p.mode == TQ_MODE_MSE || p.m == 128);
+}
 
 // Returns the cache entry for (p, current device), building it on first use.
 tq_status get_derived(const tq_params *p, const Derived **out);
@@ -47,9 +56,10 @@ tq_status get_derived(const tq_params *p, const Derived **out);
 void set_error(const char *fmt, ...);
 
 // Launchers (tq_kernels.hip).  Shapes are validated by the caller.
+size_t encode_workspace_bytes(const tq_params &p, int64_t n);
 tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n,
-                        tq_codes codes, hipStream_t stream);
-size_t score_workspace_bytes(const Derived &D, int64_t n_kv, int64_t g);
+                        tq_codes codes, void *ws, size_t ws_bytes, hipStream_t stream);
+size_t score_workspace_bytes(const tq_params &p, int64_t n_kv, int64_t g);
 tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g,
                        tq_codes codes, int64_t seq, float *logits, void *ws,
                        hipStream_t stream);

@@ -325,8 +325,8 @@ static int num_cus(int dev) {
   return cu;
 }
 
-tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n, tq_codes c,
-                        hipStream_t s) {
+static tq_status launch_encode128(const Derived &D, const void *x, int dtype, int64_t n, tq_codes c,
+                                  hipStream_t s) {
   const int64_t nbatch = (n + kEncBatch - 1) / kEncBatch;
   const int64_t need = (nbatch + kEncWaves - 1) / kEncWaves;
   // one workgroup per CU holds the 128 KB of prod-mode fragments; mse mode (64 KB) fits two
@@ -349,6 +349,417 @@ tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n, t
   }
   TQ_LAUNCH_CHECK();
   return TQ_OK;
+}
+
+// ===========================================================================
+// Encode, general shapes (d, m multiples of 128 up to 1024)
+// ===========================================================================
+// Two tiled GEMMs with fused epilogues, run over chunks of at most kGenChunk
+// vectors:
+//   1: Y^T = Pi X^T.  The epilogue bucketises, packs the index planes, forms
+//      the residual rho = y - ||x|| c[idx] and stores it as bf16 hi/lo pairs
+//      already in the second GEMM's operand layout, plus per-row-block
+//      partial sums of rho^2.
+//   2: Z^T = S' rho^T.  The epilogue packs the sign bits and finishes ||r||.
+// Workgroup tile: one 128-row block mt of the matrix x 128 vectors.  4 waves,
+// each owning 32 vectors (two 16-vector column tiles) of all 128 rows, so a
+// lane ends with whole 32-bit words of the packed layout (rows
+// 128 mt + 16 nt + 4 g + i, nt < 8, i < 4, are word 4 mt + g, bit 4 nt + i).
+// The matrix operand streams through LDS in 64-wide K stages (32 KB, double
+// buffered); the vector operand goes from global memory straight to
+// registers, one stage ahead.
+constexpr int kGW = 4;                      // waves per workgroup
+constexpr int kGCT = 2;                     // 16-vector column tiles per wave
+constexpr int kGVec = kGW * 16 * kGCT;      // vectors per workgroup tile (128)
+constexpr int kGKB = 2;                     // 32-wide K blocks per stage
+constexpr int kGStage = kGKB * 8 * 2 * 64;  // uint4 per stage (32 KB)
+constexpr int kGPer = kGStage / (kGW * 64); // uint4 per thread per stage
+constexpr int64_t kGenChunk = 32768;        // vectors per GEMM pair
+
+// Workgroup -> (vector tile, row block).  Workgroups are dispatched to the 8
+// XCDs round robin; give each XCD a contiguous range of tiles, row block
+// fastest, so the row blocks of one vector tile share that XCD's L2.
+__device__ __forceinline__ void gen_tile(int64_t T, int MT, int64_t &vt, int &mt) {
+  const int64_t bid = blockIdx.x;
+  const int64_t t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  vt = t / MT;
+  mt = (int)(t % MT);
+}
+
+// Copy one K stage of the matrix fragments (rows of block mt) to registers.
+__device__ __forceinline__ void gen_load_a(const uint4 *__restrict__ fbase, int NT, int stage,
+                                           int tid, uint4 (&r)[kGPer]) {
+#pragma unroll
+  for (int j = 0; j < kGPer; ++j) {
+    const int i = tid + j * kGW * 64;
+    const int ktl = i >> 10, rest = i & 1023;
+    r[j] = fbase[(size_t)(kGKB * stage + ktl) * NT * 128 + rest];
+  }
+}
+
+template <int B, bool PROD, bool XBF16>
+__global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
+    const void *__restrict__ x, int64_t n, int d, const uint4 *__restrict__ frag, Codebook cb,
+    uint32_t *__restrict__ idx_out, float *__restrict__ knorm_out, uint4 *__restrict__ rho,
+    float *__restrict__ rsq_part, int64_t stride) {
+  __shared__ uint4 As[2][kGStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vcol = lane & 15, g = lane >> 4;
+  const int MT = d >> 7, NT = d >> 4, KT = d >> 5, S = KT / kGKB;
+  const int64_t VT = (n + kGVec - 1) / kGVec;
+  int64_t vt;
+  int mt;
+  gen_tile(VT * MT, MT, vt, mt);
+  int64_t vrow[kGCT];
+  bool vok[kGCT];
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct) {
+    vrow[ct] = vt * kGVec + wave * (16 * kGCT) + 16 * ct + vcol;
+    vok[ct] = vrow[ct] < n;
+  }
+  const uint4 *fbase = frag + (size_t)8 * mt * 128;
+
+  // vector operand of one stage: lane (vcol, g) holds x[v][32 kt + 8 g .. + 7]
+  constexpr int XU = XBF16 ? 1 : 2;
+  uint4 xr[kGCT][kGKB][XU], xn[kGCT][kGKB][XU];
+  auto load_x = [&](int stage, uint4 (&r)[kGCT][kGKB][XU]) {
+#pragma unroll
+    for (int ct = 0; ct < kGCT; ++ct)
+#pragma unroll
+      for (int kb = 0; kb < kGKB; ++kb) {
+        const int col = 32 * (kGKB * stage + kb) + 8 * g;
+        if (XBF16) {
+          const uint4 *p = reinterpret_cast<const uint4 *>(
+              reinterpret_cast<const uint16_t *>(x) + vrow[ct] * d + col);
+          r[ct][kb][0] = vok[ct] ? p[0] : make_uint4(0, 0, 0, 0);
+        } else {
+          const uint4 *p = reinterpret_cast<const uint4 *>(
+              reinterpret_cast<const float *>(x) + vrow[ct] * d + col);
+          r[ct][kb][0] = vok[ct] ? p[0] : make_uint4(0, 0, 0, 0);
+          r[ct][kb][XU - 1] = vok[ct] ? p[XU - 1] : make_uint4(0, 0, 0, 0);
+        }
+      }
+  };
+
+  f32x4 acc[8][kGCT];
+  float ss[kGCT];
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct) {
+    ss[ct] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  uint4 ar[kGPer];
+  gen_load_a(fbase, NT, 0, tid, ar);
+  load_x(0, xr);
+#pragma unroll
+  for (int j = 0; j < kGPer; ++j) As[0][tid + j * kGW * 64] = ar[j];
+  __syncthreads();
+
+#pragma unroll 1
+  for (int st = 0; st < S; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < S) {
+      gen_load_a(fbase, NT, st + 1, tid, ar);
+      load_x(st + 1, xn);
+    }
+#pragma unroll
+    for (int kb = 0; kb < kGKB; ++kb) {
+      bf16x8 bh[kGCT], bl[kGCT];
+#pragma unroll
+      for (int ct = 0; ct < kGCT; ++ct) {
+        if (XBF16) {
+          const uint4 h = xr[ct][kb][0];
+          const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = bf16_to_f32(w[i] & 0xFFFFu), b = bf16_to_f32(w[i] >> 16);
+            ss[ct] += a * a + b * b;
+          }
+          bh[ct] = as_bf16x8(h);
+          bl[ct] = bh[ct];
+        } else {
+          const uint4 u0 = xr[ct][kb][0], u1 = xr[ct][kb][XU - 1];
+          const float v[8] = {__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z),
+                              __uint_as_float(u0.w), __uint_as_float(u1.x), __uint_as_float(u1.y),
+                              __uint_as_float(u1.z), __uint_as_float(u1.w)};
+          uint32_t h[4], l[4];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ss[ct] += v[i] * v[i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
+          bh[ct] = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+          bl[ct] = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const bf16x8 ah = as_bf16x8(As[cur][(kb * 8 + nt) * 128 + lane]);
+        const bf16x8 al = as_bf16x8(As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
+#pragma unroll
+        for (int ct = 0; ct < kGCT; ++ct) {
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[ct], acc[nt][ct], 0, 0, 0);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[ct], acc[nt][ct], 0, 0, 0);
+          if (!XBF16)
+            acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[ct], acc[nt][ct], 0, 0, 0);
+        }
+      }
+    }
+    if (st + 1 < S) {
+#pragma unroll
+      for (int j = 0; j < kGPer; ++j) As[cur ^ 1][tid + j * kGW * 64] = ar[j];
+#pragma unroll
+      for (int ct = 0; ct < kGCT; ++ct)
+#pragma unroll
+        for (int kb = 0; kb < kGKB; ++kb)
+#pragma unroll
+          for (int u = 0; u < XU; ++u) xr[ct][kb][u] = xn[ct][kb][u];
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: acc[nt][ct][i] = ||x|| u at row 128 mt + 16 nt + 4 g + i
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct) {
+    float s2 = ss[ct];
+    s2 += __shfl_xor(s2, 16);
+    s2 += __shfl_xor(s2, 32);
+    const float nu = sqrtf(s2);
+    float cs[1 << B], ts[(1 << B) > 1 ? (1 << B) - 1 : 1];
+#pragma unroll
+    for (int j = 0; j < (1 << B); ++j) cs[j] = cb.c[j] * nu;
+#pragma unroll
+    for (int j = 0; j + 1 < (1 << B); ++j) ts[j] = nu > 0.f ? cb.t[j] * nu : cb.t[j];
+    uint32_t planes[B > 0 ? B : 1];
+#pragma unroll
+    for (int p = 0; p < (B > 0 ? B : 1); ++p) planes[p] = 0u;
+    float rsq = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = acc[nt][ct][i];
+        float r = y;
+        if (B > 0) {
+          // thermometer code, parity bits shifted in (see the d = 128 kernel)
+          bool gj[(1 << B) > 1 ? (1 << B) - 1 : 1];
+          float c = cs[0];
+#pragma unroll
+          for (int j = 0; j < (1 << B) - 1; ++j) {
+            gj[j] = y >= ts[j];
+            c = gj[j] ? cs[j + 1] : c;
+          }
+#pragma unroll
+          for (int p = 0; p < B; ++p) {
+            bool bit = false;
+#pragma unroll
+            for (int j = (1 << p) - 1; j < (1 << B) - 1; j += (1 << p)) bit ^= gj[j];
+            planes[p] = planes[p] + planes[p] + (bit ? 1u : 0u);
+          }
+          r = y - c;
+        }
+        rsq = fmaf(r, r, rsq);
+        acc[nt][ct][i] = r;
+      }
+    const int64_t v = vrow[ct];
+    if (B > 0 && vok[ct]) {
+      uint32_t *dst = idx_out + (v * (d >> 5) + 4 * mt + g) * B;
+#pragma unroll
+      for (int p = 0; p < B; ++p) dst[p] = __builtin_bitreverse32(planes[p]);
+    }
+    if (mt == 0 && g == 0 && vok[ct]) knorm_out[v] = nu;
+    if (PROD) {
+      rsq += __shfl_xor(rsq, 16);
+      rsq += __shfl_xor(rsq, 32);
+      if (g == 0) rsq_part[v * MT + mt] = rsq;
+      // K block kt = 4 mt + kk of the second GEMM: element e of lane group g is
+      // coordinate 32 kt + 16 (e / 4) + 4 g + e % 4 = row tile 2 kk + e / 4, i = e % 4
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          split2(acc[2 * kk + hh][ct][0], acc[2 * kk + hh][ct][1], h[2 * hh], l[2 * hh]);
+          split2(acc[2 * kk + hh][ct][2], acc[2 * kk + hh][ct][3], h[2 * hh + 1], l[2 * hh + 1]);
+        }
+        uint4 *dst = rho + (((size_t)(4 * mt + kk) * stride + v) * 4 + g) * 2;
+        dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        dst[1] = make_uint4(l[0], l[1], l[2], l[3]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kGW * 64) void encode_gemm2_kernel(
+    const uint4 *__restrict__ rho, const float *__restrict__ rsq_part, int64_t n, int64_t stride,
+    int d, int m, const uint4 *__restrict__ frag, uint32_t *__restrict__ sgn_out,
+    float *__restrict__ rnorm_out) {
+  __shared__ uint4 As[2][kGStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vcol = lane & 15, g = lane >> 4;
+  const int MT = m >> 7, NT = m >> 4, KT = d >> 5, S = KT / kGKB;
+  const int64_t VT = (n + kGVec - 1) / kGVec;
+  int64_t vt;
+  int mt;
+  gen_tile(VT * MT, MT, vt, mt);
+  int64_t vrow[kGCT];
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct) vrow[ct] = vt * kGVec + wave * (16 * kGCT) + 16 * ct + vcol;
+  const uint4 *fbase = frag + (size_t)8 * mt * 128;
+
+  // residual operand of one stage (written for every vector of the padded tile)
+  uint4 xr[kGCT][kGKB][2], xn[kGCT][kGKB][2];
+  auto load_r = [&](int stage, uint4 (&r)[kGCT][kGKB][2]) {
+#pragma unroll
+    for (int ct = 0; ct < kGCT; ++ct)
+#pragma unroll
+      for (int kb = 0; kb < kGKB; ++kb) {
+        const uint4 *p = rho + (((size_t)(kGKB * stage + kb) * stride + vrow[ct]) * 4 + g) * 2;
+        r[ct][kb][0] = p[0];
+        r[ct][kb][1] = p[1];
+      }
+  };
+
+  f32x4 acc[8][kGCT];
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 ar[kGPer];
+  gen_load_a(fbase, NT, 0, tid, ar);
+  load_r(0, xr);
+#pragma unroll
+  for (int j = 0; j < kGPer; ++j) As[0][tid + j * kGW * 64] = ar[j];
+  __syncthreads();
+
+#pragma unroll 1
+  for (int st = 0; st < S; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < S) {
+      gen_load_a(fbase, NT, st + 1, tid, ar);
+      load_r(st + 1, xn);
+    }
+#pragma unroll
+    for (int kb = 0; kb < kGKB; ++kb) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const bf16x8 ah = as_bf16x8(As[cur][(kb * 8 + nt) * 128 + lane]);
+        const bf16x8 al = as_bf16x8(As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
+#pragma unroll
+        for (int ct = 0; ct < kGCT; ++ct) {
+          const bf16x8 bh = as_bf16x8(xr[ct][kb][0]), bl = as_bf16x8(xr[ct][kb][1]);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[nt][ct], 0, 0, 0);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[nt][ct], 0, 0, 0);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[nt][ct], 0, 0, 0);
+        }
+      }
+    }
+    if (st + 1 < S) {
+#pragma unroll
+      for (int j = 0; j < kGPer; ++j) As[cur ^ 1][tid + j * kGW * 64] = ar[j];
+#pragma unroll
+      for (int ct = 0; ct < kGCT; ++ct)
+#pragma unroll
+        for (int kb = 0; kb < kGKB; ++kb) {
+          xr[ct][kb][0] = xn[ct][kb][0];
+          xr[ct][kb][1] = xn[ct][kb][1];
+        }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: sign bit of z at row 128 mt + 16 nt + 4 g + i -> word 4 mt + g, bit 4 nt + i
+  const int QT = d >> 7;
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct) {
+    const int64_t v = vrow[ct];
+    if (v >= n) continue;
+    uint32_t w = 0;
+#pragma unroll
+    for (int nt = 7; nt >= 0; --nt)
+#pragma unroll
+      for (int i = 3; i >= 0; --i) w = w + w + (acc[nt][ct][i] >= 0.f ? 1u : 0u);
+    sgn_out[v * (m >> 5) + 4 * mt + g] = w;
+    if (mt == 0 && g == 0) {
+      float r2 = 0.f;
+      for (int j = 0; j < QT; ++j) r2 += rsq_part[v * QT + j];
+      rnorm_out[v] = sqrtf(r2);
+    }
+  }
+}
+
+size_t encode_workspace_bytes(const tq_params &p, int64_t n) {
+  if (is_d128(p) || p.mode != TQ_MODE_PROD || n <= 0) return 0;
+  const int64_t nc = std::min<int64_t>((n + kGVec - 1) / kGVec * kGVec, kGenChunk);
+  return (size_t)nc * (4 * (size_t)p.d + 4 * (size_t)(p.d / 128));
+}
+
+template <int B, bool PROD>
+static void launch_gemm1_t(const Derived &D, const void *x, int dtype, int64_t n, tq_codes c,
+                           uint4 *rho, float *rsq, int64_t stride, hipStream_t s) {
+  const int64_t grid = (n + kGVec - 1) / kGVec * (D.p.d / 128);
+  if (dtype == TQ_BF16)
+    encode_gemm1_kernel<B, PROD, true><<<dim3((unsigned)grid), dim3(kGW * 64), 0, s>>>(
+        x, n, D.p.d, D.pi_frag, D.cb, c.idx, c.knorm, rho, rsq, stride);
+  else
+    encode_gemm1_kernel<B, PROD, false><<<dim3((unsigned)grid), dim3(kGW * 64), 0, s>>>(
+        x, n, D.p.d, D.pi_frag, D.cb, c.idx, c.knorm, rho, rsq, stride);
+}
+
+static tq_status launch_encode_general(const Derived &D, const void *x, int dtype, int64_t n,
+                                       tq_codes c, void *ws, hipStream_t s) {
+  const bool prod = D.p.mode == TQ_MODE_PROD;
+  const int d = D.p.d, m = D.p.m, B = D.B;
+  const size_t esz = dtype == TQ_BF16 ? 2 : 4;
+  // mse mode needs no workspace: one launch over all vectors
+  const int64_t chunk = prod ? std::min<int64_t>((n + kGVec - 1) / kGVec * kGVec, kGenChunk) : n;
+  uint4 *rho = (uint4 *)ws;
+  float *rsq = prod ? (float *)((char *)ws + (size_t)chunk * 4 * d) : nullptr;
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    const int64_t nc = std::min<int64_t>(chunk, n - c0);
+    const void *xc = (const char *)x + (size_t)c0 * d * esz;
+    tq_codes cc;
+    cc.idx = B > 0 ? c.idx + (size_t)c0 * (d / 32) * B : nullptr;
+    cc.sgn = prod ? c.sgn + (size_t)c0 * (m / 32) : nullptr;
+    cc.knorm = c.knorm + c0;
+    cc.rnorm = prod ? c.rnorm + c0 : nullptr;
+    switch (B * 2 + (prod ? 1 : 0)) {
+      case 0 * 2 + 1: launch_gemm1_t<0, true>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      case 1 * 2 + 1: launch_gemm1_t<1, true>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      case 2 * 2 + 1: launch_gemm1_t<2, true>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      case 3 * 2 + 1: launch_gemm1_t<3, true>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      case 4 * 2 + 1: launch_gemm1_t<4, true>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      case 1 * 2 + 0: launch_gemm1_t<1, false>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      case 2 * 2 + 0: launch_gemm1_t<2, false>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      case 3 * 2 + 0: launch_gemm1_t<3, false>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      case 4 * 2 + 0: launch_gemm1_t<4, false>(D, xc, dtype, nc, cc, rho, rsq, chunk, s); break;
+      default:
+        set_error("tq_encode: unsupported B = %d", B);
+        return TQ_ERR_UNSUPPORTED;
+    }
+    TQ_LAUNCH_CHECK();
+    if (prod) {
+      const int64_t grid = (nc + kGVec - 1) / kGVec * (m / 128);
+      encode_gemm2_kernel<<<dim3((unsigned)grid), dim3(kGW * 64), 0, s>>>(
+          rho, rsq, nc, chunk, d, m, D.sp_frag, cc.sgn, cc.rnorm);
+      TQ_LAUNCH_CHECK();
+    }
+  }
+  return TQ_OK;
+}
+
+tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n, tq_codes c,
+                        void *ws, size_t ws_bytes, hipStream_t s) {
+  if (is_d128(D.p)) return launch_encode128(D, x, dtype, n, c, s);
+  if (ws_bytes < encode_workspace_bytes(D.p, n)) {
+    set_error("tq_encode: workspace too small");
+    return TQ_ERR_NO_MEMORY;
+  }
+  if (D.p.mode == TQ_MODE_MSE && (n + kGVec - 1) / kGVec * (D.p.d / 128) > 0x7fffffffLL) {
+    set_error("tq_encode: too many vectors for one launch");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  return launch_encode_general(D, x, dtype, n, c, ws, s);
 }
 
 // ===========================================================================
@@ -627,9 +1038,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
 
 static int nparts_of(int B) { return B == 0 ? 0 : (B == 1 ? 1 : B == 2 ? 2 : B == 3 ? 4 : 8); }
 
-size_t score_workspace_bytes(const Derived &D, int64_t n_kv, int64_t g) {
+static size_t score128_workspace_bytes(int B, bool prod, int64_t n_kv, int64_t g) {
   const int64_t ngroups = (g + 3) / 4;
-  const int NMF = score_mfmas(nparts_of(D.B), D.p.mode == TQ_MODE_PROD);
+  const int NMF = score_mfmas(nparts_of(B), prod);
   return (size_t)n_kv * ngroups * ((size_t)NMF * 64 * sizeof(i32x4) + 4 * sizeof(QConst));
 }
 
@@ -655,8 +1066,8 @@ static void launch_score_t(const Derived &D, const float *q, int64_t n_kv, int64
                                                              logits);
 }
 
-tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g, tq_codes c,
-                       int64_t seq, float *logits, void *ws, hipStream_t s) {
+static tq_status launch_score128(const Derived &D, const float *q, int64_t n_kv, int64_t g,
+                                 tq_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
   if ((uint64_t)n_kv * ((g + 3) / 4) > 65535u) {
     set_error("tq_score: n_kv * ceil(g/4) = %lld exceeds 65535", (long long)(n_kv * ((g + 3) / 4)));
     return TQ_ERR_UNSUPPORTED;
@@ -678,6 +1089,378 @@ tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g
   }
   TQ_LAUNCH_CHECK();
   return TQ_OK;
+}
+
+// ===========================================================================
+// Score, many queries and general shapes (d, m multiples of 128 up to 1024)
+// ===========================================================================
+// The same integer formulation as the d = 128 kernel, tiled for reuse: a
+// workgroup scores kSMCodes codes against 16 queries (kSMQB groups of 4).
+// The K dimension is walked in chunks of 128 coordinates; in chunk q, lane
+// group kg of a code holds word Qd kg + q of each index plane (and word
+// Md kg + q of the sign bits), so a lane's words for all chunks are one
+// contiguous run that it loads once.  The query operands of one chunk (all
+// parts, all 4 groups) are staged in LDS, double buffered; every bit slice a
+// wave builds from its codes feeds 4 query groups.
+constexpr int kSMWaves = 8;
+constexpr int kSMCT = 2;                          // 16-code tiles per wave
+constexpr int kSMCodes = kSMWaves * kSMCT * 16;  // codes per workgroup (256)
+constexpr int kSMQB = 4;                          // 4-query groups per workgroup
+constexpr int kSMGroup = 8;                       // query blocks per L2 group
+constexpr int kQPThreads = 256;
+constexpr int kMaxChunks = 8;                     // 1024 / 128
+
+__host__ __device__ constexpr int sm_nj(int np, bool prod) { return 2 * np + (prod ? 2 : 0); }
+
+// Query preparation for one group of 4 queries: qt = Pi q and qs = S q with
+// float64 sums, then the int8 operands of every chunk (layout
+// [head][query block][chunk][group][operand j][lane]) and the per-query
+// constants.  Operand j < 2 NP is part j / 2, half j % 2; the last two are
+// the sign part.  Lane l (row 4 jq + t: query jq, limb t; lane group kg),
+// dword w, byte e multiplies bit 8 e + sl (sl = 4 (j % 2) + w) of word
+// W = Qd kg + q, i.e. coordinate 128 (W / 4) + 32 e + 16 (sl / 4) + 4 (W % 4) + sl % 4.
+template <bool PROD>
+__global__ __launch_bounds__(kQPThreads) void qprep_many_kernel(
+    const float *__restrict__ q, int64_t g, int nqb, int d, int m, const float *__restrict__ pi,
+    const float *__restrict__ s, Codebook cb, i32x4 *__restrict__ aops, QConst *__restrict__ qc) {
+  __shared__ double qin[4][1024];
+  __shared__ double qv[2][4][1024];  // [0] = Pi q, [1] = S q
+  __shared__ int expo[4][2];
+  const int64_t gid = blockIdx.x;
+  const int qb = (int)(gid & 3);
+  const int64_t hq = gid >> 2;  // head * nqb + query block
+  const int64_t head = hq / nqb;
+  const int qblk = (int)(hq % nqb);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Qd = d >> 7, Md = PROD ? m >> 7 : 0, NCH = Qd > Md ? Qd : Md;
+  const int NP = cb.nparts, NJ = sm_nj(NP, PROD);
+  for (int i = tid; i < 4 * d; i += kQPThreads) {
+    const int jq = i / d, c = i - jq * d;
+    const int64_t qi = ((int64_t)qblk * kSMQB + qb) * 4 + jq;
+    qin[jq][c] = qi < g ? (double)q[(head * g + qi) * d + c] : 0.0;
+  }
+  __syncthreads();
+  const int rows = d + (PROD ? m : 0);
+  for (int r = wave; r < rows; r += kQPThreads / 64) {
+    const float *row = r < d ? pi + (size_t)r * d : s + (size_t)(r - d) * d;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    for (int j = lane; j < d; j += 64) {
+      const double w = (double)row[j];
+      a0 = fma(w, qin[0][j], a0);
+      a1 = fma(w, qin[1][j], a1);
+      a2 = fma(w, qin[2][j], a2);
+      a3 = fma(w, qin[3][j], a3);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      a0 += __shfl_xor(a0, off);
+      a1 += __shfl_xor(a1, off);
+      a2 += __shfl_xor(a2, off);
+      a3 += __shfl_xor(a3, off);
+    }
+    if (lane == 0) {
+      double *dst = r < d ? &qv[0][0][r] : &qv[1][0][r - d];
+      dst[0] = a0;
+      dst[1024] = a1;
+      dst[2048] = a2;
+      dst[3072] = a3;
+    }
+  }
+  __syncthreads();
+  {
+    // wave jq: max |qt|, max |qs|, sum qt, sum qs of query jq
+    const int jq = wave;
+    double mq = 0.0, ms = 0.0, sq = 0.0, ss = 0.0;
+    for (int c = lane; c < d; c += 64) {
+      mq = fmax(mq, fabs(qv[0][jq][c]));
+      sq += qv[0][jq][c];
+    }
+    if (PROD)
+      for (int c = lane; c < m; c += 64) {
+        ms = fmax(ms, fabs(qv[1][jq][c]));
+        ss += qv[1][jq][c];
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mq = fmax(mq, __shfl_xor(mq, off));
+      ms = fmax(ms, __shfl_xor(ms, off));
+      sq += __shfl_xor(sq, off);
+      ss += __shfl_xor(ss, off);
+    }
+    if (lane == 0) {
+      double acoef = 0, amax = 0;
+      for (int p = 0; p < NP; ++p) {
+        acoef += cb.coef[p];
+        amax = fmax(amax, fabs(cb.coef[p]));
+      }
+      int e1 = 0, e2 = 0, k;
+      const double A1 = 2.0 * amax * mq, A2 = 2.0 * ms;
+      if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
+      if (A2 > 0) { frexp(A2, &k); e2 = 26 - k; }
+      expo[jq][0] = e1;
+      expo[jq][1] = e2;
+      const double cq = PROD ? sqrt(M_PI / 2.0) / m : 0.0;
+      QConst o;
+      o.idx_scale = ldexp(1.0, -e1);
+      o.idx_bias = acoef * sq;
+      o.sgn_scale = cq * ldexp(1.0, -e2);
+      o.sgn_bias = cq * ss;
+      qc[hq * 16 + qb * 4 + jq] = o;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < NCH * NJ * 64; i += kQPThreads) {
+    const int l = i & 63, jl = i >> 6;
+    const int j = jl % NJ, qq = jl / NJ;
+    const int row = l & 15, kg = l >> 4, jq = row >> 2, t = row & 3;
+    const bool sgnpart = j >= 2 * NP;
+    const int h2 = j & 1;
+    const int nchunk = sgnpart ? Md : Qd;
+    int out[4] = {0, 0, 0, 0};
+    if (qq < nchunk) {
+      const double coef = sgnpart ? 2.0 : 2.0 * cb.coef[j >> 1];
+      const int E = expo[jq][sgnpart ? 1 : 0];
+      const double *src = qv[sgnpart ? 1 : 0][jq];
+      const int W = nchunk * kg + qq, qp = W >> 2, kp = W & 3;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t packed = 0;
+        const int sl = 4 * h2 + w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 128 * qp + 32 * e + 16 * (sl >> 2) + 4 * kp + (sl & 3);
+          const int Q = (int)llrint(ldexp(coef * src[c], E - (sl & 1)));
+          packed |= (uint32_t)(uint8_t)(int8_t)limb_of(Q, t) << (8 * e);
+        }
+        out[w] = (int)packed;
+      }
+    }
+    aops[(((size_t)hq * NCH + qq) * kSMQB + qb) * NJ * 64 + (size_t)j * 64 + l] =
+        i32x4{out[0], out[1], out[2], out[3]};
+  }
+}
+
+// Load n dwords (n <= N, n a runtime count) that start at a multiple of n
+// dwords: vector loads when n is a multiple of 4, dword loads otherwise.
+template <int N>
+__device__ __forceinline__ void load_run(const uint32_t *__restrict__ p, int n, uint32_t (&r)[N]) {
+  if ((n & 3) == 0) {
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j)
+      if (4 * j < n) {
+        const uint4 u = reinterpret_cast<const uint4 *>(p)[j];
+        r[4 * j] = u.x; r[4 * j + 1] = u.y; r[4 * j + 2] = u.z; r[4 * j + 3] = u.w;
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (j < n) r[j] = p[j];
+  }
+}
+
+template <int B, bool PROD>
+__global__ __launch_bounds__(kSMWaves * 64) void score_many_kernel(
+    const i32x4 *__restrict__ aops, const QConst *__restrict__ qc,
+    const uint32_t *__restrict__ idx, const uint32_t *__restrict__ sgn,
+    const float *__restrict__ knorm, const float *__restrict__ rnorm, int64_t seq, int64_t g,
+    int nqb, int Qd, int Md, Codebook cb, float *__restrict__ logits) {
+  constexpr int NP = B == 0 ? 0 : (B == 1 ? 1 : B == 2 ? 2 : B == 3 ? 4 : 8);
+  constexpr int NJ = sm_nj(NP, PROD);
+  constexpr int BB = B > 0 ? B : 1;
+  constexpr int kStage = kSMQB * NJ * 64;            // i32x4 per chunk
+  constexpr int kPer = kStage / (kSMWaves * 64);     // = NJ / 2
+  __shared__ i32x4 As[2][kStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kc = lane & 15, kg = lane >> 4;
+  const int64_t head = blockIdx.y;
+  // tile -> (query block, code block): XCD-contiguous ranges, then groups of
+  // kSMGroup query blocks walked query block fastest, so a window of tiles
+  // shares both its codes and its query operands in L2
+  const int64_t ncb = (seq + kSMCodes - 1) / kSMCodes;
+  const int64_t T = (int64_t)nqb * ncb;
+  const int64_t bid = blockIdx.x;
+  const int64_t t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  const int64_t grp = t / ((int64_t)kSMGroup * ncb);
+  const int64_t first = grp * kSMGroup;
+  const int64_t gsz = (nqb - first) < kSMGroup ? (nqb - first) : kSMGroup;
+  const int64_t within = t - grp * kSMGroup * ncb;
+  const int qblk = (int)(first + within % gsz);
+  const int64_t cblk = within / gsz;
+  const int NCH = Qd > Md ? Qd : Md;
+  const i32x4 *ablk = aops + (size_t)(head * nqb + qblk) * NCH * kStage;
+
+  // this lane's codes: all their words, loaded once
+  const int D32 = 4 * Qd, M32 = 4 * Md;
+  const uint32_t *idx_h = idx + (size_t)head * seq * D32 * BB;
+  int64_t vpos[kSMCT], vcl[kSMCT];
+  uint32_t wi[kSMCT][kMaxChunks * BB], wsg[kSMCT][kMaxChunks];
+#pragma unroll
+  for (int ct = 0; ct < kSMCT; ++ct) {
+    vpos[ct] = cblk * kSMCodes + wave * (16 * kSMCT) + 16 * ct + kc;
+    vcl[ct] = vpos[ct] < seq ? vpos[ct] : seq - 1;
+    if (B > 0) load_run(idx_h + ((size_t)vcl[ct] * D32 + (size_t)Qd * kg) * BB, Qd * BB, wi[ct]);
+    if (PROD)
+      load_run(sgn + (size_t)head * seq * M32 + (size_t)vcl[ct] * M32 + (size_t)Md * kg, Md, wsg[ct]);
+  }
+
+  i32x4 acc_i[kSMCT][kSMQB], acc_s[kSMCT][kSMQB];
+#pragma unroll
+  for (int ct = 0; ct < kSMCT; ++ct)
+#pragma unroll
+    for (int qb = 0; qb < kSMQB; ++qb) {
+      acc_i[ct][qb] = i32x4{0, 0, 0, 0};
+      acc_s[ct][qb] = i32x4{0, 0, 0, 0};
+    }
+  i32x4 ar[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) ar[j] = ablk[tid + j * kSMWaves * 64];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) As[0][tid + j * kSMWaves * 64] = ar[j];
+  __syncthreads();
+
+#pragma unroll
+  for (int q = 0; q < kMaxChunks; ++q) {
+    if (q < NCH) {
+      const int cur = q & 1;
+      if (q + 1 < NCH) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) ar[j] = ablk[(size_t)(q + 1) * kStage + tid + j * kSMWaves * 64];
+      }
+      if (NP > 0 && q < Qd) {
+#pragma unroll
+        for (int sp = 0; sp < NP; ++sp) {
+          i32x4 lo4[kSMCT], hi4[kSMCT];
+#pragma unroll
+          for (int ct = 0; ct < kSMCT; ++ct) {
+            uint32_t part = 0;
+#pragma unroll
+            for (int p = 0; p < BB; ++p)
+              if (cb.part_mask[sp] >> p & 1) part ^= wi[ct][q * BB + p];
+            bit_slices(part, lo4[ct], hi4[ct]);
+          }
+#pragma unroll
+          for (int qb = 0; qb < kSMQB; ++qb) {
+            const i32x4 a0 = As[cur][(qb * NJ + 2 * sp) * 64 + lane];
+            const i32x4 a1 = As[cur][(qb * NJ + 2 * sp + 1) * 64 + lane];
+#pragma unroll
+            for (int ct = 0; ct < kSMCT; ++ct) {
+              acc_i[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo4[ct], acc_i[ct][qb], 0, 0, 0);
+              acc_i[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi4[ct], acc_i[ct][qb], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (PROD && q < Md) {
+        i32x4 lo4[kSMCT], hi4[kSMCT];
+#pragma unroll
+        for (int ct = 0; ct < kSMCT; ++ct) bit_slices(wsg[ct][q], lo4[ct], hi4[ct]);
+#pragma unroll
+        for (int qb = 0; qb < kSMQB; ++qb) {
+          const i32x4 a0 = As[cur][(qb * NJ + 2 * NP) * 64 + lane];
+          const i32x4 a1 = As[cur][(qb * NJ + 2 * NP + 1) * 64 + lane];
+#pragma unroll
+          for (int ct = 0; ct < kSMCT; ++ct) {
+            acc_s[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo4[ct], acc_s[ct][qb], 0, 0, 0);
+            acc_s[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi4[ct], acc_s[ct][qb], 0, 0, 0);
+          }
+        }
+      }
+      if (q + 1 < NCH) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) As[cur ^ 1][tid + j * kSMWaves * 64] = ar[j];
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane (kc, kg) of tile (ct, qb) = query 4 (4 qblk + qb) + kg, code vpos[ct]
+  const float *kn_h = knorm + head * seq;
+  const float *rn_h = PROD ? rnorm + head * seq : nullptr;
+#pragma unroll
+  for (int qb = 0; qb < kSMQB; ++qb) {
+    const int64_t qi = ((int64_t)qblk * kSMQB + qb) * 4 + kg;
+    const QConst cst = qc[(head * nqb + qblk) * 16 + qb * 4 + kg];
+#pragma unroll
+    for (int ct = 0; ct < kSMCT; ++ct) {
+      double l = 0.0;
+      if (NP > 0) {
+        const i32x4 a = acc_i[ct][qb];
+        const double vi = (double)a[0] + 128.0 * (double)a[1] + 16384.0 * (double)a[2] +
+                          2097152.0 * (double)a[3];
+        l += (double)kn_h[vcl[ct]] * (vi * cst.idx_scale - cst.idx_bias);
+      }
+      if (PROD) {
+        const i32x4 a = acc_s[ct][qb];
+        const double vs = (double)a[0] + 128.0 * (double)a[1] + 16384.0 * (double)a[2] +
+                          2097152.0 * (double)a[3];
+        l += (double)rn_h[vcl[ct]] * (vs * cst.sgn_scale - cst.sgn_bias);
+      }
+      if (qi < g && vpos[ct] < seq) logits[((size_t)head * g + qi) * seq + vpos[ct]] = (float)l;
+    }
+  }
+}
+
+static size_t score_many_aops_bytes(int B, bool prod, int d, int m, int64_t n_kv, int64_t g) {
+  const int64_t nqb = (g + 4 * kSMQB - 1) / (4 * kSMQB);
+  const int Qd = d / 128, Md = prod ? m / 128 : 0, NCH = Qd > Md ? Qd : Md;
+  const size_t a = (size_t)n_kv * nqb * NCH * kSMQB * sm_nj(nparts_of(B), prod) * 64 * sizeof(i32x4);
+  return (a + 255) & ~(size_t)255;
+}
+
+size_t score_workspace_bytes(const tq_params &p, int64_t n_kv, int64_t g) {
+  const bool prod = p.mode == TQ_MODE_PROD;
+  const int B = prod ? p.b - 1 : p.b;
+  if (is_d128(p)) return score128_workspace_bytes(B, prod, n_kv, g);
+  const int64_t nqb = (g + 4 * kSMQB - 1) / (4 * kSMQB);
+  return score_many_aops_bytes(B, prod, p.d, p.m, n_kv, g) +
+         (size_t)n_kv * nqb * 4 * kSMQB * sizeof(QConst);
+}
+
+template <int B, bool PROD>
+static void launch_score_many_t(const Derived &D, const float *q, int64_t n_kv, int64_t g,
+                                tq_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
+  const int nqb = (int)((g + 4 * kSMQB - 1) / (4 * kSMQB));
+  i32x4 *aops = (i32x4 *)ws;
+  QConst *qc = (QConst *)((char *)ws + score_many_aops_bytes(B, PROD, D.p.d, D.p.m, n_kv, g));
+  qprep_many_kernel<PROD><<<dim3((unsigned)(n_kv * nqb * kSMQB)), dim3(kQPThreads), 0, s>>>(
+      q, g, nqb, D.p.d, D.p.m, D.pi32, D.s32, D.cb, aops, qc);
+  const int64_t ncb = (seq + kSMCodes - 1) / kSMCodes;
+  score_many_kernel<B, PROD><<<dim3((unsigned)(nqb * ncb), (unsigned)n_kv), dim3(kSMWaves * 64), 0, s>>>(
+      aops, qc, c.idx, c.sgn, c.knorm, c.rnorm, seq, g, nqb, D.p.d / 128, PROD ? D.p.m / 128 : 0, D.cb,
+      logits);
+}
+
+static tq_status launch_score_many(const Derived &D, const float *q, int64_t n_kv, int64_t g,
+                                   tq_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
+  const int64_t nqb = (g + 4 * kSMQB - 1) / (4 * kSMQB);
+  const int64_t ncb = (seq + kSMCodes - 1) / kSMCodes;
+  if (n_kv > 65535 || nqb * ncb > 0x7fffffffLL || n_kv * nqb * kSMQB > 0x7fffffffLL) {
+    set_error("tq_score: problem too large for one launch");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const bool prod = D.p.mode == TQ_MODE_PROD;
+  switch (D.B * 2 + (prod ? 1 : 0)) {
+    case 0 * 2 + 1: launch_score_many_t<0, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    case 1 * 2 + 1: launch_score_many_t<1, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    case 2 * 2 + 1: launch_score_many_t<2, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    case 3 * 2 + 1: launch_score_many_t<3, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    case 4 * 2 + 1: launch_score_many_t<4, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    case 1 * 2 + 0: launch_score_many_t<1, false>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    case 2 * 2 + 0: launch_score_many_t<2, false>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    case 3 * 2 + 0: launch_score_many_t<3, false>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    case 4 * 2 + 0: launch_score_many_t<4, false>(D, q, n_kv, g, c, seq, logits, ws, s); break;
+    default:
+      set_error("tq_score: unsupported B = %d", D.B);
+      return TQ_ERR_UNSUPPORTED;
+  }
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g, tq_codes c,
+                       int64_t seq, float *logits, void *ws, hipStream_t s) {
+  if (is_d128(D.p)) return launch_score128(D, q, n_kv, g, c, seq, logits, ws, s);
+  return launch_score_many(D, q, n_kv, g, c, seq, logits, ws, s);
 }
 
 // ===========================================================================

@@ -42,7 +42,8 @@ class _Codes(ctypes.Structure):
 
 
 EXPORTS = ["tq_status_string", "tq_last_error", "tq_layout_version", "tq_make_codebook",
-           "tq_codes_bytes", "tq_export_matrices", "tq_encode", "tq_score_workspace_bytes",
+           "tq_codes_bytes", "tq_export_matrices", "tq_encode_workspace_bytes", "tq_encode",
+           "tq_score_workspace_bytes",
            "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_decode",
            "tq_search_workspace_bytes", "tq_search", "tq_release_cache"]
 
@@ -66,7 +67,8 @@ def lib():
             "tq_make_codebook": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]),
             "tq_codes_bytes": (ctypes.c_int, [P, i64, ctypes.POINTER(sz)]),
             "tq_export_matrices": (ctypes.c_int, [P, vp, vp]),
-            "tq_encode": (ctypes.c_int, [P, vp, ctypes.c_int32, i64, C, vp]),
+            "tq_encode_workspace_bytes": (ctypes.c_int, [P, i64, ctypes.POINTER(sz)]),
+            "tq_encode": (ctypes.c_int, [P, vp, ctypes.c_int32, i64, C, vp, sz, vp]),
             "tq_score_workspace_bytes": (ctypes.c_int, [P, i64, i64, ctypes.POINTER(sz)]),
             "tq_score": (ctypes.c_int, [P, vp, i64, i64, C, i64, vp, vp, sz, vp]),
             "tq_attend_workspace_bytes": (ctypes.c_int, [P, P, i64, i64, i64, i64, ctypes.POINTER(sz)]),
@@ -143,6 +145,12 @@ def export_matrices(p: Params):
     return pi, s
 
 
+def encode_workspace_bytes(p: Params, n: int) -> int:
+    out = ctypes.c_size_t()
+    _check("tq_encode_workspace_bytes", lib().tq_encode_workspace_bytes(ctypes.byref(p.c()), n, ctypes.byref(out)))
+    return out.value
+
+
 def score_workspace_bytes(p: Params, n_kv: int, g: int) -> int:
     out = ctypes.c_size_t()
     _check("tq_score_workspace_bytes", lib().tq_score_workspace_bytes(ctypes.byref(p.c()), n_kv, g, ctypes.byref(out)))
@@ -184,13 +192,24 @@ def _codes(c: dict) -> _Codes:
 
 
 # ----------------------------------------------------------------- device calls
-def encode(p: Params, x, codes: dict, stream=None):
-    """x: cuda tensor [n, d] float32 or bfloat16, contiguous."""
+def alloc_workspace(nbytes: int, device="cuda"):
+    """A device byte buffer (None for 0 bytes)."""
+    import torch
+    return torch.empty((nbytes,), dtype=torch.uint8, device=device) if nbytes else None
+
+
+def encode(p: Params, x, codes: dict, workspace=None, stream=None):
+    """x: cuda tensor [n, d] float32 or bfloat16, contiguous.  workspace: a
+    device buffer of >= encode_workspace_bytes(p, n) bytes, allocated here if
+    not given."""
     import torch
     assert x.is_contiguous() and x.dim() == 2 and x.shape[1] == p.d
     dt = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    if workspace is None:
+        workspace = alloc_workspace(encode_workspace_bytes(p, x.shape[0]), x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("tq_encode", lib().tq_encode(ctypes.byref(p.c()), _ptr(x), dt, x.shape[0],
-                                        _codes(codes), _stream(stream)))
+                                        _codes(codes), _ptr(workspace), wsb, _stream(stream)))
 
 
 def score(p: Params, q, codes: dict, n_kv: int, g: int, seq: int, logits, workspace, stream=None):

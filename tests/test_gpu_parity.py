@@ -19,35 +19,8 @@ if not torch.cuda.is_available():  # pragma: no cover - the CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 from kv_cache_compression_04_amd import synth, tq  # noqa: E402
-
-DEV = "cuda"
-
-
-def _oparams(p: tq.Params) -> o.Params:
-    return o.Params(p.d, p.b, p.m, p.mode, p.seed_pi, p.seed_s)
-
-
-def _gpu_encode(p, x_dev):
-    codes = tq.alloc_codes(p, x_dev.shape[0], DEV)
-    tq.encode(p, x_dev, codes)
-    torch.cuda.synchronize()
-    return codes
-
-
-def _upload(packed: dict):
-    out = {}
-    for k in ("idx", "sgn", "knorm", "rnorm"):
-        if k in packed:
-            a = packed[k]
-            a = a.view(np.int32) if a.dtype == np.uint32 else a
-            out[k] = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-        else:
-            out[k] = None
-    return out
-
-
-def _report(name, rep):
-    print(f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in rep.items()), flush=True)
+from tests.gpu_helpers import (DEV, _gpu_encode, _oparams, _report, _upload,  # noqa: E402
+                               check_search)
 
 
 # ------------------------------------------------------------------ encode
@@ -275,25 +248,6 @@ def test_decode(b, mode):
 
 
 # ------------------------------------------------------------------ search (many-query score + top-k)
-def check_search(idx, val, ref, q, knorm, k, d=128):
-    """Returned sets equal the oracle's up to swaps among logits within tolerance."""
-    qn = np.linalg.norm(q, axis=1)
-    for r in range(ref.shape[0]):
-        row = ref[r]
-        tol = 1e-4 * np.maximum(np.abs(row), qn[r] * knorm / math.sqrt(d))
-        got = idx[r]
-        assert len(set(got.tolist())) == k and got.min() >= 0 and got.max() < row.size
-        order = np.argsort(-row, kind="stable")
-        kth = row[order[k - 1]]
-        tk = tol[order[k - 1]]
-        assert np.all(row[got] >= kth - tol[got] - tk), f"row {r}: returned a non-top-{k} key"
-        must = np.nonzero(row > kth + tol + tk)[0]
-        assert set(must.tolist()) <= set(got.tolist()), f"row {r}: missed a clear top-{k} key"
-        if val is not None:
-            assert np.all(np.abs(val[r] - row[got]) <= tol[got])
-            assert np.all(np.diff(val[r]) <= 0)
-
-
 @pytest.mark.parametrize("nq,n,k,b", [(16, 4096, 10, 3), (37, 1000, 1, 3), (4, 300, 32, 4), (5, 17, 17, 2)])
 def test_search(nq, n, k, b):
     p = tq.Params(128, b, 128, tq.MODE_PROD, 41, 42)

@@ -93,22 +93,46 @@ def test_encode_error_paths_without_a_device():
         keep.append(buf)
         ptrs.append(a)
     codes = tq._Codes(ptrs[1], ptrs[2], ptrs[3], ptrs[4])
+    enc = lambda pp, x, dt, n, c, ws=None, wsb=0: _status("tq_encode", ctypes.byref(pp), x, dt, n, c, ws, wsb, None)
     # n == 0 is a no-op even without a device
-    assert _status("tq_encode", ctypes.byref(p), ptrs[0], 0, 0, codes, None) == 0
+    assert enc(p, ptrs[0], 0, 0, codes) == 0
     # bad dtype, NULL input, misaligned input
-    assert _status("tq_encode", ctypes.byref(p), ptrs[0], 7, 4, codes, None) == 1
-    assert _status("tq_encode", ctypes.byref(p), None, 0, 4, codes, None) == 1
-    assert _status("tq_encode", ctypes.byref(p), ptrs[0] + 4, 0, 4, codes, None) == 3
+    assert enc(p, ptrs[0], 7, 4, codes) == 1
+    assert enc(p, None, 0, 4, codes) == 1
+    assert enc(p, ptrs[0] + 4, 0, 4, codes) == 3
     # missing sign array in prod mode
-    assert _status("tq_encode", ctypes.byref(p), ptrs[0], 0, 4, tq._Codes(ptrs[1], None, ptrs[3], ptrs[4]), None) == 1
-    # shapes valid for the method but without device kernels
+    assert enc(p, ptrs[0], 0, 4, tq._Codes(ptrs[1], None, ptrs[3], ptrs[4])) == 1
+    # general shapes need a residual workspace in prod mode
     p256 = tq._Params(256, 3, 128, 0, 1, 2)
-    assert _status("tq_encode", ctypes.byref(p256), ptrs[0], 0, 4, codes, None) == 2
+    assert enc(p256, ptrs[0], 0, 4, codes) == 5
+    assert enc(p256, ptrs[0], 0, 4, codes, ptrs[1], 64) == 5
+    assert enc(p256, ptrs[0], 0, 4, codes, ptrs[1] + 8, 1 << 30) == 3
     # everything valid: without a usable HIP device the call reports TQ_ERR_HIP
     import torch
     if not torch.cuda.is_available():
-        assert _status("tq_encode", ctypes.byref(p), ptrs[0], 0, 4, codes, None) == 4
+        assert enc(p, ptrs[0], 0, 4, codes) == 4
         assert b"no HIP device" in tq.lib().tq_last_error()
+
+
+def test_encode_workspace_bytes():
+    assert tq.encode_workspace_bytes(tq.Params(128, 3, 128), 10 ** 6) == 0
+    assert tq.encode_workspace_bytes(tq.Params(1024, 3, 0, tq.MODE_MSE), 10 ** 6) == 0
+    assert tq.encode_workspace_bytes(tq.Params(1024, 3, 1024), 0) == 0
+    assert tq.encode_workspace_bytes(tq.Params(1024, 3, 1024), 1) == 128 * (4 * 1024 + 4 * 8)
+    assert tq.encode_workspace_bytes(tq.Params(256, 3, 128), 300) == 384 * (4 * 256 + 4 * 2)
+    assert tq.encode_workspace_bytes(tq.Params(1024, 3, 1024), 1 << 20) == 32768 * (4 * 1024 + 4 * 8)
+    # d = 128 with m != 128 takes the general kernels
+    assert tq.encode_workspace_bytes(tq.Params(128, 3, 256), 1) == 128 * (4 * 128 + 4)
+
+
+def test_unsupported_shapes_for_attend_and_decode():
+    k = tq._Params(256, 3, 256, 0, 1, 2)
+    v = tq._Params(256, 3, 256, 1, 4, 0)
+    buf, a = _host_buf(4096)
+    codes = tq._Codes(a, a, a, a)
+    assert _status("tq_attend", ctypes.byref(k), ctypes.byref(v), a, 1, 1, 1, codes, codes, 4,
+                   ctypes.c_float(0), a, a, 4096, None) == 2
+    assert _status("tq_decode", ctypes.byref(v), codes, 4, a, None) == 2
 
 
 def test_score_and_attend_argument_checks():
