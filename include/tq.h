@@ -184,11 +184,14 @@ tq_status tq_search_workspace_bytes(const tq_params *p, int64_t nq, int64_t n,
 
 /* Top-k search over compressed vectors (vector search with the same
  * estimator as tq_score): for each of nq queries, the k database vectors of
- * largest logit, in descending order, ties broken by the lower index.
- * q: device float [nq][d]; codes: device, n vectors; out_idx: device int64
- * [nq][k]; out_val: device float [nq][k] (may be NULL).  1 <= k <= 32 and
- * k <= n.  workspace: device, >= tq_search_workspace_bytes (it holds the
- * nq x n logits).                                                          */
+ * largest logit, in descending order, ties broken by the lower index.  The
+ * logits are never materialised: workgroups keep running top-k lists over
+ * segments of the database and a final pass merges them.
+ * q: device float [nq][d]; codes: device, n vectors (n < 2^31); out_idx:
+ * device int64 [nq][k]; out_val: device float [nq][k] (may be NULL), the
+ * logits as tq_score computes them.  1 <= k <= 32 and k <= n.  workspace:
+ * device, >= tq_search_workspace_bytes (query operands and candidate lists,
+ * O(nq (d + m + k)) bytes).                                                */
 tq_status tq_search(const tq_params *p, const float *q, int64_t nq, tq_codes codes,
                     int64_t n, int32_t k, int64_t *out_idx, float *out_val,
                     void *workspace, size_t ws_bytes, void *stream);

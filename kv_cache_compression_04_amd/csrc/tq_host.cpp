@@ -229,9 +229,10 @@ static void build_codebook(int d, int nbits, Codebook &cb) {
   // c[idx] = sum over odd subsets S of the planes of coef_S * prod_{k in S} sigma_k,
   // sigma_k = 2 bit_k(idx) - 1 (the even subsets vanish because c is odd).
   int np = 0;
-  for (int size = 1; size <= nbits; size += 2)
-    for (uint32_t mask = 1; mask < (1u << nbits); ++mask)
-      if (__builtin_popcount(mask) == size) cb.part_mask[np++] = mask;
+  while (np < kMaxParts && part_mask_ct(nbits, np) != 0) {
+    cb.part_mask[np] = part_mask_ct(nbits, np);
+    ++np;
+  }
   cb.nparts = np;
   for (int s = 0; s < np; ++s) {
     double acc = 0.0;
@@ -743,9 +744,7 @@ tq_status tq_search_workspace_bytes(const tq_params *p, int64_t nq, int64_t n, i
     set_error("tq_search_workspace_bytes: bad nq/n/k");
     return TQ_ERR_INVALID_ARG;
   }
-  size_t sb = 0;
-  if ((st = tq_score_workspace_bytes(p, 1, nq > 0 ? nq : 1, &sb))) return st;
-  *bytes = ((sb + 255) & ~(size_t)255) + (size_t)nq * n * sizeof(float);
+  *bytes = search_workspace_bytes(*p, nq, n, k);
   return TQ_OK;
 }
 
@@ -763,22 +762,19 @@ tq_status tq_search(const tq_params *p, const float *q, int64_t nq, tq_codes cod
     set_error("tq_search: NULL q/out_idx/workspace");
     return TQ_ERR_INVALID_ARG;
   }
-  if (!aligned16(out_idx) || (out_val && !aligned16(out_val))) {
-    set_error("tq_search: outputs must be 16-byte aligned");
+  if ((st = check_codes(p, codes))) return st;
+  if (!aligned16(q) || !aligned16(workspace) || !aligned16(out_idx) || (out_val && !aligned16(out_val))) {
+    set_error("tq_search: pointers must be 16-byte aligned");
     return TQ_ERR_ALIGNMENT;
   }
-  size_t need = 0;
-  if ((st = tq_search_workspace_bytes(p, nq, n, k, &need))) return st;
+  const size_t need = search_workspace_bytes(*p, nq, n, k);
   if (ws_bytes < need) {
     set_error("tq_search: workspace too small (%zu < %zu)", ws_bytes, need);
     return TQ_ERR_NO_MEMORY;
   }
-  size_t sb = 0;
-  if ((st = tq_score_workspace_bytes(p, 1, nq, &sb))) return st;
-  const size_t off = (sb + 255) & ~(size_t)255;
-  float *logits = (float *)((char *)workspace + off);
-  if ((st = tq_score(p, q, 1, nq, codes, n, logits, workspace, sb, stream))) return st;
-  return launch_topk(logits, nq, n, k, out_idx, out_val, (hipStream_t)stream);
+  const Derived *D = nullptr;
+  if ((st = get_derived(p, &D))) return st;
+  return launch_search(*D, q, nq, codes, n, k, out_idx, out_val, workspace, (hipStream_t)stream);
 }
 
 tq_status tq_release_cache(void) {

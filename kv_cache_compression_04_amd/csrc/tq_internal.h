@@ -13,6 +13,26 @@ namespace tq {
 constexpr int kMaxLevels = 16;  // 2^B with B <= 4
 constexpr int kMaxParts = 8;    // odd subsets of B <= 4 bit planes
 
+// Odd subsets of B bit planes, ordered by size then by mask value: the parts
+// of the multilinear expansion of a symmetric codebook.  Shared by the host
+// (coefficients) and the kernels (which planes to XOR), so both agree on the
+// order; compile-time in the kernels.
+__host__ __device__ constexpr int popcount_ct(uint32_t x) {
+  int c = 0;
+  for (; x; x >>= 1) c += (int)(x & 1u);
+  return c;
+}
+__host__ __device__ constexpr uint32_t part_mask_ct(int B, int sp) {
+  int np = 0;
+  for (int size = 1; size <= B; size += 2)
+    for (uint32_t mask = 1; mask < (1u << B); ++mask)
+      if (popcount_ct(mask) == size) {
+        if (np == sp) return mask;
+        ++np;
+      }
+  return 0;
+}
+
 // Codebook in the form the kernels consume.  Passed by value as a kernel
 // argument.
 struct Codebook {
@@ -72,8 +92,9 @@ tq_status launch_attend(const Derived &K, const Derived &V, const float *q,
 
 tq_status launch_decode(const Derived &D, tq_codes codes, int64_t n, float *out,
                         hipStream_t stream);
-tq_status launch_topk(const float *logits, int64_t nq, int64_t n, int k, int64_t *out_idx,
-                      float *out_val, hipStream_t stream);
+size_t search_workspace_bytes(const tq_params &p, int64_t nq, int64_t n, int k);
+tq_status launch_search(const Derived &D, const float *q, int64_t nq, tq_codes codes, int64_t n,
+                        int k, int64_t *out_idx, float *out_val, void *ws, hipStream_t stream);
 
 // Fragment geometry of the d = m = 128 encode kernel: a 128 x 128 matrix is
 // stored as [16-row tile nt][32-column block kt][lane][8] bf16 values; lane l

@@ -41,6 +41,7 @@ namespace tq {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define TQ_LAUNCH_CHECK()                                                   \
   do {                                                                      \
@@ -388,13 +389,52 @@ __device__ __forceinline__ void gen_tile(int64_t T, int MT, int64_t &vt, int &mt
 
 // Copy one K stage of the matrix fragments (rows of block mt) to registers.
 __device__ __forceinline__ void gen_load_a(const uint4 *__restrict__ fbase, int NT, int stage,
-                                           int tid, uint4 (&r)[kGPer]) {
+                                           int tid, u32x4 (&r)[kGPer]) {
 #pragma unroll
   for (int j = 0; j < kGPer; ++j) {
     const int i = tid + j * kGW * 64;
     const int ktl = i >> 10, rest = i & 1023;
-    r[j] = fbase[(size_t)(kGKB * stage + ktl) * NT * 128 + rest];
+    r[j] = reinterpret_cast<const u32x4 *>(fbase)[(size_t)(kGKB * stage + ktl) * NT * 128 + rest];
   }
+}
+
+// Vector operand of one K stage for the first GEMM: lane (vcol, g) of column
+// tile ct holds x[v][32 kt + 8 g .. + 7] (two uint4 of float32, or one of bf16).
+template <bool XBF16>
+__device__ __forceinline__ void gen_load_x(const void *__restrict__ x, int d, const int64_t (&vrow)[kGCT],
+                                           const bool (&vok)[kGCT], int g, int stage,
+                                           u32x4 (&r)[kGCT][kGKB][XBF16 ? 1 : 2]) {
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct)
+#pragma unroll
+    for (int kb = 0; kb < kGKB; ++kb) {
+      const int col = 32 * (kGKB * stage + kb) + 8 * g;
+      if (XBF16) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(
+            reinterpret_cast<const uint16_t *>(x) + vrow[ct] * d + col);
+        r[ct][kb][0] = vok[ct] ? p[0] : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(
+            reinterpret_cast<const float *>(x) + vrow[ct] * d + col);
+        r[ct][kb][0] = vok[ct] ? p[0] : u32x4{0u, 0u, 0u, 0u};
+        r[ct][kb][XBF16 ? 0 : 1] = vok[ct] ? p[1] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+}
+
+// Residual operand of one K stage for the second GEMM (bf16 hi, lo).
+__device__ __forceinline__ void gen_load_rho(const uint4 *__restrict__ rho, int64_t stride,
+                                             const int64_t (&vrow)[kGCT], int g, int stage,
+                                             u32x4 (&r)[kGCT][kGKB][2]) {
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct)
+#pragma unroll
+    for (int kb = 0; kb < kGKB; ++kb) {
+      const u32x4 *p = reinterpret_cast<const u32x4 *>(rho) +
+                       (((size_t)(kGKB * stage + kb) * stride + vrow[ct]) * 4 + g) * 2;
+      r[ct][kb][0] = p[0];
+      r[ct][kb][1] = p[1];
+    }
 }
 
 template <int B, bool PROD, bool XBF16>
@@ -402,7 +442,7 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
     const void *__restrict__ x, int64_t n, int d, const uint4 *__restrict__ frag, Codebook cb,
     uint32_t *__restrict__ idx_out, float *__restrict__ knorm_out, uint4 *__restrict__ rho,
     float *__restrict__ rsq_part, int64_t stride) {
-  __shared__ uint4 As[2][kGStage];
+  __shared__ u32x4 As[2][kGStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vcol = lane & 15, g = lane >> 4;
   const int MT = d >> 7, NT = d >> 4, KT = d >> 5, S = KT / kGKB;
@@ -421,26 +461,7 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
 
   // vector operand of one stage: lane (vcol, g) holds x[v][32 kt + 8 g .. + 7]
   constexpr int XU = XBF16 ? 1 : 2;
-  uint4 xr[kGCT][kGKB][XU], xn[kGCT][kGKB][XU];
-  auto load_x = [&](int stage, uint4 (&r)[kGCT][kGKB][XU]) {
-#pragma unroll
-    for (int ct = 0; ct < kGCT; ++ct)
-#pragma unroll
-      for (int kb = 0; kb < kGKB; ++kb) {
-        const int col = 32 * (kGKB * stage + kb) + 8 * g;
-        if (XBF16) {
-          const uint4 *p = reinterpret_cast<const uint4 *>(
-              reinterpret_cast<const uint16_t *>(x) + vrow[ct] * d + col);
-          r[ct][kb][0] = vok[ct] ? p[0] : make_uint4(0, 0, 0, 0);
-        } else {
-          const uint4 *p = reinterpret_cast<const uint4 *>(
-              reinterpret_cast<const float *>(x) + vrow[ct] * d + col);
-          r[ct][kb][0] = vok[ct] ? p[0] : make_uint4(0, 0, 0, 0);
-          r[ct][kb][XU - 1] = vok[ct] ? p[XU - 1] : make_uint4(0, 0, 0, 0);
-        }
-      }
-  };
-
+  u32x4 xr[kGCT][kGKB][XU], xn[kGCT][kGKB][XU];
   f32x4 acc[8][kGCT];
   float ss[kGCT];
 #pragma unroll
@@ -449,9 +470,9 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  uint4 ar[kGPer];
+  u32x4 ar[kGPer];
   gen_load_a(fbase, NT, 0, tid, ar);
-  load_x(0, xr);
+  gen_load_x<XBF16>(x, d, vrow, vok, g, 0, xr);
 #pragma unroll
   for (int j = 0; j < kGPer; ++j) As[0][tid + j * kGW * 64] = ar[j];
   __syncthreads();
@@ -461,7 +482,7 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
     const int cur = st & 1;
     if (st + 1 < S) {
       gen_load_a(fbase, NT, st + 1, tid, ar);
-      load_x(st + 1, xn);
+      gen_load_x<XBF16>(x, d, vrow, vok, g, st + 1, xn);
     }
 #pragma unroll
     for (int kb = 0; kb < kGKB; ++kb) {
@@ -469,33 +490,33 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
 #pragma unroll
       for (int ct = 0; ct < kGCT; ++ct) {
         if (XBF16) {
-          const uint4 h = xr[ct][kb][0];
-          const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+          const u32x4 h = xr[ct][kb][0];
+          const uint32_t w[4] = {h[0], h[1], h[2], h[3]};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float a = bf16_to_f32(w[i] & 0xFFFFu), b = bf16_to_f32(w[i] >> 16);
             ss[ct] += a * a + b * b;
           }
-          bh[ct] = as_bf16x8(h);
+          bh[ct] = __builtin_bit_cast(bf16x8, h);
           bl[ct] = bh[ct];
         } else {
-          const uint4 u0 = xr[ct][kb][0], u1 = xr[ct][kb][XU - 1];
-          const float v[8] = {__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z),
-                              __uint_as_float(u0.w), __uint_as_float(u1.x), __uint_as_float(u1.y),
-                              __uint_as_float(u1.z), __uint_as_float(u1.w)};
+          const u32x4 u0 = xr[ct][kb][0], u1 = xr[ct][kb][XU - 1];
+          const float v[8] = {__uint_as_float(u0[0]), __uint_as_float(u0[1]), __uint_as_float(u0[2]),
+                              __uint_as_float(u0[3]), __uint_as_float(u1[0]), __uint_as_float(u1[1]),
+                              __uint_as_float(u1[2]), __uint_as_float(u1[3])};
           uint32_t h[4], l[4];
 #pragma unroll
           for (int i = 0; i < 8; ++i) ss[ct] += v[i] * v[i];
 #pragma unroll
           for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
-          bh[ct] = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
-          bl[ct] = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+          bh[ct] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+          bl[ct] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
         }
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const bf16x8 ah = as_bf16x8(As[cur][(kb * 8 + nt) * 128 + lane]);
-        const bf16x8 al = as_bf16x8(As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[cur][(kb * 8 + nt) * 128 + lane]);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
 #pragma unroll
         for (int ct = 0; ct < kGCT; ++ct) {
           acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[ct], acc[nt][ct], 0, 0, 0);
@@ -594,7 +615,7 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm2_kernel(
     const uint4 *__restrict__ rho, const float *__restrict__ rsq_part, int64_t n, int64_t stride,
     int d, int m, const uint4 *__restrict__ frag, uint32_t *__restrict__ sgn_out,
     float *__restrict__ rnorm_out) {
-  __shared__ uint4 As[2][kGStage];
+  __shared__ u32x4 As[2][kGStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vcol = lane & 15, g = lane >> 4;
   const int MT = m >> 7, NT = m >> 4, KT = d >> 5, S = KT / kGKB;
@@ -608,26 +629,16 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm2_kernel(
   const uint4 *fbase = frag + (size_t)8 * mt * 128;
 
   // residual operand of one stage (written for every vector of the padded tile)
-  uint4 xr[kGCT][kGKB][2], xn[kGCT][kGKB][2];
-  auto load_r = [&](int stage, uint4 (&r)[kGCT][kGKB][2]) {
-#pragma unroll
-    for (int ct = 0; ct < kGCT; ++ct)
-#pragma unroll
-      for (int kb = 0; kb < kGKB; ++kb) {
-        const uint4 *p = rho + (((size_t)(kGKB * stage + kb) * stride + vrow[ct]) * 4 + g) * 2;
-        r[ct][kb][0] = p[0];
-        r[ct][kb][1] = p[1];
-      }
-  };
+  u32x4 xr[kGCT][kGKB][2], xn[kGCT][kGKB][2];
 
   f32x4 acc[8][kGCT];
 #pragma unroll
   for (int ct = 0; ct < kGCT; ++ct)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint4 ar[kGPer];
+  u32x4 ar[kGPer];
   gen_load_a(fbase, NT, 0, tid, ar);
-  load_r(0, xr);
+  gen_load_rho(rho, stride, vrow, g, 0, xr);
 #pragma unroll
   for (int j = 0; j < kGPer; ++j) As[0][tid + j * kGW * 64] = ar[j];
   __syncthreads();
@@ -637,17 +648,17 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm2_kernel(
     const int cur = st & 1;
     if (st + 1 < S) {
       gen_load_a(fbase, NT, st + 1, tid, ar);
-      load_r(st + 1, xn);
+      gen_load_rho(rho, stride, vrow, g, st + 1, xn);
     }
 #pragma unroll
     for (int kb = 0; kb < kGKB; ++kb) {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const bf16x8 ah = as_bf16x8(As[cur][(kb * 8 + nt) * 128 + lane]);
-        const bf16x8 al = as_bf16x8(As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[cur][(kb * 8 + nt) * 128 + lane]);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
 #pragma unroll
         for (int ct = 0; ct < kGCT; ++ct) {
-          const bf16x8 bh = as_bf16x8(xr[ct][kb][0]), bl = as_bf16x8(xr[ct][kb][1]);
+          const bf16x8 bh = __builtin_bit_cast(bf16x8, xr[ct][kb][0]), bl = __builtin_bit_cast(bf16x8, xr[ct][kb][1]);
           acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[nt][ct], 0, 0, 0);
           acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[nt][ct], 0, 0, 0);
           acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[nt][ct], 0, 0, 0);
@@ -807,7 +818,7 @@ __device__ __forceinline__ double tile_logit(const i32x4 *A, const uint32_t *pla
     uint32_t part = 0;
 #pragma unroll
     for (int p = 0; p < B; ++p)
-      if (cb.part_mask[sp] >> p & 1) part ^= planes[p];
+      if (part_mask_ct(B, sp) >> p & 1) part ^= planes[p];
     i32x4 lo4, hi4;
     bit_slices(part, lo4, hi4);
     ai = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * sp], lo4, ai, 0, 0, 0);
@@ -1092,79 +1103,119 @@ static tq_status launch_score128(const Derived &D, const float *q, int64_t n_kv,
 }
 
 // ===========================================================================
-// Score, many queries and general shapes (d, m multiples of 128 up to 1024)
+// Score and search, many queries and general shapes (d, m multiples of 128)
 // ===========================================================================
 // The same integer formulation as the d = 128 kernel, tiled for reuse: a
-// workgroup scores kSMCodes codes against 16 queries (kSMQB groups of 4).
-// The K dimension is walked in chunks of 128 coordinates; in chunk q, lane
-// group kg of a code holds word Qd kg + q of each index plane (and word
-// Md kg + q of the sign bits), so a lane's words for all chunks are one
-// contiguous run that it loads once.  The query operands of one chunk (all
-// parts, all 4 groups) are staged in LDS, double buffered; every bit slice a
-// wave builds from its codes feeds 4 query groups.
+// workgroup scores blocks of kSMCodes codes against 4 QB queries (QB groups
+// of 4).  The K dimension is walked in chunks of 128 coordinates; in chunk q,
+// lane group kg of a code holds word 4 q + kg of each index plane and of the
+// sign bits (the packed layout's own order, so the four lanes of a code read
+// one contiguous run per chunk).  The query operands of one chunk (all parts,
+// all QB groups) are staged in LDS, double buffered; every bit slice a wave
+// builds from its codes feeds QB query groups.
+//
+// Search (top-k per query) runs the same kernel persistently over a segment
+// of code blocks and keeps a running top-k list per query in LDS: a block's
+// logits are merged into the list only for queries where some logit beats the
+// list's current k-th entry, which after the first blocks is rare.  A small
+// kernel merges the per-segment lists.
 constexpr int kSMWaves = 8;
 constexpr int kSMCT = 2;                          // 16-code tiles per wave
-constexpr int kSMCodes = kSMWaves * kSMCT * 16;  // codes per workgroup (256)
-constexpr int kSMQB = 4;                          // 4-query groups per workgroup
-constexpr int kSMGroup = 8;                       // query blocks per L2 group
-constexpr int kQPThreads = 256;
+constexpr int kSMCodes = kSMWaves * kSMCT * 16;  // codes per block (256)
+constexpr int kSMGroup = 4;                       // query blocks per L2 window
 constexpr int kMaxChunks = 8;                     // 1024 / 128
+constexpr int kQJR = 64, kQJQ = 16, kQJK = 64;    // projection tile: rows x queries x K
 
-__host__ __device__ constexpr int sm_nj(int np, bool prod) { return 2 * np + (prod ? 2 : 0); }
+__host__ __device__ constexpr int nparts_ct(int B) {
+  return B == 0 ? 0 : (B == 1 ? 1 : B == 2 ? 2 : B == 3 ? 4 : 8);
+}
+__host__ __device__ constexpr int sm_nj(int B, bool prod) { return 2 * nparts_ct(B) + (prod ? 2 : 0); }
+// query groups per workgroup: as many as keep the LDS stages (QB NJ KB each,
+// double buffered) and the registers (8 accumulators per group and code tile,
+// plus the code words) within budget
+// (K is the capacity of the search lists kept in LDS, 0 for plain scoring.)
+__host__ __device__ constexpr int sm_qb(int B, bool prod, int K) {
+  return K > 16 && sm_nj(B, prod) <= 6 ? 4 : (sm_nj(B, prod) <= 6 ? 8 : (sm_nj(B, prod) <= 10 ? 4 : 2));
+}
+__host__ __device__ constexpr int list_cap(int k) { return k <= 0 ? 0 : (k <= 8 ? 8 : (k <= 16 ? 16 : 32)); }
 
-// Query preparation for one group of 4 queries: qt = Pi q and qs = S q with
-// float64 sums, then the int8 operands of every chunk (layout
+// Projections of every query, float64 sums: out[i][r] = sum_j M[r][j] q_i[j]
+// with M = [Pi; S] (rows = d + m in prod mode, d in mse mode).  A workgroup
+// computes a 64-row x 16-query tile; both operands pass through LDS in
+// 64-wide K tiles.
+__global__ __launch_bounds__(256) void qproj_kernel(const float *__restrict__ q, int64_t nq, int d,
+                                                    int rows, const float *__restrict__ pi,
+                                                    const float *__restrict__ s,
+                                                    double *__restrict__ out) {
+  __shared__ float Ms[kQJR][kQJK + 1];
+  __shared__ double Qs[kQJQ][kQJK];
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.x * kQJR;
+  const int64_t q0 = (int64_t)blockIdx.y * kQJQ;
+  const int r = tid & 63, jq0 = (tid >> 6) * 4;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int j0 = 0; j0 < d; j0 += kQJK) {
+    for (int i = tid; i < kQJR * kQJK / 4; i += 256) {
+      const int rr = i >> 4, c4 = i & 15;
+      const int gr = r0 + rr;
+      const float *row = gr < d ? pi + (size_t)gr * d : s + (size_t)(gr - d) * d;
+      const float4 v = reinterpret_cast<const float4 *>(row + j0)[c4];
+      Ms[rr][4 * c4 + 0] = v.x;
+      Ms[rr][4 * c4 + 1] = v.y;
+      Ms[rr][4 * c4 + 2] = v.z;
+      Ms[rr][4 * c4 + 3] = v.w;
+    }
+    for (int i = tid; i < kQJQ * kQJK; i += 256) {
+      const int jq = i >> 6, c = i & 63;
+      const int64_t qi = q0 + jq;
+      Qs[jq][c] = qi < nq ? (double)q[qi * d + j0 + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int j = 0; j < kQJK; ++j) {
+      const double w = (double)Ms[r][j];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = fma(w, Qs[jq0 + k][j], acc[k]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t qi = q0 + jq0 + k;
+    if (qi < nq) out[qi * rows + r0 + r] = acc[k];
+  }
+}
+
+// Integer operands of every chunk for one group of 4 queries (layout
 // [head][query block][chunk][group][operand j][lane]) and the per-query
 // constants.  Operand j < 2 NP is part j / 2, half j % 2; the last two are
 // the sign part.  Lane l (row 4 jq + t: query jq, limb t; lane group kg),
 // dword w, byte e multiplies bit 8 e + sl (sl = 4 (j % 2) + w) of word
-// W = Qd kg + q, i.e. coordinate 128 (W / 4) + 32 e + 16 (sl / 4) + 4 (W % 4) + sl % 4.
+// W = 4 q + kg, i.e. coordinate 128 q + 32 e + 16 (sl / 4) + 4 kg + sl % 4.
 template <bool PROD>
-__global__ __launch_bounds__(kQPThreads) void qprep_many_kernel(
-    const float *__restrict__ q, int64_t g, int nqb, int d, int m, const float *__restrict__ pi,
-    const float *__restrict__ s, Codebook cb, i32x4 *__restrict__ aops, QConst *__restrict__ qc) {
-  __shared__ double qin[4][1024];
+__global__ __launch_bounds__(256) void qops_kernel(const double *__restrict__ qproj, int64_t g,
+                                                   int nqb, int QB, int d, int m, Codebook cb,
+                                                   i32x4 *__restrict__ aops,
+                                                   QConst *__restrict__ qc) {
   __shared__ double qv[2][4][1024];  // [0] = Pi q, [1] = S q
   __shared__ int expo[4][2];
   const int64_t gid = blockIdx.x;
-  const int qb = (int)(gid & 3);
-  const int64_t hq = gid >> 2;  // head * nqb + query block
+  const int qb = (int)(gid % QB);
+  const int64_t hq = gid / QB;  // head * nqb + query block
   const int64_t head = hq / nqb;
   const int qblk = (int)(hq % nqb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Qd = d >> 7, Md = PROD ? m >> 7 : 0, NCH = Qd > Md ? Qd : Md;
-  const int NP = cb.nparts, NJ = sm_nj(NP, PROD);
-  for (int i = tid; i < 4 * d; i += kQPThreads) {
-    const int jq = i / d, c = i - jq * d;
-    const int64_t qi = ((int64_t)qblk * kSMQB + qb) * 4 + jq;
-    qin[jq][c] = qi < g ? (double)q[(head * g + qi) * d + c] : 0.0;
-  }
-  __syncthreads();
+  const int NP = cb.nparts, NJ = 2 * NP + (PROD ? 2 : 0);
   const int rows = d + (PROD ? m : 0);
-  for (int r = wave; r < rows; r += kQPThreads / 64) {
-    const float *row = r < d ? pi + (size_t)r * d : s + (size_t)(r - d) * d;
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    for (int j = lane; j < d; j += 64) {
-      const double w = (double)row[j];
-      a0 = fma(w, qin[0][j], a0);
-      a1 = fma(w, qin[1][j], a1);
-      a2 = fma(w, qin[2][j], a2);
-      a3 = fma(w, qin[3][j], a3);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      a0 += __shfl_xor(a0, off);
-      a1 += __shfl_xor(a1, off);
-      a2 += __shfl_xor(a2, off);
-      a3 += __shfl_xor(a3, off);
-    }
-    if (lane == 0) {
-      double *dst = r < d ? &qv[0][0][r] : &qv[1][0][r - d];
-      dst[0] = a0;
-      dst[1024] = a1;
-      dst[2048] = a2;
-      dst[3072] = a3;
-    }
+  for (int i = tid; i < 4 * rows; i += 256) {
+    const int jq = i / rows, c = i - jq * rows;
+    const int64_t qi = ((int64_t)qblk * QB + qb) * 4 + jq;
+    const double v = qi < g ? qproj[(head * g + qi) * rows + c] : 0.0;
+    if (c < d)
+      qv[0][jq][c] = v;
+    else
+      qv[1][jq][c - d] = v;
   }
   __syncthreads();
   {
@@ -1193,6 +1244,7 @@ __global__ __launch_bounds__(kQPThreads) void qprep_many_kernel(
         acoef += cb.coef[p];
         amax = fmax(amax, fabs(cb.coef[p]));
       }
+      // scale the largest operand magnitude below 2^26
       int e1 = 0, e2 = 0, k;
       const double A1 = 2.0 * amax * mq, A2 = 2.0 * ms;
       if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
@@ -1205,11 +1257,11 @@ __global__ __launch_bounds__(kQPThreads) void qprep_many_kernel(
       o.idx_bias = acoef * sq;
       o.sgn_scale = cq * ldexp(1.0, -e2);
       o.sgn_bias = cq * ss;
-      qc[hq * 16 + qb * 4 + jq] = o;
+      qc[hq * 4 * QB + qb * 4 + jq] = o;
     }
   }
   __syncthreads();
-  for (int i = tid; i < NCH * NJ * 64; i += kQPThreads) {
+  for (int i = tid; i < NCH * NJ * 64; i += 256) {
     const int l = i & 63, jl = i >> 6;
     const int j = jl % NJ, qq = jl / NJ;
     const int row = l & 15, kg = l >> 4, jq = row >> 2, t = row & 3;
@@ -1221,7 +1273,7 @@ __global__ __launch_bounds__(kQPThreads) void qprep_many_kernel(
       const double coef = sgnpart ? 2.0 : 2.0 * cb.coef[j >> 1];
       const int E = expo[jq][sgnpart ? 1 : 0];
       const double *src = qv[sgnpart ? 1 : 0][jq];
-      const int W = nchunk * kg + qq, qp = W >> 2, kp = W & 3;
+      const int W = 4 * qq + kg, qp = W >> 2, kp = W & 3;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t packed = 0;
@@ -1235,7 +1287,7 @@ __global__ __launch_bounds__(kQPThreads) void qprep_many_kernel(
         out[w] = (int)packed;
       }
     }
-    aops[(((size_t)hq * NCH + qq) * kSMQB + qb) * NJ * 64 + (size_t)j * 64 + l] =
+    aops[(((size_t)hq * NCH + qq) * QB + qb) * NJ * 64 + (size_t)j * 64 + l] =
         i32x4{out[0], out[1], out[2], out[3]};
   }
 }
@@ -1248,8 +1300,8 @@ __device__ __forceinline__ void load_run(const uint32_t *__restrict__ p, int n, 
 #pragma unroll
     for (int j = 0; j < N / 4; ++j)
       if (4 * j < n) {
-        const uint4 u = reinterpret_cast<const uint4 *>(p)[j];
-        r[4 * j] = u.x; r[4 * j + 1] = u.y; r[4 * j + 2] = u.z; r[4 * j + 3] = u.w;
+        const u32x4 u = reinterpret_cast<const u32x4 *>(p)[j];
+        r[4 * j] = u[0]; r[4 * j + 1] = u[1]; r[4 * j + 2] = u[2]; r[4 * j + 3] = u[3];
       }
   } else {
 #pragma unroll
@@ -1258,201 +1310,535 @@ __device__ __forceinline__ void load_run(const uint32_t *__restrict__ p, int n, 
   }
 }
 
-template <int B, bool PROD>
-__global__ __launch_bounds__(kSMWaves * 64) void score_many_kernel(
-    const i32x4 *__restrict__ aops, const QConst *__restrict__ qc,
-    const uint32_t *__restrict__ idx, const uint32_t *__restrict__ sgn,
-    const float *__restrict__ knorm, const float *__restrict__ rnorm, int64_t seq, int64_t g,
-    int nqb, int Qd, int Md, Codebook cb, float *__restrict__ logits) {
-  constexpr int NP = B == 0 ? 0 : (B == 1 ? 1 : B == 2 ? 2 : B == 3 ? 4 : 8);
-  constexpr int NJ = sm_nj(NP, PROD);
-  constexpr int BB = B > 0 ? B : 1;
-  constexpr int kStage = kSMQB * NJ * 64;            // i32x4 per chunk
-  constexpr int kPer = kStage / (kSMWaves * 64);     // = NJ / 2
-  __shared__ i32x4 As[2][kStage];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kc = lane & 15, kg = lane >> 4;
-  const int64_t head = blockIdx.y;
-  // tile -> (query block, code block): XCD-contiguous ranges, then groups of
-  // kSMGroup query blocks walked query block fastest, so a window of tiles
-  // shares both its codes and its query operands in L2
-  const int64_t ncb = (seq + kSMCodes - 1) / kSMCodes;
-  const int64_t T = (int64_t)nqb * ncb;
-  const int64_t bid = blockIdx.x;
-  const int64_t t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
-  const int64_t grp = t / ((int64_t)kSMGroup * ncb);
-  const int64_t first = grp * kSMGroup;
-  const int64_t gsz = (nqb - first) < kSMGroup ? (nqb - first) : kSMGroup;
-  const int64_t within = t - grp * kSMGroup * ncb;
-  const int qblk = (int)(first + within % gsz);
-  const int64_t cblk = within / gsz;
-  const int NCH = Qd > Md ? Qd : Md;
-  const i32x4 *ablk = aops + (size_t)(head * nqb + qblk) * NCH * kStage;
+__device__ __forceinline__ bool better_vi(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
 
-  // this lane's codes: all their words, loaded once
-  const int D32 = 4 * Qd, M32 = 4 * Md;
-  const uint32_t *idx_h = idx + (size_t)head * seq * D32 * BB;
-  int64_t vpos[kSMCT], vcl[kSMCT];
-  uint32_t wi[kSMCT][kMaxChunks * BB], wsg[kSMCT][kMaxChunks];
+// Running top-k lists (search), one per (wave, query), in LDS: descending,
+// ties by lower index.  Insert (cv, ci) into the list of lane group kg
+// (entries r and r + 16 sit with lane r of the group) when `has`
+// (group-uniform); the last entry drops out.
+template <int K>
+__device__ __forceinline__ void group_insert(float *lv, int *li, int lane, int kg, int k, bool has,
+                                             float cv, int ci) {
+  constexpr int KR = K > 16 ? 2 : 1;
+  const int r = lane & 15;
+  float v[KR];
+  int ix[KR];
 #pragma unroll
-  for (int ct = 0; ct < kSMCT; ++ct) {
-    vpos[ct] = cblk * kSMCodes + wave * (16 * kSMCT) + 16 * ct + kc;
-    vcl[ct] = vpos[ct] < seq ? vpos[ct] : seq - 1;
-    if (B > 0) load_run(idx_h + ((size_t)vcl[ct] * D32 + (size_t)Qd * kg) * BB, Qd * BB, wi[ct]);
-    if (PROD)
-      load_run(sgn + (size_t)head * seq * M32 + (size_t)vcl[ct] * M32 + (size_t)Md * kg, Md, wsg[ct]);
+  for (int j = 0; j < KR; ++j) {
+    const int e = r + 16 * j;
+    v[j] = e < k ? lv[e] : -INFINITY;
+    ix[j] = e < k ? li[e] : 0x7fffffff;
   }
-
-  i32x4 acc_i[kSMCT][kSMQB], acc_s[kSMCT][kSMQB];
+  int pos = 0;
 #pragma unroll
-  for (int ct = 0; ct < kSMCT; ++ct)
-#pragma unroll
-    for (int qb = 0; qb < kSMQB; ++qb) {
-      acc_i[ct][qb] = i32x4{0, 0, 0, 0};
-      acc_s[ct][qb] = i32x4{0, 0, 0, 0};
-    }
-  i32x4 ar[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) ar[j] = ablk[tid + j * kSMWaves * 64];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) As[0][tid + j * kSMWaves * 64] = ar[j];
-  __syncthreads();
-
-#pragma unroll
-  for (int q = 0; q < kMaxChunks; ++q) {
-    if (q < NCH) {
-      const int cur = q & 1;
-      if (q + 1 < NCH) {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) ar[j] = ablk[(size_t)(q + 1) * kStage + tid + j * kSMWaves * 64];
-      }
-      if (NP > 0 && q < Qd) {
-#pragma unroll
-        for (int sp = 0; sp < NP; ++sp) {
-          i32x4 lo4[kSMCT], hi4[kSMCT];
-#pragma unroll
-          for (int ct = 0; ct < kSMCT; ++ct) {
-            uint32_t part = 0;
-#pragma unroll
-            for (int p = 0; p < BB; ++p)
-              if (cb.part_mask[sp] >> p & 1) part ^= wi[ct][q * BB + p];
-            bit_slices(part, lo4[ct], hi4[ct]);
-          }
-#pragma unroll
-          for (int qb = 0; qb < kSMQB; ++qb) {
-            const i32x4 a0 = As[cur][(qb * NJ + 2 * sp) * 64 + lane];
-            const i32x4 a1 = As[cur][(qb * NJ + 2 * sp + 1) * 64 + lane];
-#pragma unroll
-            for (int ct = 0; ct < kSMCT; ++ct) {
-              acc_i[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo4[ct], acc_i[ct][qb], 0, 0, 0);
-              acc_i[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi4[ct], acc_i[ct][qb], 0, 0, 0);
-            }
-          }
-        }
-      }
-      if (PROD && q < Md) {
-        i32x4 lo4[kSMCT], hi4[kSMCT];
-#pragma unroll
-        for (int ct = 0; ct < kSMCT; ++ct) bit_slices(wsg[ct][q], lo4[ct], hi4[ct]);
-#pragma unroll
-        for (int qb = 0; qb < kSMQB; ++qb) {
-          const i32x4 a0 = As[cur][(qb * NJ + 2 * NP) * 64 + lane];
-          const i32x4 a1 = As[cur][(qb * NJ + 2 * NP + 1) * 64 + lane];
-#pragma unroll
-          for (int ct = 0; ct < kSMCT; ++ct) {
-            acc_s[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo4[ct], acc_s[ct][qb], 0, 0, 0);
-            acc_s[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi4[ct], acc_s[ct][qb], 0, 0, 0);
-          }
-        }
-      }
-      if (q + 1 < NCH) {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) As[cur ^ 1][tid + j * kSMWaves * 64] = ar[j];
-      }
-      __syncthreads();
-    }
+  for (int j = 0; j < KR; ++j) {
+    const bool bt = r + 16 * j < k && better_vi(v[j], ix[j], cv, ci);
+    pos += __popc((uint32_t)(__ballot(bt) >> (16 * kg)) & 0xFFFFu);
   }
-
-  // ---- epilogue: lane (kc, kg) of tile (ct, qb) = query 4 (4 qblk + qb) + kg, code vpos[ct]
-  const float *kn_h = knorm + head * seq;
-  const float *rn_h = PROD ? rnorm + head * seq : nullptr;
+  // the entry before each slot
+  float up[KR];
+  int upi[KR];
+  up[0] = __shfl(v[0], (lane + 63) & 63);
+  upi[0] = __shfl(ix[0], (lane + 63) & 63);
+  if (KR > 1) {
+    const float a15 = __shfl(v[0], 16 * kg + 15);
+    const int ai15 = __shfl(ix[0], 16 * kg + 15);
+    const float b_ = __shfl(v[KR - 1], (lane + 63) & 63);
+    const int bi_ = __shfl(ix[KR - 1], (lane + 63) & 63);
+    up[KR - 1] = r == 0 ? a15 : b_;
+    upi[KR - 1] = r == 0 ? ai15 : bi_;
+  }
+  if (has && pos < k) {
 #pragma unroll
-  for (int qb = 0; qb < kSMQB; ++qb) {
-    const int64_t qi = ((int64_t)qblk * kSMQB + qb) * 4 + kg;
-    const QConst cst = qc[(head * nqb + qblk) * 16 + qb * 4 + kg];
-#pragma unroll
-    for (int ct = 0; ct < kSMCT; ++ct) {
-      double l = 0.0;
-      if (NP > 0) {
-        const i32x4 a = acc_i[ct][qb];
-        const double vi = (double)a[0] + 128.0 * (double)a[1] + 16384.0 * (double)a[2] +
-                          2097152.0 * (double)a[3];
-        l += (double)kn_h[vcl[ct]] * (vi * cst.idx_scale - cst.idx_bias);
+    for (int j = 0; j < KR; ++j) {
+      const int e = r + 16 * j;
+      if (e < k && e >= pos) {
+        lv[e] = e == pos ? cv : up[j];
+        li[e] = e == pos ? ci : upi[j];
       }
-      if (PROD) {
-        const i32x4 a = acc_s[ct][qb];
-        const double vs = (double)a[0] + 128.0 * (double)a[1] + 16384.0 * (double)a[2] +
-                          2097152.0 * (double)a[3];
-        l += (double)rn_h[vcl[ct]] * (vs * cst.sgn_scale - cst.sgn_bias);
-      }
-      if (qi < g && vpos[ct] < seq) logits[((size_t)head * g + qi) * seq + vpos[ct]] = (float)l;
     }
   }
 }
 
-static size_t score_many_aops_bytes(int B, bool prod, int d, int m, int64_t n_kv, int64_t g) {
-  const int64_t nqb = (g + 4 * kSMQB - 1) / (4 * kSMQB);
-  const int Qd = d / 128, Md = prod ? m / 128 : 0, NCH = Qd > Md ? Qd : Md;
-  const size_t a = (size_t)n_kv * nqb * NCH * kSMQB * sm_nj(nparts_of(B), prod) * 64 * sizeof(i32x4);
-  return (a + 255) & ~(size_t)255;
+template <int B, bool PROD, bool TOPK, int K>
+__global__ __launch_bounds__(kSMWaves * 64) void score_many_kernel(
+    const i32x4 *__restrict__ aops, const QConst *__restrict__ qc,
+    const uint32_t *__restrict__ idx, const uint32_t *__restrict__ sgn,
+    const float *__restrict__ knorm, const float *__restrict__ rnorm, int64_t seq, int64_t g,
+    int nqb, int nseg, int cps, int Qd, int Md, int k, float *__restrict__ logits,
+    float *__restrict__ cand_v, int *__restrict__ cand_i) {
+  constexpr int NP = nparts_ct(B);
+  constexpr int NJ = sm_nj(B, PROD);
+  constexpr int QB = sm_qb(B, PROD, TOPK ? K : 0);
+  constexpr int NQ = 4 * QB;
+  constexpr int BB = B > 0 ? B : 1;
+  constexpr int kStage = QB * NJ * 64;               // i32x4 per chunk
+  constexpr int kThreads = kSMWaves * 64;
+  constexpr int kPer = (kStage + kThreads - 1) / kThreads;
+  __shared__ i32x4 As[2][kStage];
+  __shared__ QConst qcs[NQ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kc = lane & 15, kg = lane >> 4;
+  const int64_t head = blockIdx.y;
+  // tile -> (query block, segment): XCD-contiguous ranges, then windows of
+  // kSMGroup query blocks walked query block fastest, so a window of tiles
+  // shares both its codes and its query operands in L2
+  const int64_t T = (int64_t)nqb * nseg;
+  const int64_t bid = blockIdx.x;
+  const int64_t t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  const int64_t grp = t / ((int64_t)kSMGroup * nseg);
+  const int64_t first = grp * kSMGroup;
+  const int64_t gsz = (nqb - first) < kSMGroup ? (nqb - first) : kSMGroup;
+  const int64_t within = t - grp * kSMGroup * nseg;
+  const int qblk = (int)(first + within % gsz);
+  const int64_t seg = within / gsz;
+  const int NCH = Qd > Md ? Qd : Md;
+  const i32x4 *ablk = aops + (size_t)(head * nqb + qblk) * NCH * kStage;
+  const QConst *qch = qc + (size_t)(head * nqb + qblk) * NQ;
+  const int D32 = 4 * Qd, M32 = 4 * Md;
+  const uint32_t *idx_h = idx + (size_t)head * seq * D32 * BB;
+  const uint32_t *sgn_h = PROD ? sgn + (size_t)head * seq * M32 : nullptr;
+  const float *kn_h = knorm + head * seq;
+  const float *rn_h = PROD ? rnorm + head * seq : nullptr;
+  const int64_t ncb = (seq + kSMCodes - 1) / kSMCodes;
+  const int64_t cb0 = seg * cps;
+  const int64_t cb1 = (cb0 + cps) < ncb ? (cb0 + cps) : ncb;
+  const int64_t nsteps = (cb1 > cb0 ? cb1 - cb0 : 0) * NCH;
+
+  // search: this wave's running top-k list of each of the NQ queries
+  __shared__ float tlv[TOPK ? kSMWaves : 1][TOPK ? NQ : 1][TOPK ? K : 1];
+  __shared__ int tli[TOPK ? kSMWaves : 1][TOPK ? NQ : 1][TOPK ? K : 1];
+  if constexpr (TOPK) {
+    for (int i = lane; i < NQ * K; i += 64) {
+      tlv[wave][i / K][i % K] = -INFINITY;
+      tli[wave][i / K][i % K] = 0x7fffffff;
+    }
+  }
+
+  // One step = one 128-coordinate chunk q of one code block.  Lane group kg of
+  // a code holds word 4 q + kg of each index plane and of the sign bits.  The
+  // words and the query operands of the next step are fetched while this
+  // step's MFMAs run; the operand stages alternate between two LDS buffers
+  // across block boundaries.
+  uint32_t wcur[kSMCT][BB], scur[kSMCT], wnx[kSMCT][BB], snx[kSMCT];
+  auto code_of = [&](int64_t cbk, int ct) -> int64_t {
+    const int64_t v = cbk * kSMCodes + wave * (16 * kSMCT) + 16 * ct + kc;
+    return v < seq ? v : seq - 1;
+  };
+#define TQ_LOAD_WORDS(CBK, Q, W, S)                                                      \
+  do {                                                                                   \
+    _Pragma("unroll") for (int ct_ = 0; ct_ < kSMCT; ++ct_) {                            \
+      const int64_t v_ = code_of((CBK), ct_);                                            \
+      if (B > 0 && (Q) < Qd) {                                                           \
+        const uint32_t *ip_ = idx_h + ((size_t)v_ * D32 + 4 * (Q) + kg) * BB;            \
+        if constexpr (BB == 2) {                                                         \
+          const uint2 u_ = *reinterpret_cast<const uint2 *>(ip_);                        \
+          W[ct_][0] = u_.x;                                                              \
+          W[ct_][BB - 1] = u_.y;                                                         \
+        } else if constexpr (BB == 4) {                                                  \
+          const u32x4 u_ = *reinterpret_cast<const u32x4 *>(ip_);                        \
+          _Pragma("unroll") for (int p_ = 0; p_ < BB; ++p_) W[ct_][p_] = u_[p_ & 3];     \
+        } else {                                                                         \
+          _Pragma("unroll") for (int p_ = 0; p_ < BB; ++p_) W[ct_][p_] = ip_[p_];        \
+        }                                                                                \
+      }                                                                                  \
+      if (PROD && (Q) < Md) S[ct_] = sgn_h[(size_t)v_ * M32 + 4 * (Q) + kg];             \
+    }                                                                                    \
+  } while (0)
+
+  i32x4 ar[kPer];
+  for (int i = tid; i < NQ; i += kThreads) qcs[i] = qch[i];
+  if (nsteps > 0) {
+    TQ_LOAD_WORDS(cb0, 0, wcur, scur);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (tid + j * kThreads < kStage) As[0][tid + j * kThreads] = ablk[tid + j * kThreads];
+  }
+  __syncthreads();
+
+  i32x4 acc_i[kSMCT][QB], acc_s[kSMCT][QB];
+#pragma unroll
+  for (int ct = 0; ct < kSMCT; ++ct)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      acc_i[ct][qb] = i32x4{0, 0, 0, 0};
+      acc_s[ct][qb] = i32x4{0, 0, 0, 0};
+    }
+  float kn[kSMCT], rn[kSMCT];
+
+  int q = 0;
+  int64_t cbk = cb0;
+#pragma unroll 1
+  for (int64_t st = 0; st < nsteps; ++st) {
+    const int cur = (int)(st & 1);
+    const bool more = st + 1 < nsteps;
+    const bool last = q == NCH - 1;
+    if (more) {
+      const int qn = last ? 0 : q + 1;
+      const int64_t cbn = last ? cbk + 1 : cbk;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (tid + j * kThreads < kStage) ar[j] = ablk[(size_t)qn * kStage + tid + j * kThreads];
+      TQ_LOAD_WORDS(cbn, qn, wnx, snx);
+    }
+    if (last) {
+#pragma unroll
+      for (int ct = 0; ct < kSMCT; ++ct) {
+        const int64_t v = code_of(cbk, ct);
+        kn[ct] = kn_h[v];
+        rn[ct] = PROD ? rn_h[v] : 0.f;
+      }
+    }
+    if (NP > 0 && q < Qd) {
+#pragma unroll
+      for (int sp = 0; sp < NP; ++sp) {
+        i32x4 lo4[kSMCT], hi4[kSMCT];
+#pragma unroll
+        for (int ct = 0; ct < kSMCT; ++ct) {
+          uint32_t part = 0;
+#pragma unroll
+          for (int p = 0; p < BB; ++p)
+            if (part_mask_ct(B, sp) >> p & 1) part ^= wcur[ct][p];
+          bit_slices(part, lo4[ct], hi4[ct]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const i32x4 a0 = As[cur][(qb * NJ + 2 * sp) * 64 + lane];
+          const i32x4 a1 = As[cur][(qb * NJ + 2 * sp + 1) * 64 + lane];
+#pragma unroll
+          for (int ct = 0; ct < kSMCT; ++ct) {
+            acc_i[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo4[ct], acc_i[ct][qb], 0, 0, 0);
+            acc_i[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi4[ct], acc_i[ct][qb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (PROD && q < Md) {
+      i32x4 lo4[kSMCT], hi4[kSMCT];
+#pragma unroll
+      for (int ct = 0; ct < kSMCT; ++ct) bit_slices(scur[ct], lo4[ct], hi4[ct]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const i32x4 a0 = As[cur][(qb * NJ + 2 * NP) * 64 + lane];
+        const i32x4 a1 = As[cur][(qb * NJ + 2 * NP + 1) * 64 + lane];
+#pragma unroll
+        for (int ct = 0; ct < kSMCT; ++ct) {
+          acc_s[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo4[ct], acc_s[ct][qb], 0, 0, 0);
+          acc_s[ct][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi4[ct], acc_s[ct][qb], 0, 0, 0);
+        }
+      }
+    }
+
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (tid + j * kThreads < kStage) As[cur ^ 1][tid + j * kThreads] = ar[j];
+#pragma unroll
+      for (int ct = 0; ct < kSMCT; ++ct) {
+#pragma unroll
+        for (int p = 0; p < BB; ++p) wcur[ct][p] = wnx[ct][p];
+        scur[ct] = snx[ct];
+      }
+    }
+    if (last) {
+      // ---- epilogue of block cbk: lane (kc, kg) of tile (ct, qb) = query
+      // 4 (QB qblk + qb) + kg, code cbk * kSMCodes + wave * 32 + 16 ct + kc
+      const int64_t vbase = cbk * kSMCodes + wave * (16 * kSMCT) + kc;
+      // logit of tile (ct, qb), exact integer sums combined in float64
+#define TQ_LOGIT(CT, QB_)                                                                    \
+  ([&]() -> float {                                                                          \
+    const QConst &cst_ = qcs[(QB_) * 4 + kg];                                                \
+    double l_ = 0.0;                                                                         \
+    if (NP > 0) {                                                                            \
+      const i32x4 a_ = acc_i[CT][QB_];                                                       \
+      const double v_ = (double)a_[0] + 128.0 * (double)a_[1] + 16384.0 * (double)a_[2] +    \
+                        2097152.0 * (double)a_[3];                                           \
+      l_ += (double)kn[CT] * (v_ * cst_.idx_scale - cst_.idx_bias);                          \
+    }                                                                                        \
+    if (PROD) {                                                                              \
+      const i32x4 a_ = acc_s[CT][QB_];                                                       \
+      const double v_ = (double)a_[0] + 128.0 * (double)a_[1] + 16384.0 * (double)a_[2] +    \
+                        2097152.0 * (double)a_[3];                                           \
+      l_ += (double)rn[CT] * (v_ * cst_.sgn_scale - cst_.sgn_bias);                          \
+    }                                                                                        \
+    return (float)l_;                                                                        \
+  }())
+      if constexpr (!TOPK) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int64_t qi = ((int64_t)qblk * QB + qb) * 4 + kg;
+#pragma unroll
+          for (int ct = 0; ct < kSMCT; ++ct) {
+            const float lf = TQ_LOGIT(ct, qb);
+            const int64_t vpos = vbase + 16 * ct;
+            if (qi < g && vpos < seq) logits[((size_t)head * g + qi) * seq + vpos] = lf;
+          }
+        }
+      } else {
+        // candidates beat their query's k-th entry; usually there are none
+        // and the block costs a compare per logit and one ballot
+        uint32_t pend = 0;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float tv = tlv[wave][qb * 4 + kg][k - 1];
+          const int ti = tli[wave][qb * 4 + kg][k - 1];
+#pragma unroll
+          for (int ct = 0; ct < kSMCT; ++ct) {
+            const int64_t vpos = vbase + 16 * ct;
+            if (vpos < seq && better_vi(TQ_LOGIT(ct, qb), (int)vpos, tv, ti)) pend |= 1u << (qb * kSMCT + ct);
+          }
+        }
+        if (__ballot(pend != 0)) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int ct = 0; ct < kSMCT; ++ct) {
+              // each lane group inserts its pending candidates one at a time
+              const int bit = qb * kSMCT + ct;
+              bool pd = (pend >> bit) & 1u;
+              uint64_t bal = __ballot(pd);
+              if (!bal) continue;
+              const float lf = TQ_LOGIT(ct, qb);
+              const int cidx = (int)(vbase + 16 * ct);
+              float *lvq = &tlv[wave][qb * 4 + kg][0];
+              int *liq = &tli[wave][qb * 4 + kg][0];
+              while (bal) {
+                const uint32_t gb = (uint32_t)(bal >> (16 * kg)) & 0xFFFFu;
+                const bool has = gb != 0;
+                const int src = 16 * kg + (has ? __ffs(gb) - 1 : 0);
+                const float cv = __shfl(lf, src);
+                const int ci = __shfl(cidx, src);
+                group_insert<K>(lvq, liq, lane, kg, k, has, cv, ci);
+                if (has && lane == src) pd = false;
+                __builtin_amdgcn_wave_barrier();
+                pd = pd && better_vi(lf, cidx, lvq[k - 1], liq[k - 1]);
+                bal = __ballot(pd);
+              }
+            }
+        }
+      }
+#undef TQ_LOGIT
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int ct = 0; ct < kSMCT; ++ct) {
+          acc_i[ct][qb] = i32x4{0, 0, 0, 0};
+          acc_s[ct][qb] = i32x4{0, 0, 0, 0};
+        }
+    }
+    if (last) {
+      q = 0;
+      ++cbk;
+    } else {
+      ++q;
+    }
+    __syncthreads();
+  }
+#undef TQ_LOAD_WORDS
+  if constexpr (TOPK) {
+    // this wave's lists -> candidates [head * g + query][segment][wave][k]
+    for (int i = lane; i < NQ * k; i += 64) {
+      const int qq = i / k, r = i % k;
+      const int64_t qi = (int64_t)qblk * NQ + qq;
+      if (qi < g) {
+        const size_t o = ((((size_t)head * g + qi) * nseg + seg) * kSMWaves + wave) * k + r;
+        cand_v[o] = tlv[wave][qq][r];
+        cand_i[o] = tli[wave][qq][r];
+      }
+    }
+  }
+}
+
+// Final top-k of each query from its segments' candidate lists: one wave per
+// query; per-lane sorted lists, then k rounds of wave-wide arg-max.
+template <int K>
+__global__ __launch_bounds__(256) void topk_merge_kernel(const float *__restrict__ cand_v,
+                                                         const int *__restrict__ cand_i,
+                                                         int64_t nrows, int ncand, int k,
+                                                         int64_t *__restrict__ out_idx,
+                                                         float *__restrict__ out_val) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const float *cv = cand_v + row * ncand;
+  const int *ci = cand_i + row * ncand;
+  float v[K];
+  int id[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) { v[i] = -INFINITY; id[i] = 0x7fffffff; }
+  for (int j = lane; j < ncand; j += 64) {
+    float cvv = cv[j];
+    int cii = ci[j];
+    if (better_vi(cvv, cii, v[K - 1], id[K - 1])) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        if (better_vi(cvv, cii, v[i], id[i])) {
+          const float tv = v[i];
+          const int ti = id[i];
+          v[i] = cvv; id[i] = cii;
+          cvv = tv; cii = ti;
+        }
+      }
+    }
+  }
+  int head = 0;
+  for (int r = 0; r < k; ++r) {
+    float hv = -INFINITY;
+    int hi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (i == head) { hv = v[i]; hi = id[i]; }
+    float bv = hv;
+    int bi = hi, bl = lane;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      const int ol = __shfl_xor(bl, off);
+      if (better_vi(ov, oi, bv, bi)) { bv = ov; bi = oi; bl = ol; }
+    }
+    if (lane == bl) ++head;
+    if (lane == 0) {
+      out_idx[row * k + r] = bi;
+      if (out_val) out_val[row * k + r] = bv;
+    }
+  }
+}
+
+// ---- workspace layout and launchers
+struct ManyLayout {
+  int QB, NJ, NCH, nqb;
+  size_t aops, qc, proj, cand_v, cand_i, total;  // byte offsets, total size
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static ManyLayout many_layout(const tq_params &p, int64_t n_kv, int64_t g, int nseg, int k) {
+  ManyLayout L;
+  const bool prod = p.mode == TQ_MODE_PROD;
+  const int B = prod ? p.b - 1 : p.b;
+  L.QB = sm_qb(B, prod, list_cap(k));
+  L.NJ = sm_nj(B, prod);
+  const int Qd = p.d / 128, Md = prod ? p.m / 128 : 0;
+  L.NCH = Qd > Md ? Qd : Md;
+  L.nqb = (int)((g + 4 * L.QB - 1) / (4 * L.QB));
+  const size_t rows = p.d + (prod ? p.m : 0);
+  size_t o = 0;
+  L.aops = o;
+  o = align256(o + (size_t)n_kv * L.nqb * L.NCH * L.QB * L.NJ * 64 * sizeof(i32x4));
+  L.qc = o;
+  o = align256(o + (size_t)n_kv * L.nqb * 4 * L.QB * sizeof(QConst));
+  L.proj = o;
+  o = align256(o + (size_t)n_kv * g * rows * sizeof(double));
+  L.cand_v = o;
+  o = align256(o + (size_t)n_kv * g * nseg * kSMWaves * k * sizeof(float));
+  L.cand_i = o;
+  o = align256(o + (size_t)n_kv * g * nseg * kSMWaves * k * sizeof(int));
+  L.total = o;
+  return L;
+}
+
+// Segments of code blocks per (head, query block): about four workgroups per
+// CU in total, every segment non-empty.
+static int many_segments(const tq_params &p, int64_t n_kv, int64_t g, int64_t n, int cus, int k) {
+  const bool prod = p.mode == TQ_MODE_PROD;
+  const int B = prod ? p.b - 1 : p.b;
+  const int QB = sm_qb(B, prod, list_cap(k));
+  const int64_t nqb = (g + 4 * QB - 1) / (4 * QB);
+  const int64_t ncb = std::max<int64_t>(1, (n + kSMCodes - 1) / kSMCodes);
+  int64_t nseg = std::max<int64_t>(1, (4LL * cus + n_kv * nqb - 1) / (n_kv * nqb));
+  nseg = std::min<int64_t>(nseg, ncb);
+  const int64_t cps = (ncb + nseg - 1) / nseg;
+  return (int)((ncb + cps - 1) / cps);
+}
+
+static int search_segments(const tq_params &p, int64_t nq, int64_t n, int k) {
+  return many_segments(p, 1, nq, n, 256, k);
+}
+
+size_t search_workspace_bytes(const tq_params &p, int64_t nq, int64_t n, int k) {
+  return many_layout(p, 1, nq, search_segments(p, nq, n, k), k).total;
+}
+
+template <int B, bool PROD, bool TOPK, int K>
+static void launch_many_t(const Derived &D, const float *q, int64_t n_kv, int64_t g, tq_codes c,
+                          int64_t seq, float *logits, char *ws, int nseg, int k, hipStream_t s) {
+  const ManyLayout L = many_layout(D.p, n_kv, g, nseg, k);
+  const int rows = D.p.d + (PROD ? D.p.m : 0);
+  double *proj = (double *)(ws + L.proj);
+  i32x4 *aops = (i32x4 *)(ws + L.aops);
+  QConst *qc = (QConst *)(ws + L.qc);
+  qproj_kernel<<<dim3(rows / kQJR, (unsigned)((n_kv * g + kQJQ - 1) / kQJQ)), dim3(256), 0, s>>>(
+      q, n_kv * g, D.p.d, rows, D.pi32, D.s32, proj);
+  qops_kernel<PROD><<<dim3((unsigned)(n_kv * L.nqb * L.QB)), dim3(256), 0, s>>>(
+      proj, g, L.nqb, L.QB, D.p.d, D.p.m, D.cb, aops, qc);
+  const int64_t ncb = (seq + kSMCodes - 1) / kSMCodes;
+  const int cps = (int)((ncb + nseg - 1) / nseg);
+  score_many_kernel<B, PROD, TOPK, K>
+      <<<dim3((unsigned)(L.nqb * nseg), (unsigned)n_kv), dim3(kSMWaves * 64), 0, s>>>(
+          aops, qc, c.idx, c.sgn, c.knorm, c.rnorm, seq, g, L.nqb, nseg, cps, D.p.d / 128,
+          PROD ? D.p.m / 128 : 0, k, logits, (float *)(ws + L.cand_v), (int *)(ws + L.cand_i));
+}
+
+template <bool TOPK, int K>
+static tq_status launch_many(const Derived &D, const float *q, int64_t n_kv, int64_t g, tq_codes c,
+                             int64_t seq, float *logits, char *ws, int nseg, int k, hipStream_t s) {
+  const ManyLayout L = many_layout(D.p, n_kv, g, nseg, k);
+  if (n_kv > 65535 || (int64_t)L.nqb * nseg > 0x7fffffffLL || n_kv * L.nqb * L.QB > 0x7fffffffLL ||
+      seq > 0x7fffffffLL) {
+    set_error("problem too large for one launch");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const bool prod = D.p.mode == TQ_MODE_PROD;
+  switch (D.B * 2 + (prod ? 1 : 0)) {
+    case 0 * 2 + 1: launch_many_t<0, true, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    case 1 * 2 + 1: launch_many_t<1, true, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    case 2 * 2 + 1: launch_many_t<2, true, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    case 3 * 2 + 1: launch_many_t<3, true, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    case 4 * 2 + 1: launch_many_t<4, true, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    case 1 * 2 + 0: launch_many_t<1, false, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    case 2 * 2 + 0: launch_many_t<2, false, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    case 3 * 2 + 0: launch_many_t<3, false, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    case 4 * 2 + 0: launch_many_t<4, false, TOPK, K>(D, q, n_kv, g, c, seq, logits, ws, nseg, k, s); break;
+    default:
+      set_error("unsupported B = %d", D.B);
+      return TQ_ERR_UNSUPPORTED;
+  }
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
 }
 
 size_t score_workspace_bytes(const tq_params &p, int64_t n_kv, int64_t g) {
   const bool prod = p.mode == TQ_MODE_PROD;
   const int B = prod ? p.b - 1 : p.b;
   if (is_d128(p)) return score128_workspace_bytes(B, prod, n_kv, g);
-  const int64_t nqb = (g + 4 * kSMQB - 1) / (4 * kSMQB);
-  return score_many_aops_bytes(B, prod, p.d, p.m, n_kv, g) +
-         (size_t)n_kv * nqb * 4 * kSMQB * sizeof(QConst);
+  return many_layout(p, n_kv, g, 1, 0).total;
 }
 
-template <int B, bool PROD>
-static void launch_score_many_t(const Derived &D, const float *q, int64_t n_kv, int64_t g,
-                                tq_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
-  const int nqb = (int)((g + 4 * kSMQB - 1) / (4 * kSMQB));
-  i32x4 *aops = (i32x4 *)ws;
-  QConst *qc = (QConst *)((char *)ws + score_many_aops_bytes(B, PROD, D.p.d, D.p.m, n_kv, g));
-  qprep_many_kernel<PROD><<<dim3((unsigned)(n_kv * nqb * kSMQB)), dim3(kQPThreads), 0, s>>>(
-      q, g, nqb, D.p.d, D.p.m, D.pi32, D.s32, D.cb, aops, qc);
-  const int64_t ncb = (seq + kSMCodes - 1) / kSMCodes;
-  score_many_kernel<B, PROD><<<dim3((unsigned)(nqb * ncb), (unsigned)n_kv), dim3(kSMWaves * 64), 0, s>>>(
-      aops, qc, c.idx, c.sgn, c.knorm, c.rnorm, seq, g, nqb, D.p.d / 128, PROD ? D.p.m / 128 : 0, D.cb,
-      logits);
-}
-
-static tq_status launch_score_many(const Derived &D, const float *q, int64_t n_kv, int64_t g,
-                                   tq_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
-  const int64_t nqb = (g + 4 * kSMQB - 1) / (4 * kSMQB);
-  const int64_t ncb = (seq + kSMCodes - 1) / kSMCodes;
-  if (n_kv > 65535 || nqb * ncb > 0x7fffffffLL || n_kv * nqb * kSMQB > 0x7fffffffLL) {
-    set_error("tq_score: problem too large for one launch");
-    return TQ_ERR_UNSUPPORTED;
-  }
-  const bool prod = D.p.mode == TQ_MODE_PROD;
-  switch (D.B * 2 + (prod ? 1 : 0)) {
-    case 0 * 2 + 1: launch_score_many_t<0, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    case 1 * 2 + 1: launch_score_many_t<1, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    case 2 * 2 + 1: launch_score_many_t<2, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    case 3 * 2 + 1: launch_score_many_t<3, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    case 4 * 2 + 1: launch_score_many_t<4, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    case 1 * 2 + 0: launch_score_many_t<1, false>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    case 2 * 2 + 0: launch_score_many_t<2, false>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    case 3 * 2 + 0: launch_score_many_t<3, false>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    case 4 * 2 + 0: launch_score_many_t<4, false>(D, q, n_kv, g, c, seq, logits, ws, s); break;
-    default:
-      set_error("tq_score: unsupported B = %d", D.B);
-      return TQ_ERR_UNSUPPORTED;
-  }
+tq_status launch_search(const Derived &D, const float *q, int64_t nq, tq_codes c, int64_t n,
+                        int k, int64_t *out_idx, float *out_val, void *ws, hipStream_t s) {
+  const int nseg = search_segments(D.p, nq, n, k);
+  tq_status st;
+  if (k <= 8)
+    st = launch_many<true, 8>(D, q, 1, nq, c, n, nullptr, (char *)ws, nseg, k, s);
+  else if (k <= 16)
+    st = launch_many<true, 16>(D, q, 1, nq, c, n, nullptr, (char *)ws, nseg, k, s);
+  else
+    st = launch_many<true, 32>(D, q, 1, nq, c, n, nullptr, (char *)ws, nseg, k, s);
+  if (st != TQ_OK) return st;
+  const ManyLayout L = many_layout(D.p, 1, nq, nseg, k);
+  const float *cv = (const float *)((char *)ws + L.cand_v);
+  const int *ci = (const int *)((char *)ws + L.cand_i);
+  const dim3 grid((unsigned)((nq + 3) / 4)), blk(256);
+  const int ncand = nseg * kSMWaves * k;
+  if (k <= 8)
+    topk_merge_kernel<8><<<grid, blk, 0, s>>>(cv, ci, nq, ncand, k, out_idx, out_val);
+  else if (k <= 16)
+    topk_merge_kernel<16><<<grid, blk, 0, s>>>(cv, ci, nq, ncand, k, out_idx, out_val);
+  else
+    topk_merge_kernel<32><<<grid, blk, 0, s>>>(cv, ci, nq, ncand, k, out_idx, out_val);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
@@ -1460,7 +1846,8 @@ static tq_status launch_score_many(const Derived &D, const float *q, int64_t n_k
 tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g, tq_codes c,
                        int64_t seq, float *logits, void *ws, hipStream_t s) {
   if (is_d128(D.p)) return launch_score128(D, q, n_kv, g, c, seq, logits, ws, s);
-  return launch_score_many(D, q, n_kv, g, c, seq, logits, ws, s);
+  const int nseg = many_segments(D.p, n_kv, g, seq, num_cus(D.device), 0);
+  return launch_many<false, 1>(D, q, n_kv, g, c, seq, logits, (char *)ws, nseg, 0, s);
 }
 
 // ===========================================================================
@@ -1670,7 +2057,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
         uint32_t pt = 0;
 #pragma unroll
         for (int p = 0; p < BV; ++p)
-          if (vcb.part_mask[sp] >> p & 1) pt ^= pd[p];
+          if (part_mask_ct(BV, sp) >> p & 1) pt ^= pd[p];
         D[sp][gi] = pt;
       }
     }
@@ -1895,111 +2282,6 @@ tq_status launch_decode(const Derived &D, tq_codes codes, int64_t n, float *out,
       set_error("tq_decode: unsupported B = %d", D.B);
       return TQ_ERR_UNSUPPORTED;
   }
-  TQ_LAUNCH_CHECK();
-  return TQ_OK;
-}
-
-// ===========================================================================
-// Top-k over rows of logits (vector search), k <= 32
-// ===========================================================================
-// One workgroup of 256 threads per query row.  Each thread keeps a sorted
-// list of its K best (value desc, index asc) over indices t, t + 256, ...;
-// waves merge their 64 lists by K rounds of arg-max extraction, then wave 0
-// merges the 4 wave lists the same way.
-template <int K>
-__device__ __forceinline__ bool better(float va, int64_t ia, float vb, int64_t ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
-template <int K>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int64_t n,
-                                                   int k, int64_t *__restrict__ out_idx,
-                                                   float *__restrict__ out_val) {
-  __shared__ float sv[4][K];
-  __shared__ int64_t si[4][K];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const float *x = logits + row * n;
-  float v[K];
-  int64_t id[K];
-#pragma unroll
-  for (int i = 0; i < K; ++i) { v[i] = -INFINITY; id[i] = INT64_MAX; }
-  for (int64_t j = tid; j < n; j += 256) {
-    const float xv = x[j];
-    if (better<K>(xv, j, v[K - 1], id[K - 1])) {
-      // insert: shift down everything worse than (xv, j)
-      float cv = xv;
-      int64_t ci = j;
-#pragma unroll
-      for (int i = 0; i < K; ++i) {
-        if (better<K>(cv, ci, v[i], id[i])) {
-          const float tv = v[i];
-          const int64_t ti = id[i];
-          v[i] = cv; id[i] = ci;
-          cv = tv; ci = ti;
-        }
-      }
-    }
-  }
-  // wave merge: K rounds, the best head among 64 lanes is popped
-  int head = 0;
-  for (int r = 0; r < k; ++r) {
-    float hv = -INFINITY;
-    int64_t hi = INT64_MAX;
-#pragma unroll
-    for (int i = 0; i < K; ++i)
-      if (i == head) { hv = v[i]; hi = id[i]; }
-    float bv = hv;
-    int64_t bi = hi;
-    int bl = lane;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int64_t oi = __shfl_xor(bi, off);
-      const int ol = __shfl_xor(bl, off);
-      if (better<K>(ov, oi, bv, bi)) { bv = ov; bi = oi; bl = ol; }
-    }
-    if (lane == bl) ++head;
-    if (lane == 0) { sv[wave][r] = bv; si[wave][r] = bi; }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // lanes 0..3 walk the four wave lists
-    int pos = 0;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int64_t bi = INT64_MAX;
-      if (lane < 4 && pos < k) { bv = sv[lane][pos]; bi = si[lane][pos]; }
-      int bl = lane;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int64_t oi = __shfl_xor(bi, off);
-        const int ol = __shfl_xor(bl, off);
-        if (better<K>(ov, oi, bv, bi)) { bv = ov; bi = oi; bl = ol; }
-      }
-      if (lane == bl) ++pos;
-      if (lane == 0) {
-        out_idx[row * k + r] = bi;
-        if (out_val) out_val[row * k + r] = bv;
-      }
-    }
-  }
-}
-
-tq_status launch_topk(const float *logits, int64_t nq, int64_t n, int k, int64_t *out_idx,
-                      float *out_val, hipStream_t s) {
-  if (nq > 0x7fffffffLL) {
-    set_error("tq_search: too many queries");
-    return TQ_ERR_UNSUPPORTED;
-  }
-  const dim3 grid((unsigned)nq), blk(256);
-  if (k <= 8)
-    topk_kernel<8><<<grid, blk, 0, s>>>(logits, n, k, out_idx, out_val);
-  else if (k <= 16)
-    topk_kernel<16><<<grid, blk, 0, s>>>(logits, n, k, out_idx, out_val);
-  else
-    topk_kernel<32><<<grid, blk, 0, s>>>(logits, n, k, out_idx, out_val);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
