@@ -1120,8 +1120,8 @@ static tq_status launch_score128(const Derived &D, const float *q, int64_t n_kv,
 // list's current k-th entry, which after the first blocks is rare.  A small
 // kernel merges the per-segment lists.
 constexpr int kSMWaves = 8;
-constexpr int kSMCT = 2;                          // 16-code tiles per wave
-constexpr int kSMCodes = kSMWaves * kSMCT * 16;  // codes per block (256)
+constexpr int kSMCT = 4;                          // 16-code tiles per wave
+constexpr int kSMCodes = kSMWaves * kSMCT * 16;  // codes per block (512)
 constexpr int kSMGroup = 4;                       // query blocks per L2 window
 constexpr int kMaxChunks = 8;                     // 1024 / 128
 constexpr int kQJR = 64, kQJQ = 16, kQJK = 64;    // projection tile: rows x queries x K
@@ -1135,7 +1135,7 @@ __host__ __device__ constexpr int sm_nj(int B, bool prod) { return 2 * nparts_ct
 // plus the code words) within budget
 // (K is the capacity of the search lists kept in LDS, 0 for plain scoring.)
 __host__ __device__ constexpr int sm_qb(int B, bool prod, int K) {
-  return K > 16 && sm_nj(B, prod) <= 6 ? 4 : (sm_nj(B, prod) <= 6 ? 8 : (sm_nj(B, prod) <= 10 ? 4 : 2));
+  return sm_nj(B, prod) <= 10 ? 4 : 2;
 }
 __host__ __device__ constexpr int list_cap(int k) { return k <= 0 ? 0 : (k <= 8 ? 8 : (k <= 16 ? 16 : 32)); }
 
@@ -1314,6 +1314,17 @@ __device__ __forceinline__ bool better_vi(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// max-update of a float in LDS (compare-and-swap on its bits)
+__device__ __forceinline__ void lds_fmax(float *addr, float v) {
+  int *ia = reinterpret_cast<int *>(addr);
+  int old = *reinterpret_cast<volatile int *>(ia);
+  while (__int_as_float(old) < v) {
+    const int assumed = old;
+    old = atomicCAS(ia, assumed, __float_as_int(v));
+    if (old == assumed) break;
+  }
+}
+
 // Running top-k lists (search), one per (wave, query), in LDS: descending,
 // ties by lower index.  Insert (cv, ci) into the list of lane group kg
 // (entries r and r + 16 sit with lane r of the group) when `has`
@@ -1408,13 +1419,17 @@ __global__ __launch_bounds__(kSMWaves * 64) void score_many_kernel(
   const int64_t nsteps = (cb1 > cb0 ? cb1 - cb0 : 0) * NCH;
 
   // search: this wave's running top-k list of each of the NQ queries
+  // and, per query, the largest k-th entry over the waves: no code below it
+  // can reach the workgroup's top k, so it is not even a candidate
   __shared__ float tlv[TOPK ? kSMWaves : 1][TOPK ? NQ : 1][TOPK ? K : 1];
   __shared__ int tli[TOPK ? kSMWaves : 1][TOPK ? NQ : 1][TOPK ? K : 1];
+  __shared__ float tau_sh[TOPK ? NQ : 1];
   if constexpr (TOPK) {
     for (int i = lane; i < NQ * K; i += 64) {
       tlv[wave][i / K][i % K] = -INFINITY;
       tli[wave][i / K][i % K] = 0x7fffffff;
     }
+    for (int i = tid; i < NQ; i += kThreads) tau_sh[i] = -INFINITY;
   }
 
   // One step = one 128-coordinate chunk q of one code block.  Lane group kg of
@@ -1544,7 +1559,7 @@ __global__ __launch_bounds__(kSMWaves * 64) void score_many_kernel(
     }
     if (last) {
       // ---- epilogue of block cbk: lane (kc, kg) of tile (ct, qb) = query
-      // 4 (QB qblk + qb) + kg, code cbk * kSMCodes + wave * 32 + 16 ct + kc
+      // 4 (QB qblk + qb) + kg, code cbk * kSMCodes + wave * 16 kSMCT + 16 ct + kc
       const int64_t vbase = cbk * kSMCodes + wave * (16 * kSMCT) + kc;
       // logit of tile (ct, qb), exact integer sums combined in float64
 #define TQ_LOGIT(CT, QB_)                                                                    \
@@ -1584,10 +1599,12 @@ __global__ __launch_bounds__(kSMWaves * 64) void score_many_kernel(
         for (int qb = 0; qb < QB; ++qb) {
           const float tv = tlv[wave][qb * 4 + kg][k - 1];
           const int ti = tli[wave][qb * 4 + kg][k - 1];
+          const float ts = tau_sh[qb * 4 + kg];
 #pragma unroll
           for (int ct = 0; ct < kSMCT; ++ct) {
             const int64_t vpos = vbase + 16 * ct;
-            if (vpos < seq && better_vi(TQ_LOGIT(ct, qb), (int)vpos, tv, ti)) pend |= 1u << (qb * kSMCT + ct);
+            const float lf = TQ_LOGIT(ct, qb);
+            if (vpos < seq && lf >= ts && better_vi(lf, (int)vpos, tv, ti)) pend |= 1u << (qb * kSMCT + ct);
           }
         }
         if (__ballot(pend != 0)) {
@@ -1617,6 +1634,9 @@ __global__ __launch_bounds__(kSMWaves * 64) void score_many_kernel(
                 bal = __ballot(pd);
               }
             }
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if ((lane & 15) == 0) lds_fmax(&tau_sh[qb * 4 + kg], tlv[wave][qb * 4 + kg][k - 1]);
         }
       }
 #undef TQ_LOGIT
