@@ -16,6 +16,9 @@ Reported on one JSON line:
   roofline     the dominant kernel (encode, a bf16 MFMA contraction)
   roofline_score  the score kernel on the 32-layer stream (HBM-bound)
   cpu_baseline the CPU oracle (numpy float64) on a bounded sample of the step
+Further sections (each can be switched off): long-context attention, the
+bit-width sweep, and high-dimensional batched search (d = m = 1024, 1M
+vectors, 1024 queries, top-10).
 """
 import argparse
 import json
@@ -29,6 +32,7 @@ sys.path.insert(0, ROOT)
 PROFILE = os.path.join(ROOT, "profiles", "bench_kernels_d128_b3.md")
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
 
 N_KV, SEQ, D, M, G = 8, 32768, 128, 128, 4
 LAYERS = 32
@@ -44,6 +48,7 @@ def _parse():
     ap.add_argument("--no-hbm-score", action="store_true")
     ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-highdim", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling PMC byte counters)")
@@ -306,6 +311,54 @@ def main():
             del cp, cm, lg, sws, xr
         out["bit_width_sweep"] = {"workload": f"{sn} x d {D} float32 (unit direction x log-normal norm), "
                                               f"{snq} N(0,1) queries, m={M}", "rows": rows}
+
+    if not args.no_highdim:
+        # high-dimensional batched scoring: 1,048,576 x d 1024 float32 vectors
+        # (N(0,1), 1% channels x10), b = 3, m = 1024; 1024 queries, top-10
+        hn, hq, hd, hk = 1 << 20, 1024, 1024, 10
+        hp = tq.Params(hd, 3, hd, tq.MODE_PROD, 2, 3)
+        hx = synth.highdim_keys(hn, d=hd, seed=1, device=dev)
+        hc = tq.alloc_codes(hp, hn, dev)
+        hws = tq.alloc_workspace(tq.encode_workspace_bytes(hp, hn), dev)
+        hqv = synth.queries(hq, d=hd, seed=5, device=dev)
+        hidx = torch.empty((hq, hk), dtype=torch.int64, device=dev)
+        hval = torch.empty((hq, hk), device=dev)
+        hsws = torch.empty(tq.search_workspace_bytes(hp, hq, hn, hk), dtype=torch.uint8, device=dev)
+        tq.encode(hp, hx, hc, workspace=hws)
+        tq.search(hp, hqv, hc, hn, hk, hidx, hval, hsws)
+        torch.cuda.synchronize()
+        reps = 3
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        for _ in range(reps):
+            tq.encode(hp, hx, hc, workspace=hws)
+        e[1].record(stream)
+        for _ in range(reps):
+            tq.search(hp, hqv, hc, hn, hk, hidx, hval, hsws)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        enc_ms = e[0].elapsed_time(e[1]) / reps
+        se_ms = e[1].elapsed_time(e[2]) / reps
+        enc_alg = (2 * hd * hd + 2 * hd * hd) * hn          # Pi x and S' r per vector
+        enc_exec = 3 * enc_alg                                # hi/lo split: 3 bf16 products each
+        pairs = hq * hn
+        sc_alg = 2 * (hd + hd) * pairs                        # 2 (d + m) per (query, code)
+        sc_exec = 2 * 4 * 3 * hd * pairs                      # 4 int8 limbs x 3 parts (2 planes + signs)
+        out["highdim"] = {
+            "workload": f"{hn} x d {hd} float32 vectors (N(0,1), 1% channels x10), b=3, m={hd}; "
+                        f"{hq} N(0,1) queries, top-{hk}",
+            "encode_ms": round(enc_ms, 3), "encode_mvectors_per_s": round(hn / (enc_ms * 1e-3) / 1e6, 2),
+            "encode_tflops_algorithmic": round(enc_alg / (enc_ms * 1e-3) / 1e12, 1),
+            "encode_tflops_executed_bf16": round(enc_exec / (enc_ms * 1e-3) / 1e12, 1),
+            "encode_frac_bf16_peak_executed": round(enc_exec / (enc_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "search_ms": round(se_ms, 3),
+            "search_gpairs_per_s": round(pairs / (se_ms * 1e-3) / 1e9, 1),
+            "search_tops_algorithmic": round(sc_alg / (se_ms * 1e-3) / 1e12, 1),
+            "search_tops_executed_int8": round(sc_exec / (se_ms * 1e-3) / 1e12, 1),
+            "search_frac_int8_peak_executed": round(sc_exec / (se_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "codes_mb": round(sum(tq.codes_bytes(hp, hn)) / 1e6, 1),
+        }
+        del hx, hc, hws, hsws
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.b, args.cpu_sample_heads)

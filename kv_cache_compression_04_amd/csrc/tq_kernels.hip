@@ -806,13 +806,15 @@ __device__ __forceinline__ void bit_slices(uint32_t w, i32x4 &lo4, i32x4 &hi4) {
               (int)(w6 & 0x02020202u)};
 }
 
-// Logit of (query kg, key kc) for one 16-key tile: lane (kc, kg) of a wave,
-// planes = the key's index words of lane group kg, sw = its sign word.
+// Integer sums of one 16-key tile: lane (kc, kg) of a wave, planes = the
+// key's index words of lane group kg, sw = its sign word.  Output rows
+// 4 kg + t of column kc are limb t of query kg: ai for the index part, as for
+// the sign part.
 template <int B, bool PROD, int NP>
-__device__ __forceinline__ double tile_logit(const i32x4 *A, const uint32_t *planes, uint32_t sw,
-                                             float kn, float rn, const QConst &cst,
-                                             const Codebook &cb) {
-  i32x4 ai = {0, 0, 0, 0}, as = {0, 0, 0, 0};
+__device__ __forceinline__ void tile_sums(const i32x4 *A, const uint32_t *planes, uint32_t sw,
+                                          i32x4 &ai, i32x4 &as) {
+  ai = i32x4{0, 0, 0, 0};
+  as = i32x4{0, 0, 0, 0};
 #pragma unroll
   for (int sp = 0; sp < NP; ++sp) {
     uint32_t part = 0;
@@ -830,7 +832,16 @@ __device__ __forceinline__ double tile_logit(const i32x4 *A, const uint32_t *pla
     as = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NP], lo4, as, 0, 0, 0);
     as = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NP + 1], hi4, as, 0, 0, 0);
   }
-  // rows 4 kg + t of column kc: limb t of query kg; combine exactly in float64
+}
+
+// Logit of (query kg, key kc) for one 16-key tile, limbs combined exactly in
+// float64 (attention: the logits are exponentiated).
+template <int B, bool PROD, int NP>
+__device__ __forceinline__ double tile_logit(const i32x4 *A, const uint32_t *planes, uint32_t sw,
+                                             float kn, float rn, const QConst &cst,
+                                             const Codebook &cb) {
+  i32x4 ai, as;
+  tile_sums<B, PROD, NP>(A, planes, sw, ai, as);
   double l = 0.0;
   if (NP > 0) {
     const double vi = (double)ai[0] + 128.0 * (double)ai[1] + 16384.0 * (double)ai[2] +
@@ -841,6 +852,30 @@ __device__ __forceinline__ double tile_logit(const i32x4 *A, const uint32_t *pla
     const double vs = (double)as[0] + 128.0 * (double)as[1] + 16384.0 * (double)as[2] +
                       2097152.0 * (double)as[3];
     l += (double)rn * (vs * cst.sgn_scale - cst.sgn_bias);
+  }
+  return l;
+}
+
+// The same in float32 (plain scores): each limb is exact in float32; the
+// Horner sum and the bias subtraction carry a few 2^-24 of the index part's
+// magnitude, which exceeds the logit's own size by a factor of order sqrt(d),
+// so the logit's relative error stays near 1e-6, far under a 1e-4 bar.
+template <int B, bool PROD, int NP>
+__device__ __forceinline__ float tile_logit_f32(const i32x4 *A, const uint32_t *planes, uint32_t sw,
+                                                float kn, float rn, float si, float bi, float ss,
+                                                float bs) {
+  i32x4 ai, as;
+  tile_sums<B, PROD, NP>(A, planes, sw, ai, as);
+  float l = 0.f;
+  if (NP > 0) {
+    const float vi = fmaf(fmaf(fmaf((float)ai[3], 128.f, (float)ai[2]), 128.f, (float)ai[1]), 128.f,
+                          (float)ai[0]);
+    l = kn * fmaf(vi, si, -bi);
+  }
+  if (PROD) {
+    const float vs = fmaf(fmaf(fmaf((float)as[3], 128.f, (float)as[2]), 128.f, (float)as[1]), 128.f,
+                          (float)as[0]);
+    l = fmaf(rn, fmaf(vs, ss, -bs), l);
   }
   return l;
 }
@@ -1001,6 +1036,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
 #pragma unroll
   for (int j = 0; j < NMF; ++j) A[j] = aops[((int64_t)hg * NMF + j) * 64 + lane];
   const QConst cst = qc[(int64_t)hg * 4 + kg];
+  const float si = (float)cst.idx_scale, bi = (float)cst.idx_bias;
+  const float ss = (float)cst.sgn_scale, bs = (float)cst.sgn_bias;
   const int64_t qh = (int64_t)grp * 4 + kg;  // this lane's output query within the head
   const bool qvalid = qh < g;
   float *out = logits + ((int64_t)h * g + qh) * seq;
@@ -1040,9 +1077,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kScoreU; ++u) {
-      const double l = tile_logit<B, PROD, NP>(A, pl[u], sw[u], kn[u], rn[u], cst, cb);
+      const float l = tile_logit_f32<B, PROD, NP>(A, pl[u], sw[u], kn[u], rn[u], si, bi, ss, bs);
       const int64_t pos = (tb + u) * 16 + kc;
-      if ((tb + u) < t1 && pos < seq && qvalid) out[pos] = (float)l;
+      if ((tb + u) < t1 && pos < seq && qvalid) out[pos] = l;
     }
   }
 }
