@@ -26,7 +26,7 @@
 //     the +-1 bit signs, so c[idx] is a short sum of coefficient * (parity of
 //     a subset of planes); the QJL term is a plain +-1 dot product.  Bits
 //     become int8 MFMA operands with one AND per 4 bytes (bit k of every byte,
-//     weight 2^k, -128 for k = 7); the query side carries the weights 2^-k and
+//     weight 2^(k mod 4)); the query side carries the weights 2^-(k mod 4) and
 //     is split into four balanced base-128 int8 limbs that fill the 16 MFMA
 //     rows (4 queries x 4 limbs).  int32 accumulation is exact.
 #include <hip/hip_runtime.h>
@@ -793,17 +793,20 @@ struct QConst {  // per query, float64 so that logits keep ~1e-8 relative accura
   double idx_bias;   // sum_S coef_S * sum_c qt_c
   double sgn_scale;  // sqrt(pi/2)/m * 2^-E'
   double sgn_bias;   // sqrt(pi/2)/m * sum_r qs_r
+  float f[4];        // the same four in float32, for the plain-score epilogue
 };
 
 // The 8 bit slices of a packed word as int8 MFMA operands: slice s keeps bit s
-// of every byte.  Words are pre-shifted by s & ~1, so a set bit weighs
-// 2^(s & 1) (1 or 2) and the query side loses at most one bit to the weight.
+// of every byte.  The upper four slices come from the word shifted by 4, so a
+// set bit weighs 2^(s & 3) (1, 2, 4 or 8): one shift and eight ANDs per word.
+// The query side carries the factor 2^-(s & 3) and so loses at most three of
+// its 26 bits to the weight.
 __device__ __forceinline__ void bit_slices(uint32_t w, i32x4 &lo4, i32x4 &hi4) {
-  const uint32_t w2 = w >> 2, w4 = w >> 4, w6 = w >> 6;
-  lo4 = i32x4{(int)(w & 0x01010101u), (int)(w & 0x02020202u), (int)(w2 & 0x01010101u),
-              (int)(w2 & 0x02020202u)};
-  hi4 = i32x4{(int)(w4 & 0x01010101u), (int)(w4 & 0x02020202u), (int)(w6 & 0x01010101u),
-              (int)(w6 & 0x02020202u)};
+  const uint32_t w4 = w >> 4;
+  lo4 = i32x4{(int)(w & 0x01010101u), (int)(w & 0x02020202u), (int)(w & 0x04040404u),
+              (int)(w & 0x08080808u)};
+  hi4 = i32x4{(int)(w4 & 0x01010101u), (int)(w4 & 0x02020202u), (int)(w4 & 0x04040404u),
+              (int)(w4 & 0x08080808u)};
 }
 
 // Integer sums of one 16-key tile: lane (kc, kg) of a wave, planes = the
@@ -856,10 +859,12 @@ __device__ __forceinline__ double tile_logit(const i32x4 *A, const uint32_t *pla
   return l;
 }
 
-// The same in float32 (plain scores): each limb is exact in float32; the
-// Horner sum and the bias subtraction carry a few 2^-24 of the index part's
-// magnitude, which exceeds the logit's own size by a factor of order sqrt(d),
-// so the logit's relative error stays near 1e-6, far under a 1e-4 bar.
+// The same in float32 (plain scores).  Each accumulated limb is below 2^19
+// in magnitude, so limbs 0 + 128 * 1 and 2 + 128 * 3 pair up exactly in int32;
+// the two conversions, the final fma and the bias subtraction carry a few
+// 2^-24 of the index part's magnitude, which exceeds the logit's own size by
+// a factor of order sqrt(d), so the logit's relative error stays near 1e-6,
+// far under a 1e-4 bar.
 template <int B, bool PROD, int NP>
 __device__ __forceinline__ float tile_logit_f32(const i32x4 *A, const uint32_t *planes, uint32_t sw,
                                                 float kn, float rn, float si, float bi, float ss,
@@ -868,13 +873,11 @@ __device__ __forceinline__ float tile_logit_f32(const i32x4 *A, const uint32_t *
   tile_sums<B, PROD, NP>(A, planes, sw, ai, as);
   float l = 0.f;
   if (NP > 0) {
-    const float vi = fmaf(fmaf(fmaf((float)ai[3], 128.f, (float)ai[2]), 128.f, (float)ai[1]), 128.f,
-                          (float)ai[0]);
+    const float vi = fmaf((float)(ai[2] + (ai[3] << 7)), 16384.f, (float)(ai[0] + (ai[1] << 7)));
     l = kn * fmaf(vi, si, -bi);
   }
   if (PROD) {
-    const float vs = fmaf(fmaf(fmaf((float)as[3], 128.f, (float)as[2]), 128.f, (float)as[1]), 128.f,
-                          (float)as[0]);
+    const float vs = fmaf((float)(as[2] + (as[3] << 7)), 16384.f, (float)(as[0] + (as[1] << 7)));
     l = fmaf(rn, fmaf(vs, ss, -bs), l);
   }
   return l;
@@ -892,27 +895,36 @@ __device__ __forceinline__ int limb_of(int Q, int t) {
   return digit;
 }
 
-// Query preparation for one (KV head, group of 4 queries): qt = Pi q and
-// qs = S q in float32, then the int8 operands of the score MFMAs.
-// One workgroup of 256 threads per group.
-constexpr int kQprepThreads = 512;
+// Query preparation for the d = 128 kernels, one workgroup of 1024 threads
+// per (KV head, group of 4 queries):
+//   1. the rows of Pi (and S) are copied into LDS with coalesced loads;
+//   2. wave w takes query w % 4 and rows 64 (w / 4) .. + 63, one per lane,
+//      and forms qt = Pi q (rows < 128) or qs = S q in float64; the query is
+//      wave-uniform, so it is read with scalar loads, and the row elements
+//      come from LDS with a padded stride (no bank conflicts);
+//   3. per query: the exponents that put the largest operand below 2^26, the
+//      per-query constants, and
+//   4. the int8 operands of the score MFMAs.  MFMA j (part j / 2, half j % 2;
+//      the sign part last) lane l = 16 kg + 4 jq + t holds limb t of query jq
+//      at the coordinates of lane group kg; one thread computes the 16 scaled
+//      values of (j, jq, kg) once and writes all four limbs.
+constexpr int kQprepThreads = 1024;
+constexpr int kQprepPad = 129;  // LDS row stride in floats: lane r reads bank (r + k) mod 64
 
 template <bool PROD>
 __global__ __launch_bounds__(kQprepThreads) void qprep128_kernel(
     const float *__restrict__ q, int64_t g, int ngroups, const float *__restrict__ pi,
     const float *__restrict__ s, Codebook cb, int m, i32x4 *__restrict__ aops,
     QConst *__restrict__ qc) {
-  __shared__ float mat[256][129];   // rows of Pi (0..127) and S (128..255), padded
-  __shared__ double qin[4][128];
-  __shared__ double qv[2][4][128];  // [0] = Pi q, [1] = S q
+  constexpr int NR = PROD ? 256 : 128;  // rows: Pi, then S
+  __shared__ float mat[NR][kQprepPad];
+  __shared__ double qvs[2][4][128];  // [0] = Pi q, [1] = S q
   __shared__ int expo[4][2];
   const int hg = blockIdx.x;
   const int h = hg / ngroups, grp = hg % ngroups;
   const int tid = threadIdx.x;
   {
-    // 64 KB (Pi) + 64 KB (S): 16 float4 per thread, all issued before any use
-    constexpr int kRows = PROD ? 256 : 128;
-    constexpr int kPer = kRows * 32 / kQprepThreads;
+    constexpr int kPer = NR * 32 / kQprepThreads;  // float4 per thread
     float4 buf[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -930,25 +942,19 @@ __global__ __launch_bounds__(kQprepThreads) void qprep128_kernel(
       mat[r][4 * c4 + 3] = buf[i].w;
     }
   }
-  for (int i = tid; i < 512; i += kQprepThreads) {
-    const int jq = i >> 7, c = i & 127;
-    const int64_t qh = (int64_t)grp * 4 + jq;
-    qin[jq][c] = qh < g ? (double)q[((int64_t)h * g + qh) * 128 + c] : 0.0;
-  }
   __syncthreads();
   {
-    // thread -> one row (Pi rows 0..127, S rows 128..255) and two queries, float64 sums
-    const int r = tid & 255, jp = tid >> 8;  // queries 2 jp, 2 jp + 1
-    if (r < 128 || PROD) {
-      double a0 = 0.0, a1 = 0.0;
-#pragma unroll 8
-      for (int j = 0; j < 128; ++j) {
-        const double w = (double)mat[r][j];
-        a0 = fma(w, qin[2 * jp][j], a0);
-        a1 = fma(w, qin[2 * jp + 1][j], a1);
-      }
-      qv[r >> 7][2 * jp][r & 127] = a0;
-      qv[r >> 7][2 * jp + 1][r & 127] = a1;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int jq = wv & 3, r = (wv >> 2) * 64 + (tid & 63);
+    const int64_t qh = (int64_t)grp * 4 + jq;
+    if (r < NR && qh < g) {
+      const float *qrow = q + ((int64_t)h * g + qh) * 128;  // wave-uniform
+      double acc = 0.0;
+#pragma unroll 16
+      for (int k = 0; k < 128; ++k) acc = fma((double)mat[r][k], (double)qrow[k], acc);
+      qvs[r >> 7][jq][r & 127] = acc;
+    } else if (r < NR) {
+      qvs[r >> 7][jq][r & 127] = 0.0;
     }
   }
   __syncthreads();
@@ -956,10 +962,10 @@ __global__ __launch_bounds__(kQprepThreads) void qprep128_kernel(
   if (tid < 256) {
     // wave w reduces query w: max |qt|, max |qs|, sum qt, sum qs
     const int jq = tid >> 6, lane = tid & 63;
-    double mq = fmax(fabs(qv[0][jq][lane]), fabs(qv[0][jq][lane + 64]));
-    double ms = PROD ? fmax(fabs(qv[1][jq][lane]), fabs(qv[1][jq][lane + 64])) : 0.0;
-    double sq = qv[0][jq][lane] + qv[0][jq][lane + 64];
-    double ss = PROD ? qv[1][jq][lane] + qv[1][jq][lane + 64] : 0.0;
+    double mq = fmax(fabs(qvs[0][jq][lane]), fabs(qvs[0][jq][lane + 64]));
+    double ms = PROD ? fmax(fabs(qvs[1][jq][lane]), fabs(qvs[1][jq][lane + 64])) : 0.0;
+    double sq = qvs[0][jq][lane] + qvs[0][jq][lane + 64];
+    double ss = PROD ? qvs[1][jq][lane] + qvs[1][jq][lane + 64] : 0.0;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       mq = fmax(mq, __shfl_xor(mq, off));
@@ -986,100 +992,194 @@ __global__ __launch_bounds__(kQprepThreads) void qprep128_kernel(
       o.idx_bias = acoef * sq;
       o.sgn_scale = cq * ldexp(1.0, -e2);
       o.sgn_bias = cq * ss;
+      o.f[0] = (float)o.idx_scale;
+      o.f[1] = (float)o.idx_bias;
+      o.f[2] = (float)o.sgn_scale;
+      o.f[3] = (float)o.sgn_bias;
       qc[(int64_t)hg * 4 + jq] = o;
     }
   }
   __syncthreads();
   const int NMF = score_mfmas(NP, PROD);
+  uint32_t *aw = reinterpret_cast<uint32_t *>(aops);
   for (int i = tid; i < NMF * 64; i += kQprepThreads) {
-    const int j = i >> 6, l = i & 63;
-    const int row = l & 15, kg = l >> 4;
-    const int jq = row >> 2, t = row & 3;
+    // unit (j, jq, kg, w): word w of the four lanes 16 kg + 4 jq + t
+    const int j = i >> 6, jq = (i >> 4) & 3, kg = (i >> 2) & 3, w = i & 3;
     const bool sgnpart = j >= 2 * NP;
-    const int h2 = j & 1;
+    const int sl = 4 * (j & 1) + w;
     const double coef = sgnpart ? 2.0 : 2.0 * cb.coef[j >> 1];
     const int E = expo[jq][sgnpart ? 1 : 0];
-    const double *src = qv[sgnpart ? 1 : 0][jq];
-    int out[4];
+    const double *src = qvs[sgnpart ? 1 : 0][jq];
+    uint32_t out[4] = {0u, 0u, 0u, 0u};  // limb t
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t packed = 0;
-      const int sl = 4 * h2 + w;
+    for (int e = 0; e < 4; ++e) {
+      const int c = 32 * e + 16 * (sl >> 2) + 4 * kg + (sl & 3);
+      int Q = (int)llrint(ldexp(coef * src[c], E - (sl & 3)));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = 32 * e + 16 * (sl >> 2) + 4 * kg + (sl & 3);
-        const int Q = (int)llrint(ldexp(coef * src[c], E - (sl & 1)));
-        packed |= (uint32_t)(uint8_t)(int8_t)limb_of(Q, t) << (8 * e);
+      for (int t = 0; t < 4; ++t) {  // balanced base-128 digits, lowest first
+        const int digit = ((Q + 64) & 127) - 64;
+        Q = (Q - digit) >> 7;  // exact: Q - digit is a multiple of 128
+        out[t] |= (uint32_t)(uint8_t)(int8_t)digit << (8 * e);
       }
-      out[w] = (int)packed;
     }
-    aops[((int64_t)hg * NMF + j) * 64 + l] = i32x4{out[0], out[1], out[2], out[3]};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) aw[(((int64_t)hg * NMF + j) * 64 + 16 * kg + 4 * jq + t) * 4 + w] = out[t];
   }
 }
 
-constexpr int kScoreU = 8;  // tiles whose loads are issued together
+template <bool PROD>
+static void launch_qprep128(const Derived &D, const float *q, int64_t g, int ngroups, int64_t nhg,
+                            i32x4 *aops, QConst *qc, hipStream_t s) {
+  qprep128_kernel<PROD><<<dim3((unsigned)nhg), dim3(kQprepThreads), 0, s>>>(q, g, ngroups, D.pi32, D.s32,
+                                                                       D.cb, D.p.m, aops, qc);
+}
+
+constexpr int kScoreU = 4;  // tiles per load batch (64 keys)
+constexpr int kScoreH = 4;  // batches per wave, all requested before any is consumed
+
+// The codes of kScoreU consecutive 16-key tiles as one lane holds them: its
+// own index and sign words of every tile, and the norms of key `lane` of the
+// batch (spread to the lanes that need them with ds_bpermute).
+template <int BB>
+struct ScoreBatch {
+  uint32_t pl[kScoreU][BB];
+  uint32_t sw[kScoreU];
+  float kn, rn;
+};
+
+// Loads of a batch whose tiles all lie inside the sequence.  The bases are
+// wave-uniform (scalar registers) and the lane offsets do not change between
+// batches, so no vector address arithmetic is spent per tile.
+template <int B, bool PROD>
+__device__ __forceinline__ void score_load_full(ScoreBatch<(B > 0 ? B : 1)> &b,
+                                                const uint32_t *idx_t, const uint32_t *sgn_t,
+                                                const float *kn_t, const float *rn_t,
+                                                uint32_t off_idx, uint32_t off_sgn, uint32_t lane) {
+  constexpr int BB = B > 0 ? B : 1;
+#pragma unroll
+  for (int u = 0; u < kScoreU; ++u) {
+    const uint32_t *ip = idx_t + (uint32_t)(u * 64 * BB) + off_idx;
+    if constexpr (B == 1) {
+      b.pl[u][0] = ip[0];
+    } else if constexpr (B == 2) {
+      const uint2 t = *reinterpret_cast<const uint2 *>(ip);
+      b.pl[u][0] = t.x; b.pl[u][1] = t.y;
+    } else if constexpr (B == 3) {
+      b.pl[u][0] = ip[0]; b.pl[u][1] = ip[1]; b.pl[u][2] = ip[2];
+    } else if constexpr (B == 4) {
+      const uint4 t = *reinterpret_cast<const uint4 *>(ip);
+      b.pl[u][0] = t.x; b.pl[u][1] = t.y; b.pl[u][2] = t.z; b.pl[u][3] = t.w;
+    } else {
+      b.pl[u][0] = 0u;
+    }
+    b.sw[u] = PROD ? sgn_t[(uint32_t)(u * 64) + off_sgn] : 0u;
+  }
+  b.kn = kn_t[lane];
+  b.rn = PROD ? rn_t[lane] : 0.f;
+}
+
+template <int B, bool PROD, int NP>
+__device__ __forceinline__ void score_store_full(const ScoreBatch<(B > 0 ? B : 1)> &b,
+                                                 const i32x4 *A, float si, float bi, float ss,
+                                                 float bs, float *out_t, bool qvalid, int kc) {
+  // One tile at a time (the scheduling barrier keeps the MFMA accumulators
+  // of different tiles from being live together), and every logit computed
+  // before the store branch so that no load is sunk into it.
+  float l[kScoreU];
+#pragma unroll
+  for (int u = 0; u < kScoreU; ++u) {
+    const int src = (16 * u + kc) * 4;  // byte address of lane 16 u + kc
+    const float kn = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, b.kn)));
+    const float rn = PROD ? __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, b.rn)))
+                          : 0.f;
+    l[u] = tile_logit_f32<B, PROD, NP>(A, b.pl[u], b.sw[u], kn, rn, si, bi, ss, bs);
+    asm volatile("" ::"v"(l[u]));  // materialise here, not inside the branch below
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int u = 0; u < kScoreU; ++u) out_t[u * 16] = l[u];
+  }
+}
 
 template <int B, bool PROD>
 __global__ __launch_bounds__(kScoreWaves * 64) void score128_kernel(
     const i32x4 *__restrict__ aops, const QConst *__restrict__ qc,
     const uint32_t *__restrict__ idx, const uint32_t *__restrict__ sgn,
     const float *__restrict__ knorm, const float *__restrict__ rnorm, int64_t seq, int64_t g,
-    int ngroups, int tiles_per_wave, Codebook cb, float *__restrict__ logits) {
+    int ngroups, Codebook cb, float *__restrict__ logits) {
   constexpr int NP = B == 0 ? 0 : (B == 1 ? 1 : B == 2 ? 2 : B == 3 ? 4 : 8);
   constexpr int NMF = score_mfmas(NP, PROD);
   constexpr int BB = B > 0 ? B : 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = blockIdx.y;
   const int h = hg / ngroups, grp = hg % ngroups;
   const int kc = lane & 15, kg = lane >> 4;
   i32x4 A[NMF];
 #pragma unroll
   for (int j = 0; j < NMF; ++j) A[j] = aops[((int64_t)hg * NMF + j) * 64 + lane];
-  const QConst cst = qc[(int64_t)hg * 4 + kg];
-  const float si = (float)cst.idx_scale, bi = (float)cst.idx_bias;
-  const float ss = (float)cst.sgn_scale, bs = (float)cst.sgn_bias;
+  // float32 constants: no conversion, so nothing waits for these loads
+  // before the first codes are requested
+  const float4 cf = *reinterpret_cast<const float4 *>(qc[(int64_t)hg * 4 + kg].f);
+  const float si = cf.x, bi = cf.y, ss = cf.z, bs = cf.w;
   const int64_t qh = (int64_t)grp * 4 + kg;  // this lane's output query within the head
   const bool qvalid = qh < g;
-  float *out = logits + ((int64_t)h * g + qh) * seq;
+  float *out = logits + ((int64_t)h * g + (qvalid ? qh : 0)) * seq;
   const uint32_t *idx_h = idx + (int64_t)h * seq * 4 * BB;
   const uint32_t *sgn_h = sgn + (int64_t)h * seq * 4;
   const float *kn_h = knorm + (int64_t)h * seq;
   const float *rn_h = rnorm + (int64_t)h * seq;
 
-  const int64_t tiles = (seq + 15) / 16;
-  const int64_t t0 = ((int64_t)blockIdx.x * kScoreWaves + wave) * tiles_per_wave;
-  const int64_t t1 = t0 + tiles_per_wave < tiles ? t0 + tiles_per_wave : tiles;
-  // Positions are clamped into the sequence so every load is in bounds and the
-  // loads of a group of kScoreU tiles issue back to back; results of
-  // out-of-range tiles are not stored.
-  for (int64_t tb = t0; tb < t1; tb += kScoreU) {
+  // Work of a wave: kScoreH consecutive batches of kScoreU tiles, whose loads
+  // are all issued at once before the first is consumed (the codes are read
+  // once; many short-lived waves on neighbouring tiles stream HBM best).
+  // Batches past the last whole one load a clamped, in-bounds copy and are
+  // not stored.  Tile indices within one head fit in 32 bits (seq < 2^35);
+  // all of this is wave-uniform.
+  const int tiles = (int)((seq + 15) / 16);
+  const int nbf = (int)(seq / 16) / kScoreU;  // batches whose tiles are all full
+  const int nw = (int)gridDim.x * kScoreWaves;
+  const int j = (int)blockIdx.x * kScoreWaves + wave;
+  const int bc = j * kScoreH;
+  if (bc < nbf) {
+    const uint32_t off_idx = (uint32_t)((kc * 4 + kg) * BB), off_sgn = (uint32_t)(kc * 4 + kg);
+    ScoreBatch<BB> bt[kScoreH];
+#pragma unroll
+    for (int u = 0; u < kScoreH; ++u) {
+      const int64_t t_ = (int64_t)(bc + u < nbf ? bc + u : nbf - 1) * kScoreU;
+      score_load_full<B, PROD>(bt[u], idx_h + t_ * 64 * BB, sgn_h + t_ * 64, kn_h + t_ * 16,
+                               rn_h + t_ * 16, off_idx, off_sgn, (uint32_t)lane);
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreH; ++u)
+      if (bc + u < nbf)
+        score_store_full<B, PROD, NP>(bt[u], A, si, bi, ss, bs,
+                                      out + (int64_t)(bc + u) * (16 * kScoreU) + kc, qvalid, kc);
+  }
+  // The rest (fewer than a batch of tiles, the last one possibly partial),
+  // taken by the last wave: positions are clamped into the sequence so every
+  // load is in bounds; results of out-of-range positions are not stored.
+  if (j != nw - 1) return;
+  for (int tb = nbf * kScoreU; tb < tiles; tb += kScoreU) {
     uint32_t pl[kScoreU][BB], sw[kScoreU];
     float kn[kScoreU], rn[kScoreU];
 #pragma unroll
     for (int u = 0; u < kScoreU; ++u) {
-      const int64_t pos = (tb + u) * 16 + kc;
-      const uint32_t vp = (uint32_t)(pos < seq ? pos : seq - 1);
-      const uint32_t *ip = idx_h + (vp * 4u + kg) * BB;
-      if constexpr (B == 1) {
-        pl[u][0] = ip[0];
-      } else if constexpr (B == 2) {
-        const uint2 t = *reinterpret_cast<const uint2 *>(ip);
-        pl[u][0] = t.x; pl[u][1] = t.y;
-      } else if constexpr (B == 3) {
-        pl[u][0] = ip[0]; pl[u][1] = ip[1]; pl[u][2] = ip[2];
-      } else if constexpr (B == 4) {
-        const uint4 t = *reinterpret_cast<const uint4 *>(ip);
-        pl[u][0] = t.x; pl[u][1] = t.y; pl[u][2] = t.z; pl[u][3] = t.w;
-      }
-      sw[u] = PROD ? sgn_h[vp * 4u + kg] : 0u;
+      const int64_t pos = (int64_t)(tb + u) * 16 + kc;
+      const int64_t vp = pos < seq ? pos : seq - 1;
+      const uint32_t *ip = idx_h + (vp * 4 + kg) * BB;
+#pragma unroll
+      for (int p = 0; p < BB; ++p) pl[u][p] = B > 0 ? ip[p] : 0u;
+      sw[u] = PROD ? sgn_h[vp * 4 + kg] : 0u;
       kn[u] = kn_h[vp];
       rn[u] = PROD ? rn_h[vp] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kScoreU; ++u) {
       const float l = tile_logit_f32<B, PROD, NP>(A, pl[u], sw[u], kn[u], rn[u], si, bi, ss, bs);
-      const int64_t pos = (tb + u) * 16 + kc;
-      if ((tb + u) < t1 && pos < seq && qvalid) out[pos] = l;
+      const int64_t pos = (int64_t)(tb + u) * 16 + kc;
+      if (pos < seq && qvalid) out[pos] = l;
     }
   }
 }
@@ -1097,21 +1197,16 @@ static void launch_score_t(const Derived &D, const float *q, int64_t n_kv, int64
                            tq_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
   const int ngroups = (int)((g + 3) / 4);
   const int NMF = score_mfmas(nparts_of(B), PROD);
+  const int64_t nhg = n_kv * ngroups;
   i32x4 *aops = (i32x4 *)ws;
-  QConst *qc = (QConst *)((char *)ws + (size_t)n_kv * ngroups * NMF * 64 * sizeof(i32x4));
-  qprep128_kernel<PROD><<<dim3((unsigned)(n_kv * ngroups)), dim3(kQprepThreads), 0, s>>>(
-      q, g, ngroups, D.pi32, D.s32, D.cb, D.p.m, aops, qc);
-  // tiles per wave: a multiple of the prefetch depth, aiming at >= 8 waves per SIMD
-  const int64_t tiles = (seq + 15) / 16;
-  const int64_t total = tiles * n_kv * ngroups;
-  const int64_t want_waves = 8LL * 4 * num_cus(D.device);
-  int tpw = (int)std::min<int64_t>(32, std::max<int64_t>(kScoreU, total / std::max<int64_t>(1, want_waves)));
-  tpw = (tpw + kScoreU - 1) / kScoreU * kScoreU;
-  const int64_t chunks = (tiles + (int64_t)tpw * kScoreWaves - 1) / ((int64_t)tpw * kScoreWaves);
+  QConst *qc = (QConst *)((char *)ws + (size_t)nhg * NMF * 64 * sizeof(i32x4));
+  launch_qprep128<PROD>(D, q, g, ngroups, nhg, aops, qc, s);
+  // Workgroups per (KV head, query group): enough waves for every batch.
+  const int64_t nb = (seq + 16 * kScoreU - 1) / (16 * kScoreU);
+  const int64_t chunks = std::max<int64_t>(1, (nb + kScoreH * kScoreWaves - 1) / (kScoreH * kScoreWaves));
   score128_kernel<B, PROD><<<dim3((unsigned)chunks, (unsigned)(n_kv * ngroups)),
                              dim3(kScoreWaves * 64), 0, s>>>(aops, qc, c.idx, c.sgn, c.knorm,
-                                                             c.rnorm, seq, g, ngroups, tpw, D.cb,
-                                                             logits);
+                                                             c.rnorm, seq, g, ngroups, D.cb, logits);
 }
 
 static tq_status launch_score128(const Derived &D, const float *q, int64_t n_kv, int64_t g,
@@ -1294,6 +1389,10 @@ __global__ __launch_bounds__(256) void qops_kernel(const double *__restrict__ qp
       o.idx_bias = acoef * sq;
       o.sgn_scale = cq * ldexp(1.0, -e2);
       o.sgn_bias = cq * ss;
+      o.f[0] = (float)o.idx_scale;
+      o.f[1] = (float)o.idx_bias;
+      o.f[2] = (float)o.sgn_scale;
+      o.f[3] = (float)o.sgn_bias;
       qc[hq * 4 * QB + qb * 4 + jq] = o;
     }
   }
@@ -1318,7 +1417,7 @@ __global__ __launch_bounds__(256) void qops_kernel(const double *__restrict__ qp
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c = 128 * qp + 32 * e + 16 * (sl >> 2) + 4 * kp + (sl & 3);
-          const int Q = (int)llrint(ldexp(coef * src[c], E - (sl & 1)));
+          const int Q = (int)llrint(ldexp(coef * src[c], E - (sl & 3)));
           packed |= (uint32_t)(uint8_t)(int8_t)limb_of(Q, t) << (8 * e);
         }
         out[w] = (int)packed;
@@ -2044,8 +2143,8 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
   // ---------------- phase 3: o_rot = sum_n w_n c_V[idx_n] as int8 MFMAs
   // B lane (c16 = (w, beta), kg) covers positions 16 kg + 4 gi + e of each
   // block: byte e of dword gi of D_beta is byte beta of index word w of
-  // position 4 gi + e.  Slice s (bit s of every byte, pre-shifted so a bit
-  // weighs 2^(s & 1)) is coordinate 32 beta + 16 (s / 4) + 4 w + s % 4.
+  // position 4 gi + e.  Slice s (bit s of every byte; a set bit weighs
+  // 2^(s & 3)) is coordinate 32 beta + 16 (s / 4) + 4 w + s % 4.
   const int w = c16 >> 2, beta = c16 & 3;
   const uint32_t sel_lo = (uint32_t)(beta | (beta + 4) << 8 | 0x0C0C0000u);
   i32x4 acc[8];
@@ -2155,7 +2254,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
       const double v = (double)a[0] + 128.0 * (double)a[1] + 16384.0 * (double)a[2] +
                        2097152.0 * (double)a[3];
       const int c = 32 * beta + 16 * (sl >> 2) + 4 * w + (sl & 3);
-      dst->o[c] = (float)(ldexp(v, -E - (sl & 1)) - qsum);
+      dst->o[c] = (float)(ldexp(v, -E - (sl & 3)) - qsum);
     }
     if (c16 == 0) {
       dst->m = m;
@@ -2242,8 +2341,7 @@ static void launch_attend_t(const Derived &K, const Derived &V, const float *q, 
   uintptr_t pp = (uintptr_t)((char *)qc + (size_t)nhg * 4 * sizeof(QConst));
   pp = (pp + 255) & ~(uintptr_t)255;
   AttPartial *part = (AttPartial *)pp;
-  qprep128_kernel<true><<<dim3((unsigned)nhg), dim3(kQprepThreads), 0, s>>>(q, g, ngroups, K.pi32, K.s32, K.cb,
-                                                                  K.p.m, aops, qc);
+  launch_qprep128<true>(K, q, g, ngroups, nhg, aops, qc, s);
   attend128_kernel<BK, BV><<<dim3((unsigned)((nsplit + kAttWaves - 1) / kAttWaves), (unsigned)nhg),
                              dim3(kAttWaves * 64), 0, s>>>(aops, qc, k.idx, k.sgn, k.knorm, k.rnorm,
                                                            v.idx, v.knorm, seq, g, ngroups, nsplit,
