@@ -2180,15 +2180,21 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
       const float wv[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
 #pragma unroll
       for (int sp = 0; sp < NPV; ++sp) {
-        const double cf = 2.0 * vcb.coef[sp];
+        // Q = 2 a_S w 2^E rounded in float32: any integer near it serves, as
+        // the MFMA sum and the correction qsum use the same Q
+        const float cf = (float)ldexp(2.0 * vcb.coef[sp], E);
         uint32_t lw[4] = {0u, 0u, 0u, 0u};
         int qs = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int Q = (int)llrint(ldexp(cf * (double)wv[e], E));
+          int Q = (int)rintf(cf * wv[e]);
           qs += Q;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) lw[t] |= (uint32_t)(uint8_t)(int8_t)limb_of(Q, t) << (8 * e);
+          for (int t = 0; t < 4; ++t) {  // balanced base-128 digits, lowest first
+            const int digit = ((Q + 64) & 127) - 64;
+            Q = (Q - digit) >> 7;  // exact: Q - digit is a multiple of 128
+            lw[t] |= (uint32_t)(digit & 0xFF) << (8 * e);
+          }
         }
         qsum += ldexp(0.5 * (double)qs, -E);
 #pragma unroll
