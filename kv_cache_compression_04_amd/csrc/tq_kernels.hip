@@ -71,6 +71,15 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
+// w = 2 w + (bit of this lane in mask): one v_addc with the lane mask as
+// carry-in, which shifts a compare result into a packed word.
+__device__ __forceinline__ uint32_t shift_in(uint32_t w, uint64_t mask) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(mask));
+  return r;
+}
+
 // ===========================================================================
 // Encode, d = m = 128
 // ===========================================================================
@@ -142,7 +151,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
     const int64_t v0 = batch * kEncBatch;
     uint4 xh[kEncCT][4], xl[kEncCT][4];
     float nu[kEncCT];
-    float cs[kEncCT][1 << B], ts[kEncCT][(1 << B) > 1 ? (1 << B) - 1 : 1];
+    // the codebook is odd: magnitudes only, scaled by ||x||
+    constexpr int kHalf = B > 0 ? 1 << (B - 1) : 1;
+    float cp[kEncCT][kHalf], tp[kEncCT][kHalf > 1 ? kHalf - 1 : 1];
 #pragma unroll
     for (int ct = 0; ct < kEncCT; ++ct) {
       const int64_t row = v0 + 16 * ct + vcol;
@@ -157,10 +168,10 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
       // residual is formed as y - c ||x|| = ||x|| (u - c), so no division is
       // needed; a zero vector gets y = 0 and a zero residual
 #pragma unroll
-      for (int j = 0; j < (1 << B); ++j) cs[ct][j] = cb.c[j] * nu[ct];
+      for (int j = 0; j < kHalf; ++j) cp[ct][j] = B > 0 ? cb.c[kHalf + j] * nu[ct] : 0.f;
       // (for a zero vector the unscaled boundaries reproduce the u = 0 decisions)
 #pragma unroll
-      for (int j = 0; j + 1 < (1 << B); ++j) ts[ct][j] = nu[ct] > 0.f ? cb.t[j] * nu[ct] : cb.t[j];
+      for (int j = 0; j + 1 < kHalf; ++j) tp[ct][j] = nu[ct] > 0.f ? cb.t[kHalf + j] * nu[ct] : cb.t[kHalf + j];
     }
 
     // Coordinates are processed in 4 blocks of 32 (kt2).  For each block:
@@ -215,24 +226,33 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
             const float y = acc[h][ct][i];  // ||x|| u
             float r = y;
             if (B > 0) {
-              // thermometer code g_j = [u >= t_j]; bit k of the index is the
-              // parity of g_{m 2^k - 1}, m = 1, 2, ...; bits are shifted in
-              // (w = 2 w + bit), so the word comes out bit-reversed
-              bool gj[(1 << B) > 1 ? (1 << B) - 1 : 1];
-              float c = cs[ct][0];
+              // The codebook is odd and its middle boundary is 0, so the top
+              // index bit is the sign s = [y >= 0] and the lower B - 1 bits
+              // are mi (s = 1) or its complement (s = 0), where mi counts the
+              // positive boundaries below |y| (a tie |y| = t goes to the
+              // larger magnitude on both sides; it lies on the boundary).
+              // Thermometer g_j = [|y| >= t_j]; bit k of mi is the parity of
+              // g_{m 2^k - 1}, m = 1, 2, ...  Bits are shifted in from the
+              // lane masks (w = 2 w + bit), so words come out bit-reversed.
+              const float a = fabsf(y);
+              const uint64_t sm = __builtin_amdgcn_ballot_w64(y >= 0.f);
+              uint64_t gm[kHalf > 1 ? kHalf - 1 : 1];
+              float cm = cp[ct][0];
 #pragma unroll
-              for (int j = 0; j < (1 << B) - 1; ++j) {
-                gj[j] = y >= ts[ct][j];
-                c = gj[j] ? cs[ct][j + 1] : c;
+              for (int j = 0; j < kHalf - 1; ++j) {
+                const bool gj = a >= tp[ct][j];
+                gm[j] = __builtin_amdgcn_ballot_w64(gj);
+                cm = gj ? cp[ct][j + 1] : cm;
               }
 #pragma unroll
-              for (int p = 0; p < B; ++p) {
-                bool bit = false;
+              for (int p = 0; p + 1 < B; ++p) {
+                uint64_t mk = 0;
 #pragma unroll
-                for (int j = (1 << p) - 1; j < (1 << B) - 1; j += (1 << p)) bit ^= gj[j];
-                planes[ct][p] = planes[ct][p] + planes[ct][p] + (bit ? 1u : 0u);
+                for (int j = (1 << p) - 1; j < kHalf - 1; j += (1 << p)) mk ^= gm[j];
+                planes[ct][p] = shift_in(planes[ct][p], ~(sm ^ mk));
               }
-              r = y - c;
+              planes[ct][B - 1] = shift_in(planes[ct][B - 1], sm);
+              r = y - __builtin_copysignf(cm, y);
             }
             rsq[ct] = fmaf(r, r, rsq[ct]);
             rho[i] = r;
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
 #pragma unroll
         for (int nt = 7; nt >= 0; --nt)
 #pragma unroll
-          for (int i = 3; i >= 0; --i) w = w + w + (acc2[nt][ct][i] >= 0.f ? 1u : 0u);
+          for (int i = 3; i >= 0; --i) w = shift_in(w, __builtin_amdgcn_ballot_w64(acc2[nt][ct][i] >= 0.f));
       }
       sbits[ct] = w;
     }
