@@ -919,9 +919,10 @@ __device__ __forceinline__ int limb_of(int Q, int t) {
 // per (KV head, group of 4 queries):
 //   1. the rows of Pi (and S) are copied into LDS with coalesced loads;
 //   2. wave w takes query w % 4 and rows 64 (w / 4) .. + 63, one per lane,
-//      and forms qt = Pi q (rows < 128) or qs = S q in float64; the query is
-//      wave-uniform, so it is read with scalar loads, and the row elements
-//      come from LDS with a padded stride (no bank conflicts);
+//      and forms qt = Pi q (rows < 128) or qs = S q (float32 partial sums of
+//      8 products, accumulated in float64); the query is wave-uniform, so it
+//      is read with scalar loads, and the row elements come from LDS with a
+//      padded stride (no bank conflicts);
 //   3. per query: the exponents that put the largest operand below 2^26, the
 //      per-query constants, and
 //   4. the int8 operands of the score MFMAs.  MFMA j (part j / 2, half j % 2;
@@ -968,10 +969,17 @@ __global__ __launch_bounds__(kQprepThreads) void qprep128_kernel(
     const int jq = wv & 3, r = (wv >> 2) * 64 + (tid & 63);
     const int64_t qh = (int64_t)grp * 4 + jq;
     if (r < NR && qh < g) {
+      // float32 partial sums of 8 products, added in float64: the error stays
+      // below 8 * 2^-24 of the sum of |products| (a few 1e-7 of |q|)
       const float *qrow = q + ((int64_t)h * g + qh) * 128;  // wave-uniform
       double acc = 0.0;
-#pragma unroll 16
-      for (int k = 0; k < 128; ++k) acc = fma((double)mat[r][k], (double)qrow[k], acc);
+#pragma unroll
+      for (int k0 = 0; k0 < 128; k0 += 8) {
+        float p = 0.f;
+#pragma unroll
+        for (int k = k0; k < k0 + 8; ++k) p = fmaf(mat[r][k], qrow[k], p);
+        acc += (double)p;
+      }
       qvs[r >> 7][jq][r & 127] = acc;
     } else if (r < NR) {
       qvs[r >> 7][jq][r & 127] = 0.0;
