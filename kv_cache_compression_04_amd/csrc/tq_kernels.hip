@@ -188,97 +188,94 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
       rsq[ct] = 0.f;
 #pragma unroll
       for (int p = 0; p < (B > 0 ? B : 1); ++p) planes[ct][p] = 0u;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc2[nt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // One 32-coordinate block kt2: GEMM 1 rows 32 kt2 .. +31, bucketise,
+    // pack, residual, GEMM-2 contribution.  The first block starts the GEMM-2
+    // accumulators from zero inside the MFMA (no register clearing).
+#define TQ_ENC_BLOCK(KT2, FIRST)                                                                                                            \
+  do {                                                                                                                                      \
+    const uint4 *Pk_ = Phi + 2 * (KT2) * 4 * 64 + lane;                                                                                     \
+    const uint4 *Sk_ = Shi + (KT2) * 64 + lane;                                                                                             \
+        f32x4 acc[2][kEncCT];                                                                                                               \
+  _Pragma("unroll")                                                                                                                         \
+        for (int h = 0; h < 2; ++h)                                                                                                         \
+  _Pragma("unroll")                                                                                                                         \
+          for (int ct = 0; ct < kEncCT; ++ct) acc[h][ct] = f32x4{0.f, 0.f, 0.f, 0.f};                                                       \
+  _Pragma("unroll")                                                                                                                         \
+        for (int kt = 0; kt < 4; ++kt) {                                                                                                    \
+  _Pragma("unroll")                                                                                                                         \
+          for (int h = 0; h < 2; ++h) {                                                                                                     \
+            const bf16x8 ah = as_bf16x8(Pk_[(h * 4 + kt) * 64]);                                                                            \
+            const bf16x8 al = as_bf16x8(Pk_[kFragU4 + (h * 4 + kt) * 64]);                                                                  \
+  _Pragma("unroll")                                                                                                                         \
+            for (int ct = 0; ct < kEncCT; ++ct) {                                                                                           \
+              const bf16x8 bh = as_bf16x8(xh[ct][kt]);                                                                                      \
+              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[h][ct], 0, 0, 0);                                            \
+              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[h][ct], 0, 0, 0);                                            \
+              if (!XBF16)                                                                                                                   \
+                acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(xl[ct][kt]), acc[h][ct], 0, 0, 0);                       \
+            }                                                                                                                               \
+          }                                                                                                                                 \
+        }                                                                                                                                   \
+        uint32_t rh[kEncCT][4], rl[kEncCT][4];                                                                                              \
+  _Pragma("unroll")                                                                                                                         \
+        for (int ct = 0; ct < kEncCT; ++ct) {                                                                                               \
+  _Pragma("unroll")                                                                                                                         \
+          for (int h = 0; h < 2; ++h) {                                                                                                     \
+            float rho[4];                                                                                                                   \
+  _Pragma("unroll")                                                                                                                         \
+            for (int i = 0; i < 4; ++i) {                                                                                                   \
+              const float y = acc[h][ct][i];                                                                                                \
+              float r = y;                                                                                                                  \
+              if (B > 0) {                                                                                                                  \
+                const float a = fabsf(y);                                                                                                   \
+                const uint64_t sm = __builtin_amdgcn_ballot_w64(y >= 0.f);                                                                  \
+                uint64_t gm[kHalf > 1 ? kHalf - 1 : 1];                                                                                     \
+                float cm = cp[ct][0];                                                                                                       \
+  _Pragma("unroll")                                                                                                                         \
+                for (int j = 0; j < kHalf - 1; ++j) {                                                                                       \
+                  const bool gj = a >= tp[ct][j];                                                                                           \
+                  gm[j] = __builtin_amdgcn_ballot_w64(gj);                                                                                  \
+                  cm = gj ? cp[ct][j + 1] : cm;                                                                                             \
+                }                                                                                                                           \
+  _Pragma("unroll")                                                                                                                         \
+                for (int p = 0; p + 1 < B; ++p) {                                                                                           \
+                  uint64_t mk = 0;                                                                                                          \
+  _Pragma("unroll")                                                                                                                         \
+                  for (int j = (1 << p) - 1; j < kHalf - 1; j += (1 << p)) mk ^= gm[j];                                                     \
+                  planes[ct][p] = shift_in(planes[ct][p], ~(sm ^ mk));                                                                      \
+                }                                                                                                                           \
+                planes[ct][B - 1] = shift_in(planes[ct][B - 1], sm);                                                                        \
+                r = y - __builtin_copysignf(cm, y);                                                                                         \
+              }                                                                                                                             \
+              rsq[ct] = fmaf(r, r, rsq[ct]);                                                                                                \
+              rho[i] = r;                                                                                                                   \
+            }                                                                                                                               \
+  _Pragma("unroll")                                                                                                                         \
+            for (int hh = 0; hh < 2; ++hh) split2(rho[2 * hh], rho[2 * hh + 1], rh[ct][2 * h + hh], rl[ct][2 * h + hh]);                    \
+          }                                                                                                                                 \
+        }                                                                                                                                   \
+        if (PROD) {                                                                                                                         \
+  _Pragma("unroll")                                                                                                                         \
+          for (int nt = 0; nt < 8; ++nt) {                                                                                                  \
+            const bf16x8 ah = as_bf16x8(Sk_[nt * 4 * 64]);                                                                                  \
+            const bf16x8 al = as_bf16x8(Sk_[kFragU4 + nt * 4 * 64]);                                                                        \
+  _Pragma("unroll")                                                                                                                         \
+            for (int ct = 0; ct < kEncCT; ++ct) {                                                                                           \
+              const bf16x8 bh = as_bf16x8(make_uint4(rh[ct][0], rh[ct][1], rh[ct][2], rh[ct][3]));                                          \
+              const bf16x8 bl = as_bf16x8(make_uint4(rl[ct][0], rl[ct][1], rl[ct][2], rl[ct][3]));                                          \
+              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, (FIRST) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc2[nt][ct], 0, 0, 0);  \
+              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc2[nt][ct], 0, 0, 0);                                        \
+              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc2[nt][ct], 0, 0, 0);                                        \
+            }                                                                                                                               \
+          }                                                                                                                                 \
+        }                                                                                                                                   \
+  } while (0)
+    TQ_ENC_BLOCK(0, true);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
-    for (int kt2 = 0; kt2 < 4; ++kt2) {
-      f32x4 acc[2][kEncCT];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int ct = 0; ct < kEncCT; ++ct) acc[h][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int nt = 2 * kt2 + h;
-          const bf16x8 ah = as_bf16x8(Phi[(nt * 4 + kt) * 64 + lane]);
-          const bf16x8 al = as_bf16x8(Plo[(nt * 4 + kt) * 64 + lane]);
-#pragma unroll
-          for (int ct = 0; ct < kEncCT; ++ct) {
-            const bf16x8 bh = as_bf16x8(xh[ct][kt]);
-            acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[h][ct], 0, 0, 0);
-            acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[h][ct], 0, 0, 0);
-            if (!XBF16)
-              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(xl[ct][kt]), acc[h][ct], 0, 0, 0);
-          }
-        }
-      }
-      uint32_t rh[kEncCT][4], rl[kEncCT][4];  // residual of this block as bf16 pairs
-#pragma unroll
-      for (int ct = 0; ct < kEncCT; ++ct) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float rho[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float y = acc[h][ct][i];  // ||x|| u
-            float r = y;
-            if (B > 0) {
-              // The codebook is odd and its middle boundary is 0, so the top
-              // index bit is the sign s = [y >= 0] and the lower B - 1 bits
-              // are mi (s = 1) or its complement (s = 0), where mi counts the
-              // positive boundaries below |y| (a tie |y| = t goes to the
-              // larger magnitude on both sides; it lies on the boundary).
-              // Thermometer g_j = [|y| >= t_j]; bit k of mi is the parity of
-              // g_{m 2^k - 1}, m = 1, 2, ...  Bits are shifted in from the
-              // lane masks (w = 2 w + bit), so words come out bit-reversed.
-              const float a = fabsf(y);
-              const uint64_t sm = __builtin_amdgcn_ballot_w64(y >= 0.f);
-              uint64_t gm[kHalf > 1 ? kHalf - 1 : 1];
-              float cm = cp[ct][0];
-#pragma unroll
-              for (int j = 0; j < kHalf - 1; ++j) {
-                const bool gj = a >= tp[ct][j];
-                gm[j] = __builtin_amdgcn_ballot_w64(gj);
-                cm = gj ? cp[ct][j + 1] : cm;
-              }
-#pragma unroll
-              for (int p = 0; p + 1 < B; ++p) {
-                uint64_t mk = 0;
-#pragma unroll
-                for (int j = (1 << p) - 1; j < kHalf - 1; j += (1 << p)) mk ^= gm[j];
-                planes[ct][p] = shift_in(planes[ct][p], ~(sm ^ mk));
-              }
-              planes[ct][B - 1] = shift_in(planes[ct][B - 1], sm);
-              r = y - __builtin_copysignf(cm, y);
-            }
-            rsq[ct] = fmaf(r, r, rsq[ct]);
-            rho[i] = r;
-          }
-          // element e of the GEMM-2 operand for block kt2 is coordinate
-          // 32 kt2 + 16 (e / 4) + 4 g + e % 4, i.e. e = 4 h + i
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) split2(rho[2 * hh], rho[2 * hh + 1], rh[ct][2 * h + hh], rl[ct][2 * h + hh]);
-        }
-      }
-      if (PROD) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const bf16x8 ah = as_bf16x8(Shi[(nt * 4 + kt2) * 64 + lane]);
-          const bf16x8 al = as_bf16x8(Slo[(nt * 4 + kt2) * 64 + lane]);
-#pragma unroll
-          for (int ct = 0; ct < kEncCT; ++ct) {
-            const bf16x8 bh = as_bf16x8(make_uint4(rh[ct][0], rh[ct][1], rh[ct][2], rh[ct][3]));
-            const bf16x8 bl = as_bf16x8(make_uint4(rl[ct][0], rl[ct][1], rl[ct][2], rl[ct][3]));
-            acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc2[nt][ct], 0, 0, 0);
-            acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc2[nt][ct], 0, 0, 0);
-            acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc2[nt][ct], 0, 0, 0);
-          }
-        }
-      }
-    }
+    for (int kt2 = 1; kt2 < 4; ++kt2) TQ_ENC_BLOCK(kt2, false);
+#undef TQ_ENC_BLOCK
     // sign bits: acc2[nt][ct][i] = z[row 16 nt + 4 g + i][vector 16 ct + vcol],
     // shifted in from the highest row down so that row 4 nt + i lands at bit 4 nt + i
     uint32_t sbits[kEncCT];
