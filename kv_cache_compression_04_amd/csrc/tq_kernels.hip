@@ -195,7 +195,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
 #define TQ_ENC_BLOCK(KT2, FIRST)                                                                                                            \
   do {                                                                                                                                      \
     const uint4 *Pk_ = Phi + 2 * (KT2) * 4 * 64 + lane;                                                                                     \
-    const uint4 *Sk_ = Shi + (KT2) * 64 + lane;                                                                                             \
+    int so_ = (KT2) * 64; asm volatile("" : "+s"(so_));                                                                                     \
+    const uint4 *Sk_ = Shi + so_ + lane;                                                                                                    \
         f32x4 acc[2][kEncCT];                                                                                                               \
   _Pragma("unroll")                                                                                                                         \
         for (int h = 0; h < 2; ++h)                                                                                                         \
