@@ -1241,6 +1241,10 @@ static tq_status launch_score128(const Derived &D, const float *q, int64_t n_kv,
     set_error("tq_score: n_kv * ceil(g/4) = %lld exceeds 65535", (long long)(n_kv * ((g + 3) / 4)));
     return TQ_ERR_UNSUPPORTED;
   }
+  if (seq >= (int64_t(1) << 34)) {  // tile indices within a head are 32-bit
+    set_error("tq_score: seq = %lld exceeds 2^34", (long long)seq);
+    return TQ_ERR_UNSUPPORTED;
+  }
   const bool prod = D.p.mode == TQ_MODE_PROD;
   switch (D.B * 2 + (prod ? 1 : 0)) {
     case 0 * 2 + 1: launch_score_t<0, true>(D, q, n_kv, g, c, seq, logits, ws, s); break;
