@@ -855,34 +855,13 @@ __device__ __forceinline__ void tile_sums(const i32x4 *A, const uint32_t *planes
   }
 }
 
-// Logit of (query kg, key kc) for one 16-key tile, limbs combined exactly in
-// float64 (attention: the logits are exponentiated).
-template <int B, bool PROD, int NP>
-__device__ __forceinline__ double tile_logit(const i32x4 *A, const uint32_t *planes, uint32_t sw,
-                                             float kn, float rn, const QConst &cst,
-                                             const Codebook &cb) {
-  i32x4 ai, as;
-  tile_sums<B, PROD, NP>(A, planes, sw, ai, as);
-  double l = 0.0;
-  if (NP > 0) {
-    const double vi = (double)ai[0] + 128.0 * (double)ai[1] + 16384.0 * (double)ai[2] +
-                      2097152.0 * (double)ai[3];
-    l += (double)kn * (vi * cst.idx_scale - cst.idx_bias);
-  }
-  if (PROD) {
-    const double vs = (double)as[0] + 128.0 * (double)as[1] + 16384.0 * (double)as[2] +
-                      2097152.0 * (double)as[3];
-    l += (double)rn * (vs * cst.sgn_scale - cst.sgn_bias);
-  }
-  return l;
-}
-
-// The same in float32 (plain scores).  Each accumulated limb is below 2^19
-// in magnitude, so limbs 0 + 128 * 1 and 2 + 128 * 3 pair up exactly in int32;
-// the two conversions, the final fma and the bias subtraction carry a few
-// 2^-24 of the index part's magnitude, which exceeds the logit's own size by
-// a factor of order sqrt(d), so the logit's relative error stays near 1e-6,
-// far under a 1e-4 bar.
+// Logit of (query kg, key kc) for one 16-key tile, in float32.  Each
+// accumulated limb is below 2^19 in magnitude, so limbs 0 + 128 * 1 and
+// 2 + 128 * 3 pair up exactly in int32; the two conversions, the final fma and
+// the bias subtraction carry a few 2^-24 of the index part's magnitude, which
+// exceeds the logit's own size by a factor of order sqrt(d), so the logit's
+// relative error stays near 1e-6, far under a 1e-4 bar (attention: the
+// softmax weights inherit it as a relative error of |logit| * 1e-6).
 template <int B, bool PROD, int NP>
 __device__ __forceinline__ float tile_logit_f32(const i32x4 *A, const uint32_t *planes, uint32_t sw,
                                                 float kn, float rn, float si, float bi, float ss,
@@ -2115,8 +2094,9 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
 #pragma unroll
       for (int u = 0; u < kAttU; ++u) {
         const int pl = (t0 + u) * 16 + c16;
-        const double lt = tile_logit<BK, true, NPK>(A, planes[u], sw[u], kv[u], rv[u], cst, kcb);
-        const float logit = pl < npos ? (float)(lt * (double)scale) : -INFINITY;
+        const float lt = tile_logit_f32<BK, true, NPK>(A, planes[u], sw[u], kv[u], rv[u], cst.f[0], cst.f[1],
+                                                       cst.f[2], cst.f[3]);
+        const float logit = pl < npos ? lt * scale : -INFINITY;
         lg[wave][kg][pl] = logit;
         mx = fmaxf(mx, logit);
       }
