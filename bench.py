@@ -10,9 +10,11 @@ bracketed by torch.cuda.synchronize().
 Reported on one JSON line:
   value        keys encoded + scored per second through the whole step (Mvectors/s)
   encode_*     the encode kernel alone (HIP events around its launch)
-  score_*      the score launch alone on the same layer (codes 14.7 MB: they sit
-               in the 256 MB last-level cache) and, separately timed, the score
-               kernel streaming 32 such layers' codes (470 MB) from HBM
+  score_*      the score share of the step on the same layer (codes 14.7 MB: they
+               sit in the 256 MB last-level cache) and, separately timed, the
+               score call streaming 32 such layers' codes (470 MB) from HBM, as
+               a fraction of the nominal peak and of a plain 1 GiB device copy
+               (hbm_stream_reference)
   roofline     the dominant kernel (encode, a bf16 MFMA contraction)
   roofline_score  the score kernel on the 32-layer stream (HBM-bound)
   cpu_baseline the CPU oracle (numpy float64) on a bounded sample of the step
@@ -194,6 +196,24 @@ def main():
                      "((2 d^2 + 2 d m) per key; the hi/lo split executes 5 bf16 passes of the two GEMMs)"},
     }
 
+    # A plain streaming kernel for reference: a 1 GiB device copy (torch),
+    # counted as bytes read + bytes written.
+    cp_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    for _ in range(3):
+        cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cp_src.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    del cp_src, cp_dst
+    out["hbm_stream_reference"] = {"kernel": "1 GiB device copy (torch)", "GBps": round(copy_gbps, 1),
+                                   "frac_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)}
+
     if not args.no_hbm_score:
         # 32 layers' codes of the same shape streamed by one launch (n_kv = 256)
         nL = N_KV * LAYERS
@@ -222,6 +242,7 @@ def main():
         out["score_hbm"] = {"workload": f"{LAYERS} layers x {N_KV} KV heads x {SEQ} positions, one launch",
                             "ms": round(ms, 4), "GBps": round(gbps, 1),
                             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                            "frac_measured_copy": round(gbps / copy_gbps, 4),
                             "bytes_per_launch": bytes_}
         out["roofline_score"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                                  "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
@@ -264,7 +285,8 @@ def main():
         out["attend_hbm"] = {"workload": f"batch {ab} x {akv} KV heads x {aseq} positions x d {D}, "
                                          f"{akv * G} query heads; K prod b=3 m={M}, V mse b=3",
                              "ms": round(ms, 4), "GBps": round(gbps, 1),
-                             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_call": nb}
+                             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                             "frac_measured_copy": round(gbps / copy_gbps, 4), "bytes_per_call": nb}
         del kc, vc
 
     if not args.no_sweep:
