@@ -171,6 +171,47 @@ tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
                     tq_codes vcodes, int64_t seq, float scale, float *out,
                     void *workspace, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Paged code cache for decoding.  The pages "TurboQuant压缩效果" (the kernel
+ * decompresses the codes as it reads them, in registers) and
+ * "刷屏的Google Research论文…", section 九 item 4 (at scale the rotation must be
+ * generated once and reused) describe the serving setting: tokens are encoded
+ * once into a cache that grows page by page, and every decode step attends
+ * over it with the same (Pi, S) of the parameters' seeds.
+ *
+ * A store of num_pages pages holds num_pages * n_kv * TQ_PAGE_POSITIONS
+ * vectors (one tq_codes set for keys, one for values); vector (page, head,
+ * offset) is (page * n_kv + head) * TQ_PAGE_POSITIONS + offset.
+ * ------------------------------------------------------------------------- */
+#define TQ_PAGE_POSITIONS 512
+
+/* Encodes n vectors like tq_encode and stores vector i at slot slots[i] of a
+ * code store of `capacity` vectors (appending new tokens to a paged cache).
+ * slots: device int64 [n], distinct (two equal slots race); slots outside
+ * [0, capacity) are skipped.  Built for d = m = 128 (TQ_ERR_UNSUPPORTED
+ * otherwise); no workspace.                                                */
+tq_status tq_encode_slots(const tq_params *p, const void *x, int32_t dtype, int64_t n,
+                          const int64_t *slots, int64_t capacity, tq_codes codes,
+                          void *stream);
+
+/* Workspace bytes tq_attend_paged needs.  Host only.                       */
+tq_status tq_attend_paged_workspace_bytes(const tq_params *kp, const tq_params *vp,
+                                          int64_t batch, int64_t n_kv, int64_t g,
+                                          int64_t max_pages, size_t *bytes);
+
+/* tq_attend over a paged store: sequence b has seq_lens[b] positions, and its
+ * positions 512 j .. 512 j + 511 live in page block_table[b][j].
+ * block_table: device int32 [batch][max_pages]; seq_lens: device int32
+ * [batch], each in [1, max_pages * TQ_PAGE_POSITIONS] (clamped into that
+ * range); page ids are clamped into [0, num_pages), so bad entries give wrong
+ * rows, never an access outside the store.  q, out, scale and the parameters
+ * as tq_attend.  max_pages * TQ_PAGE_POSITIONS < 2^28.                     */
+tq_status tq_attend_paged(const tq_params *kp, const tq_params *vp, const float *q,
+                          int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
+                          tq_codes vcodes, int64_t num_pages, const int32_t *block_table,
+                          int64_t max_pages, const int32_t *seq_lens, float scale, float *out,
+                          void *workspace, size_t ws_bytes, void *stream);
+
 /* MSE reconstruction of n vectors, x~ = ||x|| Pi^T c[idx] ([P5] 第一阶段: the
  * reconstruction whose squared error the Lloyd-Max codebook minimises).
  * Prod-mode codes decode their B = b-1 bit MSE part (the QJL bits carry no

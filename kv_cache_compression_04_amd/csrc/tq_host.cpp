@@ -706,6 +706,93 @@ tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
                        workspace, (hipStream_t)stream);
 }
 
+tq_status tq_encode_slots(const tq_params *p, const void *x, int32_t dtype, int64_t n,
+                          const int64_t *slots, int64_t capacity, tq_codes codes, void *stream) {
+  tq_status st = check_params(p);
+  if (st) return st;
+  if (n < 0 || capacity < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) {
+    set_error("tq_encode_slots: n < 0, capacity < 0 or bad dtype");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (n == 0) return TQ_OK;
+  if (!x || !slots) {
+    set_error("tq_encode_slots: x or slots is NULL");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if ((st = check_codes(p, codes))) return st;
+  if (!aligned16(x)) {
+    set_error("tq_encode_slots: x must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (!is_d128(*p)) {
+    set_error("tq_encode_slots: built for d = m = 128 (the attention shape)");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const Derived *D = nullptr;
+  if ((st = get_derived(p, &D))) return st;
+  return launch_encode(*D, x, dtype, n, codes, nullptr, 0, (hipStream_t)stream, slots, capacity);
+}
+
+tq_status tq_attend_paged_workspace_bytes(const tq_params *kp, const tq_params *vp,
+                                          int64_t batch, int64_t n_kv, int64_t g,
+                                          int64_t max_pages, size_t *bytes) {
+  if (max_pages < 0 || max_pages > (int64_t(1) << 40)) {
+    set_error("tq_attend_paged_workspace_bytes: bad max_pages");
+    return TQ_ERR_INVALID_ARG;
+  }
+  return tq_attend_workspace_bytes(kp, vp, batch, n_kv, g, max_pages * TQ_PAGE_POSITIONS, bytes);
+}
+
+tq_status tq_attend_paged(const tq_params *kp, const tq_params *vp, const float *q,
+                          int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
+                          tq_codes vcodes, int64_t num_pages, const int32_t *block_table,
+                          int64_t max_pages, const int32_t *seq_lens, float scale, float *out,
+                          void *workspace, size_t ws_bytes, void *stream) {
+  tq_status st = check_params(kp);
+  if (st) return st;
+  if ((st = check_params(vp))) return st;
+  if (kp->mode != TQ_MODE_PROD || vp->mode != TQ_MODE_MSE || kp->d != vp->d) {
+    set_error("tq_attend_paged: keys must be prod mode, values mse mode, same d");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (batch < 0 || n_kv < 0 || g < 1 || num_pages < 0 || max_pages < 0) {
+    set_error("tq_attend_paged: bad sizes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (batch == 0 || n_kv == 0) return TQ_OK;
+  if (num_pages == 0 || max_pages == 0) {
+    set_error("tq_attend_paged: softmax over an empty sequence");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (!q || !out || !workspace || !block_table || !seq_lens) {
+    set_error("tq_attend_paged: NULL q/out/workspace/block_table/seq_lens");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if ((st = check_codes(kp, kcodes)) || (st = check_codes(vp, vcodes))) return st;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) {
+    set_error("tq_attend_paged: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (!is_d128(*kp) || !is_d128(*vp)) {
+    set_error("tq_attend_paged: device kernels are built for d = m = 128 only");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  if (max_pages >= (int64_t(1) << 28) / TQ_PAGE_POSITIONS) {
+    set_error("tq_attend_paged: max_pages * %d must stay below 2^28", TQ_PAGE_POSITIONS);
+    return TQ_ERR_UNSUPPORTED;
+  }
+  const Derived *K = nullptr, *V = nullptr;
+  if ((st = get_derived(kp, &K)) || (st = get_derived(vp, &V))) return st;
+  const int64_t seq_max = max_pages * TQ_PAGE_POSITIONS;
+  if (ws_bytes < attend_workspace_bytes(*K, *V, batch, n_kv, g, seq_max)) {
+    set_error("tq_attend_paged: workspace too small");
+    return TQ_ERR_NO_MEMORY;
+  }
+  if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)kp->d);
+  return launch_attend(*K, *V, q, batch, n_kv, g, kcodes, vcodes, seq_max, scale, out, workspace,
+                       (hipStream_t)stream, block_table, max_pages, num_pages, seq_lens);
+}
+
 tq_status tq_decode(const tq_params *p, tq_codes codes, int64_t n, float *out, void *stream) {
   tq_status st = check_params(p);
   if (st) return st;

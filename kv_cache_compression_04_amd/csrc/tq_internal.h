@@ -77,18 +77,25 @@ void set_error(const char *fmt, ...);
 
 // Launchers (tq_kernels.hip).  Shapes are validated by the caller.
 size_t encode_workspace_bytes(const tq_params &p, int64_t n);
+// slots != nullptr (d = m = 128 only): vector i is stored at slot slots[i]
+// of a store of `capacity` vectors; slots outside [0, capacity) are skipped.
 tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n,
-                        tq_codes codes, void *ws, size_t ws_bytes, hipStream_t stream);
+                        tq_codes codes, void *ws, size_t ws_bytes, hipStream_t stream,
+                        const int64_t *slots = nullptr, int64_t capacity = 0);
 size_t score_workspace_bytes(const tq_params &p, int64_t n_kv, int64_t g);
 tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g,
                        tq_codes codes, int64_t seq, float *logits, void *ws,
                        hipStream_t stream);
 size_t attend_workspace_bytes(const Derived &K, const Derived &V, int64_t batch,
                               int64_t n_kv, int64_t g, int64_t seq);
+// block_table == nullptr: the plain layout.  Otherwise a paged store (pages
+// of 512 positions) and seq = max_pages * 512.
 tq_status launch_attend(const Derived &K, const Derived &V, const float *q,
                         int64_t batch, int64_t n_kv, int64_t g, tq_codes k,
                         tq_codes v, int64_t seq, float scale, float *out,
-                        void *ws, hipStream_t stream);
+                        void *ws, hipStream_t stream, const int32_t *block_table = nullptr,
+                        int64_t max_pages = 0, int64_t num_pages = 0,
+                        const int32_t *seq_lens = nullptr);
 
 tq_status launch_decode(const Derived &D, tq_codes codes, int64_t n, float *out,
                         hipStream_t stream);

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
     const uint4 *__restrict__ pi_lo, const uint4 *__restrict__ sp_hi,
     const uint4 *__restrict__ sp_lo, Codebook cb, uint32_t *__restrict__ idx_out,
     uint32_t *__restrict__ sgn_out, float *__restrict__ knorm_out,
-    float *__restrict__ rnorm_out) {
+    float *__restrict__ rnorm_out, const int64_t *__restrict__ slots, int64_t capacity) {
   constexpr int kMats = PROD ? 4 : 2;
   __shared__ uint4 lds[kMats * kFragU4];
   for (int i = threadIdx.x; i < kFragU4; i += blockDim.x) {
@@ -304,16 +304,19 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
       float r2 = rsq[ct];
       r2 += __shfl_xor(r2, 16);
       r2 += __shfl_xor(r2, 32);
-      if (row < n) {
+      // destination: the row itself, or its slot in a store (out-of-range
+      // slots are skipped)
+      const int64_t orow = slots != nullptr && row < n ? slots[row] : row;
+      if (row < n && (slots == nullptr || (orow >= 0 && orow < capacity))) {
         if (B > 0) {
-          uint32_t *dst = idx_out + (row * 4 + g) * B;
+          uint32_t *dst = idx_out + (orow * 4 + g) * B;
 #pragma unroll
           for (int p = 0; p < B; ++p) dst[p] = planes[ct][p];
         }
-        if (PROD) sgn_out[row * 4 + g] = sbits[ct];
+        if (PROD) sgn_out[orow * 4 + g] = sbits[ct];
         if (g == 0) {
-          knorm_out[row] = nu[ct];
-          if (PROD) rnorm_out[row] = sqrtf(r2);
+          knorm_out[orow] = nu[ct];
+          if (PROD) rnorm_out[orow] = sqrtf(r2);
         }
       }
     }
@@ -322,16 +325,17 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
 
 template <int B, bool PROD>
 static void launch_encode_t(const Derived &D, const void *x, int dtype, int64_t n,
-                            tq_codes c, hipStream_t s, int grid) {
+                            tq_codes c, hipStream_t s, int grid, const int64_t *slots,
+                            int64_t capacity) {
   const dim3 blk(kEncWaves * 64);
   const uint4 *ph = (const uint4 *)D.pi_hi, *pl = (const uint4 *)D.pi_lo;
   const uint4 *sh = (const uint4 *)D.sp_hi, *sl = (const uint4 *)D.sp_lo;
   if (dtype == TQ_BF16)
     encode128_kernel<B, PROD, true><<<grid, blk, 0, s>>>(x, n, ph, pl, sh, sl, D.cb, c.idx, c.sgn,
-                                                         c.knorm, c.rnorm);
+                                                         c.knorm, c.rnorm, slots, capacity);
   else
     encode128_kernel<B, PROD, false><<<grid, blk, 0, s>>>(x, n, ph, pl, sh, sl, D.cb, c.idx, c.sgn,
-                                                          c.knorm, c.rnorm);
+                                                          c.knorm, c.rnorm, slots, capacity);
 }
 
 static int num_cus(int dev) {
@@ -345,7 +349,7 @@ static int num_cus(int dev) {
 }
 
 static tq_status launch_encode128(const Derived &D, const void *x, int dtype, int64_t n, tq_codes c,
-                                  hipStream_t s) {
+                                  hipStream_t s, const int64_t *slots, int64_t capacity) {
   const int64_t nbatch = (n + kEncBatch - 1) / kEncBatch;
   const int64_t need = (nbatch + kEncWaves - 1) / kEncWaves;
   // one workgroup per CU holds the 128 KB of prod-mode fragments; mse mode (64 KB) fits two
@@ -353,15 +357,15 @@ static tq_status launch_encode128(const Derived &D, const void *x, int dtype, in
   const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * per_cu);
   const bool prod = D.p.mode == TQ_MODE_PROD;
   switch (D.B * 2 + (prod ? 1 : 0)) {
-    case 0 * 2 + 1: launch_encode_t<0, true>(D, x, dtype, n, c, s, grid); break;
-    case 1 * 2 + 1: launch_encode_t<1, true>(D, x, dtype, n, c, s, grid); break;
-    case 2 * 2 + 1: launch_encode_t<2, true>(D, x, dtype, n, c, s, grid); break;
-    case 3 * 2 + 1: launch_encode_t<3, true>(D, x, dtype, n, c, s, grid); break;
-    case 4 * 2 + 1: launch_encode_t<4, true>(D, x, dtype, n, c, s, grid); break;
-    case 1 * 2 + 0: launch_encode_t<1, false>(D, x, dtype, n, c, s, grid); break;
-    case 2 * 2 + 0: launch_encode_t<2, false>(D, x, dtype, n, c, s, grid); break;
-    case 3 * 2 + 0: launch_encode_t<3, false>(D, x, dtype, n, c, s, grid); break;
-    case 4 * 2 + 0: launch_encode_t<4, false>(D, x, dtype, n, c, s, grid); break;
+    case 0 * 2 + 1: launch_encode_t<0, true>(D, x, dtype, n, c, s, grid, slots, capacity); break;
+    case 1 * 2 + 1: launch_encode_t<1, true>(D, x, dtype, n, c, s, grid, slots, capacity); break;
+    case 2 * 2 + 1: launch_encode_t<2, true>(D, x, dtype, n, c, s, grid, slots, capacity); break;
+    case 3 * 2 + 1: launch_encode_t<3, true>(D, x, dtype, n, c, s, grid, slots, capacity); break;
+    case 4 * 2 + 1: launch_encode_t<4, true>(D, x, dtype, n, c, s, grid, slots, capacity); break;
+    case 1 * 2 + 0: launch_encode_t<1, false>(D, x, dtype, n, c, s, grid, slots, capacity); break;
+    case 2 * 2 + 0: launch_encode_t<2, false>(D, x, dtype, n, c, s, grid, slots, capacity); break;
+    case 3 * 2 + 0: launch_encode_t<3, false>(D, x, dtype, n, c, s, grid, slots, capacity); break;
+    case 4 * 2 + 0: launch_encode_t<4, false>(D, x, dtype, n, c, s, grid, slots, capacity); break;
     default:
       set_error("tq_encode: unsupported B = %d", D.B);
       return TQ_ERR_UNSUPPORTED;
@@ -778,8 +782,13 @@ static tq_status launch_encode_general(const Derived &D, const void *x, int dtyp
 }
 
 tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n, tq_codes c,
-                        void *ws, size_t ws_bytes, hipStream_t s) {
-  if (is_d128(D.p)) return launch_encode128(D, x, dtype, n, c, s);
+                        void *ws, size_t ws_bytes, hipStream_t s, const int64_t *slots,
+                        int64_t capacity) {
+  if (is_d128(D.p)) return launch_encode128(D, x, dtype, n, c, s, slots, capacity);
+  if (slots != nullptr) {
+    set_error("tq_encode_slots: built for d = m = 128");
+    return TQ_ERR_UNSUPPORTED;
+  }
   if (ws_bytes < encode_workspace_bytes(D.p, n)) {
     set_error("tq_encode: workspace too small");
     return TQ_ERR_NO_MEMORY;
@@ -2041,6 +2050,24 @@ struct AttPartial {  // per (group, split, query): m, l, o_rot[128]
   float m, l, o[128];
 };
 
+// A paged code store (block_table == nullptr: the plain layout).  Page j of
+// sequence b holds its positions 512 j .. 512 j + 511 (one attention split);
+// vector (page, head, offset) of the store is (page * n_kv + head) * 512 +
+// offset.  Sequence lengths are clamped into [1, max_pages * 512] and page
+// ids into [0, num_pages), so no input makes a kernel leave the store.
+struct PagedKV {
+  const int32_t *block_table;  // [batch][max_pages]
+  const int32_t *seq_lens;     // [batch]
+  int64_t max_pages, num_pages;
+  int32_t n_kv;
+};
+
+__device__ __forceinline__ int64_t paged_seq_len(const PagedKV &pg, int64_t b) {
+  int64_t len = pg.seq_lens[b];
+  const int64_t cap = pg.max_pages * kAttKPW;
+  return len < 1 ? 1 : (len > cap ? cap : len);
+}
+
 template <int BK, int BV>
 __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
     const i32x4 *__restrict__ aops, const QConst *__restrict__ qc,
@@ -2048,7 +2075,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
     const float *__restrict__ knorm, const float *__restrict__ rnorm,
     const uint32_t *__restrict__ vidx, const float *__restrict__ vnorm, int64_t seq, int64_t g,
     int ngroups, int nsplit, float scale, Codebook kcb, Codebook vcb,
-    AttPartial *__restrict__ part) {
+    AttPartial *__restrict__ part, PagedKV pg) {
   constexpr int NPK = BK == 0 ? 0 : (BK == 1 ? 1 : BK == 2 ? 2 : BK == 3 ? 4 : 8);
   constexpr int NPV = BV == 1 ? 1 : BV == 2 ? 2 : BV == 3 ? 4 : 8;
   constexpr int NMF = score_mfmas(NPK, true);
@@ -2062,9 +2089,23 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
   const int split = blockIdx.x * kAttWaves + wave;
   const int c16 = lane & 15, kg = lane >> 4;
   const int64_t p0 = (int64_t)split * kAttKPW;
-  if (split >= nsplit) return;  // the whole wave leaves; no workgroup barrier follows
+  // The wave's positions p0 .. p0 + npos - 1 are the vectors vb + 0 .. npos - 1
+  // of the code store: one contiguous run per (batch, KV head) in the plain
+  // layout, one page of the block table in the paged one.
+  int64_t vb;
+  if (pg.block_table) {
+    const int64_t b = hb / pg.n_kv, h = hb % pg.n_kv;
+    seq = paged_seq_len(pg, b);
+    if (p0 >= seq) return;  // past this sequence's end; no workgroup barrier follows
+    int64_t page = pg.block_table[b * pg.max_pages + split];
+    page = page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);  // never outside the store
+    vb = (page * pg.n_kv + h) * kAttKPW;
+  } else {
+    if (split >= nsplit) return;  // the whole wave leaves; no workgroup barrier follows
+    vb = (int64_t)hb * seq + p0;
+  }
   const int npos = (int)(seq - p0 < kAttKPW ? seq - p0 : kAttKPW);
-  const uint32_t last = (uint32_t)(seq - 1);
+  const uint32_t last = (uint32_t)(npos - 1);  // local index of the last position
 
   // ---------------- phase 1: logits of this wave's positions
   float m;
@@ -2073,18 +2114,18 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
 #pragma unroll
     for (int j = 0; j < NMF; ++j) A[j] = aops[((int64_t)hg * NMF + j) * 64 + lane];
     const QConst cst = qc[(int64_t)hg * 4 + kg];
-    const uint32_t *ki = kidx + ((int64_t)hb * seq) * 4 * BKK;
-    const uint32_t *ks = ksgn + (int64_t)hb * seq * 4;
-    const float *kn = knorm + (int64_t)hb * seq;
-    const float *rn = rnorm + (int64_t)hb * seq;
+    const uint32_t *ki = kidx + vb * 4 * BKK;
+    const uint32_t *ks = ksgn + vb * 4;
+    const float *kn = knorm + vb;
+    const float *rn = rnorm + vb;
     float mx = -INFINITY;
     for (int t0 = 0; t0 < kAttKPW / 16; t0 += kAttU) {
       uint32_t planes[kAttU][BKK], sw[kAttU];
       float kv[kAttU], rv[kAttU];
 #pragma unroll
       for (int u = 0; u < kAttU; ++u) {
-        const uint32_t pos = (uint32_t)(p0 + (t0 + u) * 16 + c16);
-        const uint32_t vp = pos < (uint32_t)seq ? pos : last;
+        const uint32_t pos = (uint32_t)((t0 + u) * 16 + c16);
+        const uint32_t vp = pos < (uint32_t)npos ? pos : last;
 #pragma unroll
         for (int p = 0; p < BK; ++p) planes[u][p] = ki[(vp * 4u + kg) * BKK + p];
         sw[u] = ks[vp * 4u + kg];
@@ -2113,7 +2154,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
   // lane (c16, kg): query kg, positions 4 c16 + 64 r + {0..3}
   float lsum = 0.f, wmax = 0.f;
   {
-    const float *vn = vnorm + (int64_t)hb * seq;
+    const float *vn = vnorm + vb;
 #pragma unroll
     for (int r = 0; r < kAttKPW / 64; ++r) {
       const int pl0 = 64 * r + 4 * c16;
@@ -2123,10 +2164,10 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pl = pl0 + e;
-        const uint32_t pos = (uint32_t)(p0 + pl);
+        const uint32_t pos = (uint32_t)pl;
         const float pe = pl < npos ? __expf(lvv[e] - m) : 0.f;
         lsum += pe;
-        wv[e] = pe * vn[pos < (uint32_t)seq ? pos : last];
+        wv[e] = pe * vn[pos < (uint32_t)npos ? pos : last];
         wmax = fmaxf(wmax, wv[e]);
       }
       *reinterpret_cast<float4 *>(&lg[wave][kg][pl0]) = make_float4(wv[0], wv[1], wv[2], wv[3]);
@@ -2161,7 +2202,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
 #pragma unroll
   for (int sl = 0; sl < 8; ++sl) acc[sl] = i32x4{0, 0, 0, 0};
   double qsum = 0.0;  // sum of Q / 2 * 2^-E over this lane's quantisation tasks
-  const uint32_t *vi = vidx + (int64_t)hb * seq * 4 * BV;
+  const uint32_t *vi = vidx + vb * 4 * BV;
   // quantisation of one block: lane (c16, kg) takes query kg, positions
   // 4 c16 .. 4 c16 + 3 of the block, every part
   for (int blk = 0; blk < kAttKPW / 64; ++blk) {
@@ -2171,8 +2212,8 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
     for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t pos = (uint32_t)(p0 + blk * 64 + 16 * kg + 4 * gi + e);
-        const uint32_t *src = vi + ((pos < (uint32_t)seq ? pos : last) * 4u + w) * BV;
+        const uint32_t pos = (uint32_t)(blk * 64 + 16 * kg + 4 * gi + e);
+        const uint32_t *src = vi + ((pos < (uint32_t)npos ? pos : last) * 4u + w) * BV;
         if constexpr (BV == 2) {
           const uint2 t2 = *reinterpret_cast<const uint2 *>(src);
           x[gi][e][0] = t2.x; x[gi][e][1] = t2.y;
@@ -2282,8 +2323,8 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
 // Combine the splits of one query head and rotate back: out = Pi_V^T o_rot / L.
 constexpr int kMergeThreads = 256;
 __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(
-    const AttPartial *__restrict__ part, int nsplit, int ngroups, int64_t g,
-    const float *__restrict__ piv, float *__restrict__ out) {
+    const AttPartial *__restrict__ part, int nsplit_max, int ngroups, int64_t g,
+    const float *__restrict__ piv, float *__restrict__ out, PagedKV pg) {
   __shared__ float wsp[1024];      // exp(m_s - M) per split (nsplit <= 1024 here; larger loops)
   __shared__ float red[kMergeThreads / 64][2];
   __shared__ float orot[2][128];
@@ -2292,7 +2333,11 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(
   const int64_t hg = hb * ngroups + j / 4;
   const int jq = (int)(j % 4);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const AttPartial *p = part + (int64_t)hg * nsplit * 4 + jq;
+  const AttPartial *p = part + (int64_t)hg * nsplit_max * 4 + jq;
+  // splits written for this sequence (all of them in the plain layout)
+  const int nsplit = pg.block_table
+                         ? (int)((paged_seq_len(pg, hb / pg.n_kv) + kAttKPW - 1) / kAttKPW)
+                         : nsplit_max;
   float M = -INFINITY;
   for (int sidx = tid; sidx < nsplit; sidx += kMergeThreads) M = fmaxf(M, p[(int64_t)sidx * 4].m);
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -2347,7 +2392,7 @@ size_t attend_workspace_bytes(const Derived &K, const Derived &V, int64_t batch,
 template <int BK, int BV>
 static void launch_attend_t(const Derived &K, const Derived &V, const float *q, int64_t batch,
                             int64_t n_kv, int64_t g, tq_codes k, tq_codes v, int64_t seq,
-                            float scale, float *out, void *ws, hipStream_t s) {
+                            float scale, float *out, void *ws, hipStream_t s, const PagedKV &pg) {
   const int ngroups = (int)((g + 3) / 4);
   const int64_t nhg = batch * n_kv * ngroups;
   const int nsplit = (int)((seq + kAttKPW - 1) / kAttKPW);
@@ -2361,25 +2406,28 @@ static void launch_attend_t(const Derived &K, const Derived &V, const float *q, 
   attend128_kernel<BK, BV><<<dim3((unsigned)((nsplit + kAttWaves - 1) / kAttWaves), (unsigned)nhg),
                              dim3(kAttWaves * 64), 0, s>>>(aops, qc, k.idx, k.sgn, k.knorm, k.rnorm,
                                                            v.idx, v.knorm, seq, g, ngroups, nsplit,
-                                                           scale, K.cb, V.cb, part);
+                                                           scale, K.cb, V.cb, part, pg);
   attend_merge_kernel<<<dim3((unsigned)(batch * n_kv * g)), dim3(kMergeThreads), 0, s>>>(part, nsplit, ngroups, g,
-                                                                               V.pi32, out);
+                                                                               V.pi32, out, pg);
 }
 
 tq_status launch_attend(const Derived &K, const Derived &V, const float *q, int64_t batch,
                         int64_t n_kv, int64_t g, tq_codes k, tq_codes v, int64_t seq, float scale,
-                        float *out, void *ws, hipStream_t s) {
+                        float *out, void *ws, hipStream_t s, const int32_t *block_table,
+                        int64_t max_pages, int64_t num_pages, const int32_t *seq_lens) {
   if ((uint64_t)batch * n_kv * ((g + 3) / 4) > 65535u || seq >= (1LL << 28)) {
     set_error("tq_attend: batch * n_kv * ceil(g/4) must be <= 65535 and seq < 2^28");
     return TQ_ERR_UNSUPPORTED;
   }
+  // paged: seq = max_pages * 512 sizes the grid; each sequence's length is read on the device
+  const PagedKV pg{block_table, seq_lens, max_pages, num_pages, (int32_t)n_kv};
   if (V.B < 1) {
     set_error("tq_attend: values need at least one Lloyd-Max bit");
     return TQ_ERR_UNSUPPORTED;
   }
   switch (K.B * 8 + V.B) {
 #define TQ_ATT_CASE(bk, bv) \
-    case bk * 8 + bv: launch_attend_t<bk, bv>(K, V, q, batch, n_kv, g, k, v, seq, scale, out, ws, s); break;
+    case bk * 8 + bv: launch_attend_t<bk, bv>(K, V, q, batch, n_kv, g, k, v, seq, scale, out, ws, s, pg); break;
     TQ_ATT_CASE(0, 1) TQ_ATT_CASE(0, 2) TQ_ATT_CASE(0, 3) TQ_ATT_CASE(0, 4)
     TQ_ATT_CASE(1, 1) TQ_ATT_CASE(1, 2) TQ_ATT_CASE(1, 3) TQ_ATT_CASE(1, 4)
     TQ_ATT_CASE(2, 1) TQ_ATT_CASE(2, 2) TQ_ATT_CASE(2, 3) TQ_ATT_CASE(2, 4)

@@ -45,7 +45,10 @@ EXPORTS = ["tq_status_string", "tq_last_error", "tq_layout_version", "tq_make_co
            "tq_codes_bytes", "tq_export_matrices", "tq_encode_workspace_bytes", "tq_encode",
            "tq_score_workspace_bytes",
            "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_decode",
-           "tq_search_workspace_bytes", "tq_search", "tq_release_cache"]
+           "tq_search_workspace_bytes", "tq_search", "tq_encode_slots",
+           "tq_attend_paged_workspace_bytes", "tq_attend_paged", "tq_release_cache"]
+
+PAGE_POSITIONS = 512  # TQ_PAGE_POSITIONS
 
 _lib = None
 
@@ -76,6 +79,10 @@ def lib():
             "tq_decode": (ctypes.c_int, [P, C, i64, vp, vp]),
             "tq_search_workspace_bytes": (ctypes.c_int, [P, i64, i64, ctypes.c_int32, ctypes.POINTER(sz)]),
             "tq_search": (ctypes.c_int, [P, vp, i64, C, i64, ctypes.c_int32, vp, vp, vp, sz, vp]),
+            "tq_encode_slots": (ctypes.c_int, [P, vp, ctypes.c_int32, i64, vp, i64, C, vp]),
+            "tq_attend_paged_workspace_bytes": (ctypes.c_int, [P, P, i64, i64, i64, i64, ctypes.POINTER(sz)]),
+            "tq_attend_paged": (ctypes.c_int, [P, P, vp, i64, i64, i64, C, C, i64, vp, i64, vp, ctypes.c_float,
+                                               vp, vp, sz, vp]),
             "tq_release_cache": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -242,3 +249,35 @@ def search(p: Params, q, codes: dict, n: int, k: int, out_idx, out_val, workspac
     _check("tq_search", lib().tq_search(ctypes.byref(p.c()), _ptr(q), q.shape[0], _codes(codes), n, k,
                                         _ptr(out_idx), _ptr(out_val), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def encode_slots(p: Params, x, slots, capacity: int, codes: dict, stream=None):
+    """x: [n, d] float32/bfloat16; slots: [n] int64 (device); vector i goes to
+    slot slots[i] of a store of `capacity` vectors (codes sized for it)."""
+    import torch
+    assert x.is_contiguous() and slots.is_contiguous() and slots.dtype == torch.int64
+    assert slots.numel() == x.shape[0]
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    _check("tq_encode_slots", lib().tq_encode_slots(ctypes.byref(p.c()), _ptr(x), dt, x.shape[0], _ptr(slots),
+                                                    capacity, _codes(codes), _stream(stream)))
+
+
+def attend_paged_workspace_bytes(kp: Params, vp: Params, batch: int, n_kv: int, g: int, max_pages: int) -> int:
+    out = ctypes.c_size_t()
+    _check("tq_attend_paged_workspace_bytes",
+           lib().tq_attend_paged_workspace_bytes(ctypes.byref(kp.c()), ctypes.byref(vp.c()), batch, n_kv, g,
+                                                 max_pages, ctypes.byref(out)))
+    return out.value
+
+
+def attend_paged(kp: Params, vp: Params, q, batch, n_kv, g, kcodes, vcodes, num_pages, block_table,
+                 seq_lens, out, workspace, scale: float = 0.0, stream=None):
+    """block_table: [batch, max_pages] int32; seq_lens: [batch] int32 (device);
+    q, out: [batch, n_kv*g, d] float32."""
+    import torch
+    assert q.is_contiguous() and out.is_contiguous() and block_table.is_contiguous()
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    _check("tq_attend_paged", lib().tq_attend_paged(
+        ctypes.byref(kp.c()), ctypes.byref(vp.c()), _ptr(q), batch, n_kv, g, _codes(kcodes), _codes(vcodes),
+        num_pages, _ptr(block_table), block_table.shape[1], _ptr(seq_lens), scale, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -93,3 +93,14 @@ def check_logits(got: np.ndarray, ref: np.ndarray, q: np.ndarray, knorm: np.ndar
     worst = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
     assert np.all(err <= tol), f"logit error up to {worst:.3f} x tolerance"
     return worst
+
+
+def check_attend(got, ref):
+    """max_i |o_gpu - o_ref| <= 1e-4 * max_i |o_ref| for every query head."""
+    got = np.asarray(got, np.float64).reshape(-1, ref.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    err = np.max(np.abs(got - ref), axis=1)
+    scale = np.max(np.abs(ref), axis=1)
+    worst = float(np.max(err / (1e-4 * scale)))
+    assert np.all(err <= 1e-4 * scale), f"attend error up to {worst:.3f} x tolerance"
+    return worst

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from oracle import tq_oracle as o
-from tests.parity import check_encode, check_logits, to_numpy_codes
+from tests.parity import check_attend, check_encode, check_logits, to_numpy_codes
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -154,17 +154,6 @@ def test_llama_layer_full_size(b):
 
 
 # ------------------------------------------------------------------ attend
-def check_attend(got, ref):
-    """max_i |o_gpu - o_ref| <= 1e-4 * max_i |o_ref| for every query head."""
-    got = np.asarray(got, np.float64).reshape(-1, ref.shape[-1])
-    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
-    err = np.max(np.abs(got - ref), axis=1)
-    scale = np.max(np.abs(ref), axis=1)
-    worst = float(np.max(err / (1e-4 * scale)))
-    assert np.all(err <= 1e-4 * scale), f"attend error up to {worst:.3f} x tolerance"
-    return worst
-
-
 def _attend_case(kp, vp, batch, n_kv, g, seq, seed=0):
     okp, ovp = _oparams(kp), _oparams(vp)
     k = synth.llama_keys(heads=n_kv, seq=seq, seed=seed + 1, dtype=torch.float32, batch=batch).double().numpy()

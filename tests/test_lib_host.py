@@ -151,3 +151,36 @@ def test_score_and_attend_argument_checks():
                    ctypes.c_float(0), None, None, 0, None) == 1
     assert _status("tq_attend", ctypes.byref(p), ctypes.byref(v), None, 1, 1, 1, codes, codes, 0,
                    ctypes.c_float(0), None, None, 0, None) == 1
+
+
+def test_paged_cache_argument_checks():
+    """tq_encode_slots / tq_attend_paged reject what they must before any device work."""
+    p = tq._Params(128, 3, 128, 0, 1, 2)
+    v = tq._Params(128, 3, 128, 1, 4, 0)
+    buf, a = _host_buf(1 << 16)
+    codes = tq._Codes(a, a, a, a)
+    enc = lambda pp, x, slots, n, cap: _status("tq_encode_slots", ctypes.byref(pp), x, 0, n, slots, cap, codes, None)
+    assert enc(p, a, a, 0, 16) == 0              # nothing to do
+    assert enc(p, a, None, 4, 16) == 1           # slots missing
+    assert enc(p, a, a, 4, -1) == 1              # negative capacity
+    assert enc(p, a + 4, a, 4, 16) == 3          # misaligned keys
+    p256 = tq._Params(256, 3, 256, 0, 1, 2)
+    assert enc(p256, a, a, 4, 16) == 2           # built for d = m = 128
+    ws = ctypes.c_size_t()
+    ws_plain = ctypes.c_size_t()
+    assert _status("tq_attend_paged_workspace_bytes", ctypes.byref(p), ctypes.byref(v), 2, 8, 4, 3,
+                   ctypes.byref(ws)) == 0
+    assert _status("tq_attend_workspace_bytes", ctypes.byref(p), ctypes.byref(v), 2, 8, 4, 3 * tq.PAGE_POSITIONS,
+                   ctypes.byref(ws_plain)) == 0
+    assert ws.value == ws_plain.value > 0
+    att = lambda kp, vp, num_pages, bt, max_pages, lens, out=a, w=a, wsb=1 << 16: _status(
+        "tq_attend_paged", ctypes.byref(kp), ctypes.byref(vp), a, 1, 1, 4, codes, codes, num_pages, bt,
+        max_pages, lens, ctypes.c_float(0), out, w, wsb, None)
+    assert att(v, v, 4, a, 2, a) == 1                  # keys must be prod mode
+    assert att(p, v, 0, a, 2, a) == 1                  # empty store
+    assert att(p, v, 4, None, 2, a) == 1               # no block table
+    assert att(p, v, 4, a, 2, None) == 1               # no sequence lengths
+    assert att(p, v, 4, a, 1 << 20, a) == 2            # positions beyond 2^28
+    k256 = tq._Params(256, 3, 256, 0, 1, 2)
+    v256 = tq._Params(256, 3, 256, 1, 4, 0)
+    assert att(k256, v256, 4, a, 2, a) == 2            # built for d = m = 128
