@@ -18,8 +18,8 @@ Reported on one JSON line:
   roofline     the dominant kernel (encode, a bf16 MFMA contraction)
   roofline_score  the score kernel on the 32-layer stream (HBM-bound)
   cpu_baseline the CPU oracle (numpy float64) on a bounded sample of the step
-Further sections (each can be switched off): long-context attention, the
-bit-width sweep, and high-dimensional batched search (d = m = 1024, 1M
+Further sections (each can be switched off): long-context attention (plain
+and through a paged block table), the bit-width sweep, and high-dimensional batched search (d = m = 1024, 1M
 vectors, 1024 queries, top-10).
 """
 import argparse
@@ -287,6 +287,28 @@ def main():
                              "ms": round(ms, 4), "GBps": round(gbps, 1),
                              "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                              "frac_measured_copy": round(gbps / copy_gbps, 4), "bytes_per_call": nb}
+        # the same code arrays read as a paged store (512-position pages, vector
+        # (page * n_kv + head) * 512 + offset) through a shuffled block table
+        npg = aseq // tq.PAGE_POSITIONS
+        perm = torch.randperm(ab * npg, generator=torch.Generator().manual_seed(11))
+        bt = perm.reshape(ab, npg).to(torch.int32).to(dev)
+        lens = torch.full((ab,), aseq, dtype=torch.int32, device=dev)
+        pws = torch.empty(tq.attend_paged_workspace_bytes(kp, vp, ab, akv, G, npg), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            tq.attend_paged(kp, vp, aq, ab, akv, G, kc, vc, ab * npg, bt, lens, aout, pws)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            tq.attend_paged(kp, vp, aq, ab, akv, G, kc, vc, ab * npg, bt, lens, aout, pws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbps = nb / (ms * 1e-3) / 1e9
+        out["attend_paged_hbm"] = {"workload": f"as attend_hbm, the codes as {ab * npg} pages of "
+                                               f"{tq.PAGE_POSITIONS} positions in a shuffled block table",
+                                   "ms": round(ms, 4), "GBps": round(gbps, 1),
+                                   "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                                   "frac_measured_copy": round(gbps / copy_gbps, 4), "bytes_per_call": nb}
         del kc, vc
 
     if not args.no_sweep:

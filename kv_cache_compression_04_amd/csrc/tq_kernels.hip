@@ -2069,7 +2069,7 @@ __device__ __forceinline__ int64_t paged_seq_len(const PagedKV &pg, int64_t b) {
 }
 
 template <int BK, int BV>
-__global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
+__global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
     const i32x4 *__restrict__ aops, const QConst *__restrict__ qc,
     const uint32_t *__restrict__ kidx, const uint32_t *__restrict__ ksgn,
     const float *__restrict__ knorm, const float *__restrict__ rnorm,
@@ -2080,10 +2080,17 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
   constexpr int NPV = BV == 1 ? 1 : BV == 2 ? 2 : BV == 3 ? 4 : 8;
   constexpr int NMF = score_mfmas(NPK, true);
   constexpr int BKK = BK > 0 ? BK : 1;
+  // Up to 4 parity parts share one quantisation of the weights and keep an
+  // accumulator set each; 8 parts (4-bit values) would need 256 accumulator
+  // registers, so there each part quantises its own scaled weights into one
+  // shared accumulator set.
+  constexpr bool SHARED = NPV <= 4;
+  constexpr int NQ = SHARED ? 1 : NPV;   // quantised weight sets per block
+  constexpr int NACC = SHARED ? NPV : 1;  // accumulator sets
   __shared__ __attribute__((aligned(16))) float lg[kAttWaves][4][kAttKPW];  // logits, then weights
-  // one block of quantised weights: [part][query][limb][positions / 4]
-  __shared__ __attribute__((aligned(16))) uint32_t limbs[kAttWaves][NPV][4][4][64 / 4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // one block of quantised weights: [set][query][limb][positions / 4]
+  __shared__ __attribute__((aligned(16))) uint32_t limbs[kAttWaves][NQ][4][4][64 / 4];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = blockIdx.y;  // (batch * n_kv + head) * ngroups + group
   const int hb = hg / ngroups;
   const int split = blockIdx.x * kAttWaves + wave;
@@ -2124,8 +2131,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
       float kv[kAttU], rv[kAttU];
 #pragma unroll
       for (int u = 0; u < kAttU; ++u) {
-        const uint32_t pos = (uint32_t)((t0 + u) * 16 + c16);
-        const uint32_t vp = pos < (uint32_t)npos ? pos : last;
+        const uint32_t vp = min((uint32_t)((t0 + u) * 16 + c16), last);
 #pragma unroll
         for (int p = 0; p < BK; ++p) planes[u][p] = ki[(vp * 4u + kg) * BKK + p];
         sw[u] = ks[vp * 4u + kg];
@@ -2167,7 +2173,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
         const uint32_t pos = (uint32_t)pl;
         const float pe = pl < npos ? __expf(lvv[e] - m) : 0.f;
         lsum += pe;
-        wv[e] = pe * vn[pos < (uint32_t)npos ? pos : last];
+        wv[e] = pe * vn[min(pos, last)];
         wmax = fmaxf(wmax, wv[e]);
       }
       *reinterpret_cast<float4 *>(&lg[wave][kg][pl0]) = make_float4(wv[0], wv[1], wv[2], wv[3]);
@@ -2178,15 +2184,16 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
       wmax = fmaxf(wmax, __shfl_xor(wmax, off));
     }
   }
-  // one power-of-two scale per query covering every part: |2 a_S w| 2^E < 2^26
-  double amax = 0.0;
-#pragma unroll
-  for (int sp = 0; sp < NPV; ++sp) amax = fmax(amax, fabs(vcb.coef[sp]));
+  // one power-of-two scale per query: shared, w 2^E < 2^27 (4 unsigned
+  // 7-bit limbs); per part, |2 a_S w| 2^E < 2^26 (4 balanced limbs)
   int E = 0;
   {
+    double amax = 0.0;
+#pragma unroll
+    for (int sp = 0; sp < NPV; ++sp) amax = fmax(amax, fabs(vcb.coef[sp]));
     int k;
-    const double A1 = 2.0 * amax * (double)wmax;
-    if (A1 > 0) { frexp(A1, &k); E = 26 - k; }
+    const double A1 = SHARED ? (double)wmax : 2.0 * amax * (double)wmax;
+    if (A1 > 0) { frexp(A1, &k); E = (SHARED ? 27 : 26) - k; }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -2198,13 +2205,17 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
   // 2^(s & 3)) is coordinate 32 beta + 16 (s / 4) + 4 w + s % 4.
   const int w = c16 >> 2, beta = c16 & 3;
   const uint32_t sel_lo = (uint32_t)(beta | (beta + 4) << 8 | 0x0C0C0000u);
-  i32x4 acc[8];
+  i32x4 acc[NACC][8];
 #pragma unroll
-  for (int sl = 0; sl < 8; ++sl) acc[sl] = i32x4{0, 0, 0, 0};
-  double qsum = 0.0;  // sum of Q / 2 * 2^-E over this lane's quantisation tasks
+  for (int a = 0; a < NACC; ++a)
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) acc[a][sl] = i32x4{0, 0, 0, 0};
+  // shared: sum of this lane's Q; per part: sum of Q / 2 * 2^-E
+  double qsum = 0.0;
   const uint32_t *vi = vidx + vb * 4 * BV;
+  const uint32_t woff = (uint32_t)w * (4u * BV);  // byte offset of index word w
   // quantisation of one block: lane (c16, kg) takes query kg, positions
-  // 4 c16 .. 4 c16 + 3 of the block, every part
+  // 4 c16 .. 4 c16 + 3 of the block
   for (int blk = 0; blk < kAttKPW / 64; ++blk) {
     // V index words of this lane's 16 positions (issued first)
     uint32_t x[4][4][BV];
@@ -2212,8 +2223,11 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
     for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t pos = (uint32_t)(blk * 64 + 16 * kg + 4 * gi + e);
-        const uint32_t *src = vi + ((pos < (uint32_t)npos ? pos : last) * 4u + w) * BV;
+        const uint32_t pos = min((uint32_t)(blk * 64 + 16 * kg + 4 * gi + e), last);
+        // a 32-bit byte offset from the wave-uniform base (one scalar base,
+        // one offset register per load)
+        const uint32_t *src =
+            reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(vi) + (__umul24(pos, 16u * BV) + woff));
         if constexpr (BV == 2) {
           const uint2 t2 = *reinterpret_cast<const uint2 *>(src);
           x[gi][e][0] = t2.x; x[gi][e][1] = t2.y;
@@ -2225,31 +2239,46 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
           for (int p = 0; p < BV; ++p) x[gi][e][p] = src[p];
         }
       }
-    // quantise 2 a_S w_n of this block into limb dwords
     {
       const float4 wv4 = *reinterpret_cast<const float4 *>(&lg[wave][kg][blk * 64 + 4 * c16]);
       const float wv[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
-#pragma unroll
-      for (int sp = 0; sp < NPV; ++sp) {
-        // Q = 2 a_S w 2^E rounded in float32: any integer near it serves, as
-        // the MFMA sum and the correction qsum use the same Q
-        const float cf = (float)ldexp(2.0 * vcb.coef[sp], E);
+      if constexpr (SHARED) {
+        // Q = w 2^E rounded (0 <= Q < 2^27), limbs = its base-128 digits
         uint32_t lw[4] = {0u, 0u, 0u, 0u};
-        int qs = 0;
+        uint32_t qs = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          int Q = (int)rintf(cf * wv[e]);
+          const uint32_t Q = (uint32_t)rintf(ldexpf(wv[e], E));
           qs += Q;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {  // balanced base-128 digits, lowest first
-            const int digit = ((Q + 64) & 127) - 64;
-            Q = (Q - digit) >> 7;  // exact: Q - digit is a multiple of 128
-            lw[t] |= (uint32_t)(digit & 0xFF) << (8 * e);
-          }
+          for (int t = 0; t < 4; ++t) lw[t] |= ((Q >> (7 * t)) & 127u) << (8 * e);
         }
-        qsum += ldexp(0.5 * (double)qs, -E);
+        qsum += (double)qs;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) limbs[wave][sp][kg][t][c16] = lw[t];
+        for (int t = 0; t < 4; ++t) limbs[wave][0][kg][t][c16] = lw[t];
+      } else {
+#pragma unroll
+        for (int sp = 0; sp < NQ; ++sp) {
+          // Q = 2 a_S w 2^E rounded in float32: any integer near it serves, as
+          // the MFMA sum and the correction qsum use the same Q
+          const float cf = (float)ldexp(2.0 * vcb.coef[sp], E);
+          uint32_t lw[4] = {0u, 0u, 0u, 0u};
+          int qs = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            int Q = (int)rintf(cf * wv[e]);
+            qs += Q;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {  // balanced base-128 digits, lowest first
+              const int digit = ((Q + 64) & 127) - 64;
+              Q = (Q - digit) >> 7;  // exact: Q - digit is a multiple of 128
+              lw[t] |= (uint32_t)(digit & 0xFF) << (8 * e);
+            }
+          }
+          qsum += ldexp(0.5 * (double)qs, -E);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) limbs[wave][sp][kg][t][c16] = lw[t];
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -2277,7 +2306,8 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
 #pragma unroll
     for (int sp = 0; sp < NPV; ++sp) {
       // A: rows (query c16 / 4, limb c16 % 4), positions 16 kg .. 16 kg + 15
-      const i32x4 Aw = *reinterpret_cast<const i32x4 *>(&limbs[wave][sp][c16 >> 2][c16 & 3][4 * kg]);
+      const i32x4 Aw =
+          *reinterpret_cast<const i32x4 *>(&limbs[wave][SHARED ? 0 : sp][c16 >> 2][c16 & 3][4 * kg]);
       i32x4 lo4[4], hi4[4];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
@@ -2289,29 +2319,40 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
           hi4[k][gi] = b4[k];
         }
       }
+      i32x4 *ac = acc[SHARED ? sp : 0];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        acc[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aw, lo4[k], acc[k], 0, 0, 0);
-        acc[4 + k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aw, hi4[k], acc[4 + k], 0, 0, 0);
+        ac[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aw, lo4[k], ac[k], 0, 0, 0);
+        ac[4 + k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aw, hi4[k], ac[4 + k], 0, 0, 0);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
-  // sum over the 16 lanes of query kg: sum_S sum_n Q_S,n / 2 * 2^-E
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) qsum += __shfl_xor(qsum, off);
   // ---------------- epilogue: lane (c16, kg) holds query kg, limbs t = 0..3
+  // sum_n w_n c[idx_n] = sum_S a_S (2 sum_n w_n beta_S,n - sum_n w_n)
   const int64_t qh = (int64_t)(hg % ngroups) * 4 + kg;
   AttPartial *dst = part + ((int64_t)hg * nsplit + split) * 4 + kg;
   if (qh < g) {
+    double asum = 0.0;
+#pragma unroll
+    for (int sp = 0; sp < NPV; ++sp) asum += vcb.coef[sp];
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      const i32x4 a = acc[sl];
-      const double v = (double)a[0] + 128.0 * (double)a[1] + 16384.0 * (double)a[2] +
-                       2097152.0 * (double)a[3];
+      double v = 0.0;
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) {
+        const i32x4 r = acc[a][sl];
+        const double ra = (double)r[0] + 128.0 * (double)r[1] + 16384.0 * (double)r[2] +
+                          2097152.0 * (double)r[3];
+        v += (SHARED ? 2.0 * vcb.coef[a] : 1.0) * ra;
+      }
       const int c = 32 * beta + 16 * (sl >> 2) + 4 * w + (sl & 3);
-      dst->o[c] = (float)(ldexp(v, -E - (sl & 3)) - qsum);
+      // shared: (v 2^-(s&3) - a qsum) 2^-E; per part: v 2^-(E + s&3) - qsum
+      dst->o[c] = SHARED ? (float)ldexp(ldexp(v, -(sl & 3)) - asum * qsum, -E)
+                         : (float)(ldexp(v, -E - (sl & 3)) - qsum);
     }
     if (c16 == 0) {
       dst->m = m;
@@ -2321,13 +2362,15 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend128_kernel(
 }
 
 // Combine the splits of one query head and rotate back: out = Pi_V^T o_rot / L.
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeGroups = kMergeThreads / 128;  // split groups per coordinate
 __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(
     const AttPartial *__restrict__ part, int nsplit_max, int ngroups, int64_t g,
     const float *__restrict__ piv, float *__restrict__ out, PagedKV pg) {
   __shared__ float wsp[1024];      // exp(m_s - M) per split (nsplit <= 1024 here; larger loops)
   __shared__ float red[kMergeThreads / 64][2];
-  __shared__ float orot[2][128];
+  __shared__ float orot[kMergeGroups][128];
+  __shared__ float osum[128];
   const int hq = blockIdx.x;        // (batch * n_kv + head) * g + j
   const int64_t hb = hq / g, j = hq % g;
   const int64_t hg = hb * ngroups + j / 4;
@@ -2357,21 +2400,36 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(
   __syncthreads();
   L = 0.f;
   for (int w = 0; w < kMergeThreads / 64; ++w) L += red[w][1];
-  // o_rot[c]: two halves of the splits per coordinate
-  const int c = tid & 127, half = tid >> 7;
+  // o_rot[c]: kMergeGroups interleaved groups of the splits per coordinate
+  const int c = tid & 127, grp = tid >> 7;
   float acc = 0.f;
-#pragma unroll 8
-  for (int sidx = half; sidx < nsplit; sidx += 2) {
+#pragma unroll 16
+  for (int sidx = grp; sidx < nsplit; sidx += kMergeGroups) {
     const float e = sidx < 1024 ? wsp[sidx] : __expf(p[(int64_t)sidx * 4].m - M);
     acc = fmaf(e, p[(int64_t)sidx * 4].o[c], acc);
   }
-  orot[half][c] = acc;
+  orot[grp][c] = acc;
+  __syncthreads();
+  if (tid < 128) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) t += orot[k][tid];
+    osum[tid] = t / L;
+  }
+  __syncthreads();
+  // out = Pi_V^T o_rot: thread (c, grp) sums 128 / kMergeGroups rows of Pi_V
+  {
+    constexpr int R = 128 / kMergeGroups;
+    float o = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) o = fmaf(piv[(grp * R + r) * 128 + c], osum[grp * R + r], o);
+    orot[grp][c] = o;  // every read of orot above is behind the barrier
+  }
   __syncthreads();
   if (tid < 128) {
     float o = 0.f;
-    const float inv = 1.0f / L;
-#pragma unroll 8
-    for (int cc = 0; cc < 128; ++cc) o = fmaf(piv[cc * 128 + tid], (orot[0][cc] + orot[1][cc]) * inv, o);
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) o += orot[k][tid];
     out[(int64_t)hq * 128 + tid] = o;
   }
 }
