@@ -19,8 +19,9 @@ Reported on one JSON line:
   roofline_score  the score kernel on the 32-layer stream (HBM-bound)
   cpu_baseline the CPU oracle (numpy float64) on a bounded sample of the step
 Further sections (each can be switched off): long-context attention (plain
-and through a paged block table), the bit-width sweep, and high-dimensional batched search (d = m = 1024, 1M
-vectors, 1024 queries, top-10).
+and through a paged block table), the bit-width sweep, high-dimensional batched search (d = m = 1024, 1M
+vectors, 1024 queries, top-10) and search at database scale (2^26 vectors of
+d = 128, 3.76 GB of codes, 1024 queries, top-10).
 """
 import argparse
 import json
@@ -51,6 +52,7 @@ def _parse():
     ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-highdim", action="store_true")
+    ap.add_argument("--no-searchdb", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling PMC byte counters)")
@@ -405,6 +407,47 @@ def main():
             "codes_mb": round(sum(tq.codes_bytes(hp, hn)) / 1e6, 1),
         }
         del hx, hc, hws, hsws
+
+    if not args.no_searchdb:
+        # many-query search at database scale: 2^26 vectors of d = m = 128
+        # (N(0,1), 1% channels x10, generated and encoded in 8 chunks), b = 3,
+        # 3.76 GB of codes; 1024 queries, top-10, no logit matrix
+        dn, dch, dnq, dk = 1 << 26, 1 << 23, 1024, 10
+        dp = tq.Params(D, 3, M)
+        dc = tq.alloc_codes(dp, dn, dev)
+        for c in range(dn // dch):
+            sl = slice(c * dch, (c + 1) * dch)
+            dx = synth.highdim_keys(dch, d=D, seed=100 + c, device=dev)
+            tq.encode(dp, dx, {k: (v[sl] if v is not None else None) for k, v in dc.items()})
+            del dx
+        dqv = synth.queries(dnq, d=D, seed=5, device=dev)
+        didx = torch.empty((dnq, dk), dtype=torch.int64, device=dev)
+        dval = torch.empty((dnq, dk), device=dev)
+        dws = torch.empty(tq.search_workspace_bytes(dp, dnq, dn, dk), dtype=torch.uint8, device=dev)
+        tq.search(dp, dqv, dc, dn, dk, didx, dval, dws)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            tq.search(dp, dqv, dc, dn, dk, didx, dval, dws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        se_ms = e0.elapsed_time(e1) / reps
+        pairs = dnq * dn
+        sc_exec = 2 * 4 * 3 * D * pairs                      # 4 int8 limbs x 3 parts (2 planes + signs)
+        nb = sum(tq.codes_bytes(dp, dn))
+        out["search_db"] = {
+            "workload": f"{dn} x d {D} float32 vectors (N(0,1), 1% channels x10), b=3, m={M}; "
+                        f"{dnq} N(0,1) queries, top-{dk}",
+            "codes_gb": round(nb / 1e9, 3),
+            "search_ms": round(se_ms, 3),
+            "search_gpairs_per_s": round(pairs / (se_ms * 1e-3) / 1e9, 1),
+            "search_tops_executed_int8": round(sc_exec / (se_ms * 1e-3) / 1e12, 1),
+            "search_frac_int8_peak_executed": round(sc_exec / (se_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "codes_read_gbps_once": round(nb / (se_ms * 1e-3) / 1e9, 1),
+        }
+        del dc, dws
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.b, args.cpu_sample_heads)
