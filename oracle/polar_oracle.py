@@ -1,0 +1,270 @@
+"""Plain, slow, obviously-correct CPU oracle for the PolarQuant stage-1
+variant (recursive polar transform of the rotated vector, angles quantised
+with fixed codebooks derived from their known laws).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It imports
+nothing from the product (``kv_cache_compression_04_amd``); the rotation is
+the oracle's own (``tq_oracle.rotation``).
+
+Everything is float64 numpy; ``numpy.arctan2``, ``scipy.special.betainc`` and
+composite Gauss-Legendre quadrature are the library primitives used as steps.
+
+Sources (pages cited by title and section):
+  [P3]  "TurboQuant 与 AI 效率革命：当旧数学遇到新智能", section 二
+        (极坐标的洞察: after random preconditioning a d-vector is one radius
+        and d-1 angles whose law is known in closed form, density
+        Gamma(d) / (2^(d-2) Gamma(d/2)^2) * sin^(d-1)(2 theta), mean pi/4;
+        递归极坐标变换: pair the coordinates into (radius, angle), pair the
+        radii again, log2(d) times), and section 三 (PolarQuant alone gives
+        about 4.2x).
+  [P4]  "TurboQuant压缩效果" (video transcript): the angles of every level
+        concentrate at 45 degrees; the first level takes 4 bits, the later
+        levels 2 bits, about 3 bits per coordinate in all.
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  Q1  the rotation is the TurboQuant one (y = Pi x, Pi from seed_pi); the
+      transform runs on y, and the stored radius is ||x|| in float32.
+  Q2  level 1 pairs coordinates (2j, 2j+1) into psi_j = atan2(y_2j+1, y_2j)
+      in [0, 2 pi) (atan2 mod 2 pi; the zero pair has psi = 0); level l >= 2
+      pairs the level-(l-1) radii (2j, 2j+1) into theta = atan2(r_2j+1, r_2j)
+      in [0, pi/2].  The level-l radius is the norm of its 2^l coordinates.
+  Q3  the density formula of [P3] holds at level l >= 2 with its d read as
+      k = 2^(l-1), the number of coordinates under each of the two radii
+      (sin^2 theta ~ Beta(k/2, k/2)); at level 1 the angle is uniform on
+      [0, 2 pi).
+  Q4  codebooks: level 1 uniform (the Lloyd-Max quantiser of a uniform law is
+      the uniform grid), centroids (i + 1/2) 2 pi / 2^b1, boundaries
+      i 2 pi / 2^b1; levels >= 2 Lloyd-Max for the Q3 density on [0, pi/2].
+      Code = number of boundaries <= the angle.
+  Q5  reconstruction: the radius goes down the tree, r_left = r cos(theta^),
+      r_right = r sin(theta^), level 1 gives (r cos psi^, r sin psi^); the
+      logit is <Pi q, y^>, y^ the reconstructed rotated vector.
+"""
+from __future__ import annotations
+
+import functools
+import math
+
+import numpy as np
+from scipy.special import betainc
+
+from oracle import tq_oracle as tqo
+
+
+class PolarParams:
+    """d (a power of two), bits of level 1 and of the later levels, seed of Pi."""
+
+    def __init__(self, d: int = 128, bits1: int = 4, bits: int = 2, seed_pi: int = 2):
+        assert d >= 4 and d & (d - 1) == 0
+        self.d, self.bits1, self.bits, self.seed_pi = d, bits1, bits, seed_pi
+
+    @property
+    def levels(self) -> int:
+        return int(round(math.log2(self.d)))
+
+    @property
+    def pi(self) -> np.ndarray:
+        return tqo.rotation(self.d, self.seed_pi)
+
+    def codebook(self, level: int):
+        return angle_codebook(level, self.bits1 if level == 1 else self.bits)
+
+
+# ---------------------------------------------------------------------------
+# Q2: the recursive polar transform and its inverse   ([P3] 递归极坐标变换)
+# ---------------------------------------------------------------------------
+def polar_transform(y: np.ndarray):
+    """y [n, d] -> (radius [n], [angles of level 1 .. log2 d]); level l has
+    d / 2^l angles per vector."""
+    y = np.asarray(y, dtype=np.float64)
+    angles = []
+    psi = np.mod(np.arctan2(y[:, 1::2], y[:, 0::2]), 2.0 * np.pi)
+    psi[psi >= 2.0 * np.pi] = 0.0
+    angles.append(psi)
+    r = np.hypot(y[:, 0::2], y[:, 1::2])
+    while r.shape[1] > 1:
+        angles.append(np.arctan2(r[:, 1::2], r[:, 0::2]))
+        r = np.hypot(r[:, 0::2], r[:, 1::2])
+    return r[:, 0], angles
+
+
+def polar_inverse(radius: np.ndarray, angles) -> np.ndarray:
+    """(radius, angles) -> y: each radius splits into r cos(theta), r sin(theta)."""
+    r = np.asarray(radius, dtype=np.float64)[:, None]
+    for th in reversed(angles[1:]):
+        out = np.empty((r.shape[0], 2 * r.shape[1]))
+        out[:, 0::2] = r * np.cos(th)
+        out[:, 1::2] = r * np.sin(th)
+        r = out
+    psi = angles[0]
+    y = np.empty((r.shape[0], 2 * r.shape[1]))
+    y[:, 0::2] = r * np.cos(psi)
+    y[:, 1::2] = r * np.sin(psi)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Q3: the angle laws   ([P3] 极坐标的洞察)
+# ---------------------------------------------------------------------------
+def angle_log_density(k: int, theta) -> np.ndarray:
+    """log of Gamma(k) / (2^(k-2) Gamma(k/2)^2) * sin^(k-1)(2 theta) on [0, pi/2]."""
+    theta = np.asarray(theta, dtype=np.float64)
+    logc = math.lgamma(k) - (k - 2) * math.log(2.0) - 2.0 * math.lgamma(k / 2.0)
+    with np.errstate(divide="ignore"):
+        return logc + (k - 1) * np.log(np.sin(2.0 * theta))
+
+
+def angle_density(k: int, theta) -> np.ndarray:
+    return np.exp(angle_log_density(k, theta))
+
+
+def angle_cdf(k: int, theta) -> np.ndarray:
+    """P(Theta <= theta) = I_{sin^2 theta}(k/2, k/2)."""
+    return betainc(k / 2.0, k / 2.0, np.sin(np.asarray(theta, dtype=np.float64)) ** 2)
+
+
+_GL_X, _GL_W = np.polynomial.legendre.leggauss(32)
+
+
+def _integrate(fn, a: float, b: float, pieces: int = 64) -> float:
+    """Composite 32-point Gauss-Legendre on [a, b]."""
+    if b <= a:
+        return 0.0
+    e = np.linspace(a, b, pieces + 1)
+    half = 0.5 * (e[1:] - e[:-1])
+    mid = 0.5 * (e[1:] + e[:-1])
+    x = mid[:, None] + half[:, None] * _GL_X[None, :]
+    return float(np.sum(half[:, None] * _GL_W[None, :] * fn(x)))
+
+
+# ---------------------------------------------------------------------------
+# Q4: the codebooks
+# ---------------------------------------------------------------------------
+@functools.lru_cache(maxsize=64)
+def angle_codebook(level: int, nbits: int):
+    """(centroids [2^nbits], boundaries [2^nbits - 1]) ascending, float64."""
+    L = 1 << nbits
+    if level == 1:
+        step = 2.0 * np.pi / L
+        return (np.arange(L) + 0.5) * step, np.arange(1, L) * step
+    k = 1 << (level - 1)
+    f = lambda t: angle_density(k, t)
+    tf = lambda t: t * angle_density(k, t)
+    # Lloyd-Max: boundaries at midpoints, centroids at the conditional means,
+    # started from the quantiles of the law
+    lo, hi = 0.0, 0.5 * np.pi
+    grid = np.linspace(lo, hi, 20001)
+    cdf = angle_cdf(k, grid)
+    c = np.interp((np.arange(L) + 0.5) / L, cdf, grid)
+    prev = math.inf
+    for _ in range(100000):
+        edges = np.concatenate([[lo], 0.5 * (c[:-1] + c[1:]), [hi]])
+        new = np.array([_integrate(tf, edges[j], edges[j + 1]) / _integrate(f, edges[j], edges[j + 1])
+                        for j in range(L)])
+        delta = float(np.max(np.abs(new - c)))
+        c = new
+        # converged, or stalled at the rounding floor of float64
+        if delta <= 1e-15 or (delta < 1e-13 and delta >= prev):
+            break
+        prev = delta
+    return c, 0.5 * (c[:-1] + c[1:])
+
+
+# ---------------------------------------------------------------------------
+# Encode, decode, score
+# ---------------------------------------------------------------------------
+def encode(x: np.ndarray, p: PolarParams) -> dict:
+    """codes: 'radius' float32 [n], 'level{l}' int [n, d / 2^l]; diagnostics
+    'y' (rotated vectors) and 'angles'."""
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[1] == p.d
+    y = x @ p.pi.T
+    _, angles = polar_transform(y)
+    out = {"radius": np.sqrt(np.sum(x * x, axis=1)).astype(np.float32), "y": y, "angles": angles}
+    for lev, th in enumerate(angles, start=1):
+        _, bnd = p.codebook(lev)
+        out[f"level{lev}"] = np.sum(th[:, :, None] >= bnd[None, None, :], axis=2)
+    return out
+
+
+def reconstruct_rotated(codes: dict, p: PolarParams) -> np.ndarray:
+    """y^ [n, d] from the codes (Q5)."""
+    angles = []
+    for lev in range(1, p.levels + 1):
+        cent, _ = p.codebook(lev)
+        angles.append(cent[np.asarray(codes[f"level{lev}"])])
+    return polar_inverse(np.asarray(codes["radius"], dtype=np.float64), angles)
+
+
+def decode(codes: dict, p: PolarParams) -> np.ndarray:
+    """x^ = Pi^T y^ in the original domain."""
+    return reconstruct_rotated(codes, p) @ p.pi
+
+
+def score(q: np.ndarray, codes: dict, p: PolarParams, n_kv: int, g: int, seq: int) -> np.ndarray:
+    """Logits [n_kv * g, seq]: query head h against the keys of KV head h // g
+    (rows (h // g) * seq ...), logit = <Pi q, y^>."""
+    q = np.asarray(q, dtype=np.float64).reshape(n_kv * g, p.d)
+    yh = reconstruct_rotated(codes, p).reshape(n_kv, seq, p.d)
+    qt = q @ p.pi.T
+    out = np.empty((n_kv * g, seq))
+    for h in range(n_kv * g):
+        out[h] = yh[h // g] @ qt[h]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Packed layout (a format, defined here and in include/tq.h), d = 128
+# ---------------------------------------------------------------------------
+# Word w of a record of 12 uint32 words:
+#   level 1, node j = 8 t + 2 g + i (coordinates 2j, 2j+1; t < 8, g < 4, i < 2):
+#       word 2 g + t // 4, bits 4 (2 (t % 4) + i) .. + 3
+#   level 2, node j = 4 t + g:          word 8 + g,  bits 2 t .. + 1
+#   level 3, node j = 2 t + h (h < 2):  word 8 + h,  bits 16 + 2 t
+#   level 4, node j = t:                word 10,     bits 16 + 2 t
+#   level 5, node j < 4:                word 11,     bits 16 + 2 j
+#   level 6, node j < 2:                word 11,     bits 24 + 2 j
+#   level 7, node 0:                    word 11,     bits 28
+def _slots_128():
+    """(level, node) -> (word, bit) for d = 128."""
+    s = {}
+    for j in range(64):
+        t, g, i = j // 8, (j // 2) % 4, j % 2
+        s[(1, j)] = (2 * g + t // 4, 4 * (2 * (t % 4) + i))
+    for j in range(32):
+        t, g = j // 4, j % 4
+        s[(2, j)] = (8 + g, 2 * t)
+    for j in range(16):
+        t, h = j // 2, j % 2
+        s[(3, j)] = (8 + h, 16 + 2 * t)
+    for j in range(8):
+        s[(4, j)] = (10, 16 + 2 * j)
+    for j in range(4):
+        s[(5, j)] = (11, 16 + 2 * j)
+    for j in range(2):
+        s[(6, j)] = (11, 24 + 2 * j)
+    s[(7, 0)] = (11, 28)
+    return s
+
+
+def pack(codes: dict, p: PolarParams) -> dict:
+    assert p.d == 128 and p.bits1 == 4 and p.bits == 2
+    n = codes["radius"].shape[0]
+    words = np.zeros((n, 12), dtype=np.uint64)
+    for (lev, j), (w, bit) in _slots_128().items():
+        words[:, w] |= np.asarray(codes[f"level{lev}"])[:, j].astype(np.uint64) << np.uint64(bit)
+    return {"pq": words.astype(np.uint32), "radius": np.asarray(codes["radius"], dtype=np.float32)}
+
+
+def unpack(packed: dict, p: PolarParams) -> dict:
+    assert p.d == 128 and p.bits1 == 4 and p.bits == 2
+    words = np.asarray(packed["pq"]).astype(np.uint64)
+    n = words.shape[0]
+    out = {"radius": np.asarray(packed["radius"], dtype=np.float32)}
+    for lev in range(1, 8):
+        out[f"level{lev}"] = np.zeros((n, 128 >> lev), dtype=np.int64)
+    for (lev, j), (w, bit) in _slots_128().items():
+        nb = 4 if lev == 1 else 2
+        out[f"level{lev}"][:, j] = ((words[:, w] >> np.uint64(bit)) & np.uint64((1 << nb) - 1)).astype(np.int64)
+    return out
