@@ -241,6 +241,67 @@ tq_status tq_search(const tq_params *p, const float *q, int64_t nq, tq_codes cod
  * concurrent calls into the library.                                       */
 tq_status tq_release_cache(void);
 
+/* ---------------------------------------------------------------------------
+ * PolarQuant: the stage-1 variant in which the rotated vector becomes one
+ * radius and d - 1 angles by a recursive polar transform, each angle
+ * quantised with a fixed codebook of its known law ("TurboQuant 与 AI 效率革命：
+ * 当旧数学遇到新智能", section 二, 极坐标的洞察 and 递归极坐标变换; bits per
+ * level: "TurboQuant压缩效果", 4 bits at the first level and 2 after).
+ *
+ * y = Pi x with the TurboQuant rotation of seed_pi.  Level 1 pairs y_2j,
+ * y_2j+1 into the angle atan2(y_2j+1, y_2j) in [0, 2 pi) (uniform law, bits1
+ * bits, uniform grid); level l >= 2 pairs the level-(l-1) radii (2j, 2j+1)
+ * into atan2(r_2j+1, r_2j) in [0, pi/2], whose law has density
+ * Gamma(k) / (2^(k-2) Gamma(k/2)^2) sin^(k-1)(2 theta), k = 2^(l-1)
+ * (Lloyd-Max codebook of `bits` bits).  A code is the number of boundaries at
+ * or below the angle.  The logit of a query q is <Pi q, y^>, y^ rebuilt from
+ * the radius ||x|| down the tree (r cos, r sin of the centroid angles).
+ *
+ * Packed record of one vector (d = 128, bits1 = 4, bits = 2): 12 uint32
+ * words `pq` and the float32 radius, 52 bytes.  Level 1 node j = 8 t + 2 g + i
+ * (coordinates 2j, 2j+1; t < 8, g < 4, i < 2): word 2 g + t / 4, bits
+ * 4 (2 (t % 4) + i) .. + 3.  Level 2 node 4 t + g: word 8 + g, bits 2 t.
+ * Level 3 node 2 t + h: word 8 + 2 h, bits 16 + 2 t.  Level 4 node t: word 9,
+ * bits 16 + 2 t.  Level 5 node j: word 11, bits 16 + 2 j; level 6 node j:
+ * word 11, bits 24 + 2 j; level 7: word 11, bits 28.  Other bits are zero.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t d;        /* power of two; the device kernels take d = 128 */
+  int32_t bits1;    /* bits of a level-1 angle (device: 4) */
+  int32_t bits;     /* bits of an angle at levels >= 2 (device: 2) */
+  int32_t reserved; /* 0 */
+  uint64_t seed_pi; /* rotation seed (the TurboQuant Pi) */
+} tq_polar_params;
+
+typedef struct {
+  uint32_t *pq;   /* device uint32 [n][12], caller-owned */
+  float *radius;  /* device float32 [n] */
+} tq_polar_codes;
+
+/* Codebook of level `level` (1 .. log2 d) at nbits bits (1 .. 6): float32
+ * centroids [2^nbits] and boundaries [2^nbits - 1], ascending, in radians.
+ * Host only.                                                                */
+tq_status tq_polar_make_codebook(int32_t d, int32_t level, int32_t nbits, float *centroids,
+                                 float *boundaries);
+
+/* Encodes n vectors x (row-major [n][128], TQ_F32 or TQ_BF16, device, 16-byte
+ * aligned) into codes.  Asynchronous on `stream`; no workspace.
+ * TQ_ERR_UNSUPPORTED unless d = 128, bits1 = 4, bits = 2.                  */
+tq_status tq_polar_encode(const tq_polar_params *p, const void *x, int32_t dtype, int64_t n,
+                          tq_polar_codes codes, void *stream);
+
+/* Workspace bytes tq_polar_score needs for n_kv * g queries.  Host only.   */
+tq_status tq_polar_score_workspace_bytes(const tq_polar_params *p, int64_t n_kv, int64_t g,
+                                         size_t *bytes);
+
+/* Logits [n_kv * g][seq] (float32, device) of queries q [n_kv * g][128]
+ * (float32, device) against the codes of n_kv * seq vectors (vector
+ * h * seq + pos); query head j uses KV head j / g.  Asynchronous; the caller's
+ * workspace holds the rotated queries.                                      */
+tq_status tq_polar_score(const tq_polar_params *p, const float *q, int64_t n_kv, int64_t g,
+                         tq_polar_codes codes, int64_t seq, float *logits, void *workspace,
+                         size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -473,6 +473,187 @@ tq_status get_derived(const tq_params *p, const Derived **out) {
 
 // ============================================================================
 // C ABI
+namespace tq {
+
+// --------------------------------------------------------------------------
+// PolarQuant codebooks.  Level 1: the angle of a coordinate pair is uniform on
+// [0, 2 pi), whose Lloyd-Max quantiser is the uniform grid.  Level l >= 2:
+// the angle between two radii of k = 2^(l-1) coordinates each has density
+// Gamma(k) / (2^(k-2) Gamma(k/2)^2) sin^(k-1)(2 theta) on [0, pi/2]; the
+// Lloyd-Max iteration takes cell masses and first moments by composite
+// Simpson quadrature in long double.
+// --------------------------------------------------------------------------
+static ld polar_pdf(int k, ld t) {
+  const ld s = std::sin(2.0L * t);
+  if (s <= 0.0L) return k == 1 ? std::exp(std::lgamma(1.0L) + std::log(2.0L) - 2.0L * std::lgamma(0.5L)) : 0.0L;
+  const ld logc = std::lgamma((ld)k) - (k - 2) * std::log(2.0L) - 2.0L * std::lgamma(k / 2.0L);
+  return std::exp(logc + (k - 1) * std::log(s));
+}
+
+static void polar_cell(int k, ld a, ld b, ld &m0, ld &m1) {
+  const int n = 2048;  // even
+  const ld h = (b - a) / n;
+  ld s0 = 0.0L, s1 = 0.0L;
+  for (int i = 0; i <= n; ++i) {
+    const ld t = a + h * i;
+    const ld w = (i == 0 || i == n) ? 1.0L : (i % 2 ? 4.0L : 2.0L);
+    const ld f = polar_pdf(k, t);
+    s0 += w * f;
+    s1 += w * t * f;
+  }
+  m0 = s0 * h / 3.0L;
+  m1 = s1 * h / 3.0L;
+}
+
+static void polar_codebook(int level, int nbits, std::vector<double> &cent, std::vector<double> &bnd) {
+  const int L = 1 << nbits;
+  cent.assign(L, 0.0);
+  bnd.assign(L - 1, 0.0);
+  const ld pi = 3.14159265358979323846264338327950288L;
+  if (level == 1) {
+    const ld step = 2.0L * pi / L;
+    for (int j = 0; j < L; ++j) cent[j] = (double)((j + 0.5L) * step);
+    for (int j = 1; j < L; ++j) bnd[j - 1] = (double)(j * step);
+    return;
+  }
+  const int k = 1 << (level - 1);
+  const ld lo = 0.0L, hi = pi / 2.0L;
+  // start: equal steps over pi/4 +- 2 standard deviations of the law
+  ld m0, m1, var = 0.0L;
+  {
+    const int n = 4096;
+    const ld h = (hi - lo) / n;
+    for (int i = 0; i <= n; ++i) {
+      const ld t = lo + h * i;
+      const ld w = (i == 0 || i == n) ? 1.0L : (i % 2 ? 4.0L : 2.0L);
+      var += w * (t - pi / 4) * (t - pi / 4) * polar_pdf(k, t);
+    }
+    var *= h / 3.0L;
+  }
+  const ld half = std::min<ld>(2.0L * std::sqrt(var), pi / 4);
+  std::vector<ld> c(L), nc(L), e(L + 1);
+  for (int j = 0; j < L; ++j) c[j] = pi / 4 - half + (2.0L * half) * (j + 0.5L) / L;
+  ld prev = 1.0L;
+  for (int it = 0; it < 100000; ++it) {
+    e[0] = lo;
+    e[L] = hi;
+    for (int j = 1; j < L; ++j) e[j] = 0.5L * (c[j - 1] + c[j]);
+    ld delta = 0.0L;
+    for (int j = 0; j < L; ++j) {
+      polar_cell(k, e[j], e[j + 1], m0, m1);
+      nc[j] = m1 / m0;
+      delta = std::max(delta, std::fabs(nc[j] - c[j]));
+    }
+    c.swap(nc);
+    if (delta <= 1e-17L) break;
+    if (delta < 1e-14L && delta >= prev) break;
+    prev = delta;
+  }
+  for (int j = 0; j < L; ++j) cent[j] = (double)c[j];
+  for (int j = 1; j < L; ++j) bnd[j - 1] = 0.5 * (cent[j - 1] + cent[j]);
+}
+
+// Kernel constants for d = 128, bits1 = 4, bits = 2 (built once).
+static const PolarTables &polar_tables() {
+  static PolarTables T;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    std::memset(&T, 0, sizeof(T));
+    std::vector<double> c, b;
+    polar_codebook(1, 4, c, b);
+    for (int j = 0; j < 16; ++j) {
+      T.c1[j] = (float)std::cos(c[j]);
+      T.s1[j] = (float)std::sin(c[j]);
+    }
+    for (int j = 0; j < 3; ++j) {  // boundaries pi/8, pi/4, 3 pi/8 inside a quadrant
+      T.dc1[j] = (float)std::cos(b[j]);
+      T.ds1[j] = (float)std::sin(b[j]);
+    }
+    for (int lev = 2; lev <= 7; ++lev) {
+      polar_codebook(lev, 2, c, b);
+      for (int j = 0; j < 4; ++j) {
+        T.cl[lev - 2][j] = (float)std::cos(c[j]);
+        T.sl[lev - 2][j] = (float)std::sin(c[j]);
+      }
+      for (int j = 0; j < 3; ++j) {
+        const double cj = std::cos(b[j]), sj = std::sin(b[j]);
+        T.dC[lev - 2][j] = (float)(cj * cj);
+        T.dS[lev - 2][j] = (float)(sj * sj);
+      }
+    }
+  });
+  return T;
+}
+
+// The tables on the current device (uploaded on first use, freed by
+// tq_release_cache).
+static std::mutex g_polar_mu;
+static std::map<int, PolarTables *> g_polar_dev;
+
+static tq_status polar_tables_device(const PolarTables **out) {
+  int dev = 0;
+  TQ_HIP_CHECK(hipGetDevice(&dev));
+  const PolarTables &host = polar_tables();
+  std::lock_guard<std::mutex> lock(g_polar_mu);
+  auto it = g_polar_dev.find(dev);
+  if (it == g_polar_dev.end()) {
+    PolarTables *d = nullptr;
+    TQ_HIP_CHECK(hipMalloc((void **)&d, sizeof(PolarTables)));
+    const hipError_t e = hipMemcpy(d, &host, sizeof(PolarTables), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(d);
+      set_error("hipMemcpy of the polar tables failed: %s", hipGetErrorString(e));
+      return TQ_ERR_HIP;
+    }
+    it = g_polar_dev.emplace(dev, d).first;
+  }
+  *out = it->second;
+  return TQ_OK;
+}
+
+static void polar_tables_release() {
+  std::lock_guard<std::mutex> lock(g_polar_mu);
+  for (auto &kv : g_polar_dev) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(kv.first);
+    (void)hipFree(kv.second);
+    (void)hipSetDevice(cur);
+  }
+  g_polar_dev.clear();
+}
+
+static tq_status check_polar(const tq_polar_params *p, const char *fn) {
+  if (!p) {
+    set_error("%s: params is NULL", fn);
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (p->d < 4 || (p->d & (p->d - 1)) || p->bits1 < 1 || p->bits1 > 6 || p->bits < 1 || p->bits > 6 ||
+      p->reserved != 0) {
+    set_error("%s: need d a power of two >= 4, 1 <= bits1, bits <= 6, reserved = 0", fn);
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (p->d != 128 || p->bits1 != 4 || p->bits != 2) {
+    set_error("%s: device kernels are built for d = 128, bits1 = 4, bits = 2", fn);
+    return TQ_ERR_UNSUPPORTED;
+  }
+  return TQ_OK;
+}
+
+// the TurboQuant parameters whose cache entry holds the rotation of seed_pi
+static tq_params polar_rotation_params(const tq_polar_params *p) {
+  tq_params t;
+  t.d = p->d;
+  t.b = 1;
+  t.m = 128;
+  t.mode = TQ_MODE_MSE;
+  t.seed_pi = p->seed_pi;
+  t.seed_s = 0;
+  return t;
+}
+
+}  // namespace tq
+
 // ============================================================================
 using namespace tq;
 
@@ -864,7 +1045,91 @@ tq_status tq_search(const tq_params *p, const float *q, int64_t nq, tq_codes cod
   return launch_search(*D, q, nq, codes, n, k, out_idx, out_val, workspace, (hipStream_t)stream);
 }
 
+tq_status tq_polar_make_codebook(int32_t d, int32_t level, int32_t nbits, float *centroids,
+                                 float *boundaries) {
+  int levels = 0;
+  while ((1 << (levels + 1)) <= d) ++levels;
+  if (d < 4 || (d & (d - 1)) || level < 1 || level > levels || nbits < 1 || nbits > 6 || !centroids ||
+      (nbits > 0 && !boundaries)) {
+    set_error("tq_polar_make_codebook: need d a power of two >= 4, 1 <= level <= log2 d, 1 <= nbits <= 6");
+    return TQ_ERR_INVALID_ARG;
+  }
+  std::vector<double> c, b;
+  polar_codebook(level, nbits, c, b);
+  for (size_t j = 0; j < c.size(); ++j) centroids[j] = (float)c[j];
+  for (size_t j = 0; j < b.size(); ++j) boundaries[j] = (float)b[j];
+  return TQ_OK;
+}
+
+tq_status tq_polar_encode(const tq_polar_params *p, const void *x, int32_t dtype, int64_t n,
+                          tq_polar_codes codes, void *stream) {
+  tq_status st = check_polar(p, "tq_polar_encode");
+  if (st) return st;
+  if (n < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) {
+    set_error("tq_polar_encode: n < 0 or bad dtype");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (n == 0) return TQ_OK;
+  if (!x || !codes.pq || !codes.radius) {
+    set_error("tq_polar_encode: NULL x/pq/radius");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (!aligned16(x) || !aligned16(codes.pq) || !aligned16(codes.radius)) {
+    set_error("tq_polar_encode: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  const tq_params tp = polar_rotation_params(p);
+  const Derived *D = nullptr;
+  if ((st = get_derived(&tp, &D))) return st;
+  const PolarTables *T = nullptr;
+  if ((st = polar_tables_device(&T))) return st;
+  return launch_polar_encode(*D, T, x, dtype, n, codes, (hipStream_t)stream);
+}
+
+tq_status tq_polar_score_workspace_bytes(const tq_polar_params *p, int64_t n_kv, int64_t g,
+                                         size_t *bytes) {
+  tq_status st = check_polar(p, "tq_polar_score_workspace_bytes");
+  if (st) return st;
+  if (n_kv < 0 || g < 1 || !bytes) {
+    set_error("tq_polar_score_workspace_bytes: bad sizes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  *bytes = polar_score_workspace_bytes(n_kv * g);
+  return TQ_OK;
+}
+
+tq_status tq_polar_score(const tq_polar_params *p, const float *q, int64_t n_kv, int64_t g,
+                         tq_polar_codes codes, int64_t seq, float *logits, void *workspace,
+                         size_t ws_bytes, void *stream) {
+  tq_status st = check_polar(p, "tq_polar_score");
+  if (st) return st;
+  if (n_kv < 0 || g < 1 || seq < 0) {
+    set_error("tq_polar_score: bad sizes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (n_kv == 0 || seq == 0) return TQ_OK;
+  if (!q || !logits || !workspace || !codes.pq || !codes.radius) {
+    set_error("tq_polar_score: NULL q/logits/workspace/pq/radius");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (!aligned16(q) || !aligned16(workspace) || !aligned16(codes.pq) || !aligned16(codes.radius)) {
+    set_error("tq_polar_score: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (ws_bytes < polar_score_workspace_bytes(n_kv * g)) {
+    set_error("tq_polar_score: workspace too small");
+    return TQ_ERR_NO_MEMORY;
+  }
+  const tq_params tp = polar_rotation_params(p);
+  const Derived *D = nullptr;
+  if ((st = get_derived(&tp, &D))) return st;
+  const PolarTables *T = nullptr;
+  if ((st = polar_tables_device(&T))) return st;
+  return launch_polar_score(*D, T, q, n_kv, g, codes, seq, logits, workspace, (hipStream_t)stream);
+}
+
 tq_status tq_release_cache(void) {
+  polar_tables_release();
   std::lock_guard<std::mutex> lock(g_cache_mu);
   for (auto &kv : g_cache) free_derived(kv.second);
   g_cache.clear();

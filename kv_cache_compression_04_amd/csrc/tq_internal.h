@@ -103,6 +103,21 @@ size_t search_workspace_bytes(const tq_params &p, int64_t nq, int64_t n, int k);
 tq_status launch_search(const Derived &D, const float *q, int64_t nq, tq_codes codes, int64_t n,
                         int k, int64_t *out_idx, float *out_val, void *ws, hipStream_t stream);
 
+// PolarQuant constants for d = 128 (level-1 bits 4, later levels 2 bits), in
+// the form the kernels consume (one device copy per GPU).
+struct PolarTables {
+  float c1[16], s1[16];      // cos, sin of the level-1 centroid angles
+  float cl[6][4], sl[6][4];  // cos, sin of the level-(2 + i) centroid angles
+  float dc1[3], ds1[3];      // cos, sin of the level-1 boundaries pi/8, pi/4, 3 pi/8 within a quadrant
+  float dC[6][3], dS[6][3];  // cos^2, sin^2 of the level-(2 + i) boundaries
+};
+tq_status launch_polar_encode(const Derived &D, const PolarTables *T, const void *x, int dtype,
+                              int64_t n, tq_polar_codes codes, hipStream_t stream);
+size_t polar_score_workspace_bytes(int64_t nq);
+tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float *q, int64_t n_kv,
+                             int64_t g, tq_polar_codes codes, int64_t seq, float *logits, void *ws,
+                             hipStream_t stream);
+
 // Fragment geometry of the d = m = 128 encode kernel: a 128 x 128 matrix is
 // stored as [16-row tile nt][32-column block kt][lane][8] bf16 values; lane l
 // covers row 16 nt + l % 16 and lane group l / 16.

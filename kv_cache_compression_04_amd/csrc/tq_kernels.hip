@@ -2563,4 +2563,284 @@ tq_status launch_decode(const Derived &D, tq_codes codes, int64_t n, float *out,
   return TQ_OK;
 }
 
+// ===========================================================================
+// PolarQuant, d = 128 (level 1: 4 bits, levels 2..7: 2 bits)
+// ===========================================================================
+// Encode: the rotation is the TurboQuant GEMM 1 (bf16 hi/lo fragments of Pi
+// in LDS), one 16-row tile nt at a time: lane (v, g) receives
+// y[16 nt + 4 g + i] of vector v.  Levels 1 and 2 pair coordinates inside
+// the lane; level 3 pairs lane groups g, g ^ 1 and level 4 g, g ^ 2 (one
+// shuffle each); levels 5..7 pair the tiles nt inside the lane.  Every level
+// >= 2 decision is taken on squared radii (theta >= t  <=>
+// r_R^2 cos^2 t >= r_L^2 sin^2 t), so no square root or arctangent is needed;
+// level 1 takes the quadrant from the signs and the sector within it from
+// two-sided products with the boundary's cosine and sine.
+constexpr int kPolWaves = 16;
+
+__device__ __forceinline__ uint32_t polar_sector(float a, float b, const PolarTables *__restrict__ T) {
+  // quadrant q: psi in [q pi/2, (q + 1) pi/2); (a', b') = (a, b) turned back by q pi/2
+  const bool q1 = a <= 0.f && b > 0.f, q2 = a < 0.f && b <= 0.f, q3 = a >= 0.f && b < 0.f;
+  const float ap = q1 ? b : (q2 ? -a : (q3 ? -b : a));
+  const float bp = q1 ? -a : (q2 ? -b : (q3 ? a : b));
+  const uint32_t q = q1 ? 1u : (q2 ? 2u : (q3 ? 3u : 0u));
+  uint32_t sub = 0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) sub += (bp * T->dc1[j] >= ap * T->ds1[j]) ? 1u : 0u;
+  const bool zero = a == 0.f && b == 0.f;  // the zero pair has angle 0
+  return zero ? 0u : 4u * q + sub;
+}
+
+// code of the angle between radii with squares sl (left) and sr (right)
+__device__ __forceinline__ uint32_t polar_level_code(float sl, float sr, const float *C, const float *S) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) c += (sr * C[j] >= sl * S[j]) ? 1u : 0u;
+  return sl + sr > 0.f ? c : 0u;
+}
+
+template <bool XBF16>
+__global__ __launch_bounds__(kPolWaves * 64) void polar_encode128_kernel(
+    const void *__restrict__ x, int64_t n, const uint4 *__restrict__ pi_hi,
+    const uint4 *__restrict__ pi_lo, const PolarTables *__restrict__ T, uint32_t *__restrict__ pq,
+    float *__restrict__ radius) {
+  __shared__ uint4 lds[2 * kFragU4];
+  for (int i = threadIdx.x; i < kFragU4; i += blockDim.x) {
+    lds[i] = pi_hi[i];
+    lds[kFragU4 + i] = pi_lo[i];
+  }
+  __syncthreads();
+  const uint4 *Phi = lds + (threadIdx.x & 63), *Plo = lds + kFragU4 + (threadIdx.x & 63);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int vcol = lane & 15, g = lane >> 4;
+  const int64_t nbatch = (n + 15) / 16;
+  for (int64_t batch = (int64_t)blockIdx.x * kPolWaves + wave; batch < nbatch;
+       batch += (int64_t)gridDim.x * kPolWaves) {
+    const int64_t row = batch * 16 + vcol;
+    const bool valid = row < n;
+    uint4 xh[4], xl[4];
+    float ss = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) load_x_frag<XBF16>(x, row, valid, kt, g, xh[kt], xl[kt], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    uint32_t w1[2] = {0u, 0u}, w8 = 0u;
+    float s2[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8 ah = as_bf16x8(Phi[(nt * 4 + kt) * 64]);
+        const bf16x8 al = as_bf16x8(Plo[(nt * 4 + kt) * 64]);
+        const bf16x8 bh = as_bf16x8(xh[kt]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        if (!XBF16) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(xl[kt]), acc, 0, 0, 0);
+      }
+      float sp[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float a = acc[2 * i], b = acc[2 * i + 1];
+        w1[nt >> 2] |= polar_sector(a, b, T) << (4 * (2 * (nt & 3) + i));
+        sp[i] = fmaf(b, b, a * a);
+      }
+      w8 |= polar_level_code(sp[0], sp[1], T->dC[0], T->dS[0]) << (2 * nt);
+      s2[nt] = sp[0] + sp[1];
+      // one tile's fragments in flight at a time (no hoisting of all 64 reads)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // level 3: node (nt, g / 2) pairs lane groups 2h, 2h + 1; kept by g = 2h
+    // level 4: node nt pairs h = 0 (g < 2) and h = 1; kept by g = 1
+    uint32_t hi3 = 0u, hi4 = 0u;
+    float s4[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const float o = __shfl_xor(s2[nt], 16);
+      const float sl = (g & 1) ? o : s2[nt], sr = (g & 1) ? s2[nt] : o;
+      hi3 |= polar_level_code(sl, sr, T->dC[1], T->dS[1]) << (2 * nt);
+      const float s3 = sl + sr;
+      const float o3 = __shfl_xor(s3, 32);
+      const float tl = (g & 2) ? o3 : s3, tr = (g & 2) ? s3 : o3;
+      hi4 |= polar_level_code(tl, tr, T->dC[2], T->dS[2]) << (2 * nt);
+      s4[nt] = tl + tr;
+    }
+    // levels 5..7 inside the lane; kept by g = 3
+    uint32_t hi5 = 0u;
+    float s5[4], s6[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hi5 |= polar_level_code(s4[2 * j], s4[2 * j + 1], T->dC[3], T->dS[3]) << (2 * j);
+      s5[j] = s4[2 * j] + s4[2 * j + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      hi5 |= polar_level_code(s5[2 * j], s5[2 * j + 1], T->dC[4], T->dS[4]) << (8 + 2 * j);
+      s6[j] = s5[2 * j] + s5[2 * j + 1];
+    }
+    hi5 |= polar_level_code(s6[0], s6[1], T->dC[5], T->dS[5]) << 12;
+    const uint32_t hi = g == 0 ? hi3 : (g == 1 ? hi4 : (g == 2 ? hi3 : hi5));
+    w8 |= hi << 16;
+    if (valid) {
+      uint32_t *dst = pq + row * 12;
+      *reinterpret_cast<uint2 *>(dst + 2 * g) = make_uint2(w1[0], w1[1]);
+      dst[8 + g] = w8;
+      if (g == 0) radius[row] = sqrtf(ss);
+    }
+  }
+}
+
+// Rotated queries qt = Pi q (float64 sums), one workgroup of 128 threads per query.
+__global__ __launch_bounds__(128) void polar_qrot_kernel(const float *__restrict__ q,
+                                                         const double *__restrict__ pi64,
+                                                         float *__restrict__ qt) {
+  __shared__ double qs[128];
+  const int64_t j = blockIdx.x;
+  const int r = threadIdx.x;
+  qs[r] = (double)q[j * 128 + r];
+  __syncthreads();
+  double acc = 0.0;
+  for (int k = 0; k < 128; ++k) acc = fma(pi64[r * 128 + k], qs[k], acc);
+  qt[j * 128 + r] = (float)acc;
+}
+
+// Score: one key per thread and the (up to) 4 query heads of a group.  The
+// tree is folded bottom-up: a level-1 node gives c q_2j + s q_2j+1 per query,
+// a node above gives c f_left + s f_right, and the root times the radius is
+// the logit <Pi q, y^>.  Rotated queries and the cos / sin tables sit in LDS
+// (the query reads are broadcasts, the table reads 16 distinct float2 at most).
+constexpr int kPolScoreThreads = 256;
+__global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
+    const float *__restrict__ qt, const uint32_t *__restrict__ pq, const float *__restrict__ radius,
+    int64_t seq, int64_t g, int ngroups, const PolarTables *__restrict__ T, float *__restrict__ logits) {
+  __shared__ float4 qs[128];
+  __shared__ float2 t1[16];
+  __shared__ float2 tl[6][4];
+  const int hg = blockIdx.y, h = hg / ngroups, grp = hg % ngroups;
+  const int tid = threadIdx.x;
+  if (tid < 128) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t qh = (int64_t)grp * 4 + j;
+      v[j] = qh < g ? qt[((int64_t)h * g + qh) * 128 + tid] : 0.f;
+    }
+    qs[tid] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  if (tid < 16) t1[tid] = make_float2(T->c1[tid], T->s1[tid]);
+  if (tid < 24) tl[tid / 4][tid % 4] = make_float2(T->cl[tid / 4][tid % 4], T->sl[tid / 4][tid % 4]);
+  __syncthreads();
+  const int64_t pos = (int64_t)blockIdx.x * kPolScoreThreads + tid;
+  if (pos >= seq) return;  // no barrier follows
+  const int64_t v = (int64_t)h * seq + pos;
+  const uint4 *src = reinterpret_cast<const uint4 *>(pq + v * 12);
+  const uint4 u0 = src[0], u1 = src[1], u2 = src[2];
+  const uint32_t wd[12] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w, u2.x, u2.y, u2.z, u2.w};
+  const float R = radius[v];
+  // Blocks of 32 coordinates (t2) one loop iteration at a time, so that the
+  // query and table reads of one block are not all hoisted and held together;
+  // the level-5 and level-6 left siblings wait in p5, p6.
+  float p5[4] = {0.f, 0.f, 0.f, 0.f}, p6[4] = {0.f, 0.f, 0.f, 0.f}, f7[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int t2 = 0; t2 < 4; ++t2) {
+    float f4[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = 2 * t2 + tt;
+      float f3[2][4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float f2[2][4];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int gl = 2 * hh + gg;
+          const uint32_t w1 = t2 >= 2 ? wd[2 * gl + 1] : wd[2 * gl];
+          float f1[2][4];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint32_t code = (w1 >> (4 * (2 * (t & 3) + i))) & 15u;
+            const float2 cs = t1[code];
+            const int c0 = 16 * t + 4 * gl + 2 * i;
+            const float4 qa = qs[c0], qb = qs[c0 + 1];
+            f1[i][0] = fmaf(cs.x, qa.x, cs.y * qb.x);
+            f1[i][1] = fmaf(cs.x, qa.y, cs.y * qb.y);
+            f1[i][2] = fmaf(cs.x, qa.z, cs.y * qb.z);
+            f1[i][3] = fmaf(cs.x, qa.w, cs.y * qb.w);
+          }
+          const float2 c2 = tl[0][(wd[8 + gl] >> (2 * t)) & 3u];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) f2[gg][j] = fmaf(c2.x, f1[0][j], c2.y * f1[1][j]);
+        }
+        const float2 c3 = tl[1][(wd[8 + 2 * hh] >> (16 + 2 * t)) & 3u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f3[hh][j] = fmaf(c3.x, f2[0][j], c3.y * f2[1][j]);
+      }
+      const float2 c4 = tl[2][(wd[9] >> (16 + 2 * t)) & 3u];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f4[tt][j] = fmaf(c4.x, f3[0][j], c4.y * f3[1][j]);
+    }
+    float f5[4];
+    const float2 c5 = tl[3][(wd[11] >> (16 + 2 * t2)) & 3u];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f5[j] = fmaf(c5.x, f4[0][j], c5.y * f4[1][j]);
+    if (t2 & 1) {
+      float f6[4];
+      const float2 c6 = tl[4][(wd[11] >> (24 + (t2 & 2))) & 3u];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f6[j] = fmaf(c6.x, p5[j], c6.y * f5[j]);
+      if (t2 == 3) {
+        const float2 c7 = tl[5][(wd[11] >> 28) & 3u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f7[j] = fmaf(c7.x, p6[j], c7.y * f6[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p6[j] = f6[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p5[j] = f5[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t qh = (int64_t)grp * 4 + j;
+    if (qh < g) logits[((int64_t)h * g + qh) * seq + pos] = R * f7[j];
+  }
+}
+
+tq_status launch_polar_encode(const Derived &D, const PolarTables *T, const void *x, int dtype,
+                              int64_t n, tq_polar_codes c, hipStream_t s) {
+  const int64_t nbatch = (n + 15) / 16;
+  const int64_t need = (nbatch + kPolWaves - 1) / kPolWaves;
+  // 64 KB of fragments per workgroup: two workgroups per CU
+  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * 2);
+  const uint4 *ph = reinterpret_cast<const uint4 *>(D.pi_hi), *pl = reinterpret_cast<const uint4 *>(D.pi_lo);
+  if (dtype == TQ_BF16)
+    polar_encode128_kernel<true><<<grid, kPolWaves * 64, 0, s>>>(x, n, ph, pl, T, c.pq, c.radius);
+  else
+    polar_encode128_kernel<false><<<grid, kPolWaves * 64, 0, s>>>(x, n, ph, pl, T, c.pq, c.radius);
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+size_t polar_score_workspace_bytes(int64_t nq) { return (size_t)nq * 128 * sizeof(float); }
+
+tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float *q, int64_t n_kv,
+                             int64_t g, tq_polar_codes c, int64_t seq, float *logits, void *ws,
+                             hipStream_t s) {
+  const int ngroups = (int)((g + 3) / 4);
+  const int64_t nhg = n_kv * ngroups;
+  const int64_t nblk = (seq + kPolScoreThreads - 1) / kPolScoreThreads;
+  if (nhg > 65535 || nblk > 0x7fffffffLL || n_kv * g > 0x7fffffffLL) {
+    set_error("tq_polar_score: problem too large for one launch");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  float *qt = (float *)ws;
+  polar_qrot_kernel<<<(unsigned)(n_kv * g), 128, 0, s>>>(q, D.pi64, qt);
+  polar_score128_kernel<<<dim3((unsigned)nblk, (unsigned)nhg), kPolScoreThreads, 0, s>>>(
+      qt, c.pq, c.radius, seq, g, ngroups, T, logits);
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
 }  // namespace tq

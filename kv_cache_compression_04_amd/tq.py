@@ -36,6 +36,15 @@ class _Params(ctypes.Structure):
                 ("mode", ctypes.c_int32), ("seed_pi", ctypes.c_uint64), ("seed_s", ctypes.c_uint64)]
 
 
+class _PolarParams(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("bits1", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("seed_pi", ctypes.c_uint64)]
+
+
+class _PolarCodes(ctypes.Structure):
+    _fields_ = [("pq", ctypes.c_void_p), ("radius", ctypes.c_void_p)]
+
+
 class _Codes(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("sgn", ctypes.c_void_p),
                 ("knorm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p)]
@@ -46,7 +55,8 @@ EXPORTS = ["tq_status_string", "tq_last_error", "tq_layout_version", "tq_make_co
            "tq_score_workspace_bytes",
            "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_decode",
            "tq_search_workspace_bytes", "tq_search", "tq_encode_slots",
-           "tq_attend_paged_workspace_bytes", "tq_attend_paged", "tq_release_cache"]
+           "tq_attend_paged_workspace_bytes", "tq_attend_paged", "tq_polar_make_codebook", "tq_polar_encode",
+           "tq_polar_score_workspace_bytes", "tq_polar_score", "tq_release_cache"]
 
 PAGE_POSITIONS = 512  # TQ_PAGE_POSITIONS
 
@@ -63,6 +73,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, C, vp, i64 = ctypes.POINTER(_Params), _Codes, ctypes.c_void_p, ctypes.c_int64
         sz = ctypes.c_size_t
+        PP, PC = ctypes.POINTER(_PolarParams), _PolarCodes
         sig = {
             "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "tq_last_error": (ctypes.c_char_p, []),
@@ -83,6 +94,10 @@ def lib():
             "tq_attend_paged_workspace_bytes": (ctypes.c_int, [P, P, i64, i64, i64, i64, ctypes.POINTER(sz)]),
             "tq_attend_paged": (ctypes.c_int, [P, P, vp, i64, i64, i64, C, C, i64, vp, i64, vp, ctypes.c_float,
                                                vp, vp, sz, vp]),
+            "tq_polar_make_codebook": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]),
+            "tq_polar_encode": (ctypes.c_int, [PP, vp, ctypes.c_int32, i64, PC, vp]),
+            "tq_polar_score_workspace_bytes": (ctypes.c_int, [PP, i64, i64, ctypes.POINTER(sz)]),
+            "tq_polar_score": (ctypes.c_int, [PP, vp, i64, i64, PC, i64, vp, vp, sz, vp]),
             "tq_release_cache": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -281,3 +296,60 @@ def attend_paged(kp: Params, vp: Params, q, batch, n_kv, g, kcodes, vcodes, num_
         ctypes.byref(kp.c()), ctypes.byref(vp.c()), _ptr(q), batch, n_kv, g, _codes(kcodes), _codes(vcodes),
         num_pages, _ptr(block_table), block_table.shape[1], _ptr(seq_lens), scale, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ----------------------------------------------------------------- PolarQuant
+@dataclass(frozen=True)
+class PolarParams:
+    """d, bits of a level-1 angle, bits of the later levels, seed of Pi."""
+    d: int = 128
+    bits1: int = 4
+    bits: int = 2
+    seed_pi: int = 2
+
+    def c(self) -> _PolarParams:
+        return _PolarParams(self.d, self.bits1, self.bits, 0, self.seed_pi)
+
+
+POLAR_WORDS = 12  # uint32 words of a packed record at d = 128
+
+
+def polar_make_codebook(d: int, level: int, nbits: int):
+    c = np.zeros(1 << nbits, dtype=np.float32)
+    t = np.zeros((1 << nbits) - 1, dtype=np.float32)
+    _check("tq_polar_make_codebook", lib().tq_polar_make_codebook(d, level, nbits, c.ctypes.data, t.ctypes.data))
+    return c, t
+
+
+def alloc_polar_codes(n: int, device="cuda"):
+    import torch
+    return {"pq": torch.empty((n, POLAR_WORDS), dtype=torch.int32, device=device),
+            "radius": torch.empty((n,), dtype=torch.float32, device=device)}
+
+
+def _pcodes(c: dict) -> _PolarCodes:
+    return _PolarCodes(c["pq"].data_ptr(), c["radius"].data_ptr())
+
+
+def polar_encode(p: PolarParams, x, codes: dict, stream=None):
+    """x: cuda tensor [n, d] float32 or bfloat16, contiguous."""
+    import torch
+    assert x.is_contiguous()
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    _check("tq_polar_encode", lib().tq_polar_encode(ctypes.byref(p.c()), _ptr(x), dt, x.shape[0], _pcodes(codes),
+                                                    _stream(stream)))
+
+
+def polar_score_workspace_bytes(p: PolarParams, n_kv: int, g: int) -> int:
+    out = ctypes.c_size_t()
+    _check("tq_polar_score_workspace_bytes",
+           lib().tq_polar_score_workspace_bytes(ctypes.byref(p.c()), n_kv, g, ctypes.byref(out)))
+    return out.value
+
+
+def polar_score(p: PolarParams, q, codes: dict, n_kv: int, g: int, seq: int, logits, workspace, stream=None):
+    """q: [n_kv*g, d] float32; logits: [n_kv*g, seq] float32 (written)."""
+    assert q.is_contiguous() and logits.is_contiguous()
+    _check("tq_polar_score", lib().tq_polar_score(ctypes.byref(p.c()), _ptr(q), n_kv, g, _pcodes(codes), seq,
+                                                  _ptr(logits), _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(), _stream(stream)))

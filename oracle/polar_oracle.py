@@ -221,8 +221,8 @@ def score(q: np.ndarray, codes: dict, p: PolarParams, n_kv: int, g: int, seq: in
 #   level 1, node j = 8 t + 2 g + i (coordinates 2j, 2j+1; t < 8, g < 4, i < 2):
 #       word 2 g + t // 4, bits 4 (2 (t % 4) + i) .. + 3
 #   level 2, node j = 4 t + g:          word 8 + g,  bits 2 t .. + 1
-#   level 3, node j = 2 t + h (h < 2):  word 8 + h,  bits 16 + 2 t
-#   level 4, node j = t:                word 10,     bits 16 + 2 t
+#   level 3, node j = 2 t + h (h < 2):  word 8 + 2 h, bits 16 + 2 t
+#   level 4, node j = t:                word 9,      bits 16 + 2 t
 #   level 5, node j < 4:                word 11,     bits 16 + 2 j
 #   level 6, node j < 2:                word 11,     bits 24 + 2 j
 #   level 7, node 0:                    word 11,     bits 28
@@ -237,9 +237,9 @@ def _slots_128():
         s[(2, j)] = (8 + g, 2 * t)
     for j in range(16):
         t, h = j // 2, j % 2
-        s[(3, j)] = (8 + h, 16 + 2 * t)
+        s[(3, j)] = (8 + 2 * h, 16 + 2 * t)
     for j in range(8):
-        s[(4, j)] = (10, 16 + 2 * j)
+        s[(4, j)] = (9, 16 + 2 * j)
     for j in range(4):
         s[(5, j)] = (11, 16 + 2 * j)
     for j in range(2):

@@ -1,0 +1,161 @@
+"""GPU parity of the PolarQuant variant (d = 128, 4 bits at level 1, 2 bits
+above) against the oracle: codes of every level, radius, and logits."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import polar_oracle as po
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - the CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from kv_cache_compression_04_amd import synth, tq  # noqa: E402
+from tests.gpu_helpers import DEV  # noqa: E402
+
+P = tq.PolarParams(128, 4, 2, 2)
+OP = po.PolarParams(128, 4, 2, 2)
+WINDOW = 1e-5          # a decision may differ only this close to a boundary (relative to ||x||)
+MAX_MISMATCH = 1e-4    # and for at most this fraction of the angles
+
+
+def _gpu_codes(codes):
+    pq = codes["pq"].cpu().numpy().view(np.uint32)
+    return {"pq": pq, "radius": codes["radius"].cpu().numpy()}
+
+
+def check_polar_encode(x: np.ndarray, got_packed: dict):
+    """Every level's codes equal the oracle's except within the window."""
+    ref = po.encode(x, OP)
+    got = po.unpack(got_packed, OP)
+    nrm = np.linalg.norm(x, axis=1)
+    assert np.all(np.abs(got["radius"].astype(np.float64) - nrm) <= 2e-6 * nrm + 1e-30)
+    y = ref["y"]
+    # node radii per level (level 1: pair radii; level l: radius of the node's 2^l coordinates)
+    radii = [np.hypot(y[:, 0::2], y[:, 1::2])]
+    while radii[-1].shape[1] > 1:
+        r = radii[-1]
+        radii.append(np.hypot(r[:, 0::2], r[:, 1::2]))
+    total, bad_total = 0, 0
+    stats = {}
+    for lev in range(1, 8):
+        g_, r_ = got[f"level{lev}"], ref[f"level{lev}"]
+        th = ref["angles"][lev - 1]
+        _, bnd = OP.codebook(lev)
+        mism = g_ != r_
+        total += mism.size
+        bad_total += int(mism.sum())
+        stats[lev] = int(mism.sum())
+        if not mism.any():
+            continue
+        rows, cols = np.nonzero(mism)
+        for rr, cc in zip(rows, cols):
+            a, b = sorted((int(g_[rr, cc]), int(r_[rr, cc])))
+            if lev == 1 and (a, b) == (0, 15):
+                t = 0.0 if th[rr, cc] < math.pi else 2 * math.pi      # the wrap at angle 0
+            else:
+                assert b == a + 1, f"level {lev}: codes {a}, {b} are not neighbours"
+                t = bnd[a]
+            node_r = radii[lev - 1][rr, cc]
+            assert abs(th[rr, cc] - t) * node_r <= WINDOW * nrm[rr], \
+                f"level {lev} row {rr}: mismatch {abs(th[rr, cc] - t) * node_r / nrm[rr]:.2e} from a boundary"
+    assert bad_total <= MAX_MISMATCH * total, f"{bad_total} of {total} angle codes differ"
+    return ref, stats
+
+
+@pytest.mark.parametrize("kind,n", [("bf16", 3000), ("f32", 1037), ("bf16", 1), ("f32", 16)])
+def test_polar_encode_matches_oracle(kind, n):
+    if kind == "bf16":
+        x = synth.llama_keys(heads=1, seq=n, seed=n, device=DEV)
+    else:
+        x = synth.sweep_keys(n=n, seed=n, device=DEV)
+    codes = tq.alloc_polar_codes(n, DEV)
+    tq.polar_encode(P, x, codes)
+    torch.cuda.synchronize()
+    _, stats = check_polar_encode(x.double().cpu().numpy(), _gpu_codes(codes))
+    print(f"[parity] polar encode {kind} n={n}: mismatches per level {stats}", flush=True)
+
+
+def test_polar_encode_zero_vectors():
+    x = torch.zeros((40, 128), device=DEV)
+    codes = tq.alloc_polar_codes(40, DEV)
+    codes["pq"].fill_(-1)
+    tq.polar_encode(P, x, codes)
+    torch.cuda.synchronize()
+    assert int(codes["pq"].abs().sum()) == 0 and float(codes["radius"].abs().sum()) == 0.0
+
+
+def _check_logits(got, ref, q, radius, n_kv, g, seq):
+    got = np.asarray(got, np.float64).reshape(n_kv * g, seq)
+    qn = np.linalg.norm(q.reshape(n_kv * g, -1), axis=1)
+    R = np.asarray(radius, np.float64).reshape(n_kv, seq)
+    floor = qn[:, None] * R[np.arange(n_kv * g) // g] / math.sqrt(128)
+    tol = 1e-4 * np.maximum(np.abs(ref), floor)
+    err = np.abs(got - ref)
+    worst = float(np.max(err / np.maximum(tol, 1e-300)))
+    assert np.all(err <= tol), f"polar logit error up to {worst:.3f} x tolerance"
+    return worst
+
+
+@pytest.mark.parametrize("n_kv,g,seq", [(2, 4, 1000), (1, 5, 300), (3, 1, 257), (1, 4, 1)])
+def test_polar_score_matches_oracle(n_kv, g, seq):
+    """Oracle codes in, GPU logits out; and GPU codes in, checked against the
+    oracle's estimator on those same codes."""
+    x = synth.llama_keys(heads=n_kv, seq=seq, seed=seq + g, dtype=torch.float32)
+    xn = x.double().numpy()
+    q = synth.queries(n_kv * g, seed=g).numpy().astype(np.float64)
+    dq = torch.from_numpy(q.astype(np.float32)).to(DEV)
+    ws = torch.empty(tq.polar_score_workspace_bytes(P, n_kv, g), dtype=torch.uint8, device=DEV)
+    logits = torch.empty((n_kv * g, seq), device=DEV)
+    # (1) oracle codes
+    oc = po.encode(xn, OP)
+    pk = po.pack(oc, OP)
+    codes = {"pq": torch.from_numpy(pk["pq"].view(np.int32)).to(DEV), "radius": torch.from_numpy(pk["radius"]).to(DEV)}
+    tq.polar_score(P, dq, codes, n_kv, g, seq, logits, ws)
+    torch.cuda.synchronize()
+    ref = po.score(q, oc, OP, n_kv, g, seq)
+    w1 = _check_logits(logits.cpu().numpy(), ref, q, oc["radius"], n_kv, g, seq)
+    # (2) GPU codes
+    gcodes = tq.alloc_polar_codes(n_kv * seq, DEV)
+    tq.polar_encode(P, x.to(DEV), gcodes)
+    tq.polar_score(P, dq, gcodes, n_kv, g, seq, logits, ws)
+    torch.cuda.synchronize()
+    gu = po.unpack(_gpu_codes(gcodes), OP)
+    ref2 = po.score(q, gu, OP, n_kv, g, seq)
+    w2 = _check_logits(logits.cpu().numpy(), ref2, q, gu["radius"], n_kv, g, seq)
+    print(f"[parity] polar score n_kv={n_kv} g={g} seq={seq}: worst/tol {w1:.4f} (oracle codes), "
+          f"{w2:.4f} (GPU codes)", flush=True)
+
+
+def test_polar_full_size_layer():
+    """8 KV heads x 32768 positions of bfloat16 keys, 32 query heads: sampled
+    rows of the codes and logits against the oracle."""
+    n_kv, seq, g = 8, 32768, 4
+    x = synth.llama_keys(heads=n_kv, seq=seq, seed=1, device=DEV)
+    codes = tq.alloc_polar_codes(n_kv * seq, DEV)
+    tq.polar_encode(P, x, codes)
+    q = synth.queries(n_kv * g, seed=5, device=DEV)
+    logits = torch.empty((n_kv * g, seq), device=DEV)
+    ws = torch.empty(tq.polar_score_workspace_bytes(P, n_kv, g), dtype=torch.uint8, device=DEV)
+    tq.polar_score(P, q, codes, n_kv, g, seq, logits, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([rng.choice(n_kv * seq, 4000, replace=False), [0, n_kv * seq - 1]]))
+    gp = _gpu_codes(codes)
+    sub = {"pq": gp["pq"][rows], "radius": gp["radius"][rows]}
+    check_polar_encode(x[torch.from_numpy(rows).to(DEV)].double().cpu().numpy(), sub)
+    gu = po.unpack(sub, OP)
+    qn = q.double().cpu().numpy()
+    lg = logits.cpu().numpy()
+    yh = po.reconstruct_rotated(gu, OP)
+    qt = qn @ OP.pi.T
+    for j, r in enumerate(rows):
+        h = r // seq
+        for qq in range(h * g, (h + 1) * g):
+            ref = float(yh[j] @ qt[qq])
+            tol = 1e-4 * max(abs(ref), np.linalg.norm(qn[qq]) * float(gu["radius"][j]) / math.sqrt(128))
+            assert abs(lg[qq, r % seq] - ref) <= tol
+    print(f"[parity] polar full layer: {len(rows)} sampled keys x 4 queries consistent", flush=True)

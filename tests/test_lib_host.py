@@ -184,3 +184,43 @@ def test_paged_cache_argument_checks():
     k256 = tq._Params(256, 3, 256, 0, 1, 2)
     v256 = tq._Params(256, 3, 256, 1, 4, 0)
     assert att(k256, v256, 4, a, 2, a) == 2            # built for d = m = 128
+
+
+def test_polar_codebooks_match_oracle():
+    """The library's PolarQuant codebooks (C++ Simpson quadrature) against the
+    oracle's (numpy Gauss-Legendre): two implementations of the same laws."""
+    from oracle import polar_oracle as po
+    for lev in range(1, 8):
+        for nb in ((4,) if lev == 1 else (1, 2, 3)):
+            c, t = tq.polar_make_codebook(128, lev, nb)
+            oc, ot = po.angle_codebook(lev, nb)
+            assert np.allclose(c, oc, rtol=0, atol=1e-6), (lev, nb)
+            assert np.allclose(t, ot, rtol=0, atol=1e-6), (lev, nb)
+    c = np.zeros(4, np.float32)
+    t = np.zeros(3, np.float32)
+    assert _status("tq_polar_make_codebook", 128, 8, 2, c.ctypes.data, t.ctypes.data) == 1   # level > log2 d
+    assert _status("tq_polar_make_codebook", 96, 1, 2, c.ctypes.data, t.ctypes.data) == 1    # d not a power of two
+
+
+def test_polar_argument_checks():
+    """tq_polar_* reject what they must before any device work."""
+    buf, a = _host_buf(1 << 16)
+    codes = tq._PolarCodes(a, a)
+    ok = tq._PolarParams(128, 4, 2, 0, 2)
+    enc = lambda pp, x=a, n=4, dt=0, cd=codes: _status("tq_polar_encode", ctypes.byref(pp), x, dt, n, cd, None)
+    assert enc(ok, n=0) == 0                                        # nothing to do
+    assert enc(ok, x=None) == 1                                     # NULL keys
+    assert enc(ok, dt=7) == 1                                       # bad dtype
+    assert enc(ok, x=a + 4) == 3                                    # misaligned
+    assert enc(tq._PolarParams(128, 4, 2, 1, 2)) == 1               # reserved field
+    assert enc(tq._PolarParams(100, 4, 2, 0, 2)) == 1               # d not a power of two
+    assert enc(tq._PolarParams(256, 4, 2, 0, 2)) == 2               # kernels built for d = 128
+    assert enc(tq._PolarParams(128, 3, 2, 0, 2)) == 2               # and 4 / 2 bits
+    ws = ctypes.c_size_t()
+    assert _status("tq_polar_score_workspace_bytes", ctypes.byref(ok), 2, 4, ctypes.byref(ws)) == 0
+    assert ws.value == 2 * 4 * 128 * 4
+    sc = lambda n_kv=1, g=4, seq=8, q=a, w=a, wsb=1 << 16: _status(
+        "tq_polar_score", ctypes.byref(ok), q, n_kv, g, codes, seq, a, w, wsb, None)
+    assert sc(seq=0) == 0 and sc(n_kv=0) == 0                      # nothing to do
+    assert sc(g=0) == 1 and sc(q=None) == 1 and sc(w=None) == 1
+    assert sc(wsb=16) == 5                                          # workspace too small
