@@ -19,7 +19,8 @@ Reported on one JSON line:
   roofline_score  the score kernel on the 32-layer stream (HBM-bound)
   cpu_baseline the CPU oracle (numpy float64) on a bounded sample of the step
 Further sections (each can be switched off): long-context attention (plain
-and through a paged block table), the bit-width sweep, high-dimensional batched search (d = m = 1024, 1M
+and through a paged block table), the PolarQuant variant on the same layer,
+the bit-width sweep, high-dimensional batched search (d = m = 1024, 1M
 vectors, 1024 queries, top-10) and search at database scale (2^26 vectors of
 d = 128, 3.76 GB of codes, 1024 queries, top-10).
 """
@@ -53,6 +54,7 @@ def _parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-highdim", action="store_true")
     ap.add_argument("--no-searchdb", action="store_true")
+    ap.add_argument("--no-polar", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling PMC byte counters)")
@@ -312,6 +314,53 @@ def main():
                                    "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                                    "frac_measured_copy": round(gbps / copy_gbps, 4), "bytes_per_call": nb}
         del kc, vc
+
+    if not args.no_polar:
+        # PolarQuant variant (4 bits at level 1, 2 bits above: 52 B per key) on the
+        # same Llama-shaped layer: encode of 8 x 32768 bf16 keys, and the score of
+        # 32 query heads streaming 32 such layers' codes from HBM
+        pp = tq.PolarParams(D, 4, 2, 2)
+        px = synth.llama_keys(heads=N_KV, seq=SEQ, seed=1, device=dev)
+        pc = tq.alloc_polar_codes(N_KV * SEQ, dev)
+        nL = LAYERS * N_KV
+        pbig = tq.alloc_polar_codes(nL * SEQ, dev)
+        for layer in range(LAYERS):
+            xl = synth.llama_keys(heads=N_KV, seq=SEQ, seed=100 + layer, device=dev)
+            sl = slice(layer * N_KV * SEQ, (layer + 1) * N_KV * SEQ)
+            tq.polar_encode(pp, xl, {k: v[sl] for k, v in pbig.items()})
+        del xl
+        pq_ = synth.queries(nL * G, seed=6, device=dev)
+        plg = torch.empty((nL * G, SEQ), device=dev)
+        pws = torch.empty(tq.polar_score_workspace_bytes(pp, nL, G), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            tq.polar_encode(pp, px, pc)
+            tq.polar_score(pp, pq_, pbig, nL, G, SEQ, plg, pws)
+        torch.cuda.synchronize()
+        reps = max(5, args.steps // 2)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        for _ in range(reps):
+            tq.polar_encode(pp, px, pc)
+        e[1].record(stream)
+        for _ in range(reps):
+            tq.polar_score(pp, pq_, pbig, nL, G, SEQ, plg, pws)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        enc_ms = e[0].elapsed_time(e[1]) / reps
+        sc_ms = e[1].elapsed_time(e[2]) / reps
+        n1 = N_KV * SEQ
+        enc_exec = 2 * (2 * D * D) * n1                      # Pi x in 2 bf16 passes (hi, lo of Pi)
+        sbytes = 52 * nL * SEQ + 4 * nL * G * SEQ
+        out["polar"] = {
+            "workload": f"PolarQuant d {D} (level 1: 4 bits, levels 2..7: 2 bits; 52 B per key); encode "
+                        f"{N_KV} x {SEQ} bf16 Llama-shaped keys; score {nL * G} query heads over "
+                        f"{LAYERS} layers x {N_KV} KV heads x {SEQ} positions",
+            "encode_us": round(enc_ms * 1e3, 2), "encode_mvectors_per_s": round(n1 / (enc_ms * 1e-3) / 1e6, 1),
+            "encode_frac_bf16_peak_executed": round(enc_exec / (enc_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "score_ms": round(sc_ms, 4), "score_GBps": round(sbytes / (sc_ms * 1e-3) / 1e9, 1),
+            "score_frac_hbm_peak": round(sbytes / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        }
+        del px, pc, pbig, plg, pws
 
     if not args.no_sweep:
         # bit-width sweep: 65536 unit-direction x log-normal-norm float32 vectors, 1024 queries

@@ -2590,7 +2590,8 @@ __device__ __forceinline__ uint32_t polar_sector(float a, float b, const PolarTa
   return zero ? 0u : 4u * q + sub;
 }
 
-// code of the angle between radii with squares sl (left) and sr (right)
+// code of the angle between radii with squares sl (left) and sr (right); C, S
+// are cos^2 and sin^2 of the level's boundaries
 __device__ __forceinline__ uint32_t polar_level_code(float sl, float sr, const float *C, const float *S) {
   uint32_t c = 0;
 #pragma unroll
@@ -2690,31 +2691,18 @@ __global__ __launch_bounds__(kPolWaves * 64) void polar_encode128_kernel(
   }
 }
 
-// Rotated queries qt = Pi q (float64 sums), one workgroup of 128 threads per query.
-__global__ __launch_bounds__(128) void polar_qrot_kernel(const float *__restrict__ q,
-                                                         const double *__restrict__ pi64,
-                                                         float *__restrict__ qt) {
-  __shared__ double qs[128];
-  const int64_t j = blockIdx.x;
-  const int r = threadIdx.x;
-  qs[r] = (double)q[j * 128 + r];
-  __syncthreads();
-  double acc = 0.0;
-  for (int k = 0; k < 128; ++k) acc = fma(pi64[r * 128 + k], qs[k], acc);
-  qt[j * 128 + r] = (float)acc;
-}
-
 // Score: one key per thread and the (up to) 4 query heads of a group.  The
-// tree is folded bottom-up: a level-1 node gives c q_2j + s q_2j+1 per query,
+// tree is folded bottom-up: a level-1 node gives c q_2j + s q_2j+1 per query
+// (looked up from a table of all 16 codes of every node, built per workgroup),
 // a node above gives c f_left + s f_right, and the root times the radius is
-// the logit <Pi q, y^>.  Rotated queries and the cos / sin tables sit in LDS
-// (the query reads are broadcasts, the table reads 16 distinct float2 at most).
+// the logit <Pi q, y^>.  The rotated queries come from qproj_kernel (float64
+// sums).
 constexpr int kPolScoreThreads = 256;
 __global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
-    const float *__restrict__ qt, const uint32_t *__restrict__ pq, const float *__restrict__ radius,
+    const double *__restrict__ qt, const uint32_t *__restrict__ pq, const float *__restrict__ radius,
     int64_t seq, int64_t g, int ngroups, const PolarTables *__restrict__ T, float *__restrict__ logits) {
   __shared__ float4 qs[128];
-  __shared__ float2 t1[16];
+  __shared__ float4 L1[64][16];  // level-1 node j, code k: c_k q_2j + s_k q_2j+1 for the 4 queries
   __shared__ float2 tl[6][4];
   const int hg = blockIdx.y, h = hg / ngroups, grp = hg % ngroups;
   const int tid = threadIdx.x;
@@ -2723,12 +2711,21 @@ __global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t qh = (int64_t)grp * 4 + j;
-      v[j] = qh < g ? qt[((int64_t)h * g + qh) * 128 + tid] : 0.f;
+      v[j] = qh < g ? (float)qt[((int64_t)h * g + qh) * 128 + tid] : 0.f;
     }
     qs[tid] = make_float4(v[0], v[1], v[2], v[3]);
   }
-  if (tid < 16) t1[tid] = make_float2(T->c1[tid], T->s1[tid]);
   if (tid < 24) tl[tid / 4][tid % 4] = make_float2(T->cl[tid / 4][tid % 4], T->sl[tid / 4][tid % 4]);
+  __syncthreads();
+  // the level-1 products of every (node, code): 64 x 16 entries, a gather per
+  // node below (16 entries of 16 bytes cover the 64 banks once: no conflicts)
+  for (int e = tid; e < 64 * 16; e += kPolScoreThreads) {
+    const int j = e >> 4, k = e & 15;
+    const float c = T->c1[k], sn = T->s1[k];
+    const float4 qa = qs[2 * j], qb = qs[2 * j + 1];
+    L1[j][k] = make_float4(fmaf(c, qa.x, sn * qb.x), fmaf(c, qa.y, sn * qb.y), fmaf(c, qa.z, sn * qb.z),
+                           fmaf(c, qa.w, sn * qb.w));
+  }
   __syncthreads();
   const int64_t pos = (int64_t)blockIdx.x * kPolScoreThreads + tid;
   if (pos >= seq) return;  // no barrier follows
@@ -2759,13 +2756,11 @@ __global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const uint32_t code = (w1 >> (4 * (2 * (t & 3) + i))) & 15u;
-            const float2 cs = t1[code];
-            const int c0 = 16 * t + 4 * gl + 2 * i;
-            const float4 qa = qs[c0], qb = qs[c0 + 1];
-            f1[i][0] = fmaf(cs.x, qa.x, cs.y * qb.x);
-            f1[i][1] = fmaf(cs.x, qa.y, cs.y * qb.y);
-            f1[i][2] = fmaf(cs.x, qa.z, cs.y * qb.z);
-            f1[i][3] = fmaf(cs.x, qa.w, cs.y * qb.w);
+            const float4 l1 = L1[8 * t + 2 * gl + i][code];
+            f1[i][0] = l1.x;
+            f1[i][1] = l1.y;
+            f1[i][2] = l1.z;
+            f1[i][3] = l1.w;
           }
           const float2 c2 = tl[0][(wd[8 + gl] >> (2 * t)) & 3u];
 #pragma unroll
@@ -2823,7 +2818,7 @@ tq_status launch_polar_encode(const Derived &D, const PolarTables *T, const void
   return TQ_OK;
 }
 
-size_t polar_score_workspace_bytes(int64_t nq) { return (size_t)nq * 128 * sizeof(float); }
+size_t polar_score_workspace_bytes(int64_t nq) { return (size_t)nq * 128 * sizeof(double); }
 
 tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float *q, int64_t n_kv,
                              int64_t g, tq_polar_codes c, int64_t seq, float *logits, void *ws,
@@ -2835,8 +2830,13 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
     set_error("tq_polar_score: problem too large for one launch");
     return TQ_ERR_UNSUPPORTED;
   }
-  float *qt = (float *)ws;
-  polar_qrot_kernel<<<(unsigned)(n_kv * g), 128, 0, s>>>(q, D.pi64, qt);
+  if ((n_kv * g + kQJQ - 1) / kQJQ > 65535) {
+    set_error("tq_polar_score: too many queries for one launch");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  double *qt = (double *)ws;
+  qproj_kernel<<<dim3(128 / kQJR, (unsigned)((n_kv * g + kQJQ - 1) / kQJQ)), dim3(256), 0, s>>>(
+      q, n_kv * g, 128, 128, D.pi32, nullptr, qt);
   polar_score128_kernel<<<dim3((unsigned)nblk, (unsigned)nhg), kPolScoreThreads, 0, s>>>(
       qt, c.pq, c.radius, seq, g, ngroups, T, logits);
   TQ_LAUNCH_CHECK();

@@ -218,7 +218,7 @@ def test_polar_argument_checks():
     assert enc(tq._PolarParams(128, 3, 2, 0, 2)) == 2               # and 4 / 2 bits
     ws = ctypes.c_size_t()
     assert _status("tq_polar_score_workspace_bytes", ctypes.byref(ok), 2, 4, ctypes.byref(ws)) == 0
-    assert ws.value == 2 * 4 * 128 * 4
+    assert ws.value == 2 * 4 * 128 * 8
     sc = lambda n_kv=1, g=4, seq=8, q=a, w=a, wsb=1 << 16: _status(
         "tq_polar_score", ctypes.byref(ok), q, n_kv, g, codes, seq, a, w, wsb, None)
     assert sc(seq=0) == 0 and sc(n_kv=0) == 0                      # nothing to do
