@@ -4,8 +4,10 @@ One step = the whole hot path on the Llama-3.1-8B-shaped decode layer:
   tq_encode of all 8 KV heads x 32768 positions x d 128 bf16 keys (b = 3:
   2-bit Lloyd-Max + 1-bit QJL, m = 128), then tq_score of one decode step
   (32 query heads, grouped 4:1) from the packed codes.
-Inputs are resident in HBM before the timed region; the timed region is
-bracketed by torch.cuda.synchronize().
+Inputs are resident in HBM before the timed region; the K timed steps are
+captured once as a HIP graph (replays checked equal to the eager step) and
+one replay is timed, bracketed by torch.cuda.synchronize(); the same K steps
+issued eagerly are reported beside it (eager_ms_per_step).
 
 Reported on one JSON line:
   value        keys encoded + scored per second through the whole step (Mvectors/s)
@@ -143,34 +145,59 @@ def main():
     code_bytes = sum(tq.codes_bytes(p, 1))
     stream = torch.cuda.current_stream()
 
-    # Events bracket the encode launch only (each event record is a marker in
-    # the queue and costs a few microseconds of GPU time); the score share of
-    # a step is the step time minus the encode time.
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         tq.encode(p, x, codes)
-        if ev is not None:
-            ev[1].record(stream)
         tq.score(p, q, codes, N_KV, G, SEQ, logits, ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ref_logits = logits.clone()
+    ref_codes = {k: v.clone() for k, v in codes.items() if v is not None}
+    # The K timed steps are captured once as a HIP graph (one launch for the
+    # whole sequence of kernels, so the host's per-call marshalling does not
+    # pace the GPU), and so are K encodes alone for the encode share.
+    graph, enc_graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step()
+    with torch.cuda.graph(enc_graph):
+        for _ in range(args.steps):
+            tq.encode(p, x, codes)
+    # every replay reproduces the eager step exactly (eager work in between)
+    for _ in range(2):
+        logits.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(logits, ref_logits) and all(torch.equal(codes[k], v) for k, v in ref_codes.items())
+        if not same:
+            raise RuntimeError("graph replay differs from the eager step")
+        step()
+        torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for k in range(args.steps):
-        step(evs[k])
+    graph.replay()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    enc_graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    enc_ms = e0.elapsed_time(e1) / args.steps
     sc_ms = ms_step - enc_ms
+    # the same K steps issued eagerly, one library call at a time (reference)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
     enc_flops = (2 * D * D + 2 * D * M) * n
     enc_tflops = enc_flops / (enc_ms * 1e-3) / 1e12
     score_bytes_layer = code_bytes * n + 4 * N_KV * G * SEQ
@@ -189,7 +216,10 @@ def main():
         "encode_ms": round(enc_ms, 5),
         "encode_mvectors_per_s": round(n / (enc_ms * 1e-3) / 1e6, 2),
         "score_ms_one_layer": round(sc_ms, 5),
-        "step_timing": "HIP events around every encode launch of the timed steps; score = step - encode",
+        "step_timing": "K steps captured as one HIP graph, timed with HIP events around one replay (replays "
+                       "checked equal to the eager step); encode share from a graph of K encodes; score = "
+                       "step - encode",
+        "eager_ms_per_step": round(eager_ms, 5),
         "score_gbps_one_layer_cache_resident": round(score_bytes_layer / (sc_ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "mfma", "achieved": round(enc_tflops, 2), "peak": BF16_PEAK_TFLOPS,
