@@ -58,10 +58,11 @@ def _fill_store(store, p, slots, codes):
         store[k][sl] = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def test_encode_slots_matches_oracle():
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_encode_slots_matches_oracle(dtype):
     cap = 4096
     n = 1500
-    x = synth.llama_keys(heads=1, seq=n, seed=11, dtype=torch.float32).to(DEV)
+    x = synth.llama_keys(heads=1, seq=n, seed=11, dtype=dtype).to(DEV)
     rng = np.random.default_rng(3)
     slots = rng.permutation(cap)[:n].astype(np.int64)
     slots[5], slots[77] = cap, -1  # outside the store: skipped
@@ -76,14 +77,18 @@ def test_encode_slots_matches_oracle():
     rep = {}
     check_encode(x.double().cpu().numpy()[rows], {k: v[slots[rows]] for k, v in got.items()},
                  _oparams(KP), rep)
-    _report("encode_slots 1500 vectors into 4096 slots", rep)
+    _report(f"encode_slots {dtype} 1500 vectors into 4096 slots", rep)
     untouched = np.setdiff1d(np.arange(cap), slots[ok])
     assert np.all(got["knorm"][untouched] == -1.0)
     assert np.all(got["sgn"][untouched] == np.uint32(0xFFFFFFFF))
 
 
-@pytest.mark.parametrize("lens,n_kv,g", [((1, 700, 1537), 2, 4), ((512, 513), 1, 5), ((2048,), 2, 1)])
-def test_attend_paged_matches_oracle(lens, n_kv, g):
+@pytest.mark.parametrize("lens,n_kv,g,kb,vb", [((1, 700, 1537), 2, 4, 3, 3), ((512, 513), 1, 5, 3, 3),
+                                                ((2048,), 2, 1, 3, 3), ((300, 1100), 2, 4, 2, 4),
+                                                ((64, 1030), 1, 8, 5, 1)])
+def test_attend_paged_matches_oracle(lens, n_kv, g, kb, vb):
+    KP = tq.Params(128, kb, 128, tq.MODE_PROD, 2, 3)
+    VP = tq.Params(128, vb, 128, tq.MODE_MSE, 4, 0)
     batch = len(lens)
     bt, num_pages = _page_plan(lens, n_kv, spare=3, seed=sum(lens))
     okp, ovp = _oparams(KP), _oparams(VP)
@@ -113,7 +118,8 @@ def test_attend_paged_matches_oracle(lens, n_kv, g):
     got = out.cpu().numpy()
     for b in range(batch):
         worst = check_attend(got[b], refs[b])
-        print(f"[parity] attend_paged lens={lens} n_kv={n_kv} g={g} b={b}: worst/tol={worst:.4f}", flush=True)
+        print(f"[parity] attend_paged lens={lens} n_kv={n_kv} g={g} kb={kb} vb={vb} b={b}: worst/tol={worst:.4f}",
+              flush=True)
 
 
 def test_append_then_attend():
