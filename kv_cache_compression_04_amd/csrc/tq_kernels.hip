@@ -2045,6 +2045,7 @@ tq_status launch_score(const Derived &D, const float *q, int64_t n_kv, int64_t g
 constexpr int kAttKPW = 512;   // positions per wave
 constexpr int kAttWaves = 4;
 constexpr int kAttU = 8;       // key tiles whose loads are issued together
+static_assert(kAttWaves == 4, "the in-workgroup merge gives wave j query j of a group of 4");
 
 struct AttPartial {  // per (group, split, query): m, l, o_rot[128]
   float m, l, o[128];
@@ -2099,18 +2100,28 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   // The wave's positions p0 .. p0 + npos - 1 are the vectors vb + 0 .. npos - 1
   // of the code store: one contiguous run per (batch, KV head) in the plain
   // layout, one page of the block table in the paged one.
-  int64_t vb;
+  // A wave past the end of its sequence computes nothing but still takes part
+  // in the workgroup's merge of its waves' partial results below.
+  int64_t vb = 0;
+  bool active;
   if (pg.block_table) {
     const int64_t b = hb / pg.n_kv, h = hb % pg.n_kv;
     seq = paged_seq_len(pg, b);
-    if (p0 >= seq) return;  // past this sequence's end; no workgroup barrier follows
-    int64_t page = pg.block_table[b * pg.max_pages + split];
-    page = page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);  // never outside the store
-    vb = (page * pg.n_kv + h) * kAttKPW;
+    active = p0 < seq;
+    if (active) {
+      int64_t page = pg.block_table[b * pg.max_pages + split];
+      page = page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);  // never outside the store
+      vb = (page * pg.n_kv + h) * kAttKPW;
+    }
   } else {
-    if (split >= nsplit) return;  // the whole wave leaves; no workgroup barrier follows
+    active = split < nsplit;
     vb = (int64_t)hb * seq + p0;
   }
+  // this lane's 8 output coordinates of o_rot (query kg), and m, l of the query
+  float ov[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float m_out = -INFINITY, l_out = 0.f;
+  const int w = c16 >> 2, beta = c16 & 3;
+  if (active) {
   const int npos = (int)(seq - p0 < kAttKPW ? seq - p0 : kAttKPW);
   const uint32_t last = (uint32_t)(npos - 1);  // local index of the last position
 
@@ -2203,7 +2214,6 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   // block: byte e of dword gi of D_beta is byte beta of index word w of
   // position 4 gi + e.  Slice s (bit s of every byte; a set bit weighs
   // 2^(s & 3)) is coordinate 32 beta + 16 (s / 4) + 4 w + s % 4.
-  const int w = c16 >> 2, beta = c16 & 3;
   const uint32_t sel_lo = (uint32_t)(beta | (beta + 4) << 8 | 0x0C0C0000u);
   i32x4 acc[NACC][8];
 #pragma unroll
@@ -2333,9 +2343,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   for (int off = 8; off >= 1; off >>= 1) qsum += __shfl_xor(qsum, off);
   // ---------------- epilogue: lane (c16, kg) holds query kg, limbs t = 0..3
   // sum_n w_n c[idx_n] = sum_S a_S (2 sum_n w_n beta_S,n - sum_n w_n)
-  const int64_t qh = (int64_t)(hg % ngroups) * 4 + kg;
-  AttPartial *dst = part + ((int64_t)hg * nsplit + split) * 4 + kg;
-  if (qh < g) {
+  {
     double asum = 0.0;
 #pragma unroll
     for (int sp = 0; sp < NPV; ++sp) asum += vcb.coef[sp];
@@ -2349,14 +2357,58 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
                           2097152.0 * (double)r[3];
         v += (SHARED ? 2.0 * vcb.coef[a] : 1.0) * ra;
       }
-      const int c = 32 * beta + 16 * (sl >> 2) + 4 * w + (sl & 3);
       // shared: (v 2^-(s&3) - a qsum) 2^-E; per part: v 2^-(E + s&3) - qsum
-      dst->o[c] = SHARED ? (float)ldexp(ldexp(v, -(sl & 3)) - asum * qsum, -E)
-                         : (float)(ldexp(v, -E - (sl & 3)) - qsum);
+      ov[sl] = SHARED ? (float)ldexp(ldexp(v, -(sl & 3)) - asum * qsum, -E)
+                      : (float)(ldexp(v, -E - (sl & 3)) - qsum);
     }
+    m_out = m;
+    l_out = lsum;
+  }
+  }  // active
+
+  // ---------------- merge of the workgroup's waves (consecutive splits):
+  // the waves' (m, l, o_rot) go through LDS (each wave's logit buffer, free
+  // now) and wave j combines query j:  M = max m_w, L = sum l_w e^(m_w - M),
+  // O = sum o_w e^(m_w - M).  Inactive waves carry m = -inf, l = 0, o = 0.
+  {
+    float *mine = &lg[wave][kg][0];
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) mine[32 * beta + 16 * (sl >> 2) + 4 * w + (sl & 3)] = ov[sl];
     if (c16 == 0) {
-      dst->m = m;
-      dst->l = lsum;
+      mine[128] = m_out;
+      mine[129] = l_out;
+    }
+  }
+  __syncthreads();
+  {
+    const int jq = wave;  // query of the group this wave combines
+    const int64_t qh = (int64_t)(hg % ngroups) * 4 + jq;
+    float mw[kAttWaves], M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kAttWaves; ++v) {
+      mw[v] = lg[v][jq][128];
+      M = fmaxf(M, mw[v]);
+    }
+    float sc[kAttWaves], L = 0.f;
+#pragma unroll
+    for (int v = 0; v < kAttWaves; ++v) {
+      sc[v] = M == -INFINITY ? 0.f : __expf(mw[v] - M);
+      L = fmaf(lg[v][jq][129], sc[v], L);
+    }
+    float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < kAttWaves; ++v) {
+      o0 = fmaf(lg[v][jq][lane], sc[v], o0);
+      o1 = fmaf(lg[v][jq][64 + lane], sc[v], o1);
+    }
+    if (qh < g) {
+      AttPartial *dst = part + ((int64_t)hg * gridDim.x + blockIdx.x) * 4 + jq;
+      dst->o[lane] = o0;
+      dst->o[64 + lane] = o1;
+      if (lane == 0) {
+        dst->m = M;
+        dst->l = L;
+      }
     }
   }
 }
@@ -2377,9 +2429,11 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(
   const int jq = (int)(j % 4);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const AttPartial *p = part + (int64_t)hg * nsplit_max * 4 + jq;
-  // splits written for this sequence (all of them in the plain layout)
+  // partials written for this sequence, one per workgroup of kAttWaves
+  // splits (all of them in the plain layout)
   const int nsplit = pg.block_table
-                         ? (int)((paged_seq_len(pg, hb / pg.n_kv) + kAttKPW - 1) / kAttKPW)
+                         ? (int)((paged_seq_len(pg, hb / pg.n_kv) + kAttKPW * kAttWaves - 1) /
+                                 (kAttKPW * kAttWaves))
                          : nsplit_max;
   float M = -INFINITY;
   for (int sidx = tid; sidx < nsplit; sidx += kMergeThreads) M = fmaxf(M, p[(int64_t)sidx * 4].m);
@@ -2465,7 +2519,8 @@ static void launch_attend_t(const Derived &K, const Derived &V, const float *q, 
                              dim3(kAttWaves * 64), 0, s>>>(aops, qc, k.idx, k.sgn, k.knorm, k.rnorm,
                                                            v.idx, v.knorm, seq, g, ngroups, nsplit,
                                                            scale, K.cb, V.cb, part, pg);
-  attend_merge_kernel<<<dim3((unsigned)(batch * n_kv * g)), dim3(kMergeThreads), 0, s>>>(part, nsplit, ngroups, g,
+  const int nblk = (nsplit + kAttWaves - 1) / kAttWaves;  // partials per query head
+  attend_merge_kernel<<<dim3((unsigned)(batch * n_kv * g)), dim3(kMergeThreads), 0, s>>>(part, nblk, ngroups, g,
                                                                                V.pi32, out, pg);
 }
 
