@@ -2413,21 +2413,29 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   }
 }
 
-// Combine the splits of one query head and rotate back: out = Pi_V^T o_rot / L.
+// Combine the partials of one query head and rotate back: out = Pi_V^T o_rot / L.
+// Thread (c, grp) runs an online softmax over partials grp, grp + 8, ... for
+// coordinate c (one pass; the loads do not wait on a reduction), the 8 groups
+// are combined through LDS, and the rows of Pi_V this thread needs are loaded
+// before any of it.
 constexpr int kMergeThreads = 1024;
-constexpr int kMergeGroups = kMergeThreads / 128;  // split groups per coordinate
+constexpr int kMergeGroups = kMergeThreads / 128;  // partial groups per coordinate
 __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(
     const AttPartial *__restrict__ part, int nsplit_max, int ngroups, int64_t g,
     const float *__restrict__ piv, float *__restrict__ out, PagedKV pg) {
-  __shared__ float wsp[1024];      // exp(m_s - M) per split (nsplit <= 1024 here; larger loops)
-  __shared__ float red[kMergeThreads / 64][2];
+  constexpr int R = 128 / kMergeGroups;  // rows of Pi_V per thread in the rotation
+  __shared__ float gm[kMergeGroups], gl[kMergeGroups];
   __shared__ float orot[kMergeGroups][128];
   __shared__ float osum[128];
   const int hq = blockIdx.x;        // (batch * n_kv + head) * g + j
   const int64_t hb = hq / g, j = hq % g;
   const int64_t hg = hb * ngroups + j / 4;
   const int jq = (int)(j % 4);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
+  const int c = tid & 127, grp = tid >> 7;
+  float pv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) pv[r] = piv[(grp * R + r) * 128 + c];
   const AttPartial *p = part + (int64_t)hg * nsplit_max * 4 + jq;
   // partials written for this sequence, one per workgroup of kAttWaves
   // splits (all of them in the plain layout)
@@ -2435,56 +2443,48 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(
                          ? (int)((paged_seq_len(pg, hb / pg.n_kv) + kAttKPW * kAttWaves - 1) /
                                  (kAttKPW * kAttWaves))
                          : nsplit_max;
-  float M = -INFINITY;
-  for (int sidx = tid; sidx < nsplit; sidx += kMergeThreads) M = fmaxf(M, p[(int64_t)sidx * 4].m);
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red[wv][0] = M;
-  __syncthreads();
-  M = red[0][0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w][0]);
-  float L = 0.f;
-  for (int sidx = tid; sidx < nsplit; sidx += kMergeThreads) {
-    const float e = __expf(p[(int64_t)sidx * 4].m - M);
-    if (sidx < 1024) wsp[sidx] = e;
-    L += p[(int64_t)sidx * 4].l * e;
-  }
-  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-  __syncthreads();
-  if (lane == 0) red[wv][1] = L;
-  __syncthreads();
-  L = 0.f;
-  for (int w = 0; w < kMergeThreads / 64; ++w) L += red[w][1];
-  // o_rot[c]: kMergeGroups interleaved groups of the splits per coordinate
-  const int c = tid & 127, grp = tid >> 7;
-  float acc = 0.f;
-#pragma unroll 16
+  float M = -INFINITY, L = 0.f, O = 0.f;
+#pragma unroll 4
   for (int sidx = grp; sidx < nsplit; sidx += kMergeGroups) {
-    const float e = sidx < 1024 ? wsp[sidx] : __expf(p[(int64_t)sidx * 4].m - M);
-    acc = fmaf(e, p[(int64_t)sidx * 4].o[c], acc);
+    const AttPartial *ps = p + (int64_t)sidx * 4;
+    const float ms = ps->m, ls = ps->l, os = ps->o[c];
+    const float mn = fmaxf(M, ms);
+    const float a = M == -INFINITY ? 0.f : __expf(M - mn), b = __expf(ms - mn);
+    L = fmaf(L, a, ls * b);
+    O = fmaf(O, a, os * b);
+    M = mn;
   }
-  orot[grp][c] = acc;
+  orot[grp][c] = O;
+  if (c == 0) {
+    gm[grp] = M;
+    gl[grp] = L;
+  }
+  __syncthreads();
+  if (tid < 128) {
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) Mx = fmaxf(Mx, gm[k]);
+    float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) {
+      const float e = gm[k] == -INFINITY ? 0.f : __expf(gm[k] - Mx);
+      Lt = fmaf(gl[k], e, Lt);
+      Ot = fmaf(orot[k][tid], e, Ot);
+    }
+    osum[tid] = Ot / Lt;
+  }
+  __syncthreads();
+  // out = Pi_V^T o_rot: thread (c, grp) sums rows grp R .. grp R + R - 1
+  float o = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) o = fmaf(pv[r], osum[grp * R + r], o);
+  orot[grp][c] = o;  // every read of orot above is behind the barrier
   __syncthreads();
   if (tid < 128) {
     float t = 0.f;
 #pragma unroll
     for (int k = 0; k < kMergeGroups; ++k) t += orot[k][tid];
-    osum[tid] = t / L;
-  }
-  __syncthreads();
-  // out = Pi_V^T o_rot: thread (c, grp) sums 128 / kMergeGroups rows of Pi_V
-  {
-    constexpr int R = 128 / kMergeGroups;
-    float o = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) o = fmaf(piv[(grp * R + r) * 128 + c], osum[grp * R + r], o);
-    orot[grp][c] = o;  // every read of orot above is behind the barrier
-  }
-  __syncthreads();
-  if (tid < 128) {
-    float o = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMergeGroups; ++k) o += orot[k][tid];
-    out[(int64_t)hq * 128 + tid] = o;
+    out[(int64_t)hq * 128 + tid] = t;
   }
 }
 
