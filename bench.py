@@ -280,7 +280,10 @@ def main():
                             "bytes_per_launch": bytes_}
         out["roofline_score"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                                  "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                                 "traffic": profiled_traffic(f"tq::score128_kernel<{args.b - 1}, true>"),
+                                 # the launch of this workload: one 64-thread wave per 256 keys of each
+                                 # (KV head, group of 4 query heads)
+                                 "traffic": profiled_traffic(f"tq::score128_kernel<{args.b - 1}, true>",
+                                                             nL * ((G + 3) // 4) * ((SEQ + 255) // 256) * 64),
                                  "kernel": "score128_kernel (+ qprep128_kernel)",
                                  "algorithmic_per_launch": f"{bytes_} B ({code_bytes} B of codes per key + 4 B per logit)"}
         del big, lb
