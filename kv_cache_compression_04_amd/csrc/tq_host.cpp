@@ -569,8 +569,12 @@ static const PolarTables &polar_tables() {
       T.dc1[j] = (float)std::cos(b[j]);
       T.ds1[j] = (float)std::sin(b[j]);
     }
+    T.tau1[0] = (float)std::tan(b[0]);
+    T.tau1[1] = (float)std::tan(b[2]);
     for (int lev = 2; lev <= 7; ++lev) {
       polar_codebook(lev, 2, c, b);
+      const double tb = std::tan(b[0]);
+      T.tau[lev - 2] = (float)(tb * tb);
       for (int j = 0; j < 4; ++j) {
         T.cl[lev - 2][j] = (float)std::cos(c[j]);
         T.sl[lev - 2][j] = (float)std::sin(c[j]);

@@ -110,6 +110,12 @@ struct PolarTables {
   float cl[6][4], sl[6][4];  // cos, sin of the level-(2 + i) centroid angles
   float dc1[3], ds1[3];      // cos, sin of the level-1 boundaries pi/8, pi/4, 3 pi/8 within a quadrant
   float dC[6][3], dS[6][3];  // cos^2, sin^2 of the level-(2 + i) boundaries
+  // The encoder's decision constants: tan(pi/8), tan(3 pi/8) for level 1, and
+  // tan^2 of the lowest boundary of each level >= 2 (the codebooks are
+  // symmetric about pi/4, so the highest boundary is its complement and the
+  // middle one is pi/4 itself).
+  float tau1[2];
+  float tau[6];
 };
 tq_status launch_polar_encode(const Derived &D, const PolarTables *T, const void *x, int dtype,
                               int64_t n, tq_polar_codes codes, hipStream_t stream);

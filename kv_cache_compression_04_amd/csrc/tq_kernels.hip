@@ -2627,30 +2627,28 @@ tq_status launch_decode(const Derived &D, tq_codes codes, int64_t n, float *out,
 // the lane; level 3 pairs lane groups g, g ^ 1 and level 4 g, g ^ 2 (one
 // shuffle each); levels 5..7 pair the tiles nt inside the lane.  Every level
 // >= 2 decision is taken on squared radii (theta >= t  <=>
-// r_R^2 cos^2 t >= r_L^2 sin^2 t), so no square root or arctangent is needed;
+// r_R^2 >= tan^2(t) r_L^2), so no square root or arctangent is needed;
 // level 1 takes the quadrant from the signs and the sector within it from
-// two-sided products with the boundary's cosine and sine.
+// the turned pair against tan of the sub-sector boundaries.
 constexpr int kPolWaves = 16;
 
-__device__ __forceinline__ uint32_t polar_sector(float a, float b, const PolarTables *__restrict__ T) {
+__device__ __forceinline__ uint32_t polar_sector(float a, float b, float t8, float t38) {
   // quadrant q: psi in [q pi/2, (q + 1) pi/2); (a', b') = (a, b) turned back by q pi/2
   const bool q1 = a <= 0.f && b > 0.f, q2 = a < 0.f && b <= 0.f, q3 = a >= 0.f && b < 0.f;
   const float ap = q1 ? b : (q2 ? -a : (q3 ? -b : a));
   const float bp = q1 ? -a : (q2 ? -b : (q3 ? a : b));
   const uint32_t q = q1 ? 1u : (q2 ? 2u : (q3 ? 3u : 0u));
-  uint32_t sub = 0;
-#pragma unroll
-  for (int j = 0; j < 3; ++j) sub += (bp * T->dc1[j] >= ap * T->ds1[j]) ? 1u : 0u;
+  // sub-sector: angle >= pi/8, pi/4, 3 pi/8  <=>  b' >= a' tan(boundary)
+  const uint32_t sub = (bp >= ap * t8 ? 1u : 0u) + (bp >= ap ? 1u : 0u) + (bp >= ap * t38 ? 1u : 0u);
   const bool zero = a == 0.f && b == 0.f;  // the zero pair has angle 0
   return zero ? 0u : 4u * q + sub;
 }
 
-// code of the angle between radii with squares sl (left) and sr (right); C, S
-// are cos^2 and sin^2 of the level's boundaries
-__device__ __forceinline__ uint32_t polar_level_code(float sl, float sr, const float *C, const float *S) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int j = 0; j < 3; ++j) c += (sr * C[j] >= sl * S[j]) ? 1u : 0u;
+// Code of the angle between radii with squares sl (left) and sr (right):
+// theta >= t  <=>  sr >= tan^2(t) sl.  The level's boundaries are t1, pi/4
+// and pi/2 - t1 (tau = tan^2 t1; tan^2(pi/2 - t1) = 1 / tau).
+__device__ __forceinline__ uint32_t polar_level_code(float sl, float sr, float tau) {
+  const uint32_t c = (sr >= tau * sl ? 1u : 0u) + (sr >= sl ? 1u : 0u) + (tau * sr >= sl ? 1u : 0u);
   return sl + sr > 0.f ? c : 0u;
 }
 
@@ -2670,6 +2668,10 @@ __global__ __launch_bounds__(kPolWaves * 64) void polar_encode128_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int vcol = lane & 15, g = lane >> 4;
   const int64_t nbatch = (n + 15) / 16;
+  const float t8 = T->tau1[0], t38 = T->tau1[1];
+  float tau[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) tau[i] = T->tau[i];
   for (int64_t batch = (int64_t)blockIdx.x * kPolWaves + wave; batch < nbatch;
        batch += (int64_t)gridDim.x * kPolWaves) {
     const int64_t row = batch * 16 + vcol;
@@ -2698,10 +2700,10 @@ __global__ __launch_bounds__(kPolWaves * 64) void polar_encode128_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const float a = acc[2 * i], b = acc[2 * i + 1];
-        w1[nt >> 2] |= polar_sector(a, b, T) << (4 * (2 * (nt & 3) + i));
+        w1[nt >> 2] |= polar_sector(a, b, t8, t38) << (4 * (2 * (nt & 3) + i));
         sp[i] = fmaf(b, b, a * a);
       }
-      w8 |= polar_level_code(sp[0], sp[1], T->dC[0], T->dS[0]) << (2 * nt);
+      w8 |= polar_level_code(sp[0], sp[1], tau[0]) << (2 * nt);
       s2[nt] = sp[0] + sp[1];
       // one tile's fragments in flight at a time (no hoisting of all 64 reads)
       __builtin_amdgcn_sched_barrier(0);
@@ -2714,11 +2716,11 @@ __global__ __launch_bounds__(kPolWaves * 64) void polar_encode128_kernel(
     for (int nt = 0; nt < 8; ++nt) {
       const float o = __shfl_xor(s2[nt], 16);
       const float sl = (g & 1) ? o : s2[nt], sr = (g & 1) ? s2[nt] : o;
-      hi3 |= polar_level_code(sl, sr, T->dC[1], T->dS[1]) << (2 * nt);
+      hi3 |= polar_level_code(sl, sr, tau[1]) << (2 * nt);
       const float s3 = sl + sr;
       const float o3 = __shfl_xor(s3, 32);
       const float tl = (g & 2) ? o3 : s3, tr = (g & 2) ? s3 : o3;
-      hi4 |= polar_level_code(tl, tr, T->dC[2], T->dS[2]) << (2 * nt);
+      hi4 |= polar_level_code(tl, tr, tau[2]) << (2 * nt);
       s4[nt] = tl + tr;
     }
     // levels 5..7 inside the lane; kept by g = 3
@@ -2726,15 +2728,15 @@ __global__ __launch_bounds__(kPolWaves * 64) void polar_encode128_kernel(
     float s5[4], s6[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      hi5 |= polar_level_code(s4[2 * j], s4[2 * j + 1], T->dC[3], T->dS[3]) << (2 * j);
+      hi5 |= polar_level_code(s4[2 * j], s4[2 * j + 1], tau[3]) << (2 * j);
       s5[j] = s4[2 * j] + s4[2 * j + 1];
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      hi5 |= polar_level_code(s5[2 * j], s5[2 * j + 1], T->dC[4], T->dS[4]) << (8 + 2 * j);
+      hi5 |= polar_level_code(s5[2 * j], s5[2 * j + 1], tau[4]) << (8 + 2 * j);
       s6[j] = s5[2 * j] + s5[2 * j + 1];
     }
-    hi5 |= polar_level_code(s6[0], s6[1], T->dC[5], T->dS[5]) << 12;
+    hi5 |= polar_level_code(s6[0], s6[1], tau[5]) << 12;
     const uint32_t hi = g == 0 ? hi3 : (g == 1 ? hi4 : (g == 2 ? hi3 : hi5));
     w8 |= hi << 16;
     if (valid) {
