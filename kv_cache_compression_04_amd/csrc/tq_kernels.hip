@@ -98,10 +98,12 @@ __device__ __forceinline__ void load_x_frag(const void *__restrict__ x, int64_t 
         reinterpret_cast<const uint16_t *>(x) + row * 128 + 32 * kt + 8 * g);
     hi = valid ? *p : make_uint4(0, 0, 0, 0);
     const uint32_t w[4] = {hi.x, hi.y, hi.z, hi.w};
+    // squares of both bfloat16 halves in one v_dot2 each (the products are exact in float32)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float a = bf16_to_f32(w[i] & 0xFFFFu), b = bf16_to_f32(w[i] >> 16);
-      sumsq += a * a + b * b;
+      const bf16x2 v = __builtin_bit_cast(bf16x2, w[i]);
+      sumsq = __builtin_amdgcn_fdot2_f32_bf16(v, v, sumsq, false);
     }
   } else {
     const float4 *p = reinterpret_cast<const float4 *>(
