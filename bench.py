@@ -296,12 +296,16 @@ def main():
         vp = tq.Params(D, 3, M, tq.MODE_MSE, 4, 0)
         kc = tq.alloc_codes(kp, ab * akv * aseq, dev)
         vc = tq.alloc_codes(vp, ab * akv * aseq, dev)
+        # encoded in pieces of one layer's size (262 144 vectors), so that every
+        # launch of the layer's encode kernel in a profile has the same work
+        piece = N_KV * SEQ
         for b in range(ab):
-            sl = slice(b * akv * aseq, (b + 1) * akv * aseq)
             kx = synth.llama_keys(heads=akv, seq=aseq, seed=200 + b, device=dev)
-            tq.encode(kp, kx, {k: (v[sl] if v is not None else None) for k, v in kc.items()})
             vx = synth.llama_keys(heads=akv, seq=aseq, seed=300 + b, device=dev)
-            tq.encode(vp, vx, {k: (v[sl] if v is not None else None) for k, v in vc.items()})
+            for o in range(0, akv * aseq, piece):
+                sl = slice(b * akv * aseq + o, b * akv * aseq + o + piece)
+                tq.encode(kp, kx[o:o + piece], {k: (v[sl] if v is not None else None) for k, v in kc.items()})
+                tq.encode(vp, vx[o:o + piece], {k: (v[sl] if v is not None else None) for k, v in vc.items()})
         del kx, vx
         aq = synth.queries(ab * akv * G, seed=7, device=dev).reshape(ab, akv * G, D)
         aout = torch.empty((ab, akv * G, D), device=dev)

@@ -79,9 +79,12 @@ def main():
              "Commands (run from /tmp with TMPDIR=/tmp, R = repository root):", ""]
     lines += [f"    {c}" for c in a.cmd]
     lines += ["", "## Kernel trace (durations in microseconds)", "",
-              "| kernel | grid threads | launches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+              "| kernel | grid threads | launches | avg us | median us | min us | max us |",
+              "|---|---|---|---|---|---|---|"]
     for (k, grid), v in sorted(trace_stats(a.trace).items()):
-        lines.append(f"| {k} | {grid} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
+        med = sorted(v)[len(v) // 2]
+        lines.append(f"| {k} | {grid} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {med / 1e3:.2f} | "
+                     f"{min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
 
     scale_f = scale_w = None
     if a.copy_fetch and a.copy_write:
