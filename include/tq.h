@@ -24,13 +24,15 @@
  *     Device entry points only enqueue kernels on it and return; asynchronous
  *     faults surface at the caller's next synchronisation.
  *   - The library allocates device memory only for its per-(parameters,
- *     device) cache of the rotation, the JL matrix and the codebook, built on
- *     the first call that needs them and freed by tq_release_cache().  The
- *     hot-path calls allocate nothing; scratch comes in through `workspace`.
+ *     device) cache of the rotation, the JL matrix and the codebook (and, for
+ *     the PolarQuant calls, one small table per device), built on the first
+ *     call that needs them and freed by tq_release_cache().  The hot-path
+ *     calls allocate nothing and record no memset (they can be captured in a
+ *     HIP graph); scratch comes in through `workspace`.
  *   - Sizes: d and m must be multiples of 128 in [128, 1024].  tq_encode,
- *     tq_score and tq_search take every such shape; tq_attend and tq_decode
- *     are built for d == 128 (and m == 128 for prod-mode keys) and return
- *     TQ_ERR_UNSUPPORTED otherwise.  b in [1, 5] (prod) or [1, 4] (mse) with
+ *     tq_score and tq_search take every such shape; tq_attend, tq_decode,
+ *     tq_encode_slots and tq_attend_paged are built for d == 128 (and
+ *     m == 128 for prod-mode keys) and return TQ_ERR_UNSUPPORTED otherwise.  b in [1, 5] (prod) or [1, 4] (mse) with
  *     the number of Lloyd-Max bits B <= 4.  n == 0 (or seq == 0) is a no-op.
  *   - Device pointers must be 16-byte aligned (TQ_ERR_ALIGNMENT otherwise).
  *   - Inputs must be finite (precondition, not checked).
