@@ -244,6 +244,62 @@ tq_status tq_search(const tq_params *p, const float *q, int64_t nq, tq_codes cod
 tq_status tq_release_cache(void);
 
 /* ---------------------------------------------------------------------------
+ * Outlier-channel mixed bit widths (2.5 and 3.5 bits per coordinate): the
+ * channels of a head are split into outlier channels that get one bit more
+ * and the ordinary ones ("TurboQuant压缩效果": 3 bits on the outlier
+ * channels, 2 on the rest, over 128 channels).  An average of b_rest + 1/2
+ * bits with b_out = b_rest + 1 puts half of the channels in each group.  The
+ * split is made before the rotation; each group of 64 channels is its own
+ * prod-mode TurboQuant instance of dimension 64 with m = 64 (rotation seed
+ * seed_pi + g, JL seed seed_s + g; g = 0 outliers, 1 the rest), and the logit
+ * is the sum of the two groups' estimators.
+ *
+ * channels: a permutation of 0 .. 127 whose first 64 entries are the
+ * outlier channels (chosen by the caller, e.g. the channels of largest mean
+ * square in a prompt's keys).
+ *
+ * Packed record (d = 128): tq_split_words() uint32 words per vector, group 0
+ * then group 1; a group with B = b - 1 Lloyd-Max bits holds its B index
+ * planes and then its sign plane, two words each (coordinate c of the group,
+ * after its rotation, at word c / 32, bit c % 32); and float32 norms [n][4]:
+ * ||x_0||, ||r_0||, ||x_1||, ||r_1||.  10 words + 16 bytes (56 bytes) at
+ * 2.5 bits, 14 words + 16 bytes (72 bytes) at 3.5 bits.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t d;             /* 128 */
+  int32_t b_out;         /* bits of the outlier channels: b_rest + 1 */
+  int32_t b_rest;        /* 2 (2.5 bits) or 3 (3.5 bits) */
+  int32_t reserved;      /* 0 */
+  uint64_t seed_pi;
+  uint64_t seed_s;
+  int32_t channels[128]; /* host copy of the channel order */
+} tq_split_params;
+
+typedef struct {
+  uint32_t *words;  /* device uint32 [n][tq_split_words()] */
+  float *norms;     /* device float32 [n][4] */
+} tq_split_codes;
+
+/* uint32 words per vector.  Host only.                                      */
+tq_status tq_split_words(const tq_split_params *p, int32_t *words);
+
+/* Encodes n vectors x (row-major [n][128], TQ_F32 or TQ_BF16, device,
+ * 16-byte aligned).  Asynchronous on `stream`; no workspace.               */
+tq_status tq_split_encode(const tq_split_params *p, const void *x, int32_t dtype, int64_t n,
+                          tq_split_codes codes, void *stream);
+
+/* Workspace bytes tq_split_score needs for n_kv * g queries.  Host only.   */
+tq_status tq_split_score_workspace_bytes(const tq_split_params *p, int64_t n_kv, int64_t g,
+                                         size_t *bytes);
+
+/* Logits [n_kv * g][seq] (float32, device) of queries q [n_kv * g][128]
+ * against the codes of n_kv * seq vectors (vector h * seq + pos); query head
+ * j uses KV head j / g.  Asynchronous.                                      */
+tq_status tq_split_score(const tq_split_params *p, const float *q, int64_t n_kv, int64_t g,
+                         tq_split_codes codes, int64_t seq, float *logits, void *workspace,
+                         size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * PolarQuant: the stage-1 variant in which the rotated vector becomes one
  * radius and d - 1 angles by a recursive polar transform, each angle
  * quantised with a fixed codebook of its known law ("TurboQuant 与 AI 效率革命：

@@ -656,6 +656,109 @@ static tq_params polar_rotation_params(const tq_polar_params *p) {
   return t;
 }
 
+// --------------------------------------------------------------------------
+// Mixed bit widths: two 64-channel TurboQuant groups of one head (d = 128).
+// --------------------------------------------------------------------------
+static tq_status check_split(const tq_split_params *p, const char *fn) {
+  if (!p) {
+    set_error("%s: params is NULL", fn);
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (p->reserved != 0 || p->b_out != p->b_rest + 1 || p->b_rest < 1 || p->b_rest > 4) {
+    set_error("%s: need b_out = b_rest + 1, 1 <= b_rest <= 4, reserved = 0", fn);
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (p->d != 128) {
+    set_error("%s: built for d = 128", fn);
+    return TQ_ERR_UNSUPPORTED;
+  }
+  bool seen[128] = {false};
+  for (int i = 0; i < 128; ++i) {
+    const int c = p->channels[i];
+    if (c < 0 || c >= 128 || seen[c]) {
+      set_error("%s: channels must be a permutation of 0 .. 127", fn);
+      return TQ_ERR_INVALID_ARG;
+    }
+    seen[c] = true;
+  }
+  if (p->b_rest != 2 && p->b_rest != 3) {
+    set_error("%s: device kernels are built for 2.5 and 3.5 bits (b_rest = 2 or 3)", fn);
+    return TQ_ERR_UNSUPPORTED;
+  }
+  return TQ_OK;
+}
+
+static tq_status build_split(const tq_split_params *p, int dev, SplitDerived *D) {
+  D->device = dev;
+  const int b[2] = {p->b_out, p->b_rest};
+  std::vector<float> mat(4 * 64 * 64 + 32, 0.f), proj(256 * 128, 0.f);
+  for (int g = 0; g < 2; ++g) {
+    D->B[g] = b[g] - 1;  // prod mode: b - 1 Lloyd-Max bits + the QJL bit
+    std::vector<double> gs, pi, sm;
+    seeded_gaussian(p->seed_pi + g, 64, 64, gs);
+    rotation_from_gaussian(64, gs, pi);
+    seeded_gaussian(p->seed_s + g, 64, 64, sm);
+    for (int r = 0; r < 64; ++r)
+      for (int k = 0; k < 64; ++k) {
+        mat[(2 * g) * 4096 + r * 64 + k] = (float)pi[r * 64 + k];
+        double sp = 0.0;  // S' = S Pi^T: S r = S' (Pi r)
+        for (int j = 0; j < 64; ++j) sp += sm[r * 64 + j] * pi[k * 64 + j];
+        mat[(2 * g + 1) * 4096 + r * 64 + k] = (float)sp;
+        const int ch = p->channels[64 * g + k];
+        proj[(64 * g + r) * 128 + ch] = (float)pi[r * 64 + k];
+        proj[(128 + 64 * g + r) * 128 + ch] = (float)sm[r * 64 + k];
+      }
+    Codebook cb;
+    build_codebook(64, D->B[g], cb);
+    for (int j = 0; j < (1 << D->B[g]); ++j) mat[4 * 4096 + 8 * g + j] = cb.c[j];
+    for (int j = 0; j + 1 < (1 << D->B[g]); ++j) mat[4 * 4096 + 16 + 8 * g + j] = cb.t[j];
+  }
+  std::vector<int32_t> ch(p->channels, p->channels + 128);
+  tq_status st;
+  if ((st = upload(&D->mat, mat)) || (st = upload(&D->proj, proj)) || (st = upload(&D->chan, ch))) return st;
+  return TQ_OK;
+}
+
+static std::mutex g_split_mu;
+static std::map<std::pair<std::string, int>, SplitDerived *> g_split;
+
+static tq_status get_split(const tq_split_params *p, const SplitDerived **out) {
+  int dev = 0;
+  TQ_HIP_CHECK(hipGetDevice(&dev));
+  const std::string key(reinterpret_cast<const char *>(p), sizeof(tq_split_params));
+  std::lock_guard<std::mutex> lock(g_split_mu);
+  auto it = g_split.find({key, dev});
+  if (it == g_split.end()) {
+    SplitDerived *D = new SplitDerived();
+    const tq_status st = build_split(p, dev, D);
+    if (st) {
+      (void)hipFree(D->mat);
+      (void)hipFree(D->proj);
+      (void)hipFree(D->chan);
+      delete D;
+      return st;
+    }
+    it = g_split.emplace(std::make_pair(key, dev), D).first;
+  }
+  *out = it->second;
+  return TQ_OK;
+}
+
+static void split_release() {
+  std::lock_guard<std::mutex> lock(g_split_mu);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (auto &kv : g_split) {
+    (void)hipSetDevice(kv.first.second);
+    (void)hipFree(kv.second->mat);
+    (void)hipFree(kv.second->proj);
+    (void)hipFree(kv.second->chan);
+    delete kv.second;
+  }
+  (void)hipSetDevice(cur);
+  g_split.clear();
+}
+
 }  // namespace tq
 
 // ============================================================================
@@ -1132,8 +1235,81 @@ tq_status tq_polar_score(const tq_polar_params *p, const float *q, int64_t n_kv,
   return launch_polar_score(*D, T, q, n_kv, g, codes, seq, logits, workspace, (hipStream_t)stream);
 }
 
+tq_status tq_split_words(const tq_split_params *p, int32_t *words) {
+  tq_status st = check_split(p, "tq_split_words");
+  if (st) return st;
+  if (!words) {
+    set_error("tq_split_words: words is NULL");
+    return TQ_ERR_INVALID_ARG;
+  }
+  *words = 2 * ((p->b_out - 1) + 1 + (p->b_rest - 1) + 1);
+  return TQ_OK;
+}
+
+tq_status tq_split_encode(const tq_split_params *p, const void *x, int32_t dtype, int64_t n,
+                          tq_split_codes codes, void *stream) {
+  tq_status st = check_split(p, "tq_split_encode");
+  if (st) return st;
+  if (n < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) {
+    set_error("tq_split_encode: n < 0 or bad dtype");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (n == 0) return TQ_OK;
+  if (!x || !codes.words || !codes.norms) {
+    set_error("tq_split_encode: NULL x/words/norms");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (!aligned16(x) || !aligned16(codes.words) || !aligned16(codes.norms)) {
+    set_error("tq_split_encode: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  const SplitDerived *D = nullptr;
+  if ((st = get_split(p, &D))) return st;
+  return launch_split_encode(*D, x, dtype, n, codes, (hipStream_t)stream);
+}
+
+tq_status tq_split_score_workspace_bytes(const tq_split_params *p, int64_t n_kv, int64_t g,
+                                         size_t *bytes) {
+  tq_status st = check_split(p, "tq_split_score_workspace_bytes");
+  if (st) return st;
+  if (n_kv < 0 || g < 1 || !bytes) {
+    set_error("tq_split_score_workspace_bytes: bad sizes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  *bytes = split_score_workspace_bytes(n_kv * g);
+  return TQ_OK;
+}
+
+tq_status tq_split_score(const tq_split_params *p, const float *q, int64_t n_kv, int64_t g,
+                         tq_split_codes codes, int64_t seq, float *logits, void *workspace,
+                         size_t ws_bytes, void *stream) {
+  tq_status st = check_split(p, "tq_split_score");
+  if (st) return st;
+  if (n_kv < 0 || g < 1 || seq < 0) {
+    set_error("tq_split_score: bad sizes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (n_kv == 0 || seq == 0) return TQ_OK;
+  if (!q || !logits || !workspace || !codes.words || !codes.norms) {
+    set_error("tq_split_score: NULL q/logits/workspace/words/norms");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (!aligned16(q) || !aligned16(workspace) || !aligned16(codes.words) || !aligned16(codes.norms)) {
+    set_error("tq_split_score: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (ws_bytes < split_score_workspace_bytes(n_kv * g)) {
+    set_error("tq_split_score: workspace too small");
+    return TQ_ERR_NO_MEMORY;
+  }
+  const SplitDerived *D = nullptr;
+  if ((st = get_split(p, &D))) return st;
+  return launch_split_score(*D, q, n_kv, g, codes, seq, logits, workspace, (hipStream_t)stream);
+}
+
 tq_status tq_release_cache(void) {
   polar_tables_release();
+  split_release();
   std::lock_guard<std::mutex> lock(g_cache_mu);
   for (auto &kv : g_cache) free_derived(kv.second);
   g_cache.clear();

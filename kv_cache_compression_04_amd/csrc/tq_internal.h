@@ -124,6 +124,26 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
                              int64_t g, tq_polar_codes codes, int64_t seq, float *logits, void *ws,
                              hipStream_t stream);
 
+// Mixed bit widths (two 64-channel groups), d = 128: device buffers of one
+// tq_split_params on one device.
+struct SplitDerived {
+  int device;
+  int B[2];             // Lloyd-Max bits of the groups
+  // fp32 [4][64][64]: Pi_0, S'_0 = S_0 Pi_0^T, Pi_1, S'_1; then the codebooks:
+  // centroids [2][8], boundaries [2][8] (ascending, unused entries 0)
+  float *mat = nullptr;
+  // fp32 [256][128]: rows 0..127 the rotations and rows 128..255 the JL
+  // matrices of both groups on the original channels (the query projections)
+  float *proj = nullptr;
+  int32_t *chan = nullptr;  // [128] channel order
+};
+tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
+                              tq_split_codes codes, hipStream_t stream);
+size_t split_score_workspace_bytes(int64_t nq);
+tq_status launch_split_score(const SplitDerived &D, const float *q, int64_t n_kv, int64_t g,
+                             tq_split_codes codes, int64_t seq, float *logits, void *ws,
+                             hipStream_t stream);
+
 // Fragment geometry of the d = m = 128 encode kernel: a 128 x 128 matrix is
 // stored as [16-row tile nt][32-column block kt][lane][8] bf16 values; lane l
 // covers row 16 nt + l % 16 and lane group l / 16.

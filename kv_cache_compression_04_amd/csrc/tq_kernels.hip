@@ -2902,4 +2902,239 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
   return TQ_OK;
 }
 
+// ===========================================================================
+// Mixed bit widths: two 64-channel TurboQuant groups, d = 128
+// ===========================================================================
+// Encode: one wave per (vector, group); lane r owns rotated coordinate r of
+// its group.  The group's channels are gathered, the rotation and the JL
+// projection of the residual are 64-term float32 dot products against padded
+// LDS rows (conflict-free), norms are wave reductions, and every index plane
+// and the sign plane are wave ballots (bit r = lane r).
+constexpr int kSplitPad = 65;
+constexpr int kSplitMat = 64 * 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <bool XBF16>
+__global__ __launch_bounds__(256) void split_encode128_kernel(
+    const void *__restrict__ x, int64_t n, const float *__restrict__ mat,
+    const int32_t *__restrict__ chan, int B0, int B1, int W, uint32_t *__restrict__ words,
+    float *__restrict__ norms) {
+  __shared__ float M[4][64][kSplitPad];  // Pi_0, S'_0, Pi_1, S'_1
+  __shared__ float xs[4][64], rs[4][64];
+  __shared__ float cbc[2][8], cbt[2][8];
+  for (int i = threadIdx.x; i < 4 * kSplitMat; i += 256) M[i >> 12][(i >> 6) & 63][i & 63] = mat[i];
+  if (threadIdx.x < 32) {
+    const int t = threadIdx.x;
+    const float v = mat[4 * kSplitMat + t];
+    if (t < 16) cbc[t >> 3][t & 7] = v;
+    else cbt[(t - 16) >> 3][(t - 16) & 7] = v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = wave & 1, slot = wave >> 1;
+  const int Bg = g ? B1 : B0;
+  const int nbnd = (1 << Bg) - 1;
+  const int off = g ? 2 * (B0 + 1) : 0;  // first word of this group's planes
+  const int ch = chan[64 * g + lane];
+  const float *Pr = &M[2 * g][lane][0], *Sr = &M[2 * g + 1][lane][0];
+  for (int64_t v = (int64_t)blockIdx.x * 2 + slot; v < n; v += (int64_t)gridDim.x * 2) {
+    float xv;
+    if (XBF16) {
+      const uint16_t h = reinterpret_cast<const uint16_t *>(x)[v * 128 + ch];
+      xv = __uint_as_float((uint32_t)h << 16);
+    } else {
+      xv = reinterpret_cast<const float *>(x)[v * 128 + ch];
+    }
+    const float nu = sqrtf(wave_sum(xv * xv));
+    xs[wave][lane] = xv;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float y = 0.f;
+#pragma unroll 16
+    for (int k = 0; k < 64; ++k) y = fmaf(Pr[k], xs[wave][k], y);
+    // idx = number of boundaries at or below u = y / nu, decided on y against
+    // the scaled boundaries (a zero vector compares 0 with the unscaled ones)
+    int idx = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+      if (j < nbnd) idx += y >= (nu > 0.f ? cbt[g][j] * nu : cbt[g][j]) ? 1 : 0;
+    const float rho = y - cbc[g][idx] * nu;
+    const float rn = sqrtf(wave_sum(rho * rho));
+    rs[wave][lane] = rho;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float z = 0.f;
+#pragma unroll 16
+    for (int k = 0; k < 64; ++k) z = fmaf(Sr[k], rs[wave][k], z);
+    uint32_t *dst = words + v * W + off;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      if (p < Bg) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(((idx >> p) & 1) != 0);
+        if (lane < 2) dst[2 * p + lane] = (uint32_t)(lane ? m >> 32 : m);
+      }
+    }
+    const uint64_t sm = __builtin_amdgcn_ballot_w64(z >= 0.f);
+    if (lane < 2) dst[2 * Bg + lane] = (uint32_t)(lane ? sm >> 32 : sm);
+    if (lane == 0) {
+      norms[v * 4 + 2 * g] = nu;
+      norms[v * 4 + 2 * g + 1] = rn;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Score: one key per thread, the (up to) 4 query heads of a group.  Per
+// workgroup, tables of c_g[k] (Pi_g q)_c for every coordinate c and code k
+// (a gather per coordinate) and the JL projections S_g q (a broadcast read
+// per coordinate; a set sign bit adds it, the estimator takes 2 acc - sum).
+// The projections come from qproj_kernel (float64 sums).
+constexpr int kSplitScoreThreads = 256;
+template <int B0, int B1>
+__global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
+    const double *__restrict__ pq, const float *__restrict__ mat, const uint32_t *__restrict__ words,
+    const float *__restrict__ norms, int64_t seq, int64_t g, int ngroups, float kq,
+    float *__restrict__ logits) {
+  constexpr int W = 2 * (B0 + 1 + B1 + 1);
+  __shared__ float4 TI[128][8];  // coordinate c (group c / 64), code k: c_g[k] (Pi_g q)_c
+  __shared__ float4 TS[128];     // (S_g q)_c
+  __shared__ float4 SS[2];       // sum over the group's rows of S_g q
+  const int hg = blockIdx.y, h = hg / ngroups, grp = hg % ngroups;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 128 * 8; e += kSplitScoreThreads) {
+    const int c = e >> 3, k = e & 7, gg = c >> 6;
+    const float cent = mat[4 * kSplitMat + gg * 8 + k];
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t qh = (int64_t)grp * 4 + j;
+      v[j] = qh < g ? cent * (float)pq[((int64_t)h * g + qh) * 256 + c] : 0.f;
+    }
+    TI[c][k] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  if (tid < 128) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t qh = (int64_t)grp * 4 + j;
+      v[j] = qh < g ? (float)pq[((int64_t)h * g + qh) * 256 + 128 + tid] : 0.f;
+    }
+    TS[tid] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __syncthreads();
+  if (tid < 2) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 64 * tid; c < 64 * tid + 64; ++c) {
+      a.x += TS[c].x; a.y += TS[c].y; a.z += TS[c].z; a.w += TS[c].w;
+    }
+    SS[tid] = a;
+  }
+  __syncthreads();
+  const int64_t pos = (int64_t)blockIdx.x * kSplitScoreThreads + tid;
+  if (pos >= seq) return;  // no barrier follows
+  const int64_t v = (int64_t)h * seq + pos;
+  uint32_t wd[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) wd[i] = words[v * W + i];
+  const float4 nr = *reinterpret_cast<const float4 *>(norms + v * 4);
+  float acc[2][4], accs[2][4];
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[gg][j] = accs[gg][j] = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg) {
+    constexpr int Bx[2] = {B0, B1};
+    const int B = Bx[gg];
+    const int off = gg ? 2 * (B0 + 1) : 0;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      uint32_t pl[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) pl[p] = p < B ? (half ? wd[off + 2 * p + 1] : wd[off + 2 * p]) : 0u;
+      const uint32_t sw = half ? wd[off + 2 * B + 1] : wd[off + 2 * B];
+#pragma unroll
+      for (int b = 0; b < 32; ++b) {
+        const int c = 64 * gg + 32 * half + b;
+        uint32_t k = 0;
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          if (p < B) k |= ((pl[p] >> b) & 1u) << p;
+        const float4 t = TI[c][k];
+        acc[gg][0] += t.x; acc[gg][1] += t.y; acc[gg][2] += t.z; acc[gg][3] += t.w;
+        const float bit = (float)((sw >> b) & 1u);
+        const float4 s = TS[c];
+        accs[gg][0] = fmaf(bit, s.x, accs[gg][0]);
+        accs[gg][1] = fmaf(bit, s.y, accs[gg][1]);
+        accs[gg][2] = fmaf(bit, s.z, accs[gg][2]);
+        accs[gg][3] = fmaf(bit, s.w, accs[gg][3]);
+      }
+    }
+  }
+  const float nrm[4] = {nr.x, nr.y, nr.z, nr.w};
+  const float ssum[2][4] = {{SS[0].x, SS[0].y, SS[0].z, SS[0].w}, {SS[1].x, SS[1].y, SS[1].z, SS[1].w}};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t qh = (int64_t)grp * 4 + j;
+    if (qh < g) {
+      float l = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+        l += nrm[2 * gg] * acc[gg][j] + kq * nrm[2 * gg + 1] * (2.f * accs[gg][j] - ssum[gg][j]);
+      logits[((int64_t)h * g + qh) * seq + pos] = l;
+    }
+  }
+}
+
+tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
+                              tq_split_codes c, hipStream_t s) {
+  const int W = 2 * (D.B[0] + 1 + D.B[1] + 1);
+  const int64_t need = (n + 1) / 2;
+  // 68 KB of LDS per workgroup: two workgroups per CU
+  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * 2);
+  if (dtype == TQ_BF16)
+    split_encode128_kernel<true><<<grid, 256, 0, s>>>(x, n, D.mat, D.chan, D.B[0], D.B[1], W, c.words, c.norms);
+  else
+    split_encode128_kernel<false><<<grid, 256, 0, s>>>(x, n, D.mat, D.chan, D.B[0], D.B[1], W, c.words, c.norms);
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+size_t split_score_workspace_bytes(int64_t nq) { return (size_t)nq * 256 * sizeof(double); }
+
+tq_status launch_split_score(const SplitDerived &D, const float *q, int64_t n_kv, int64_t g,
+                             tq_split_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
+  const int ngroups = (int)((g + 3) / 4);
+  const int64_t nhg = n_kv * ngroups;
+  const int64_t nblk = (seq + kSplitScoreThreads - 1) / kSplitScoreThreads;
+  if (nhg > 65535 || nblk > 0x7fffffffLL || (n_kv * g + kQJQ - 1) / kQJQ > 65535) {
+    set_error("tq_split_score: problem too large for one launch");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  double *pq = (double *)ws;
+  qproj_kernel<<<dim3(256 / kQJR, (unsigned)((n_kv * g + kQJQ - 1) / kQJQ)), dim3(256), 0, s>>>(
+      q, n_kv * g, 128, 256, D.proj, D.proj + 128 * 128, pq);
+  const dim3 grid((unsigned)nblk, (unsigned)nhg);
+  const float kq = (float)(std::sqrt(M_PI / 2.0) / 64.0);  // the QJL constant of a 64-row group
+  if (D.B[0] == 2 && D.B[1] == 1)
+    split_score128_kernel<2, 1><<<grid, kSplitScoreThreads, 0, s>>>(pq, D.mat, c.words, c.norms, seq, g, ngroups,
+                                                                    kq, logits);
+  else if (D.B[0] == 3 && D.B[1] == 2)
+    split_score128_kernel<3, 2><<<grid, kSplitScoreThreads, 0, s>>>(pq, D.mat, c.words, c.norms, seq, g, ngroups,
+                                                                    kq, logits);
+  else {
+    set_error("tq_split_score: built for 2.5 and 3.5 bits");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
 }  // namespace tq

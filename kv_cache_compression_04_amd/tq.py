@@ -45,6 +45,16 @@ class _PolarCodes(ctypes.Structure):
     _fields_ = [("pq", ctypes.c_void_p), ("radius", ctypes.c_void_p)]
 
 
+class _SplitParams(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("b_out", ctypes.c_int32), ("b_rest", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("seed_pi", ctypes.c_uint64), ("seed_s", ctypes.c_uint64),
+                ("channels", ctypes.c_int32 * 128)]
+
+
+class _SplitCodes(ctypes.Structure):
+    _fields_ = [("words", ctypes.c_void_p), ("norms", ctypes.c_void_p)]
+
+
 class _Codes(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("sgn", ctypes.c_void_p),
                 ("knorm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p)]
@@ -56,7 +66,8 @@ EXPORTS = ["tq_status_string", "tq_last_error", "tq_layout_version", "tq_make_co
            "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_decode",
            "tq_search_workspace_bytes", "tq_search", "tq_encode_slots",
            "tq_attend_paged_workspace_bytes", "tq_attend_paged", "tq_polar_make_codebook", "tq_polar_encode",
-           "tq_polar_score_workspace_bytes", "tq_polar_score", "tq_release_cache"]
+           "tq_polar_score_workspace_bytes", "tq_polar_score", "tq_split_words", "tq_split_encode",
+           "tq_split_score_workspace_bytes", "tq_split_score", "tq_release_cache"]
 
 PAGE_POSITIONS = 512  # TQ_PAGE_POSITIONS
 
@@ -74,6 +85,7 @@ def lib():
         P, C, vp, i64 = ctypes.POINTER(_Params), _Codes, ctypes.c_void_p, ctypes.c_int64
         sz = ctypes.c_size_t
         PP, PC = ctypes.POINTER(_PolarParams), _PolarCodes
+        SP, SC = ctypes.POINTER(_SplitParams), _SplitCodes
         sig = {
             "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "tq_last_error": (ctypes.c_char_p, []),
@@ -98,6 +110,10 @@ def lib():
             "tq_polar_encode": (ctypes.c_int, [PP, vp, ctypes.c_int32, i64, PC, vp]),
             "tq_polar_score_workspace_bytes": (ctypes.c_int, [PP, i64, i64, ctypes.POINTER(sz)]),
             "tq_polar_score": (ctypes.c_int, [PP, vp, i64, i64, PC, i64, vp, vp, sz, vp]),
+            "tq_split_words": (ctypes.c_int, [SP, ctypes.POINTER(ctypes.c_int32)]),
+            "tq_split_encode": (ctypes.c_int, [SP, vp, ctypes.c_int32, i64, SC, vp]),
+            "tq_split_score_workspace_bytes": (ctypes.c_int, [SP, i64, i64, ctypes.POINTER(sz)]),
+            "tq_split_score": (ctypes.c_int, [SP, vp, i64, i64, SC, i64, vp, vp, sz, vp]),
             "tq_release_cache": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -351,5 +367,59 @@ def polar_score(p: PolarParams, q, codes: dict, n_kv: int, g: int, seq: int, log
     """q: [n_kv*g, d] float32; logits: [n_kv*g, seq] float32 (written)."""
     assert q.is_contiguous() and logits.is_contiguous()
     _check("tq_polar_score", lib().tq_polar_score(ctypes.byref(p.c()), _ptr(q), n_kv, g, _pcodes(codes), seq,
+                                                  _ptr(logits), _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ----------------------------------------------------------------- mixed bit widths
+class SplitParams:
+    """Outlier-channel split of a d = 128 head: channels (a permutation of
+    0..127, the first 64 are the outlier channels), b_out = b_rest + 1."""
+
+    def __init__(self, channels, b_out: int = 3, b_rest: int = 2, seed_pi: int = 2, seed_s: int = 3):
+        ch = [int(c) for c in channels]
+        assert len(ch) == 128
+        self.channels, self.b_out, self.b_rest, self.seed_pi, self.seed_s = ch, b_out, b_rest, seed_pi, seed_s
+
+    def c(self) -> _SplitParams:
+        return _SplitParams(128, self.b_out, self.b_rest, 0, self.seed_pi, self.seed_s,
+                            (ctypes.c_int32 * 128)(*self.channels))
+
+
+def split_words(p: SplitParams) -> int:
+    out = ctypes.c_int32()
+    _check("tq_split_words", lib().tq_split_words(ctypes.byref(p.c()), ctypes.byref(out)))
+    return out.value
+
+
+def alloc_split_codes(p: SplitParams, n: int, device="cuda"):
+    import torch
+    return {"words": torch.empty((n, split_words(p)), dtype=torch.int32, device=device),
+            "norms": torch.empty((n, 4), dtype=torch.float32, device=device)}
+
+
+def _scodes(c: dict) -> _SplitCodes:
+    return _SplitCodes(c["words"].data_ptr(), c["norms"].data_ptr())
+
+
+def split_encode(p: SplitParams, x, codes: dict, stream=None):
+    import torch
+    assert x.is_contiguous()
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    _check("tq_split_encode", lib().tq_split_encode(ctypes.byref(p.c()), _ptr(x), dt, x.shape[0], _scodes(codes),
+                                                    _stream(stream)))
+
+
+def split_score_workspace_bytes(p: SplitParams, n_kv: int, g: int) -> int:
+    out = ctypes.c_size_t()
+    _check("tq_split_score_workspace_bytes",
+           lib().tq_split_score_workspace_bytes(ctypes.byref(p.c()), n_kv, g, ctypes.byref(out)))
+    return out.value
+
+
+def split_score(p: SplitParams, q, codes: dict, n_kv: int, g: int, seq: int, logits, workspace, stream=None):
+    """q: [n_kv*g, 128] float32; logits: [n_kv*g, seq] float32 (written)."""
+    assert q.is_contiguous() and logits.is_contiguous()
+    _check("tq_split_score", lib().tq_split_score(ctypes.byref(p.c()), _ptr(q), n_kv, g, _scodes(codes), seq,
                                                   _ptr(logits), _ptr(workspace),
                                                   workspace.numel() * workspace.element_size(), _stream(stream)))

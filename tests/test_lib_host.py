@@ -224,3 +224,31 @@ def test_polar_argument_checks():
     assert sc(seq=0) == 0 and sc(n_kv=0) == 0                      # nothing to do
     assert sc(g=0) == 1 and sc(q=None) == 1 and sc(w=None) == 1
     assert sc(wsb=16) == 5                                          # workspace too small
+
+
+def test_split_argument_checks():
+    """tq_split_* reject what they must before any device work."""
+    buf, a = _host_buf(1 << 16)
+    ch = list(range(128))
+    ok = tq.SplitParams(ch, 3, 2).c()
+    w = ctypes.c_int32()
+    assert _status("tq_split_words", ctypes.byref(ok), ctypes.byref(w)) == 0 and w.value == 10
+    assert _status("tq_split_words", ctypes.byref(tq.SplitParams(ch, 4, 3).c()), ctypes.byref(w)) == 0
+    assert w.value == 14
+    codes = tq._SplitCodes(a, a)
+    enc = lambda pp, x=a, n=4, dt=0: _status("tq_split_encode", ctypes.byref(pp), x, dt, n, codes, None)
+    assert enc(ok, n=0) == 0
+    assert enc(ok, x=None) == 1
+    assert enc(ok, x=a + 4) == 3
+    assert enc(tq.SplitParams(ch, 3, 3).c()) == 1                       # b_out must be b_rest + 1
+    assert enc(tq.SplitParams([0] * 128, 3, 2).c()) == 1                 # not a permutation
+    assert enc(tq.SplitParams(ch, 5, 4).c()) == 2                        # kernels built for 2.5 / 3.5 bits
+    bad_d = tq.SplitParams(ch, 3, 2).c()
+    bad_d.d = 64
+    assert enc(bad_d) == 2
+    ws = ctypes.c_size_t()
+    assert _status("tq_split_score_workspace_bytes", ctypes.byref(ok), 2, 4, ctypes.byref(ws)) == 0
+    assert ws.value == 2 * 4 * 256 * 8
+    sc = lambda seq=8, q=a, wsb=1 << 16: _status("tq_split_score", ctypes.byref(ok), q, 1, 4, codes, seq, a, a,
+                                                  wsb, None)
+    assert sc(seq=0) == 0 and sc(q=None) == 1 and sc(wsb=16) == 5
