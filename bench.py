@@ -21,7 +21,8 @@ Reported on one JSON line:
   roofline_score  the score kernel on the 32-layer stream (HBM-bound)
   cpu_baseline the CPU oracle (numpy float64) on a bounded sample of the step
 Further sections (each can be switched off): long-context attention (plain
-and through a paged block table), the PolarQuant variant on the same layer,
+and through a paged block table), the PolarQuant variant and the
+outlier-channel mixed bit widths (2.5 / 3.5 bits) on the same layer,
 the bit-width sweep, high-dimensional batched search (d = m = 1024, 1M
 vectors, 1024 queries, top-10) and search at database scale (2^26 vectors of
 d = 128, 3.76 GB of codes, 1024 queries, top-10).
@@ -57,6 +58,7 @@ def _parse():
     ap.add_argument("--no-highdim", action="store_true")
     ap.add_argument("--no-searchdb", action="store_true")
     ap.add_argument("--no-polar", action="store_true")
+    ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling PMC byte counters)")
@@ -398,6 +400,58 @@ def main():
             "score_frac_hbm_peak": round(sbytes / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         }
         del px, pc, pbig, plg, pws
+
+    if not args.no_split:
+        # outlier-channel mixed bit widths (2.5 and 3.5 bits) on the same layer:
+        # the 64 channels of largest mean square in head 0's keys form the
+        # outlier group (one channel list for the layer; a list per head is a
+        # launch per head); encode of the 8 x 32768 bf16 keys, and the score of
+        # 1024 query heads over 32 such layers' codes
+        sx = synth.llama_keys(heads=N_KV, seq=SEQ, seed=1, device=dev)
+        ms = (sx[:SEQ].float() ** 2).mean(dim=0)
+        order = torch.argsort(-ms, stable=True).cpu()
+        chans = torch.cat([torch.sort(order[:64]).values, torch.sort(order[64:]).values]).tolist()
+        nL = LAYERS * N_KV
+        sq_ = synth.queries(nL * G, seed=6, device=dev)
+        slg = torch.empty((nL * G, SEQ), device=dev)
+        res = []
+        for b_rest in (2, 3):
+            sp_ = tq.SplitParams(chans, b_rest + 1, b_rest, 2, 3)
+            sc1 = tq.alloc_split_codes(sp_, N_KV * SEQ, dev)
+            sbig = tq.alloc_split_codes(sp_, nL * SEQ, dev)
+            for layer in range(LAYERS):
+                xl = synth.llama_keys(heads=N_KV, seq=SEQ, seed=100 + layer, device=dev)
+                sl = slice(layer * N_KV * SEQ, (layer + 1) * N_KV * SEQ)
+                tq.split_encode(sp_, xl, {k: v[sl] for k, v in sbig.items()})
+            del xl
+            sws = torch.empty(tq.split_score_workspace_bytes(sp_, nL, G), dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                tq.split_encode(sp_, sx, sc1)
+                tq.split_score(sp_, sq_, sbig, nL, G, SEQ, slg, sws)
+            torch.cuda.synchronize()
+            reps = max(3, args.steps // 10)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            for _ in range(reps):
+                tq.split_encode(sp_, sx, sc1)
+            e[1].record(stream)
+            for _ in range(reps):
+                tq.split_score(sp_, sq_, sbig, nL, G, SEQ, slg, sws)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            enc_ms = e[0].elapsed_time(e[1]) / reps
+            sc_ms = e[1].elapsed_time(e[2]) / reps
+            rec = 4 * tq.split_words(sp_) + 16
+            sbytes = rec * nL * SEQ + 4 * nL * G * SEQ
+            res.append({"bits": b_rest + 0.5, "bytes_per_key": rec, "encode_us": round(enc_ms * 1e3, 2),
+                        "encode_mvectors_per_s": round(N_KV * SEQ / (enc_ms * 1e-3) / 1e6, 1),
+                        "score_ms": round(sc_ms, 4), "score_GBps": round(sbytes / (sc_ms * 1e-3) / 1e9, 1),
+                        "score_frac_hbm_peak": round(sbytes / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+            del sc1, sbig, sws
+        out["split"] = {"workload": f"outlier-channel split (64 + 64 channels) of {N_KV} x {SEQ} bf16 Llama-shaped "
+                                    f"keys; score {nL * G} query heads over {LAYERS} layers",
+                        "rows": res}
+        del sx, slg
 
     if not args.no_sweep:
         # bit-width sweep: 65536 unit-direction x log-normal-norm float32 vectors, 1024 queries

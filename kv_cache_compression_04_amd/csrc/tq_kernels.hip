@@ -2910,7 +2910,7 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
 // projection of the residual are 64-term float32 dot products against padded
 // LDS rows (conflict-free), norms are wave reductions, and every index plane
 // and the sign plane are wave ballots (bit r = lane r).
-constexpr int kSplitPad = 65;
+constexpr int kSplitPad = 68;  // rows 16-byte aligned; b128 row reads of 16 lanes hit 64 distinct banks
 constexpr int kSplitMat = 64 * 64;
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -2919,15 +2919,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+constexpr int kSplitVPW = 4;  // vectors per wave iteration (independent chains, shared row reads)
+
+constexpr int kSplitSlots = 8;  // vector slots per workgroup (two waves each: one per group)
+
 template <bool XBF16>
-__global__ __launch_bounds__(256) void split_encode128_kernel(
+__device__ __forceinline__ float split_load_x(const void *__restrict__ x, int64_t v, int ch) {
+  if (XBF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(x)[v * 128 + ch] << 16);
+  return reinterpret_cast<const float *>(x)[v * 128 + ch];
+}
+
+template <bool XBF16>
+__global__ __launch_bounds__(kSplitSlots * 128) void split_encode128_kernel(
     const void *__restrict__ x, int64_t n, const float *__restrict__ mat,
     const int32_t *__restrict__ chan, int B0, int B1, int W, uint32_t *__restrict__ words,
     float *__restrict__ norms) {
-  __shared__ float M[4][64][kSplitPad];  // Pi_0, S'_0, Pi_1, S'_1
-  __shared__ float xs[4][64], rs[4][64];
+  constexpr int V = kSplitVPW;
+  __shared__ __attribute__((aligned(16))) float M[4][64][kSplitPad];  // Pi_0, S'_0, Pi_1, S'_1
+  __shared__ __attribute__((aligned(16))) float xs[2 * kSplitSlots][V][64], rs[2 * kSplitSlots][V][64];
   __shared__ float cbc[2][8], cbt[2][8];
-  for (int i = threadIdx.x; i < 4 * kSplitMat; i += 256) M[i >> 12][(i >> 6) & 63][i & 63] = mat[i];
+  for (int i = threadIdx.x; i < 4 * kSplitMat; i += blockDim.x) M[i >> 12][(i >> 6) & 63][i & 63] = mat[i];
   if (threadIdx.x < 32) {
     const int t = threadIdx.x;
     const float v = mat[4 * kSplitMat + t];
@@ -2943,48 +2954,86 @@ __global__ __launch_bounds__(256) void split_encode128_kernel(
   const int off = g ? 2 * (B0 + 1) : 0;  // first word of this group's planes
   const int ch = chan[64 * g + lane];
   const float *Pr = &M[2 * g][lane][0], *Sr = &M[2 * g + 1][lane][0];
-  for (int64_t v = (int64_t)blockIdx.x * 2 + slot; v < n; v += (int64_t)gridDim.x * 2) {
-    float xv;
-    if (XBF16) {
-      const uint16_t h = reinterpret_cast<const uint16_t *>(x)[v * 128 + ch];
-      xv = __uint_as_float((uint32_t)h << 16);
-    } else {
-      xv = reinterpret_cast<const float *>(x)[v * 128 + ch];
+  const int64_t stride = (int64_t)gridDim.x * kSplitSlots * V;
+  // the keys of the next iteration are requested while this one computes
+  // (a slot past the end repeats the last vector and is not stored)
+  float xn[V];
+  int64_t v0 = ((int64_t)blockIdx.x * kSplitSlots + slot) * V;
+#pragma unroll
+  for (int i = 0; i < V; ++i) xn[i] = v0 < n ? split_load_x<XBF16>(x, v0 + i < n ? v0 + i : n - 1, ch) : 0.f;
+  for (; v0 < n; v0 += stride) {
+    float xv[V], nu[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) xv[i] = xn[i];
+    const int64_t v1 = v0 + stride;
+#pragma unroll
+    for (int i = 0; i < V; ++i) xn[i] = v1 < n ? split_load_x<XBF16>(x, v1 + i < n ? v1 + i : n - 1, ch) : 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      nu[i] = sqrtf(wave_sum(xv[i] * xv[i]));
+      xs[wave][i][lane] = xv[i];
     }
-    const float nu = sqrtf(wave_sum(xv * xv));
-    xs[wave][lane] = xv;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    float y = 0.f;
-#pragma unroll 16
-    for (int k = 0; k < 64; ++k) y = fmaf(Pr[k], xs[wave][k], y);
-    // idx = number of boundaries at or below u = y / nu, decided on y against
-    // the scaled boundaries (a zero vector compares 0 with the unscaled ones)
-    int idx = 0;
+    float y[V];
 #pragma unroll
-    for (int j = 0; j < 7; ++j)
-      if (j < nbnd) idx += y >= (nu > 0.f ? cbt[g][j] * nu : cbt[g][j]) ? 1 : 0;
-    const float rho = y - cbc[g][idx] * nu;
-    const float rn = sqrtf(wave_sum(rho * rho));
-    rs[wave][lane] = rho;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    float z = 0.f;
-#pragma unroll 16
-    for (int k = 0; k < 64; ++k) z = fmaf(Sr[k], rs[wave][k], z);
-    uint32_t *dst = words + v * W + off;
+    for (int i = 0; i < V; ++i) y[i] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < 64; k += 4) {
+      const float4 p4 = *reinterpret_cast<const float4 *>(Pr + k);
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      if (p < Bg) {
-        const uint64_t m = __builtin_amdgcn_ballot_w64(((idx >> p) & 1) != 0);
-        if (lane < 2) dst[2 * p + lane] = (uint32_t)(lane ? m >> 32 : m);
+      for (int i = 0; i < V; ++i) {
+        const float4 x4 = *reinterpret_cast<const float4 *>(&xs[wave][i][k]);  // broadcast
+        y[i] = fmaf(p4.x, x4.x, fmaf(p4.y, x4.y, fmaf(p4.z, x4.z, fmaf(p4.w, x4.w, y[i]))));
       }
     }
-    const uint64_t sm = __builtin_amdgcn_ballot_w64(z >= 0.f);
-    if (lane < 2) dst[2 * Bg + lane] = (uint32_t)(lane ? sm >> 32 : sm);
-    if (lane == 0) {
-      norms[v * 4 + 2 * g] = nu;
-      norms[v * 4 + 2 * g + 1] = rn;
+    int idx[V];
+    float rn[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      // idx = number of boundaries at or below u = y / nu, decided on y against
+      // the scaled boundaries (a zero vector compares 0 with the unscaled ones)
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < 7; ++j)
+        if (j < nbnd) c += y[i] >= (nu[i] > 0.f ? cbt[g][j] * nu[i] : cbt[g][j]) ? 1 : 0;
+      idx[i] = c;
+      const float rho = y[i] - cbc[g][c] * nu[i];
+      rn[i] = sqrtf(wave_sum(rho * rho));
+      rs[wave][i][lane] = rho;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float z[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) z[i] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < 64; k += 4) {
+      const float4 s4 = *reinterpret_cast<const float4 *>(Sr + k);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const float4 r4 = *reinterpret_cast<const float4 *>(&rs[wave][i][k]);  // broadcast
+        z[i] = fmaf(s4.x, r4.x, fmaf(s4.y, r4.y, fmaf(s4.z, r4.z, fmaf(s4.w, r4.w, z[i]))));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int64_t v = v0 + i;
+      uint64_t m[4];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) m[p] = __builtin_amdgcn_ballot_w64(((idx[i] >> p) & 1) != 0);
+      m[3] = __builtin_amdgcn_ballot_w64(z[i] >= 0.f);
+      if (v < n) {
+        uint32_t *dst = words + v * W + off;
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          if (p < Bg && lane < 2) dst[2 * p + lane] = (uint32_t)(lane ? m[p] >> 32 : m[p]);
+        if (lane < 2) dst[2 * Bg + lane] = (uint32_t)(lane ? m[3] >> 32 : m[3]);
+        if (lane == 0) {
+          norms[v * 4 + 2 * g] = nu[i];
+          norms[v * 4 + 2 * g + 1] = rn[i];
+        }
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -3096,13 +3145,14 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
 tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
                               tq_split_codes c, hipStream_t s) {
   const int W = 2 * (D.B[0] + 1 + D.B[1] + 1);
-  const int64_t need = (n + 1) / 2;
-  // 68 KB of LDS per workgroup: two workgroups per CU
-  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * 2);
+  const int64_t need = (n + kSplitSlots * kSplitVPW - 1) / (kSplitSlots * kSplitVPW);
+  // about 100 KB of LDS per workgroup of 16 waves: one workgroup per CU
+  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device));
+  const int threads = kSplitSlots * 128;
   if (dtype == TQ_BF16)
-    split_encode128_kernel<true><<<grid, 256, 0, s>>>(x, n, D.mat, D.chan, D.B[0], D.B[1], W, c.words, c.norms);
+    split_encode128_kernel<true><<<grid, threads, 0, s>>>(x, n, D.mat, D.chan, D.B[0], D.B[1], W, c.words, c.norms);
   else
-    split_encode128_kernel<false><<<grid, 256, 0, s>>>(x, n, D.mat, D.chan, D.B[0], D.B[1], W, c.words, c.norms);
+    split_encode128_kernel<false><<<grid, threads, 0, s>>>(x, n, D.mat, D.chan, D.B[0], D.B[1], W, c.words, c.norms);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
