@@ -72,7 +72,7 @@ def test_graph_encode_score_attend_search():
     print("[parity] graph replays of encode/score/attend/search equal the eager results", flush=True)
 
 
-def test_graph_paged_and_polar():
+def test_graph_paged_polar_and_split():
     kp = tq.Params(128, 3, 128, tq.MODE_PROD, 2, 3)
     vp = tq.Params(128, 3, 128, tq.MODE_MSE, 4, 0)
     n_kv, g, npg = 2, 4, 3
@@ -94,13 +94,19 @@ def test_graph_paged_and_polar():
     plog = torch.empty((4, 700), device=DEV)
     pws = torch.empty(tq.polar_score_workspace_bytes(pp, 1, 4), dtype=torch.uint8, device=DEV)
     pq = synth.queries(4, seed=13, device=DEV)
+    sp = tq.SplitParams(list(range(64, 128)) + list(range(64)), 3, 2)
+    sc = tq.alloc_split_codes(sp, 700, DEV)
+    slog = torch.empty((4, 700), device=DEV)
+    sws = torch.empty(tq.split_score_workspace_bytes(sp, 1, 4), dtype=torch.uint8, device=DEV)
 
     def run():
         tq.encode_slots(kp, newk, slots, cap, kc)
         tq.attend_paged(kp, vp, q, 1, n_kv, g, kc, vc, npg, bt, lens, out, ws)
         tq.polar_encode(pp, px, pc)
         tq.polar_score(pp, pq, pc, 1, 4, 700, plog, pws)
+        tq.split_encode(sp, px, sc)
+        tq.split_score(sp, pq, sc, 1, 4, 700, slog, sws)
 
-    _replays_match(run, [out, pc["pq"], pc["radius"], plog],
+    _replays_match(run, [out, pc["pq"], pc["radius"], plog, sc["words"], sc["norms"], slog],
                    rows=[(kc["idx"], slots), (kc["sgn"], slots), (kc["knorm"], slots), (kc["rnorm"], slots)])
-    print("[parity] graph replays of slot encode/paged attend/polar equal the eager results", flush=True)
+    print("[parity] graph replays of slot encode/paged attend/polar/split equal the eager results", flush=True)
