@@ -33,6 +33,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "tq_internal.h"
 
@@ -3041,105 +3042,139 @@ __global__ __launch_bounds__(kSplitSlots * 128) void split_encode128_kernel(
 }
 
 // Score: one key per thread, the (up to) 4 query heads of a group.  Per
-// workgroup, tables of c_g[k] (Pi_g q)_c for every coordinate c and code k
-// (a gather per coordinate) and the JL projections S_g q (a broadcast read
-// per coordinate; a set sign bit adds it, the estimator takes 2 acc - sum).
+// workgroup, tables over chunks of coordinates: for a chunk of S coordinates
+// of group g (S = 2, or 4 for 1-bit groups) and each combination `code` of
+// their index bits, the sum of c_g[idx] (Pi_g q)_c over the chunk; for a
+// chunk of 4 sign bits, the sum of (S_g q)_c over the set bits (the estimator
+// takes 2 sum - total).  A key then costs one gather and four adds per chunk.
 // The projections come from qproj_kernel (float64 sums).
 constexpr int kSplitScoreThreads = 256;
+constexpr int kSplitKPT = 4;  // keys per thread
+
+__host__ __device__ constexpr int split_chunk(int B) { return B >= 2 ? 2 : 4; }
+
 template <int B0, int B1>
 __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
     const double *__restrict__ pq, const float *__restrict__ mat, const uint32_t *__restrict__ words,
     const float *__restrict__ norms, int64_t seq, int64_t g, int ngroups, float kq,
     float *__restrict__ logits) {
   constexpr int W = 2 * (B0 + 1 + B1 + 1);
-  __shared__ float4 TI[128][8];  // coordinate c (group c / 64), code k: c_g[k] (Pi_g q)_c
-  __shared__ float4 TS[128];     // (S_g q)_c
-  __shared__ float4 SS[2];       // sum over the group's rows of S_g q
+  constexpr int S0 = split_chunk(B0), S1 = split_chunk(B1);
+  constexpr int C0 = 1 << (B0 * S0), C1 = 1 << (B1 * S1);  // codes per chunk
+  constexpr int N0 = 64 / S0, N1 = 64 / S1;                 // chunks per group
+  __shared__ float4 qs4[256];               // (Pi q)_c for c < 128, then (S q)_c
+  __shared__ float4 TI0[N0 * C0], TI1[N1 * C1];
+  __shared__ float4 TS[2][16][16];          // group, sign chunk, code
+  __shared__ float4 SS[2];
   const int hg = blockIdx.y, h = hg / ngroups, grp = hg % ngroups;
   const int tid = threadIdx.x;
-  for (int e = tid; e < 128 * 8; e += kSplitScoreThreads) {
-    const int c = e >> 3, k = e & 7, gg = c >> 6;
-    const float cent = mat[4 * kSplitMat + gg * 8 + k];
+  {
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t qh = (int64_t)grp * 4 + j;
-      v[j] = qh < g ? cent * (float)pq[((int64_t)h * g + qh) * 256 + c] : 0.f;
+      v[j] = qh < g ? (float)pq[((int64_t)h * g + qh) * 256 + tid] : 0.f;
     }
-    TI[c][k] = make_float4(v[0], v[1], v[2], v[3]);
-  }
-  if (tid < 128) {
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t qh = (int64_t)grp * 4 + j;
-      v[j] = qh < g ? (float)pq[((int64_t)h * g + qh) * 256 + 128 + tid] : 0.f;
-    }
-    TS[tid] = make_float4(v[0], v[1], v[2], v[3]);
+    qs4[tid] = make_float4(v[0], v[1], v[2], v[3]);
   }
   __syncthreads();
+  for (int e = tid; e < N0 * C0 + N1 * C1; e += kSplitScoreThreads) {
+    const bool g1 = e >= N0 * C0;
+    const int ee = g1 ? e - N0 * C0 : e;
+    const int S = g1 ? S1 : S0, B = g1 ? B1 : B0, C = g1 ? C1 : C0;
+    const int chunk = ee / C, code = ee % C;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < S; ++j) {
+      int idx = 0;
+      for (int p = 0; p < B; ++p) idx |= ((code >> (p * S + j)) & 1) << p;
+      const float cent = mat[4 * kSplitMat + (g1 ? 8 : 0) + idx];
+      const float4 q = qs4[64 * (g1 ? 1 : 0) + chunk * S + j];
+      a.x = fmaf(cent, q.x, a.x); a.y = fmaf(cent, q.y, a.y); a.z = fmaf(cent, q.z, a.z); a.w = fmaf(cent, q.w, a.w);
+    }
+    if (g1) TI1[ee] = a;
+    else TI0[ee] = a;
+  }
+  for (int e = tid; e < 2 * 16 * 16; e += kSplitScoreThreads) {
+    const int gg = e >> 8, chunk = (e >> 4) & 15, code = e & 15;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < 4; ++j)
+      if ((code >> j) & 1) {
+        const float4 q = qs4[128 + 64 * gg + 4 * chunk + j];
+        a.x += q.x; a.y += q.y; a.z += q.z; a.w += q.w;
+      }
+    TS[gg][chunk][code] = a;
+  }
   if (tid < 2) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c = 64 * tid; c < 64 * tid + 64; ++c) {
-      a.x += TS[c].x; a.y += TS[c].y; a.z += TS[c].z; a.w += TS[c].w;
+    for (int c = 128 + 64 * tid; c < 128 + 64 * tid + 64; ++c) {
+      a.x += qs4[c].x; a.y += qs4[c].y; a.z += qs4[c].z; a.w += qs4[c].w;
     }
     SS[tid] = a;
   }
   __syncthreads();
-  const int64_t pos = (int64_t)blockIdx.x * kSplitScoreThreads + tid;
-  if (pos >= seq) return;  // no barrier follows
+  // kSplitKPT keys per thread amortise the tables over 1024 keys
+#pragma unroll 1
+  for (int r = 0; r < kSplitKPT; ++r) {
+  const int64_t pos = ((int64_t)blockIdx.x * kSplitKPT + r) * kSplitScoreThreads + tid;
+  if (pos >= seq) break;  // no barrier follows
   const int64_t v = (int64_t)h * seq + pos;
   uint32_t wd[W];
 #pragma unroll
   for (int i = 0; i < W; ++i) wd[i] = words[v * W + i];
   const float4 nr = *reinterpret_cast<const float4 *>(norms + v * 4);
-  float acc[2][4], accs[2][4];
-#pragma unroll
-  for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[gg][j] = accs[gg][j] = 0.f;
+  float4 acc[2], accs[2];
 #pragma unroll
   for (int gg = 0; gg < 2; ++gg) {
-    constexpr int Bx[2] = {B0, B1};
-    const int B = Bx[gg];
-    const int off = gg ? 2 * (B0 + 1) : 0;
+    acc[gg] = make_float4(0.f, 0.f, 0.f, 0.f);
+    accs[gg] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // one group and one 32-coordinate half per loop iteration (the gathers of
+  // an iteration are not all hoisted together; words picked by uniform selects)
+  auto group = [&](auto gc) {
+    constexpr int gg = decltype(gc)::value;
+    constexpr int B = gg ? B1 : B0, S = gg ? S1 : S0, C = gg ? C1 : C0;
+    constexpr int off = gg ? 2 * (B0 + 1) : 0;
+    const float4 *TI = gg ? TI1 : TI0;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
       uint32_t pl[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p) pl[p] = p < B ? (half ? wd[off + 2 * p + 1] : wd[off + 2 * p]) : 0u;
       const uint32_t sw = half ? wd[off + 2 * B + 1] : wd[off + 2 * B];
+      const float4 *TIh = TI + half * (32 / S) * C;
 #pragma unroll
-      for (int b = 0; b < 32; ++b) {
-        const int c = 64 * gg + 32 * half + b;
-        uint32_t k = 0;
+      for (int k = 0; k < 32 / S; ++k) {
+        uint32_t code = 0;
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          if (p < B) k |= ((pl[p] >> b) & 1u) << p;
-        const float4 t = TI[c][k];
-        acc[gg][0] += t.x; acc[gg][1] += t.y; acc[gg][2] += t.z; acc[gg][3] += t.w;
-        const float bit = (float)((sw >> b) & 1u);
-        const float4 s = TS[c];
-        accs[gg][0] = fmaf(bit, s.x, accs[gg][0]);
-        accs[gg][1] = fmaf(bit, s.y, accs[gg][1]);
-        accs[gg][2] = fmaf(bit, s.z, accs[gg][2]);
-        accs[gg][3] = fmaf(bit, s.w, accs[gg][3]);
+          if (p < B) code |= ((pl[p] >> (S * k)) & ((1u << S) - 1u)) << (p * S);
+        const float4 t = TIh[k * C + code];
+        acc[gg].x += t.x; acc[gg].y += t.y; acc[gg].z += t.z; acc[gg].w += t.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 t = TS[gg][8 * half + k][(sw >> (4 * k)) & 15u];
+        accs[gg].x += t.x; accs[gg].y += t.y; accs[gg].z += t.z; accs[gg].w += t.w;
       }
     }
-  }
+  };
+  group(std::integral_constant<int, 0>{});
+  group(std::integral_constant<int, 1>{});
   const float nrm[4] = {nr.x, nr.y, nr.z, nr.w};
-  const float ssum[2][4] = {{SS[0].x, SS[0].y, SS[0].z, SS[0].w}, {SS[1].x, SS[1].y, SS[1].z, SS[1].w}};
+  const float a0[4] = {acc[0].x, acc[0].y, acc[0].z, acc[0].w}, a1[4] = {acc[1].x, acc[1].y, acc[1].z, acc[1].w};
+  const float s0[4] = {accs[0].x, accs[0].y, accs[0].z, accs[0].w};
+  const float s1[4] = {accs[1].x, accs[1].y, accs[1].z, accs[1].w};
+  const float t0[4] = {SS[0].x, SS[0].y, SS[0].z, SS[0].w}, t1[4] = {SS[1].x, SS[1].y, SS[1].z, SS[1].w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t qh = (int64_t)grp * 4 + j;
     if (qh < g) {
-      float l = 0.f;
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg)
-        l += nrm[2 * gg] * acc[gg][j] + kq * nrm[2 * gg + 1] * (2.f * accs[gg][j] - ssum[gg][j]);
+      const float l = nrm[0] * a0[j] + kq * nrm[1] * (2.f * s0[j] - t0[j]) + nrm[2] * a1[j] +
+                      kq * nrm[3] * (2.f * s1[j] - t1[j]);
       logits[((int64_t)h * g + qh) * seq + pos] = l;
     }
   }
+  }  // keys of this thread
 }
 
 tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
@@ -3163,7 +3198,7 @@ tq_status launch_split_score(const SplitDerived &D, const float *q, int64_t n_kv
                              tq_split_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
   const int ngroups = (int)((g + 3) / 4);
   const int64_t nhg = n_kv * ngroups;
-  const int64_t nblk = (seq + kSplitScoreThreads - 1) / kSplitScoreThreads;
+  const int64_t nblk = (seq + kSplitKPT * kSplitScoreThreads - 1) / (kSplitKPT * kSplitScoreThreads);
   if (nhg > 65535 || nblk > 0x7fffffffLL || (n_kv * g + kQJQ - 1) / kQJQ > 65535) {
     set_error("tq_split_score: problem too large for one launch");
     return TQ_ERR_UNSUPPORTED;
