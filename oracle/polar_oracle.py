@@ -22,7 +22,7 @@ Sources (pages cited by title and section):
         concentrate at 45 degrees; the first level takes 4 bits, the later
         levels 2 bits, about 3 bits per coordinate in all.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent (numbered; tests and comments refer to them):
   Q1  the rotation is the TurboQuant one (y = Pi x, Pi from seed_pi); the
       transform runs on y, and the stored radius is ||x|| in float32.
   Q2  level 1 pairs coordinates (2j, 2j+1) into psi_j = atan2(y_2j+1, y_2j)

@@ -14,7 +14,7 @@ Sources (pages cited by title and section):
       第二阶段: each group is quantised by the two-stage method (rotation +
       Lloyd-Max on b-1 bits, then 1-bit QJL of the residual).
 
-Readings (each also listed in the design doc):
+Readings (numbered; tests and comments refer to them):
   M1  the average fixes the split: with b_out = b_rest + 1 bits, an average of
       b_rest + 1/2 bits needs half of the d channels in the outlier group
       (the page's "a few" outlier channels cannot give 2.5 with 3 / 2 bits).

@@ -21,7 +21,7 @@ Sources (the pages are cited by title and section):
   [P1]  the yeyulingfeng.com bilingual explainer, section "TurboQuant：6倍压缩，
         零损失" (rotate, then quantise with a precomputed Lloyd-Max codebook).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent (numbered; tests and comments refer to them):
   R1  random numbers: SplitMix64 (Steele, Lea & Flood 2014), counter-addressable;
       Gaussians by Box-Muller.  Exact recipe in ``splitmix64`` / ``gaussian``.
   R2  Pi = Q of the QR factorisation of a seeded Gaussian d x d matrix, with

@@ -1,6 +1,6 @@
 """Comparison helpers for the GPU-vs-oracle parity tests (test code only).
 
-Tolerances (readings of the stated parity bar, also listed in the design doc):
+Tolerances (readings of the stated parity bar):
   * index planes and sign bits are bit-exact, except where the decided point
     lies within 1e-5 * ||x|| of its decision boundary: for an index, the
     rotated coordinate ||x|| u_i against ||x|| t_j; for a sign bit, the
