@@ -260,8 +260,9 @@ tq_status tq_release_cache(void);
  *
  * Packed record (d = 128): tq_split_words() uint32 words per vector, group 0
  * then group 1; a group with B = b - 1 Lloyd-Max bits holds its B index
- * planes and then its sign plane, two words each (coordinate c of the group,
- * after its rotation, at word c / 32, bit c % 32); and float32 norms [n][4]:
+ * planes and then its sign plane, two words each (rotated coordinate
+ * c = 16 t + 4 k + i of the group at word k / 2, bit 16 (k % 2) + 4 t + i);
+ * and float32 norms [n][4]:
  * ||x_0||, ||r_0||, ||x_1||, ||r_1||.  10 words + 16 bytes (56 bytes) at
  * 2.5 bits, 14 words + 16 bytes (72 bytes) at 3.5 bits.
  * ------------------------------------------------------------------------- */

@@ -713,9 +713,34 @@ static tq_status build_split(const tq_split_params *p, int dev, SplitDerived *D)
     for (int j = 0; j < (1 << D->B[g]); ++j) mat[4 * 4096 + 8 * g + j] = cb.c[j];
     for (int j = 0; j + 1 < (1 << D->B[g]); ++j) mat[4 * 4096 + 16 + 8 * g + j] = cb.t[j];
   }
+  // bf16 hi / lo fragments of the 64 x 64 matrices for the encode MFMAs:
+  // [nt (4)][kt (2)][lane (64)][e (8)], element (lane, e) = M[16 nt + lane % 16]
+  // [col(kt, lane / 16, e)].  Pi: col = 32 kt + 8 g + e (the gathered keys);
+  // S': col = 32 kt + 16 (e / 4) + 4 g + e % 4 (the residual in the layout of
+  // the first product's output).
+  std::vector<uint16_t> frag(8 * 4096);
+  for (int g = 0; g < 2; ++g)
+    for (int m = 0; m < 2; ++m) {
+      const float *src = &mat[(2 * g + m) * 4096];
+      uint16_t *hi = &frag[(4 * g + 2 * m) * 4096], *lo = hi + 4096;
+      size_t o = 0;
+      for (int nt = 0; nt < 4; ++nt)
+        for (int kt = 0; kt < 2; ++kt)
+          for (int l = 0; l < 64; ++l)
+            for (int e = 0; e < 8; ++e, ++o) {
+              const int gg = l >> 4;
+              const int col = m == 0 ? 32 * kt + 8 * gg + e : 32 * kt + 16 * (e / 4) + 4 * gg + e % 4;
+              const double v = src[(16 * nt + (l & 15)) * 64 + col];
+              const uint16_t h = bf16_bits((float)v);
+              hi[o] = h;
+              lo[o] = bf16_bits((float)(v - bf16_value(h)));
+            }
+    }
   std::vector<int32_t> ch(p->channels, p->channels + 128);
   tq_status st;
-  if ((st = upload(&D->mat, mat)) || (st = upload(&D->proj, proj)) || (st = upload(&D->chan, ch))) return st;
+  if ((st = upload(&D->mat, mat)) || (st = upload(&D->proj, proj)) || (st = upload(&D->chan, ch)) ||
+      (st = upload(&D->frag, frag)))
+    return st;
   return TQ_OK;
 }
 
@@ -735,6 +760,7 @@ static tq_status get_split(const tq_split_params *p, const SplitDerived **out) {
       (void)hipFree(D->mat);
       (void)hipFree(D->proj);
       (void)hipFree(D->chan);
+      (void)hipFree(D->frag);
       delete D;
       return st;
     }
@@ -753,6 +779,7 @@ static void split_release() {
     (void)hipFree(kv.second->mat);
     (void)hipFree(kv.second->proj);
     (void)hipFree(kv.second->chan);
+    (void)hipFree(kv.second->frag);
     delete kv.second;
   }
   (void)hipSetDevice(cur);

@@ -136,6 +136,9 @@ struct SplitDerived {
   // matrices of both groups on the original channels (the query projections)
   float *proj = nullptr;
   int32_t *chan = nullptr;  // [128] channel order
+  // bf16 MFMA fragments, uint4 [8][4 row tiles x 2 column blocks][64 lanes]:
+  // Pi_0 hi, lo, S'_0 hi, lo, Pi_1 hi, lo, S'_1 hi, lo (see build_split)
+  uint16_t *frag = nullptr;
 };
 tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
                               tq_split_codes codes, hipStream_t stream);

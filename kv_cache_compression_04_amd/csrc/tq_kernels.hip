@@ -2906,40 +2906,29 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
 // ===========================================================================
 // Mixed bit widths: two 64-channel TurboQuant groups, d = 128
 // ===========================================================================
-// Encode: one wave per (vector, group); lane r owns rotated coordinate r of
-// its group.  The group's channels are gathered, the rotation and the JL
-// projection of the residual are 64-term float32 dot products against padded
-// LDS rows (conflict-free), norms are wave reductions, and every index plane
-// and the sign plane are wave ballots (bit r = lane r).
-constexpr int kSplitPad = 68;  // rows 16-byte aligned; b128 row reads of 16 lanes hit 64 distinct banks
+// Encode: one wave per 16 vectors, the two channel groups in turn, as bf16
+// hi / lo MFMAs like the d = 128 encoder: Y_g = Pi_g X_g with X_g the keys'
+// channels of group g gathered into the B operand (lane (v, k) holds the
+// group's channels 32 kt + 8 k .. + 7 of vector v), so lane (v, k) receives
+// rotated coordinates 16 t + 4 k + i; bucketisation and the residual stay in
+// registers, Z_g = S'_g rho_g reads the residual in that layout (S'_g's
+// columns are arranged for it), and each lane packs the 16 bits of its
+// coordinates (16 t + 4 k + i -> word k / 2, bit 16 (k % 2) + 4 t + i), two
+// lane groups sharing a word.
 constexpr int kSplitMat = 64 * 64;
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-constexpr int kSplitVPW = 4;  // vectors per wave iteration (independent chains, shared row reads)
-
-constexpr int kSplitSlots = 8;  // vector slots per workgroup (two waves each: one per group)
+constexpr int kSplitWaves = 16;
+constexpr int kSplitFragU4 = 4 * 2 * 64;  // uint4 per 64 x 64 fragment half
 
 template <bool XBF16>
-__device__ __forceinline__ float split_load_x(const void *__restrict__ x, int64_t v, int ch) {
-  if (XBF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(x)[v * 128 + ch] << 16);
-  return reinterpret_cast<const float *>(x)[v * 128 + ch];
-}
-
-template <bool XBF16>
-__global__ __launch_bounds__(kSplitSlots * 128) void split_encode128_kernel(
-    const void *__restrict__ x, int64_t n, const float *__restrict__ mat,
+__global__ __launch_bounds__(kSplitWaves * 64) void split_encode128_kernel(
+    const void *__restrict__ x, int64_t n, const uint4 *__restrict__ frag, const float *__restrict__ mat,
     const int32_t *__restrict__ chan, int B0, int B1, int W, uint32_t *__restrict__ words,
     float *__restrict__ norms) {
-  constexpr int V = kSplitVPW;
-  __shared__ __attribute__((aligned(16))) float M[4][64][kSplitPad];  // Pi_0, S'_0, Pi_1, S'_1
-  __shared__ __attribute__((aligned(16))) float xs[2 * kSplitSlots][V][64], rs[2 * kSplitSlots][V][64];
+  __shared__ uint4 F[8][kSplitFragU4];  // Pi_0 hi, lo, S'_0 hi, lo, Pi_1 hi, lo, S'_1 hi, lo
+  __shared__ int chs[128];
   __shared__ float cbc[2][8], cbt[2][8];
-  for (int i = threadIdx.x; i < 4 * kSplitMat; i += blockDim.x) M[i >> 12][(i >> 6) & 63][i & 63] = mat[i];
+  for (int i = threadIdx.x; i < 8 * kSplitFragU4; i += blockDim.x) F[i / kSplitFragU4][i % kSplitFragU4] = frag[i];
+  if (threadIdx.x < 128) chs[threadIdx.x] = chan[threadIdx.x];
   if (threadIdx.x < 32) {
     const int t = threadIdx.x;
     const float v = mat[4 * kSplitMat + t];
@@ -2949,95 +2938,119 @@ __global__ __launch_bounds__(kSplitSlots * 128) void split_encode128_kernel(
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = wave & 1, slot = wave >> 1;
-  const int Bg = g ? B1 : B0;
-  const int nbnd = (1 << Bg) - 1;
-  const int off = g ? 2 * (B0 + 1) : 0;  // first word of this group's planes
-  const int ch = chan[64 * g + lane];
-  const float *Pr = &M[2 * g][lane][0], *Sr = &M[2 * g + 1][lane][0];
-  const int64_t stride = (int64_t)gridDim.x * kSplitSlots * V;
-  // the keys of the next iteration are requested while this one computes
-  // (a slot past the end repeats the last vector and is not stored)
-  float xn[V];
-  int64_t v0 = ((int64_t)blockIdx.x * kSplitSlots + slot) * V;
+  const int vcol = lane & 15, kg = lane >> 4;
+  const int64_t nbatch = (n + 15) / 16;
+  for (int64_t batch = (int64_t)blockIdx.x * kSplitWaves + wave; batch < nbatch;
+       batch += (int64_t)gridDim.x * kSplitWaves) {
+    const int64_t row = batch * 16 + vcol;
+    const bool valid = row < n;
+    const int64_t rr = valid ? row : n - 1;  // loads stay in bounds; results of rr != row are not stored
+#pragma unroll 1
+    for (int g = 0; g < 2; ++g) {
+      const int B = g ? B1 : B0;
+      const int nbnd = (1 << B) - 1;
+      const int off = g ? 2 * (B0 + 1) : 0;
+      const uint4 *Ph = F[4 * g] + lane, *Pl = F[4 * g + 1] + lane;
+      const uint4 *Sh = F[4 * g + 2] + lane, *Sl = F[4 * g + 3] + lane;
+      // B operand: the group's channels 32 kt + 8 kg + e of vector rr
+      uint4 xh[2], xl[2];
+      float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < V; ++i) xn[i] = v0 < n ? split_load_x<XBF16>(x, v0 + i < n ? v0 + i : n - 1, ch) : 0.f;
-  for (; v0 < n; v0 += stride) {
-    float xv[V], nu[V];
+      for (int kt = 0; kt < 2; ++kt) {
+        float v[8];
 #pragma unroll
-    for (int i = 0; i < V; ++i) xv[i] = xn[i];
-    const int64_t v1 = v0 + stride;
+        for (int e = 0; e < 8; ++e) {
+          const int c = chs[64 * g + 32 * kt + 8 * kg + e];
+          v[e] = XBF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(x)[rr * 128 + c] << 16)
+                       : reinterpret_cast<const float *>(x)[rr * 128 + c];
+          ss = fmaf(v[e], v[e], ss);
+        }
+        uint32_t h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < V; ++i) xn[i] = v1 < n ? split_load_x<XBF16>(x, v1 + i < n ? v1 + i : n - 1, ch) : 0.f;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      nu[i] = sqrtf(wave_sum(xv[i] * xv[i]));
-      xs[wave][i][lane] = xv[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    float y[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) y[i] = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < 64; k += 4) {
-      const float4 p4 = *reinterpret_cast<const float4 *>(Pr + k);
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const float4 x4 = *reinterpret_cast<const float4 *>(&xs[wave][i][k]);  // broadcast
-        y[i] = fmaf(p4.x, x4.x, fmaf(p4.y, x4.y, fmaf(p4.z, x4.z, fmaf(p4.w, x4.w, y[i]))));
+        for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
+        xh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
+        xl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
       }
-    }
-    int idx[V];
-    float rn[V];
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const float nu = sqrtf(ss);
+      f32x4 acc[4];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      // idx = number of boundaries at or below u = y / nu, decided on y against
-      // the scaled boundaries (a zero vector compares 0 with the unscaled ones)
-      int c = 0;
+      for (int nt = 0; nt < 4; ++nt) {
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 7; ++j)
-        if (j < nbnd) c += y[i] >= (nu[i] > 0.f ? cbt[g][j] * nu[i] : cbt[g][j]) ? 1 : 0;
-      idx[i] = c;
-      const float rho = y[i] - cbc[g][c] * nu[i];
-      rn[i] = sqrtf(wave_sum(rho * rho));
-      rs[wave][i][lane] = rho;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    float z[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) z[i] = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < 64; k += 4) {
-      const float4 s4 = *reinterpret_cast<const float4 *>(Sr + k);
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const float4 r4 = *reinterpret_cast<const float4 *>(&rs[wave][i][k]);  // broadcast
-        z[i] = fmaf(s4.x, r4.x, fmaf(s4.y, r4.y, fmaf(s4.z, r4.z, fmaf(s4.w, r4.w, z[i]))));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int64_t v = v0 + i;
-      uint64_t m[4];
-#pragma unroll
-      for (int p = 0; p < 3; ++p) m[p] = __builtin_amdgcn_ballot_w64(((idx[i] >> p) & 1) != 0);
-      m[3] = __builtin_amdgcn_ballot_w64(z[i] >= 0.f);
-      if (v < n) {
-        uint32_t *dst = words + v * W + off;
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-          if (p < Bg && lane < 2) dst[2 * p + lane] = (uint32_t)(lane ? m[p] >> 32 : m[p]);
-        if (lane < 2) dst[2 * Bg + lane] = (uint32_t)(lane ? m[3] >> 32 : m[3]);
-        if (lane == 0) {
-          norms[v * 4 + 2 * g] = nu[i];
-          norms[v * 4 + 2 * g + 1] = rn[i];
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 ah = as_bf16x8(Ph[(nt * 2 + kt) * 64]), al = as_bf16x8(Pl[(nt * 2 + kt) * 64]);
+          const bf16x8 bh = as_bf16x8(xh[kt]);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[nt], 0, 0, 0);
+          if (!XBF16) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(xl[kt]), acc[nt], 0, 0, 0);
         }
       }
+      // buckets (decided on y against the scaled boundaries; a zero vector
+      // compares 0 with the unscaled ones), index bits, residual
+      uint32_t pw[3] = {0u, 0u, 0u};
+      float rho[4][4], rsq = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = acc[nt][i];
+          int idx = 0;
+#pragma unroll
+          for (int j = 0; j < 7; ++j)
+            if (j < nbnd) idx += y >= (nu > 0.f ? cbt[g][j] * nu : cbt[g][j]) ? 1 : 0;
+#pragma unroll
+          for (int p = 0; p < 3; ++p) pw[p] |= (uint32_t)((idx >> p) & 1) << (4 * nt + i);
+          const float r = y - cbc[g][idx] * nu;
+          rsq = fmaf(r, r, rsq);
+          rho[nt][i] = r;
+        }
+      rsq += __shfl_xor(rsq, 16);
+      rsq += __shfl_xor(rsq, 32);
+      // Z = S' rho: K block kt element e of lane group kg = coordinate 32 kt + 16 (e / 4) + 4 kg + e % 4
+      uint4 rh[2], rl[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e0 = 2 * i, e1 = 2 * i + 1;
+          split2(rho[2 * kt + e0 / 4][e0 % 4], rho[2 * kt + e1 / 4][e1 % 4], h[i], l[i]);
+        }
+        rh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
+        rl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
+      }
+      uint32_t sw = 0u;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 ah = as_bf16x8(Sh[(nt * 2 + kt) * 64]), al = as_bf16x8(Sl[(nt * 2 + kt) * 64]);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(rh[kt]), z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(rl[kt]), z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, as_bf16x8(rh[kt]), z, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sw |= (z[i] >= 0.f ? 1u : 0u) << (4 * nt + i);
+      }
+      // two lane groups share a word: kg even takes the low half
+      uint32_t *dst = words + rr * W + off + (kg >> 1);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        if (p < B) {
+          const uint32_t o = __shfl_xor(pw[p], 16);
+          if (valid && !(kg & 1)) dst[2 * p] = pw[p] | o << 16;
+        }
+      }
+      const uint32_t os = __shfl_xor(sw, 16);
+      if (valid && !(kg & 1)) dst[2 * B] = sw | os << 16;
+      if (valid && kg == 0) {
+        norms[row * 4 + 2 * g] = nu;
+        norms[row * 4 + 2 * g + 1] = sqrtf(rsq);
+      }
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -3141,21 +3154,29 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
 #pragma unroll
       for (int p = 0; p < 3; ++p) pl[p] = p < B ? (half ? wd[off + 2 * p + 1] : wd[off + 2 * p]) : 0u;
       const uint32_t sw = half ? wd[off + 2 * B + 1] : wd[off + 2 * B];
-      const float4 *TIh = TI + half * (32 / S) * C;
+      // word `half` holds coordinates 16 t + 4 (2 half + kk) + i at bit 16 kk + 4 t + i
+      const float4 *TIh = TI + (8 * half / S) * C;
 #pragma unroll
-      for (int k = 0; k < 32 / S; ++k) {
-        uint32_t code = 0;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-          if (p < B) code |= ((pl[p] >> (S * k)) & ((1u << S) - 1u)) << (p * S);
-        const float4 t = TIh[k * C + code];
-        acc[gg].x += t.x; acc[gg].y += t.y; acc[gg].z += t.z; acc[gg].w += t.w;
-      }
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float4 t = TS[gg][8 * half + k][(sw >> (4 * k)) & 15u];
-        accs[gg].x += t.x; accs[gg].y += t.y; accs[gg].z += t.z; accs[gg].w += t.w;
-      }
+          for (int i0 = 0; i0 < 4; i0 += S) {
+            const int b0 = 16 * kk + 4 * t + i0;
+            uint32_t code = 0;
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+              if (p < B) code |= ((pl[p] >> b0) & ((1u << S) - 1u)) << (p * S);
+            const float4 tv = TIh[((16 * t + 4 * kk + i0) / S) * C + code];
+            acc[gg].x += tv.x; acc[gg].y += tv.y; acc[gg].z += tv.z; acc[gg].w += tv.w;
+          }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const float4 tv = TS[gg][4 * t + kk + 2 * half][(sw >> (16 * kk + 4 * t)) & 15u];
+          accs[gg].x += tv.x; accs[gg].y += tv.y; accs[gg].z += tv.z; accs[gg].w += tv.w;
+        }
     }
   };
   group(std::integral_constant<int, 0>{});
@@ -3180,14 +3201,17 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
 tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
                               tq_split_codes c, hipStream_t s) {
   const int W = 2 * (D.B[0] + 1 + D.B[1] + 1);
-  const int64_t need = (n + kSplitSlots * kSplitVPW - 1) / (kSplitSlots * kSplitVPW);
-  // about 100 KB of LDS per workgroup of 16 waves: one workgroup per CU
-  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device));
-  const int threads = kSplitSlots * 128;
+  const int64_t nbatch = (n + 15) / 16;
+  const int64_t need = (nbatch + kSplitWaves - 1) / kSplitWaves;
+  // 64 KB of fragments per workgroup of 16 waves: two workgroups per CU
+  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * 2);
+  const uint4 *fr = reinterpret_cast<const uint4 *>(D.frag);
   if (dtype == TQ_BF16)
-    split_encode128_kernel<true><<<grid, threads, 0, s>>>(x, n, D.mat, D.chan, D.B[0], D.B[1], W, c.words, c.norms);
+    split_encode128_kernel<true><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, D.B[0], D.B[1], W,
+                                                                    c.words, c.norms);
   else
-    split_encode128_kernel<false><<<grid, threads, 0, s>>>(x, n, D.mat, D.chan, D.B[0], D.B[1], W, c.words, c.norms);
+    split_encode128_kernel<false><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, D.B[0], D.B[1], W,
+                                                                     c.words, c.norms);
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }

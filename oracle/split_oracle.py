@@ -80,11 +80,16 @@ def score(q: np.ndarray, codes: list, p: SplitParams, n_kv: int, g: int, seq: in
 # Packed layout (a format, defined here and in include/tq.h), d = 128
 # ---------------------------------------------------------------------------
 # Per vector: uint32 words, group 0 then group 1; a group of B Lloyd-Max bits
-# holds B index planes then its sign plane, each plane two words (coordinate c
-# of the group at word c / 32, bit c % 32).  float32 norms [n][4]:
-# ||x_0||, ||r_0||, ||x_1||, ||r_1||.
+# holds B index planes then its sign plane, each plane two words: coordinate
+# c = 16 t + 4 k + i of the group (t, k, i < 4) at word k // 2, bit
+# 16 (k % 2) + 4 t + i.  float32 norms [n][4]: ||x_0||, ||r_0||, ||x_1||, ||r_1||.
 def words_per_vector(p: SplitParams) -> int:
     return 2 * (p.groups[0].B + 1 + p.groups[1].B + 1)
+
+
+def _word_bit(c: int):
+    t, k, i = c // 16, (c // 4) % 4, c % 4
+    return k // 2, 16 * (k % 2) + 4 * t + i
 
 
 def _plane_bits(bits: np.ndarray) -> np.ndarray:
@@ -92,13 +97,18 @@ def _plane_bits(bits: np.ndarray) -> np.ndarray:
     n = bits.shape[0]
     w = np.zeros((n, 2), dtype=np.uint64)
     for c in range(64):
-        w[:, c // 32] |= bits[:, c].astype(np.uint64) << np.uint64(c % 32)
+        wi, b = _word_bit(c)
+        w[:, wi] |= bits[:, c].astype(np.uint64) << np.uint64(b)
     return w.astype(np.uint32)
 
 
 def _plane_unbits(w: np.ndarray) -> np.ndarray:
     w = w.astype(np.uint64)
-    return np.stack([((w[:, c // 32] >> np.uint64(c % 32)) & np.uint64(1)).astype(bool) for c in range(64)], axis=1)
+    out = []
+    for c in range(64):
+        wi, b = _word_bit(c)
+        out.append(((w[:, wi] >> np.uint64(b)) & np.uint64(1)).astype(bool))
+    return np.stack(out, axis=1)
 
 
 def pack(codes: list, p: SplitParams) -> dict:
