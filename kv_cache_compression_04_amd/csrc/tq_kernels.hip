@@ -3062,7 +3062,7 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_encode128_kernel(
 // takes 2 sum - total).  A key then costs one gather and four adds per chunk.
 // The projections come from qproj_kernel (float64 sums).
 constexpr int kSplitScoreThreads = 256;
-constexpr int kSplitKPT = 4;  // keys per thread
+constexpr int kSplitKPT = 16;  // keys per thread (the tables amortised over 4096 keys)
 
 __host__ __device__ constexpr int split_chunk(int B) { return B >= 2 ? 2 : 4; }
 
@@ -3125,7 +3125,7 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
     SS[tid] = a;
   }
   __syncthreads();
-  // kSplitKPT keys per thread amortise the tables over 1024 keys
+  // kSplitKPT keys per thread amortise the tables
 #pragma unroll 1
   for (int r = 0; r < kSplitKPT; ++r) {
   const int64_t pos = ((int64_t)blockIdx.x * kSplitKPT + r) * kSplitScoreThreads + tid;
