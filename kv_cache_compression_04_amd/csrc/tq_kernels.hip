@@ -2758,6 +2758,7 @@ __global__ __launch_bounds__(kPolWaves * 64) void polar_encode128_kernel(
 // the logit <Pi q, y^>.  The rotated queries come from qproj_kernel (float64
 // sums).
 constexpr int kPolScoreThreads = 256;
+constexpr int kPolKPT = 8;  // keys per thread
 __global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
     const double *__restrict__ qt, const uint32_t *__restrict__ pq, const float *__restrict__ radius,
     int64_t seq, int64_t g, int ngroups, const PolarTables *__restrict__ T, float *__restrict__ logits) {
@@ -2787,8 +2788,11 @@ __global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
                            fmaf(c, qa.w, sn * qb.w));
   }
   __syncthreads();
-  const int64_t pos = (int64_t)blockIdx.x * kPolScoreThreads + tid;
-  if (pos >= seq) return;  // no barrier follows
+  // kPolKPT keys per thread amortise the level-1 table
+#pragma unroll 1
+  for (int kr = 0; kr < kPolKPT; ++kr) {
+  const int64_t pos = ((int64_t)blockIdx.x * kPolKPT + kr) * kPolScoreThreads + tid;
+  if (pos >= seq) break;  // no barrier follows
   const int64_t v = (int64_t)h * seq + pos;
   const uint4 *src = reinterpret_cast<const uint4 *>(pq + v * 12);
   const uint4 u0 = src[0], u1 = src[1], u2 = src[2];
@@ -2861,6 +2865,7 @@ __global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
     const int64_t qh = (int64_t)grp * 4 + j;
     if (qh < g) logits[((int64_t)h * g + qh) * seq + pos] = R * f7[j];
   }
+  }  // keys of this thread
 }
 
 tq_status launch_polar_encode(const Derived &D, const PolarTables *T, const void *x, int dtype,
@@ -2885,7 +2890,7 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
                              hipStream_t s) {
   const int ngroups = (int)((g + 3) / 4);
   const int64_t nhg = n_kv * ngroups;
-  const int64_t nblk = (seq + kPolScoreThreads - 1) / kPolScoreThreads;
+  const int64_t nblk = (seq + kPolKPT * kPolScoreThreads - 1) / (kPolKPT * kPolScoreThreads);
   if (nhg > 65535 || nblk > 0x7fffffffLL || n_kv * g > 0x7fffffffLL) {
     set_error("tq_polar_score: problem too large for one launch");
     return TQ_ERR_UNSUPPORTED;
