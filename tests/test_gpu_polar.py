@@ -100,7 +100,8 @@ def _check_logits(got, ref, q, radius, n_kv, g, seq):
     return worst
 
 
-@pytest.mark.parametrize("n_kv,g,seq", [(2, 4, 1000), (1, 5, 300), (3, 1, 257), (1, 4, 1)])
+# 5000 positions: two full workgroups of 2048 and a ragged third
+@pytest.mark.parametrize("n_kv,g,seq", [(2, 4, 1000), (1, 5, 300), (3, 1, 257), (1, 4, 1), (1, 4, 5000)])
 def test_polar_score_matches_oracle(n_kv, g, seq):
     """Oracle codes in, GPU logits out; and GPU codes in, checked against the
     oracle's estimator on those same codes."""

@@ -95,7 +95,9 @@ def _check_logits(got, ref, q, codes, n_kv, g, seq):
     return worst
 
 
-@pytest.mark.parametrize("b_rest,n_kv,g,seq", [(2, 2, 4, 1000), (3, 1, 5, 300), (2, 3, 1, 257), (3, 1, 4, 1)])
+# 9000 positions: two full workgroups of 4096 and a ragged third
+@pytest.mark.parametrize("b_rest,n_kv,g,seq", [(2, 2, 4, 1000), (3, 1, 5, 300), (2, 3, 1, 257), (3, 1, 4, 1),
+                                               (2, 1, 4, 9000)])
 def test_split_score_matches_oracle(b_rest, n_kv, g, seq):
     x = synth.llama_keys(heads=n_kv, seq=seq, seed=seq + g, dtype=torch.float32)
     xs = x.double().numpy()
