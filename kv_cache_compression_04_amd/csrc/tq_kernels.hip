@@ -2924,11 +2924,131 @@ constexpr int kSplitMat = 64 * 64;
 constexpr int kSplitWaves = 16;
 constexpr int kSplitFragU4 = 4 * 2 * 64;  // uint4 per 64 x 64 fragment half
 
-template <bool XBF16>
+// One channel group g with B Lloyd-Max bits for the wave's 16 vectors.
+template <bool XBF16, int B>
+__device__ __forceinline__ void split_encode_group(
+    const int g, const void *__restrict__ x, const int64_t rr, const int64_t row, const bool valid,
+    const int lane, const int kg, const uint4 (*F)[kSplitFragU4], const int *chs, const float (*cbc)[8],
+    const float (*cbt)[8], const int off, const int W, uint32_t *__restrict__ words,
+    float *__restrict__ norms) {
+  constexpr int nbnd = (1 << B) - 1;
+  const uint4 *Ph = F[4 * g] + lane, *Pl = F[4 * g + 1] + lane;
+  const uint4 *Sh = F[4 * g + 2] + lane, *Sl = F[4 * g + 3] + lane;
+  // B operand: the group's channels 32 kt + 8 kg + e of vector rr
+  uint4 xh[2], xl[2];
+  float ss = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = chs[64 * g + 32 * kt + 8 * kg + e];
+      v[e] = XBF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(x)[rr * 128 + c] << 16)
+                   : reinterpret_cast<const float *>(x)[rr * 128 + c];
+      ss = fmaf(v[e], v[e], ss);
+    }
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
+    xh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
+    xl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const float nu = sqrtf(ss);
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const bf16x8 ah = as_bf16x8(Ph[(nt * 2 + kt) * 64]), al = as_bf16x8(Pl[(nt * 2 + kt) * 64]);
+      const bf16x8 bh = as_bf16x8(xh[kt]);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[nt], 0, 0, 0);
+      if (!XBF16) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(xl[kt]), acc[nt], 0, 0, 0);
+    }
+  }
+  // buckets (decided on y against the boundaries scaled by ||x_g||; a zero
+  // vector compares 0 with the unscaled ones), index bits, residual
+  // y - c ||x_g|| with one rounding
+  float tb[nbnd], cv[nbnd + 1];
+#pragma unroll
+  for (int j = 0; j < nbnd; ++j) tb[j] = nu > 0.f ? cbt[g][j] * nu : cbt[g][j];
+#pragma unroll
+  for (int j = 0; j <= nbnd; ++j) cv[j] = cbc[g][j];
+  uint32_t pw[B];
+#pragma unroll
+  for (int p = 0; p < B; ++p) pw[p] = 0u;
+  float rho[4][4], rsq = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = acc[nt][i];
+      int idx = 0;
+      float cm = cv[0];
+#pragma unroll
+      for (int j = 0; j < nbnd; ++j) {  // the boundaries ascend
+        const bool ge = y >= tb[j];
+        idx += ge ? 1 : 0;
+        cm = ge ? cv[j + 1] : cm;
+      }
+#pragma unroll
+      for (int p = 0; p < B; ++p) pw[p] |= (uint32_t)((idx >> p) & 1) << (4 * nt + i);
+      const float r = fmaf(-cm, nu, y);
+      rsq = fmaf(r, r, rsq);
+      rho[nt][i] = r;
+    }
+  rsq += __shfl_xor(rsq, 16);
+  rsq += __shfl_xor(rsq, 32);
+  // Z = S' rho: K block kt element e of lane group kg = coordinate 32 kt + 16 (e / 4) + 4 kg + e % 4
+  uint4 rh[2], rl[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = 2 * i, e1 = 2 * i + 1;
+      split2(rho[2 * kt + e0 / 4][e0 % 4], rho[2 * kt + e1 / 4][e1 % 4], h[i], l[i]);
+    }
+    rh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
+    rl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+  uint32_t sw = 0u;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const bf16x8 ah = as_bf16x8(Sh[(nt * 2 + kt) * 64]), al = as_bf16x8(Sl[(nt * 2 + kt) * 64]);
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(rh[kt]), z, 0, 0, 0);
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(rl[kt]), z, 0, 0, 0);
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, as_bf16x8(rh[kt]), z, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sw |= (z[i] >= 0.f ? 1u : 0u) << (4 * nt + i);
+  }
+  // two lane groups share a word: kg even takes the low half
+  uint32_t *dst = words + rr * W + off + (kg >> 1);
+#pragma unroll
+  for (int p = 0; p < B; ++p) {
+    const uint32_t o = __shfl_xor(pw[p], 16);
+    if (valid && !(kg & 1)) dst[2 * p] = pw[p] | o << 16;
+  }
+  const uint32_t os = __shfl_xor(sw, 16);
+  if (valid && !(kg & 1)) dst[2 * B] = sw | os << 16;
+  if (valid && kg == 0) {
+    norms[row * 4 + 2 * g] = nu;
+    norms[row * 4 + 2 * g + 1] = sqrtf(rsq);
+  }
+}
+
+template <bool XBF16, int B0, int B1>
 __global__ __launch_bounds__(kSplitWaves * 64) void split_encode128_kernel(
     const void *__restrict__ x, int64_t n, const uint4 *__restrict__ frag, const float *__restrict__ mat,
-    const int32_t *__restrict__ chan, int B0, int B1, int W, uint32_t *__restrict__ words,
-    float *__restrict__ norms) {
+    const int32_t *__restrict__ chan, uint32_t *__restrict__ words, float *__restrict__ norms) {
+  constexpr int W = 2 * (B0 + 1 + B1 + 1);
   __shared__ uint4 F[8][kSplitFragU4];  // Pi_0 hi, lo, S'_0 hi, lo, Pi_1 hi, lo, S'_1 hi, lo
   __shared__ int chs[128];
   __shared__ float cbc[2][8], cbt[2][8];
@@ -2950,112 +3070,11 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_encode128_kernel(
     const int64_t row = batch * 16 + vcol;
     const bool valid = row < n;
     const int64_t rr = valid ? row : n - 1;  // loads stay in bounds; results of rr != row are not stored
-#pragma unroll 1
-    for (int g = 0; g < 2; ++g) {
-      const int B = g ? B1 : B0;
-      const int nbnd = (1 << B) - 1;
-      const int off = g ? 2 * (B0 + 1) : 0;
-      const uint4 *Ph = F[4 * g] + lane, *Pl = F[4 * g + 1] + lane;
-      const uint4 *Sh = F[4 * g + 2] + lane, *Sl = F[4 * g + 3] + lane;
-      // B operand: the group's channels 32 kt + 8 kg + e of vector rr
-      uint4 xh[2], xl[2];
-      float ss = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = chs[64 * g + 32 * kt + 8 * kg + e];
-          v[e] = XBF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(x)[rr * 128 + c] << 16)
-                       : reinterpret_cast<const float *>(x)[rr * 128 + c];
-          ss = fmaf(v[e], v[e], ss);
-        }
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
-        xh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
-        xl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
-      }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      const float nu = sqrtf(ss);
-      f32x4 acc[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 ah = as_bf16x8(Ph[(nt * 2 + kt) * 64]), al = as_bf16x8(Pl[(nt * 2 + kt) * 64]);
-          const bf16x8 bh = as_bf16x8(xh[kt]);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[nt], 0, 0, 0);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[nt], 0, 0, 0);
-          if (!XBF16) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(xl[kt]), acc[nt], 0, 0, 0);
-        }
-      }
-      // buckets (decided on y against the scaled boundaries; a zero vector
-      // compares 0 with the unscaled ones), index bits, residual
-      uint32_t pw[3] = {0u, 0u, 0u};
-      float rho[4][4], rsq = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float y = acc[nt][i];
-          int idx = 0;
-#pragma unroll
-          for (int j = 0; j < 7; ++j)
-            if (j < nbnd) idx += y >= (nu > 0.f ? cbt[g][j] * nu : cbt[g][j]) ? 1 : 0;
-#pragma unroll
-          for (int p = 0; p < 3; ++p) pw[p] |= (uint32_t)((idx >> p) & 1) << (4 * nt + i);
-          const float r = y - cbc[g][idx] * nu;
-          rsq = fmaf(r, r, rsq);
-          rho[nt][i] = r;
-        }
-      rsq += __shfl_xor(rsq, 16);
-      rsq += __shfl_xor(rsq, 32);
-      // Z = S' rho: K block kt element e of lane group kg = coordinate 32 kt + 16 (e / 4) + 4 kg + e % 4
-      uint4 rh[2], rl[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e0 = 2 * i, e1 = 2 * i + 1;
-          split2(rho[2 * kt + e0 / 4][e0 % 4], rho[2 * kt + e1 / 4][e1 % 4], h[i], l[i]);
-        }
-        rh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
-        rl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
-      }
-      uint32_t sw = 0u;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 ah = as_bf16x8(Sh[(nt * 2 + kt) * 64]), al = as_bf16x8(Sl[(nt * 2 + kt) * 64]);
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(rh[kt]), z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(rl[kt]), z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, as_bf16x8(rh[kt]), z, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sw |= (z[i] >= 0.f ? 1u : 0u) << (4 * nt + i);
-      }
-      // two lane groups share a word: kg even takes the low half
-      uint32_t *dst = words + rr * W + off + (kg >> 1);
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        if (p < B) {
-          const uint32_t o = __shfl_xor(pw[p], 16);
-          if (valid && !(kg & 1)) dst[2 * p] = pw[p] | o << 16;
-        }
-      }
-      const uint32_t os = __shfl_xor(sw, 16);
-      if (valid && !(kg & 1)) dst[2 * B] = sw | os << 16;
-      if (valid && kg == 0) {
-        norms[row * 4 + 2 * g] = nu;
-        norms[row * 4 + 2 * g + 1] = sqrtf(rsq);
-      }
-    }
+    split_encode_group<XBF16, B0>(0, x, rr, row, valid, lane, kg, F, chs, cbc, cbt, 0, W, words, norms);
+    __builtin_amdgcn_sched_barrier(0);
+    split_encode_group<XBF16, B1>(1, x, rr, row, valid, lane, kg, F, chs, cbc, cbt, 2 * (B0 + 1), W, words,
+                                  norms);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -3205,18 +3224,22 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
 
 tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
                               tq_split_codes c, hipStream_t s) {
-  const int W = 2 * (D.B[0] + 1 + D.B[1] + 1);
   const int64_t nbatch = (n + 15) / 16;
   const int64_t need = (nbatch + kSplitWaves - 1) / kSplitWaves;
   // 64 KB of fragments per workgroup of 16 waves: two workgroups per CU
   const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * 2);
   const uint4 *fr = reinterpret_cast<const uint4 *>(D.frag);
-  if (dtype == TQ_BF16)
-    split_encode128_kernel<true><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, D.B[0], D.B[1], W,
-                                                                    c.words, c.norms);
-  else
-    split_encode128_kernel<false><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, D.B[0], D.B[1], W,
-                                                                     c.words, c.norms);
+  const bool bf = dtype == TQ_BF16;
+  if (D.B[0] == 2 && D.B[1] == 1) {
+    if (bf) split_encode128_kernel<true, 2, 1><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, c.words, c.norms);
+    else split_encode128_kernel<false, 2, 1><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, c.words, c.norms);
+  } else if (D.B[0] == 3 && D.B[1] == 2) {
+    if (bf) split_encode128_kernel<true, 3, 2><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, c.words, c.norms);
+    else split_encode128_kernel<false, 3, 2><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, c.words, c.norms);
+  } else {
+    set_error("tq_split_encode: no kernel for Lloyd-Max bits (%d, %d)", D.B[0], D.B[1]);
+    return TQ_ERR_UNSUPPORTED;
+  }
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
