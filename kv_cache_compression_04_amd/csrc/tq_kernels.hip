@@ -2923,11 +2923,13 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
 constexpr int kSplitMat = 64 * 64;
 constexpr int kSplitWaves = 16;
 constexpr int kSplitFragU4 = 4 * 2 * 64;  // uint4 per 64 x 64 fragment half
+constexpr int kSplitRowB = 272;           // LDS bytes per staged bfloat16 row (256 + 16)
 
 // One channel group g with B Lloyd-Max bits for the wave's 16 vectors.
 template <bool XBF16, int B>
 __device__ __forceinline__ void split_encode_group(
-    const int g, const void *__restrict__ x, const int64_t rr, const int64_t row, const bool valid,
+    const int g, const void *__restrict__ x, const uint16_t *xrow, const int64_t rr, const int64_t row,
+    const bool valid,
     const int lane, const int kg, const uint4 (*F)[kSplitFragU4], const int *chs, const float (*cbc)[8],
     const float (*cbt)[8], const int off, const int W, uint32_t *__restrict__ words,
     float *__restrict__ norms) {
@@ -2943,8 +2945,7 @@ __device__ __forceinline__ void split_encode_group(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = chs[64 * g + 32 * kt + 8 * kg + e];
-      v[e] = XBF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(x)[rr * 128 + c] << 16)
-                   : reinterpret_cast<const float *>(x)[rr * 128 + c];
+      v[e] = XBF16 ? __uint_as_float((uint32_t)xrow[c] << 16) : reinterpret_cast<const float *>(x)[rr * 128 + c];
       ss = fmaf(v[e], v[e], ss);
     }
     uint32_t h[4], l[4];
@@ -3050,6 +3051,9 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_encode128_kernel(
     const int32_t *__restrict__ chan, uint32_t *__restrict__ words, float *__restrict__ norms) {
   constexpr int W = 2 * (B0 + 1 + B1 + 1);
   __shared__ uint4 F[8][kSplitFragU4];  // Pi_0 hi, lo, S'_0 hi, lo, Pi_1 hi, lo, S'_1 hi, lo
+  // bfloat16 keys: each wave's 16 rows, loaded whole (coalesced) and gathered
+  // from here; rows padded to 272 bytes to spread the gathers over the banks
+  __shared__ __attribute__((aligned(16))) unsigned char xs[XBF16 ? kSplitWaves : 1][16 * kSplitRowB];
   __shared__ int chs[128];
   __shared__ float cbc[2][8], cbt[2][8];
   for (int i = threadIdx.x; i < 8 * kSplitFragU4; i += blockDim.x) F[i / kSplitFragU4][i % kSplitFragU4] = frag[i];
@@ -3070,10 +3074,27 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_encode128_kernel(
     const int64_t row = batch * 16 + vcol;
     const bool valid = row < n;
     const int64_t rr = valid ? row : n - 1;  // loads stay in bounds; results of rr != row are not stored
-    split_encode_group<XBF16, B0>(0, x, rr, row, valid, lane, kg, F, chs, cbc, cbt, 0, W, words, norms);
+    const uint16_t *xrow = nullptr;
+    if constexpr (XBF16) {
+      // rows batch * 16 + r (clamped to n - 1, as rr is), 16 uint4 each; the
+      // previous batch's gathers are done before the rows are overwritten
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const uint4 *src = reinterpret_cast<const uint4 *>(x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = lane + 64 * i, r = q >> 4, c4 = q & 15;
+        const int64_t gr = batch * 16 + r < n ? batch * 16 + r : n - 1;
+        *reinterpret_cast<uint4 *>(&xs[wave][r * kSplitRowB + 16 * c4]) = src[gr * 16 + c4];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      xrow = reinterpret_cast<const uint16_t *>(&xs[wave][vcol * kSplitRowB]);
+    }
+    split_encode_group<XBF16, B0>(0, x, xrow, rr, row, valid, lane, kg, F, chs, cbc, cbt, 0, W, words, norms);
     __builtin_amdgcn_sched_barrier(0);
-    split_encode_group<XBF16, B1>(1, x, rr, row, valid, lane, kg, F, chs, cbc, cbt, 2 * (B0 + 1), W, words,
-                                  norms);
+    split_encode_group<XBF16, B1>(1, x, xrow, rr, row, valid, lane, kg, F, chs, cbc, cbt, 2 * (B0 + 1), W,
+                                  words, norms);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
