@@ -1,11 +1,14 @@
 """Comparison helpers for the GPU-vs-oracle parity tests (test code only).
 
 Tolerances (readings of the stated parity bar):
-  * index planes and sign bits are bit-exact, except where the decided point
+  * index planes and sign bits are bit-exact, except where the decided value
     lies within 1e-5 * ||x|| of its decision boundary: for an index, the
-    rotated coordinate ||x|| u_i against ||x|| t_j; for a sign bit, the
-    residual r against the hyperplane S_j . y = 0, i.e. |(S r)_j| / ||S_j||.
-    The fraction of such mismatches must stay below 1e-4.
+    rotated coordinate y_i = ||x|| u_i against ||x|| t_j; for a sign bit, the
+    raw projection z_j = (S r)_j against 0 (z on the S r scale, S with
+    N(0,1) entries, no normalisation by ||S_j||).  The fraction of
+    mismatched codes must stay below 1e-4.  Both the mismatch count and the
+    population of the window are reported, with the largest
+    distance-to-boundary / ||x|| among the mismatches.
   * logits computed from identical codes agree within
     1e-4 * max(|logit_ref|, ||q|| * knorm / sqrt(d)).
   * norms: knorm within 2e-6 relative.  rnorm = ||x|| ||u - c[idx]|| inherits
@@ -34,6 +37,39 @@ def to_numpy_codes(codes: dict) -> dict:
     return out
 
 
+def check_index_codes(u: np.ndarray, got_idx: np.ndarray, ref_idx: np.ndarray, t32: np.ndarray,
+                      stats: dict):
+    """Index codes: every mismatch within WINDOW (in units of ||x||) of a
+    boundary, mismatch fraction below MAX_MISMATCH_FRACTION."""
+    mism = got_idx != ref_idx
+    dist = np.min(np.abs(u[:, :, None] - t32.astype(np.float64)[None, None, :]), axis=2)
+    stats["idx_mismatch"] = int(mism.sum())
+    stats["idx_window"] = int((dist < WINDOW).sum())
+    stats["idx_codes"] = int(mism.size)
+    stats["idx_max_mis_dist"] = float(dist[mism].max()) if mism.any() else 0.0
+    bad = mism & (dist >= WINDOW)
+    assert not bad.any(), (f"{int(bad.sum())} index mismatches outside the boundary window "
+                           f"(largest distance {stats['idx_max_mis_dist']:.3e} x ||x||)")
+    assert mism.mean() < MAX_MISMATCH_FRACTION, f"index mismatch fraction {mism.mean()}"
+    return ~mism.any(axis=1)
+
+
+def check_sign_codes(z: np.ndarray, got_sign: np.ndarray, ref_sign: np.ndarray, knorm: np.ndarray,
+                     stats: dict):
+    """Sign bits: every mismatch has |z_j| < WINDOW * ||x|| (raw S r scale),
+    mismatch fraction below MAX_MISMATCH_FRACTION."""
+    smis = got_sign != ref_sign
+    zk = np.abs(z) / np.where(knorm > 0, knorm, 1.0)[:, None]
+    stats["sign_mismatch"] = int(smis.sum())
+    stats["sign_window"] = int((zk < WINDOW).sum())
+    stats["sign_codes"] = int(smis.size)
+    stats["sign_max_mis_zk"] = float(zk[smis].max()) if smis.any() else 0.0
+    bad = smis & (zk >= WINDOW)
+    assert not bad.any(), (f"{int(bad.sum())} sign mismatches outside the window "
+                           f"(largest |z|/||x|| {stats['sign_max_mis_zk']:.3e})")
+    assert smis.mean() < MAX_MISMATCH_FRACTION, f"sign mismatch fraction {smis.mean()}"
+
+
 def check_encode(x: np.ndarray, gpu_packed: dict, p: o.Params, report: dict = None):
     """Compare GPU-packed codes of the rows of x with the oracle's."""
     x = np.asarray(x, dtype=np.float64)
@@ -46,15 +82,8 @@ def check_encode(x: np.ndarray, gpu_packed: dict, p: o.Params, report: dict = No
     stats = {"n": n, "idx_mismatch": 0, "idx_window": 0, "sign_mismatch": 0}
     idx_rows_ok = np.ones(n, dtype=bool)
     if p.B > 0:
-        c32, t32 = p.codebook
-        mism = got["idx"] != ref["idx"]
-        stats["idx_mismatch"] = int(mism.sum())
-        dist = np.min(np.abs(ref["u"][:, :, None] - t32.astype(np.float64)[None, None, :]), axis=2)
-        stats["idx_window"] = int((dist < WINDOW).sum())
-        bad = mism & (dist >= WINDOW)
-        assert not bad.any(), f"{int(bad.sum())} index mismatches outside the boundary window"
-        assert mism.mean() < MAX_MISMATCH_FRACTION, f"index mismatch fraction {mism.mean()}"
-        idx_rows_ok = ~mism.any(axis=1)
+        _, t32 = p.codebook
+        idx_rows_ok = check_index_codes(ref["u"], got["idx"], ref["idx"], t32, stats)
     if p.prod:
         # the QJL stage of rows whose indices differ is checked against the
         # oracle's residual for the GPU's indices
@@ -65,13 +94,7 @@ def check_encode(x: np.ndarray, gpu_packed: dict, p: o.Params, report: dict = No
             rows = np.nonzero(~idx_rows_ok)[0]
             rs = o.residual_signs(x[rows], got["idx"][rows], p)
             z[rows], sign_ref[rows], rn_ref[rows] = rs["z"], rs["sign"], rs["rnorm"]
-        smis = got["sign"] != sign_ref
-        stats["sign_mismatch"] = int(smis.sum())
-        srow = np.linalg.norm(p.s, axis=1)
-        zrel = np.abs(z) / srow[None, :] / np.where(kn_ref > 0, kn_ref, 1.0)[:, None]
-        bad = smis & (zrel >= WINDOW)
-        assert not bad.any(), f"{int(bad.sum())} sign mismatches outside the window"
-        assert smis.mean() < MAX_MISMATCH_FRACTION, f"sign mismatch fraction {smis.mean()}"
+        check_sign_codes(z, got["sign"], sign_ref, kn_ref, stats)
         rn = got["rnorm"].astype(np.float64)
         tol = 2e-5 * kn_ref + 1e-6 * rn_ref
         assert np.all(np.abs(rn - rn_ref) <= tol), \

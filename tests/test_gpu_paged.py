@@ -83,10 +83,12 @@ def test_encode_slots_matches_oracle(dtype):
     assert np.all(got["sgn"][untouched] == np.uint32(0xFFFFFFFF))
 
 
-@pytest.mark.parametrize("lens,n_kv,g,kb,vb", [((1, 700, 1537), 2, 4, 3, 3), ((512, 513), 1, 5, 3, 3),
-                                                ((2048,), 2, 1, 3, 3), ((300, 1100), 2, 4, 2, 4),
-                                                ((64, 1030), 1, 8, 5, 1)])
-def test_attend_paged_matches_oracle(lens, n_kv, g, kb, vb):
+@pytest.mark.parametrize("lens,n_kv,g,kb,vb,scale", [((1, 700, 1537), 2, 4, 3, 3, None),
+                                                      ((512, 513), 1, 5, 3, 3, None),
+                                                      ((2048,), 2, 1, 3, 3, None), ((300, 1100), 2, 4, 2, 4, None),
+                                                      ((64, 1030), 1, 8, 5, 1, None),
+                                                      ((900, 1600), 2, 4, 3, 3, 0.37)])
+def test_attend_paged_matches_oracle(lens, n_kv, g, kb, vb, scale):
     KP = tq.Params(128, kb, 128, tq.MODE_PROD, 2, 3)
     VP = tq.Params(128, vb, 128, tq.MODE_MSE, 4, 0)
     batch = len(lens)
@@ -103,7 +105,7 @@ def test_attend_paged_matches_oracle(lens, n_kv, g, kb, vb):
         k = synth.llama_keys(heads=n_kv, seq=L, seed=20 + b, dtype=torch.float32).double().numpy()
         v = synth.llama_keys(heads=n_kv, seq=L, seed=40 + b, dtype=torch.float32).double().numpy()
         kc, vc = o.encode(k, okp), o.encode(v, ovp)
-        refs.append(o.attend(q[b], kc, vc, okp, ovp, 1, n_kv, g, L)[0])
+        refs.append(o.attend(q[b], kc, vc, okp, ovp, 1, n_kv, g, L, scale=scale)[0])
         for h in range(n_kv):
             sl = _slots(bt, b, h, n_kv, np.arange(L))
             _fill_store(kstore, KP, sl, {kk: vv[h * L:(h + 1) * L] for kk, vv in kc.items()})
@@ -113,12 +115,13 @@ def test_attend_paged_matches_oracle(lens, n_kv, g, kb, vb):
                      device=DEV)
     tq.attend_paged(KP, VP, torch.from_numpy(q.astype(np.float32)).to(DEV), batch, n_kv, g, kstore, vstore,
                     num_pages, torch.from_numpy(bt).to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
-                    out, ws)
+                    out, ws, scale=0.0 if scale is None else scale)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     for b in range(batch):
         worst = check_attend(got[b], refs[b])
-        print(f"[parity] attend_paged lens={lens} n_kv={n_kv} g={g} kb={kb} vb={vb} b={b}: worst/tol={worst:.4f}",
+        print(f"[parity] attend_paged lens={lens} n_kv={n_kv} g={g} kb={kb} vb={vb} scale={scale} b={b}: "
+              f"worst/tol={worst:.4f}",
               flush=True)
 
 

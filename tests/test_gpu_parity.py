@@ -154,21 +154,22 @@ def test_llama_layer_full_size(b):
 
 
 # ------------------------------------------------------------------ attend
-def _attend_case(kp, vp, batch, n_kv, g, seq, seed=0):
+def _attend_case(kp, vp, batch, n_kv, g, seq, seed=0, scale=None):
     okp, ovp = _oparams(kp), _oparams(vp)
     k = synth.llama_keys(heads=n_kv, seq=seq, seed=seed + 1, dtype=torch.float32, batch=batch).double().numpy()
     v = synth.llama_keys(heads=n_kv, seq=seq, seed=seed + 2, dtype=torch.float32, batch=batch).double().numpy()
     q = synth.queries(batch * n_kv * g, seed=seed + 5).numpy().astype(np.float64)
     kc, vc = o.encode(k, okp), o.encode(v, ovp)
-    ref = o.attend(q, kc, vc, okp, ovp, batch, n_kv, g, seq)
+    ref = o.attend(q, kc, vc, okp, ovp, batch, n_kv, g, seq, scale=scale)
     out = torch.full((batch, n_kv * g, kp.d), float("nan"), device=DEV)
     ws = torch.empty(tq.attend_workspace_bytes(kp, vp, batch, n_kv, g, seq), dtype=torch.uint8, device=DEV)
     tq.attend(kp, vp, torch.from_numpy(q.astype(np.float32)).to(DEV).reshape(batch, n_kv * g, kp.d),
-              batch, n_kv, g, _upload(o.pack(kc, okp)), _upload(o.pack(vc, ovp)), seq, out, ws)
+              batch, n_kv, g, _upload(o.pack(kc, okp)), _upload(o.pack(vc, ovp)), seq, out, ws,
+              scale=0.0 if scale is None else scale)
     torch.cuda.synchronize()
     worst = check_attend(out.cpu().numpy(), ref)
-    print(f"[parity] attend kb={kp.b} vb={vp.b} batch={batch} n_kv={n_kv} g={g} seq={seq}: worst/tol={worst:.4f}",
-          flush=True)
+    print(f"[parity] attend kb={kp.b} vb={vp.b} batch={batch} n_kv={n_kv} g={g} seq={seq} scale={scale}: "
+          f"worst/tol={worst:.4f}", flush=True)
 
 
 KP = tq.Params(128, 3, 128, tq.MODE_PROD, 2, 3)
@@ -179,6 +180,12 @@ VP = tq.Params(128, 3, 128, tq.MODE_MSE, 4, 0)
                                               (1, 1, 4, 512), (1, 2, 4, 4096)])
 def test_attend_shapes(batch, n_kv, g, seq):
     _attend_case(KP, VP, batch, n_kv, g, seq)
+
+
+@pytest.mark.parametrize("scale", [0.37, 0.02, 0.25])
+def test_attend_explicit_scale(scale):
+    """A caller-given softmax temperature on both sides (the default is 1/sqrt(d))."""
+    _attend_case(KP, VP, 1, 2, 4, 1500, seed=3, scale=scale)
 
 
 @pytest.mark.parametrize("kb,vb", [(1, 3), (2, 1), (4, 2), (5, 4), (3, 4), (4, 3)])

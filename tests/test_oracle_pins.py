@@ -378,3 +378,96 @@ def test_attend_with_a_dominant_key_returns_its_value():
     kc, vc = o.encode(k, kp), o.encode(v, vp)
     out = o.attend(q, kc, vc, kp, vp, 1, 1, 1, seq)
     assert np.allclose(out[0, 0], o.dequantize(vc, vp)[17], atol=1e-9)
+
+
+def _temperature_case(kp, vp, nus, vnus):
+    """Hand-built codes whose logits are known in closed form.
+
+    Query q = Pi^T 1, so Pi q is the all-ones vector.  Key j has every index in
+    the top bucket, knorm nus[j] and rnorm 0, so its logit is
+    nus[j] * c_top * d exactly (the QJL term vanishes with rnorm = 0).  Value j
+    has every index in the top bucket and knorm vnus[j], so its
+    reconstruction is vnus[j] * c_top_V * Pi_V^T 1.
+    """
+    d, n = kp.d, len(nus)
+    ctop_k = float(kp.codebook[0][-1])
+    ctop_v = float(vp.codebook[0][-1])
+    kc = {"idx": np.full((n, d), (1 << kp.B) - 1), "knorm": np.asarray(nus, np.float32),
+          "sign": np.ones((n, kp.m), bool), "rnorm": np.zeros(n, np.float32)}
+    vc = {"idx": np.full((n, d), (1 << vp.B) - 1), "knorm": np.asarray(vnus, np.float32)}
+    q = (kp.pi.T @ np.ones(d))[None, :]
+    logits = np.asarray(nus, np.float32).astype(np.float64) * ctop_k * d
+    return q, kc, vc, logits, ctop_v
+
+
+@pytest.mark.parametrize("scale", [None, 0.37, 0.05])
+def test_attend_temperature_closed_form(scale):
+    """softmax(scale * logit) with scale = 1/sqrt(d) by default, checked on 2
+    and 3 keys against the closed form: with Pi_V out = w . vnus * c_top * 1,
+    so each weight is read off one value at a time."""
+    kp = _params(b=3, seed_pi=2)
+    vp = _params(b=3, mode=o.MODE_MSE, seed_pi=4)
+    d = kp.d
+    s = 1.0 / math.sqrt(d) if scale is None else scale
+    ctop_k = float(kp.codebook[0][-1])
+    for gaps in ([0.0, 1.3], [0.0, 0.8, 2.1]):
+        # knorms chosen so that the scaled logits are close to `gaps`
+        nus = [gp / (s * ctop_k * d) for gp in gaps]
+        n = len(nus)
+        for j in range(n):
+            vnus = [1.0 if i == j else 0.0 for i in range(n)]
+            q, kc, vc, logits, ctop_v = _temperature_case(kp, vp, nus, vnus)
+            out = o.attend(q, kc, vc, kp, vp, 1, 1, 1, n, scale=scale)[0, 0]
+            e = np.exp(s * logits - np.max(s * logits))
+            w = e / e.sum()
+            rot = vp.pi @ out                     # Pi_V out = w_j * c_top_V * 1
+            assert np.allclose(rot, w[j] * ctop_v, rtol=1e-12, atol=1e-15), (gaps, j)
+        # a wrong temperature would move the weights: the check above has teeth
+        e_wrong = np.exp(logits / d - np.max(logits / d))
+        assert abs(e_wrong[-1] / e_wrong.sum() - w[-1]) > 1e-3
+
+
+def test_ip_error_bias_of_one_bit_mse_on_aligned_queries():
+    """mse mode, b = 1: for q = x/||x|| the normalised estimate is
+    <u, c[idx]> = c_1 ||u||_1, whose mean is d c_1^2 (the 1-bit shrinkage of
+    the MSE quantiser, 2/pi in the Gaussian limit); so the bias of ip_error is
+    d c_1^2 - 1 = -0.3609 at d = 128, with c_1 from the closed form
+    Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))."""
+    d = 128
+    p = _params(d=d, b=1, mode=o.MODE_MSE, seed_pi=21)
+    c1 = math.exp(math.lgamma(d / 2) - math.lgamma((d + 1) / 2)) / math.sqrt(math.pi)
+    rng = np.random.default_rng(31)
+    biases = []
+    for _ in range(200):
+        x = rng.standard_normal((1, d)) * rng.uniform(0.5, 3.0)
+        bias, rmse = o.ip_error(x, x / np.linalg.norm(x), p)
+        assert abs(abs(bias) - rmse) < 1e-12          # one pair: |bias| = rmse
+        biases.append(bias)
+    # the spread of c_1 ||u||_1 over random directions is ~ c_1 sqrt(d (1 - 2/pi)) / sqrt(d) ~ 0.04
+    assert abs(np.mean(biases) - (d * c1 * c1 - 1.0)) < 0.01
+
+
+def test_ip_error_rmse_of_pure_qjl_matches_closed_form_variance():
+    """prod mode, b = 1 (no MSE bits, r = x): for fixed q, x and S ~ N(0,1)^{m x d},
+    the estimator has mean <q, x> and variance ((pi/2) ||q||^2 ||x||^2 - <q,x>^2) / m,
+    so the normalised error has E[err^2] = (pi/2 - cos^2) / m.  Averaged over
+    independent draws of S (seeds) and pairs, ip_error's RMSE^2 matches the
+    mean of that closed form, and its bias is zero within sampling error."""
+    d, m = 128, 128
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((48, d)) * np.exp(0.5 * rng.standard_normal((48, 1)))
+    q = rng.standard_normal((24, d))
+    q[:6] = x[:6] + 0.3 * rng.standard_normal((6, d))          # a few correlated pairs
+    cos = (q @ x.T) / np.linalg.norm(q, axis=1)[:, None] / np.linalg.norm(x, axis=1)[None, :]
+    expect = float(np.mean((math.pi / 2 - cos ** 2) / m))
+    ms, bs = [], []
+    for seed in range(40):
+        p = _params(d=d, b=1, m=m, seed_s=1000 + seed)
+        bias, rmse = o.ip_error(x, q, p)
+        ms.append(rmse ** 2)
+        bs.append(bias)
+    # 40 draws of S x 1152 pairs: relative standard error of the mean square ~1-2%
+    assert abs(np.mean(ms) / expect - 1.0) < 0.06, (np.mean(ms), expect)
+    assert abs(np.mean(bs)) < 3 * math.sqrt(expect / (40 * 48))
+    # a dropped sqrt(pi/2) (or an m in place of sqrt(m)) is far outside that band
+    assert abs((2 / math.pi) * np.mean(ms) / expect - 1.0) > 0.2
