@@ -306,6 +306,31 @@ static double bf16_value(uint16_t h) {
   return (double)f;
 }
 
+// IEEE binary16 bits of v (round to nearest even, subnormals kept, |v| well
+// inside the finite range).
+static uint16_t f16_bits(double v) {
+  const uint16_t sign = std::signbit(v) ? 0x8000u : 0u;
+  double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  std::frexp(a, &e);                                  // a = f 2^e, f in [0.5, 1)
+  const int lsb = e - 11 < -24 ? -24 : e - 11;        // weight of the last kept bit
+  const double k = std::nearbyint(std::ldexp(a, -lsb));  // exact scaling, RNE
+  a = std::ldexp(k, lsb);
+  if (a < 0x1p-14) return (uint16_t)(sign | (uint16_t)k);  // subnormal (k < 1024)
+  std::frexp(a, &e);
+  const uint32_t field = (uint32_t)(e + 14);          // biased exponent of a in [2^(e-1), 2^e)
+  const uint32_t mant = (uint32_t)(std::ldexp(a, 11 - e) - 1024.0);
+  return (uint16_t)(sign | (field << 10) | mant);
+}
+
+static double f16_value(uint16_t h) {
+  const int field = (h >> 10) & 31, mant = h & 1023;
+  const double a = field == 0 ? std::ldexp((double)mant, -24)
+                              : std::ldexp((double)(mant + 1024), field - 25);
+  return (h & 0x8000u) ? -a : a;
+}
+
 // Split a 128 x 128 row-major double matrix into hi/lo bf16 fragments.
 // col_of(kt, lanegroup, e) gives the matrix column that element e of a lane
 // in lane group `lanegroup` holds within column block kt.
@@ -328,9 +353,32 @@ static void make_fragments(const std::vector<double> &mat, ColOf col_of,
         }
 }
 
-// Split an R x K row-major double matrix into the general-shape GEMM
-// fragments: uint4 [K/32 block kt][R/16 tile nt][hi, lo][lane], element e of
-// lane l = mat[16 nt + l % 16][col_of(kt, l / 16, e)].
+// The same fragment order with scale * mat split into fp16 hi + lo (the hi
+// part keeps 11 significant bits, the lo part the next 11, so hi + lo carries
+// scale * mat to about 2^-23 relative; the encode kernels take the power of
+// two `scale` back out of their results).
+template <typename ColOf>
+static void make_fragments_f16(const std::vector<double> &mat, double scale, ColOf col_of,
+                               std::vector<uint16_t> &hi, std::vector<uint16_t> &lo) {
+  hi.assign(kFragElems, 0);
+  lo.assign(kFragElems, 0);
+  size_t o = 0;
+  for (int nt = 0; nt < 8; ++nt)
+    for (int kt = 0; kt < 4; ++kt)
+      for (int l = 0; l < 64; ++l)
+        for (int e = 0; e < 8; ++e, ++o) {
+          const int row = 16 * nt + (l & 15);
+          const int col = col_of(kt, l >> 4, e);
+          const double v = scale * mat[(size_t)row * 128 + col];
+          const uint16_t h = f16_bits(v);
+          hi[o] = h;
+          lo[o] = f16_bits(v - f16_value(h));
+        }
+}
+
+// Split kEncScale * (an R x K row-major double matrix) into the general-shape
+// GEMM fragments, fp16 hi + lo: uint4 [K/32 block kt][R/16 tile nt][hi, lo][lane],
+// element e of lane l = mat[16 nt + l % 16][col_of(kt, l / 16, e)].
 template <typename ColOf>
 static void make_gemm_fragments(const std::vector<double> &mat, int R, int K, ColOf col_of,
                                 std::vector<uint4> &out) {
@@ -341,9 +389,9 @@ static void make_gemm_fragments(const std::vector<double> &mat, int R, int K, Co
       for (int l = 0; l < 64; ++l) {
         uint16_t h[8], lo[8];
         for (int e = 0; e < 8; ++e) {
-          const double v = mat[(size_t)(16 * nt + (l & 15)) * K + col_of(kt, l >> 4, e)];
-          h[e] = bf16_bits((float)v);
-          lo[e] = bf16_bits((float)(v - bf16_value(h[e])));
+          const double v = kEncScale * mat[(size_t)(16 * nt + (l & 15)) * K + col_of(kt, l >> 4, e)];
+          h[e] = f16_bits(v);
+          lo[e] = f16_bits(v - f16_value(h[e]));
         }
         uint4 vh, vl;
         std::memcpy(&vh, h, 16);
@@ -394,15 +442,20 @@ static tq_status build_derived(const tq_params *p, int dev, Derived *D) {
   if (is_d128(*p)) {
     std::vector<uint16_t> hi, lo;
     // GEMM 1 (Pi x): element e of lane group g in block kt is column 32 kt + 8 g + e
-    make_fragments(pi, [](int kt, int g, int e) { return 32 * kt + 8 * g + e; }, hi, lo);
+    const auto col1 = [](int kt, int g, int e) { return 32 * kt + 8 * g + e; };
+    make_fragments_f16(pi, kEncScale, col1, hi, lo);
+    if ((st = upload(&D->pi16_hi, hi)) || (st = upload(&D->pi16_lo, lo))) return st;
+    // (bf16 split of Pi for the PolarQuant encoder)
+    make_fragments(pi, col1, hi, lo);
     if ((st = upload(&D->pi_hi, hi)) || (st = upload(&D->pi_lo, lo))) return st;
     if (prod) {
       // S' is consumed against the residual held in the layout of the first
       // GEMM's output: element e of lane group g in block kt is coordinate
       // 32 kt + 16 (e / 4) + 4 g + e % 4.
-      make_fragments(sp, [](int kt, int g, int e) { return 32 * kt + 16 * (e / 4) + 4 * g + e % 4; },
-                     hi, lo);
-      if ((st = upload(&D->sp_hi, hi)) || (st = upload(&D->sp_lo, lo))) return st;
+      make_fragments_f16(sp, kEncScale,
+                         [](int kt, int g, int e) { return 32 * kt + 16 * (e / 4) + 4 * g + e % 4; }, hi,
+                         lo);
+      if ((st = upload(&D->sp16_hi, hi)) || (st = upload(&D->sp16_lo, lo))) return st;
     }
   } else {
     // same column maps, general shapes, K-block-major fragments
@@ -428,8 +481,10 @@ static void free_derived(Derived *D) {
   (void)hipFree(D->s64);
   (void)hipFree(D->pi_hi);
   (void)hipFree(D->pi_lo);
-  (void)hipFree(D->sp_hi);
-  (void)hipFree(D->sp_lo);
+  (void)hipFree(D->pi16_hi);
+  (void)hipFree(D->pi16_lo);
+  (void)hipFree(D->sp16_hi);
+  (void)hipFree(D->sp16_lo);
   (void)hipFree(D->pi_frag);
   (void)hipFree(D->sp_frag);
   (void)hipSetDevice(cur);

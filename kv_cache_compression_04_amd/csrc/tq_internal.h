@@ -55,12 +55,17 @@ struct Derived {
   float *s32 = nullptr;        // [m][d]   S
   double *pi64 = nullptr;      // the same in float64 (query preparation)
   double *s64 = nullptr;
-  uint16_t *pi_hi = nullptr;   // bf16 fragments of Pi for the encode GEMM
+  uint16_t *pi_hi = nullptr;   // bf16 fragments of Pi (PolarQuant encoder)
   uint16_t *pi_lo = nullptr;
-  uint16_t *sp_hi = nullptr;   // bf16 fragments of S' = S Pi^T
-  uint16_t *sp_lo = nullptr;
+  // fp16 fragments of kEncScale * Pi and kEncScale * S' (S' = S Pi^T) for the
+  // d = m = 128 encoder, hi + lo
+  uint16_t *pi16_hi = nullptr;
+  uint16_t *pi16_lo = nullptr;
+  uint16_t *sp16_hi = nullptr;
+  uint16_t *sp16_lo = nullptr;
   // General shapes (d, m multiples of 128 other than d = m = 128): GEMM
-  // fragments [K/32 block kt][16-row tile nt][hi, lo][lane] of uint4 (8 bf16).
+  // fragments [K/32 block kt][16-row tile nt][hi, lo][lane] of uint4 (8 fp16
+  // of kEncScale * the matrix).
   uint4 *pi_frag = nullptr;    // Pi,  d x d
   uint4 *sp_frag = nullptr;    // S',  m x d
 };
@@ -146,6 +151,14 @@ size_t split_score_workspace_bytes(int64_t nq);
 tq_status launch_split_score(const SplitDerived &D, const float *q, int64_t n_kv, int64_t g,
                              tq_split_codes codes, int64_t seq, float *logits, void *ws,
                              hipStream_t stream);
+
+// The encoders' fp16 matrix fragments hold kEncScale times the matrix (Pi,
+// S'), which keeps the lo parts of small entries out of the fp16 subnormals;
+// the kernels scale every input vector by a power of two so that its norm is
+// in [1, 2).  Both factors are powers of two, so they leave every decision
+// unchanged and come back out exactly.
+constexpr double kEncScale = 16.0;
+constexpr int kEncScaleLog2 = 4;
 
 // Fragment geometry of the d = m = 128 encode kernel: a 128 x 128 matrix is
 // stored as [16-row tile nt][32-column block kt][lane][8] bf16 values; lane l

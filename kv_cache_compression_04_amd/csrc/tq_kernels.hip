@@ -72,6 +72,32 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// two floats -> packed fp16, rounded toward zero (one v_cvt_pkrtz_f16_f32)
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// (a, b) -> packed fp16 hi and the packed fp16 of the remainders a - hi,
+// b - hi (exact in float32): hi + lo carries a, b to about 2^-21 relative
+__device__ __forceinline__ void split2h(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pk_f16(a, b);
+  const f16x2 h = __builtin_bit_cast(f16x2, hi);
+  lo = pk_f16(a - (float)h[0], b - (float)h[1]);
+}
+
+// Power-of-two scale of one encoded vector: with e the exponent of its norm
+// nu (nu = f 2^e, f in [0.5, 1)), the kernels feed x 2^(1-e) (norm in [1, 2))
+// to fp16 MFMAs against kEncScale times the matrices, so rotated coordinates
+// and residuals come out multiplied by 2^(kEncScaleLog2 + 1 - e).  Returns
+// that exponent (0 for a zero vector, whose inputs are all zero anyway).
+__device__ __forceinline__ int enc_scale_exp(float nu) {
+  return nu > 0.f ? kEncScaleLog2 + 1 - __builtin_amdgcn_frexp_expf(nu) : 0;
+}
+
 // w = 2 w + (bit of this lane in mask): one v_addc with the lane mask as
 // carry-in, which shifts a compare result into a packed word.
 __device__ __forceinline__ uint32_t shift_in(uint32_t w, uint64_t mask) {
@@ -90,15 +116,16 @@ constexpr int kEncBatch = 16 * kEncCT;  // vectors per wave batch
 constexpr int kFragU4 = kFragElems / 8;  // uint4 per fragment matrix (2048)
 
 // X^T fragment of one 16-vector column tile, column block kt: lane (v, g)
-// holds x[v][32 kt + 8 g .. + 7]; hi/lo bf16 split for float32 inputs.
+// holds x[v][32 kt + 8 g .. + 7], as loaded (8 bf16 in raw[0], or 8 float32
+// in raw[0], raw[1]), and adds their squares to sumsq.
 template <bool XBF16>
-__device__ __forceinline__ void load_x_frag(const void *__restrict__ x, int64_t row, bool valid,
-                                            int kt, int g, uint4 &hi, uint4 &lo, float &sumsq) {
+__device__ __forceinline__ void load_x_raw(const void *__restrict__ x, int64_t row, bool valid,
+                                           int kt, int g, uint4 (&raw)[2], float &sumsq) {
   if (XBF16) {
     const uint4 *p = reinterpret_cast<const uint4 *>(
         reinterpret_cast<const uint16_t *>(x) + row * 128 + 32 * kt + 8 * g);
-    hi = valid ? *p : make_uint4(0, 0, 0, 0);
-    const uint32_t w[4] = {hi.x, hi.y, hi.z, hi.w};
+    raw[0] = valid ? *p : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
     // squares of both bfloat16 halves in one v_dot2 each (the products are exact in float32)
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -107,16 +134,54 @@ __device__ __forceinline__ void load_x_frag(const void *__restrict__ x, int64_t 
       sumsq = __builtin_amdgcn_fdot2_f32_bf16(v, v, sumsq, false);
     }
   } else {
-    const float4 *p = reinterpret_cast<const float4 *>(
+    const uint4 *p = reinterpret_cast<const uint4 *>(
         reinterpret_cast<const float *>(x) + row * 128 + 32 * kt + 8 * g);
-    float4 a = valid ? p[0] : make_float4(0, 0, 0, 0);
-    float4 b = valid ? p[1] : make_float4(0, 0, 0, 0);
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    raw[0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
+    raw[1] = valid ? p[1] : make_uint4(0, 0, 0, 0);
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sumsq = fmaf(__uint_as_float(w[i]), __uint_as_float(w[i]), sumsq);
+  }
+}
+
+// bf16 MFMA operand of the same fragment (PolarQuant encoder): bf16 inputs
+// as they are, float32 inputs split hi/lo.
+template <bool XBF16>
+__device__ __forceinline__ void load_x_frag(const void *__restrict__ x, int64_t row, bool valid,
+                                            int kt, int g, uint4 &hi, uint4 &lo, float &sumsq) {
+  uint4 raw[2];
+  load_x_raw<XBF16>(x, row, valid, kt, g, raw, sumsq);
+  if (XBF16) {
+    hi = lo = raw[0];
+  } else {
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
     uint32_t h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sumsq += v[i] * v[i];
+    for (int i = 0; i < 4; ++i) split2(__uint_as_float(w[2 * i]), __uint_as_float(w[2 * i + 1]), h[i], l[i]);
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+}
+
+// The fp16 MFMA operand of a loaded fragment, scaled by 2^sh (exact): bf16
+// values fit fp16 exactly once the vector's norm is near 1; float32 values
+// become fp16 hi + lo.
+template <bool XBF16>
+__device__ __forceinline__ void x_frag_f16(const uint4 (&raw)[2], int sh, uint4 &hi, uint4 &lo) {
+  if (XBF16) {
+    const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+    uint32_t h[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
+    for (int i = 0; i < 4; ++i)
+      h[i] = pk_f16(ldexpf(__uint_as_float(w[i] << 16), sh), ldexpf(__uint_as_float(w[i] & 0xFFFF0000u), sh));
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = hi;
+  } else {
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      split2h(ldexpf(__uint_as_float(w[2 * i]), sh), ldexpf(__uint_as_float(w[2 * i + 1]), sh), h[i], l[i]);
     hi = make_uint4(h[0], h[1], h[2], h[3]);
     lo = make_uint4(l[0], l[1], l[2], l[3]);
   }
@@ -154,7 +219,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
     const int64_t v0 = batch * kEncBatch;
     uint4 xh[kEncCT][4], xl[kEncCT][4];
     float nu[kEncCT];
-    // the codebook is odd: magnitudes only, scaled by ||x||
+    int esh[kEncCT];
+    // the codebook is odd: magnitudes only, scaled by ||x|| 2^esh
     constexpr int kHalf = B > 0 ? 1 << (B - 1) : 1;
     float cp[kEncCT][kHalf], tp[kEncCT][kHalf > 1 ? kHalf - 1 : 1];
 #pragma unroll
@@ -162,19 +228,26 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
       const int64_t row = v0 + 16 * ct + vcol;
       const bool valid = row < n;
       float ss = 0.f;
+      uint4 raw[4][2];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) load_x_frag<XBF16>(x, row, valid, kt, g, xh[ct][kt], xl[ct][kt], ss);
+      for (int kt = 0; kt < 4; ++kt) load_x_raw<XBF16>(x, row, valid, kt, g, raw[kt], ss);
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
       nu[ct] = sqrtf(ss);
-      // the codebook scaled by ||x||: y = Pi x is compared with t_j ||x|| and the
-      // residual is formed as y - c ||x|| = ||x|| (u - c), so no division is
-      // needed; a zero vector gets y = 0 and a zero residual
+      // x enters the fp16 MFMAs as x 2^(1-e) (norm in [1, 2)) against
+      // kEncScale Pi, so y' = Pi x 2^esh; the codebook is scaled by the same
+      // ||x|| 2^esh: y' is compared with t_j ||x|| 2^esh and the residual is
+      // formed as y' - c ||x|| 2^esh = ||x|| 2^esh (u - c), with no division;
+      // a zero vector gets y' = 0 and a zero residual
+      esh[ct] = enc_scale_exp(nu[ct]);
+      const float nus = ldexpf(nu[ct], esh[ct]);
 #pragma unroll
-      for (int j = 0; j < kHalf; ++j) cp[ct][j] = B > 0 ? cb.c[kHalf + j] * nu[ct] : 0.f;
+      for (int kt = 0; kt < 4; ++kt) x_frag_f16<XBF16>(raw[kt], esh[ct] - kEncScaleLog2, xh[ct][kt], xl[ct][kt]);
+#pragma unroll
+      for (int j = 0; j < kHalf; ++j) cp[ct][j] = B > 0 ? cb.c[kHalf + j] * nus : 0.f;
       // (for a zero vector the unscaled boundaries reproduce the u = 0 decisions)
 #pragma unroll
-      for (int j = 0; j + 1 < kHalf; ++j) tp[ct][j] = nu[ct] > 0.f ? cb.t[kHalf + j] * nu[ct] : cb.t[kHalf + j];
+      for (int j = 0; j + 1 < kHalf; ++j) tp[ct][j] = nu[ct] > 0.f ? cb.t[kHalf + j] * nus : cb.t[kHalf + j];
     }
 
     // Coordinates are processed in 4 blocks of 32 (kt2).  For each block:
@@ -209,15 +282,15 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
         for (int kt = 0; kt < 4; ++kt) {                                                                                                    \
   _Pragma("unroll")                                                                                                                         \
           for (int h = 0; h < 2; ++h) {                                                                                                     \
-            const bf16x8 ah = as_bf16x8(Pk_[(h * 4 + kt) * 64]);                                                                            \
-            const bf16x8 al = as_bf16x8(Pk_[kFragU4 + (h * 4 + kt) * 64]);                                                                  \
+            const f16x8 ah = as_f16x8(Pk_[(h * 4 + kt) * 64]);                                                                              \
+            const f16x8 al = as_f16x8(Pk_[kFragU4 + (h * 4 + kt) * 64]);                                                                    \
   _Pragma("unroll")                                                                                                                         \
             for (int ct = 0; ct < kEncCT; ++ct) {                                                                                           \
-              const bf16x8 bh = as_bf16x8(xh[ct][kt]);                                                                                      \
-              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[h][ct], 0, 0, 0);                                            \
-              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[h][ct], 0, 0, 0);                                            \
+              const f16x8 bh = as_f16x8(xh[ct][kt]);                                                                                        \
+              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[h][ct], 0, 0, 0);                                             \
+              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[h][ct], 0, 0, 0);                                             \
               if (!XBF16)                                                                                                                   \
-                acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(xl[ct][kt]), acc[h][ct], 0, 0, 0);                       \
+                acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xl[ct][kt]), acc[h][ct], 0, 0, 0);                         \
             }                                                                                                                               \
           }                                                                                                                                 \
         }                                                                                                                                   \
@@ -256,21 +329,21 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
               rho[i] = r;                                                                                                                   \
             }                                                                                                                               \
   _Pragma("unroll")                                                                                                                         \
-            for (int hh = 0; hh < 2; ++hh) split2(rho[2 * hh], rho[2 * hh + 1], rh[ct][2 * h + hh], rl[ct][2 * h + hh]);                    \
+            for (int hh = 0; hh < 2; ++hh) split2h(rho[2 * hh], rho[2 * hh + 1], rh[ct][2 * h + hh], rl[ct][2 * h + hh]);                   \
           }                                                                                                                                 \
         }                                                                                                                                   \
         if (PROD) {                                                                                                                         \
   _Pragma("unroll")                                                                                                                         \
           for (int nt = 0; nt < 8; ++nt) {                                                                                                  \
-            const bf16x8 ah = as_bf16x8(Sk_[nt * 4 * 64]);                                                                                  \
-            const bf16x8 al = as_bf16x8(Sk_[kFragU4 + nt * 4 * 64]);                                                                        \
+            const f16x8 ah = as_f16x8(Sk_[nt * 4 * 64]);                                                                                    \
+            const f16x8 al = as_f16x8(Sk_[kFragU4 + nt * 4 * 64]);                                                                          \
   _Pragma("unroll")                                                                                                                         \
             for (int ct = 0; ct < kEncCT; ++ct) {                                                                                           \
-              const bf16x8 bh = as_bf16x8(make_uint4(rh[ct][0], rh[ct][1], rh[ct][2], rh[ct][3]));                                          \
-              const bf16x8 bl = as_bf16x8(make_uint4(rl[ct][0], rl[ct][1], rl[ct][2], rl[ct][3]));                                          \
-              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, (FIRST) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc2[nt][ct], 0, 0, 0);  \
-              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc2[nt][ct], 0, 0, 0);                                        \
-              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc2[nt][ct], 0, 0, 0);                                        \
+              const f16x8 bh = as_f16x8(make_uint4(rh[ct][0], rh[ct][1], rh[ct][2], rh[ct][3]));                                            \
+              const f16x8 bl = as_f16x8(make_uint4(rl[ct][0], rl[ct][1], rl[ct][2], rl[ct][3]));                                            \
+              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, (FIRST) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc2[nt][ct], 0, 0, 0);   \
+              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc2[nt][ct], 0, 0, 0);                                         \
+              acc2[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc2[nt][ct], 0, 0, 0);                                         \
             }                                                                                                                               \
           }                                                                                                                                 \
         }                                                                                                                                   \
@@ -319,7 +392,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
         if (PROD) sgn_out[orow * 4 + g] = sbits[ct];
         if (g == 0) {
           knorm_out[orow] = nu[ct];
-          if (PROD) rnorm_out[orow] = sqrtf(r2);
+          if (PROD) rnorm_out[orow] = ldexpf(sqrtf(r2), -esh[ct]);
         }
       }
     }
@@ -331,8 +404,8 @@ static void launch_encode_t(const Derived &D, const void *x, int dtype, int64_t 
                             tq_codes c, hipStream_t s, int grid, const int64_t *slots,
                             int64_t capacity) {
   const dim3 blk(kEncWaves * 64);
-  const uint4 *ph = (const uint4 *)D.pi_hi, *pl = (const uint4 *)D.pi_lo;
-  const uint4 *sh = (const uint4 *)D.sp_hi, *sl = (const uint4 *)D.sp_lo;
+  const uint4 *ph = (const uint4 *)D.pi16_hi, *pl = (const uint4 *)D.pi16_lo;
+  const uint4 *sh = (const uint4 *)D.sp16_hi, *sl = (const uint4 *)D.sp16_lo;
   if (dtype == TQ_BF16)
     encode128_kernel<B, PROD, true><<<grid, blk, 0, s>>>(x, n, ph, pl, sh, sl, D.cb, c.idx, c.sgn,
                                                          c.knorm, c.rnorm, slots, capacity);
@@ -465,7 +538,7 @@ __device__ __forceinline__ void gen_load_rho(const uint4 *__restrict__ rho, int6
 template <int B, bool PROD, bool XBF16>
 __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
     const void *__restrict__ x, int64_t n, int d, const uint4 *__restrict__ frag, Codebook cb,
-    uint32_t *__restrict__ idx_out, float *__restrict__ knorm_out, uint4 *__restrict__ rho,
+    uint32_t *__restrict__ idx_out, const float *__restrict__ knorm, uint4 *__restrict__ rho,
     float *__restrict__ rsq_part, int64_t stride) {
   __shared__ u32x4 As[2][kGStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -483,15 +556,21 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
     vok[ct] = vrow[ct] < n;
   }
   const uint4 *fbase = frag + (size_t)8 * mt * 128;
+  // the norms (from the norm pass) and each vector's power-of-two scale
+  float nu[kGCT];
+  int esh[kGCT];
+#pragma unroll
+  for (int ct = 0; ct < kGCT; ++ct) {
+    nu[ct] = vok[ct] ? knorm[vrow[ct]] : 0.f;
+    esh[ct] = enc_scale_exp(nu[ct]);
+  }
 
   // vector operand of one stage: lane (vcol, g) holds x[v][32 kt + 8 g .. + 7]
   constexpr int XU = XBF16 ? 1 : 2;
   u32x4 xr[kGCT][kGKB][XU], xn[kGCT][kGKB][XU];
   f32x4 acc[8][kGCT];
-  float ss[kGCT];
 #pragma unroll
   for (int ct = 0; ct < kGCT; ++ct) {
-    ss[ct] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -511,43 +590,28 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
     }
 #pragma unroll
     for (int kb = 0; kb < kGKB; ++kb) {
-      bf16x8 bh[kGCT], bl[kGCT];
+      f16x8 bh[kGCT], bl[kGCT];
 #pragma unroll
       for (int ct = 0; ct < kGCT; ++ct) {
-        if (XBF16) {
-          const u32x4 h = xr[ct][kb][0];
-          const uint32_t w[4] = {h[0], h[1], h[2], h[3]};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = bf16_to_f32(w[i] & 0xFFFFu), b = bf16_to_f32(w[i] >> 16);
-            ss[ct] += a * a + b * b;
-          }
-          bh[ct] = __builtin_bit_cast(bf16x8, h);
-          bl[ct] = bh[ct];
-        } else {
-          const u32x4 u0 = xr[ct][kb][0], u1 = xr[ct][kb][XU - 1];
-          const float v[8] = {__uint_as_float(u0[0]), __uint_as_float(u0[1]), __uint_as_float(u0[2]),
-                              __uint_as_float(u0[3]), __uint_as_float(u1[0]), __uint_as_float(u1[1]),
-                              __uint_as_float(u1[2]), __uint_as_float(u1[3])};
-          uint32_t h[4], l[4];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) ss[ct] += v[i] * v[i];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
-          bh[ct] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
-          bl[ct] = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
-        }
+        // x 2^(1-e) as fp16 (hi + lo for float32 inputs)
+        uint4 raw[2], h, l;
+        raw[0] = make_uint4(xr[ct][kb][0][0], xr[ct][kb][0][1], xr[ct][kb][0][2], xr[ct][kb][0][3]);
+        raw[1] = make_uint4(xr[ct][kb][XU - 1][0], xr[ct][kb][XU - 1][1], xr[ct][kb][XU - 1][2],
+                            xr[ct][kb][XU - 1][3]);
+        x_frag_f16<XBF16>(raw, esh[ct] - kEncScaleLog2, h, l);
+        bh[ct] = as_f16x8(h);
+        bl[ct] = as_f16x8(l);
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[cur][(kb * 8 + nt) * 128 + lane]);
-        const bf16x8 al = __builtin_bit_cast(bf16x8, As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
+        const f16x8 ah = __builtin_bit_cast(f16x8, As[cur][(kb * 8 + nt) * 128 + lane]);
+        const f16x8 al = __builtin_bit_cast(f16x8, As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
 #pragma unroll
         for (int ct = 0; ct < kGCT; ++ct) {
-          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[ct], acc[nt][ct], 0, 0, 0);
-          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[ct], acc[nt][ct], 0, 0, 0);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh[ct], acc[nt][ct], 0, 0, 0);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh[ct], acc[nt][ct], 0, 0, 0);
           if (!XBF16)
-            acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[ct], acc[nt][ct], 0, 0, 0);
+            acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[ct], acc[nt][ct], 0, 0, 0);
         }
       }
     }
@@ -564,18 +628,15 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue: acc[nt][ct][i] = ||x|| u at row 128 mt + 16 nt + 4 g + i
+  // ---- epilogue: acc[nt][ct][i] = ||x|| 2^esh u at row 128 mt + 16 nt + 4 g + i
 #pragma unroll
   for (int ct = 0; ct < kGCT; ++ct) {
-    float s2 = ss[ct];
-    s2 += __shfl_xor(s2, 16);
-    s2 += __shfl_xor(s2, 32);
-    const float nu = sqrtf(s2);
+    const float nus = ldexpf(nu[ct], esh[ct]);
     float cs[1 << B], ts[(1 << B) > 1 ? (1 << B) - 1 : 1];
 #pragma unroll
-    for (int j = 0; j < (1 << B); ++j) cs[j] = cb.c[j] * nu;
+    for (int j = 0; j < (1 << B); ++j) cs[j] = cb.c[j] * nus;
 #pragma unroll
-    for (int j = 0; j + 1 < (1 << B); ++j) ts[j] = nu > 0.f ? cb.t[j] * nu : cb.t[j];
+    for (int j = 0; j + 1 < (1 << B); ++j) ts[j] = nu[ct] > 0.f ? cb.t[j] * nus : cb.t[j];
     uint32_t planes[B > 0 ? B : 1];
 #pragma unroll
     for (int p = 0; p < (B > 0 ? B : 1); ++p) planes[p] = 0u;
@@ -613,7 +674,6 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
 #pragma unroll
       for (int p = 0; p < B; ++p) dst[p] = __builtin_bitreverse32(planes[p]);
     }
-    if (mt == 0 && g == 0 && vok[ct]) knorm_out[v] = nu;
     if (PROD) {
       rsq += __shfl_xor(rsq, 16);
       rsq += __shfl_xor(rsq, 32);
@@ -625,8 +685,8 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
         uint32_t h[4], l[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          split2(acc[2 * kk + hh][ct][0], acc[2 * kk + hh][ct][1], h[2 * hh], l[2 * hh]);
-          split2(acc[2 * kk + hh][ct][2], acc[2 * kk + hh][ct][3], h[2 * hh + 1], l[2 * hh + 1]);
+          split2h(acc[2 * kk + hh][ct][0], acc[2 * kk + hh][ct][1], h[2 * hh], l[2 * hh]);
+          split2h(acc[2 * kk + hh][ct][2], acc[2 * kk + hh][ct][3], h[2 * hh + 1], l[2 * hh + 1]);
         }
         uint4 *dst = rho + (((size_t)(4 * mt + kk) * stride + v) * 4 + g) * 2;
         dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
@@ -638,8 +698,8 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm1_kernel(
 
 __global__ __launch_bounds__(kGW * 64) void encode_gemm2_kernel(
     const uint4 *__restrict__ rho, const float *__restrict__ rsq_part, int64_t n, int64_t stride,
-    int d, int m, const uint4 *__restrict__ frag, uint32_t *__restrict__ sgn_out,
-    float *__restrict__ rnorm_out) {
+    int d, int m, const uint4 *__restrict__ frag, const float *__restrict__ knorm,
+    uint32_t *__restrict__ sgn_out, float *__restrict__ rnorm_out) {
   __shared__ u32x4 As[2][kGStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vcol = lane & 15, g = lane >> 4;
@@ -679,14 +739,14 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm2_kernel(
     for (int kb = 0; kb < kGKB; ++kb) {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[cur][(kb * 8 + nt) * 128 + lane]);
-        const bf16x8 al = __builtin_bit_cast(bf16x8, As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
+        const f16x8 ah = __builtin_bit_cast(f16x8, As[cur][(kb * 8 + nt) * 128 + lane]);
+        const f16x8 al = __builtin_bit_cast(f16x8, As[cur][(kb * 8 + nt) * 128 + 64 + lane]);
 #pragma unroll
         for (int ct = 0; ct < kGCT; ++ct) {
-          const bf16x8 bh = __builtin_bit_cast(bf16x8, xr[ct][kb][0]), bl = __builtin_bit_cast(bf16x8, xr[ct][kb][1]);
-          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[nt][ct], 0, 0, 0);
-          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[nt][ct], 0, 0, 0);
-          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[nt][ct], 0, 0, 0);
+          const f16x8 bh = __builtin_bit_cast(f16x8, xr[ct][kb][0]), bl = __builtin_bit_cast(f16x8, xr[ct][kb][1]);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[nt][ct], 0, 0, 0);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc[nt][ct], 0, 0, 0);
+          acc[nt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[nt][ct], 0, 0, 0);
         }
       }
     }
@@ -719,7 +779,7 @@ __global__ __launch_bounds__(kGW * 64) void encode_gemm2_kernel(
     if (mt == 0 && g == 0) {
       float r2 = 0.f;
       for (int j = 0; j < QT; ++j) r2 += rsq_part[v * QT + j];
-      rnorm_out[v] = sqrtf(r2);
+      rnorm_out[v] = ldexpf(sqrtf(r2), -enc_scale_exp(knorm[v]));
     }
   }
 }
@@ -730,16 +790,57 @@ size_t encode_workspace_bytes(const tq_params &p, int64_t n) {
   return (size_t)nc * (4 * (size_t)p.d + 4 * (size_t)(p.d / 128));
 }
 
+// Norms of the vectors of a chunk (general shapes), needed before the first
+// GEMM because they fix each vector's fp16 scale: one wave per vector,
+// float32 partial sums per lane combined across the wave.
+template <bool XBF16>
+__global__ __launch_bounds__(256) void vec_norm_kernel(const void *__restrict__ x, int64_t n, int d,
+                                                       float *__restrict__ knorm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (v >= n) return;  // wave-uniform
+  float ss = 0.f;
+  if (XBF16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + v * d);
+    for (int i = lane; i < d / 8; i += 64) {
+      const uint4 w = p[i];
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x2 b = __builtin_bit_cast(bf16x2, u[k]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(b, b, ss, false);
+      }
+    }
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + v * d);
+    for (int i = lane; i < d / 4; i += 64) {
+      const float4 a = p[i];
+      ss = fmaf(a.x, a.x, ss);
+      ss = fmaf(a.y, a.y, ss);
+      ss = fmaf(a.z, a.z, ss);
+      ss = fmaf(a.w, a.w, ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if (lane == 0) knorm[v] = sqrtf(ss);
+}
+
 template <int B, bool PROD>
 static void launch_gemm1_t(const Derived &D, const void *x, int dtype, int64_t n, tq_codes c,
                            uint4 *rho, float *rsq, int64_t stride, hipStream_t s) {
   const int64_t grid = (n + kGVec - 1) / kGVec * (D.p.d / 128);
-  if (dtype == TQ_BF16)
+  const unsigned ngrid = (unsigned)((n + 3) / 4);
+  if (dtype == TQ_BF16) {
+    vec_norm_kernel<true><<<dim3(ngrid), dim3(256), 0, s>>>(x, n, D.p.d, c.knorm);
     encode_gemm1_kernel<B, PROD, true><<<dim3((unsigned)grid), dim3(kGW * 64), 0, s>>>(
         x, n, D.p.d, D.pi_frag, D.cb, c.idx, c.knorm, rho, rsq, stride);
-  else
+  } else {
+    vec_norm_kernel<false><<<dim3(ngrid), dim3(256), 0, s>>>(x, n, D.p.d, c.knorm);
     encode_gemm1_kernel<B, PROD, false><<<dim3((unsigned)grid), dim3(kGW * 64), 0, s>>>(
         x, n, D.p.d, D.pi_frag, D.cb, c.idx, c.knorm, rho, rsq, stride);
+  }
 }
 
 static tq_status launch_encode_general(const Derived &D, const void *x, int dtype, int64_t n,
@@ -777,7 +878,7 @@ static tq_status launch_encode_general(const Derived &D, const void *x, int dtyp
     if (prod) {
       const int64_t grid = (nc + kGVec - 1) / kGVec * (m / 128);
       encode_gemm2_kernel<<<dim3((unsigned)grid), dim3(kGW * 64), 0, s>>>(
-          rho, rsq, nc, chunk, d, m, D.sp_frag, cc.sgn, cc.rnorm);
+          rho, rsq, nc, chunk, d, m, D.sp_frag, cc.knorm, cc.sgn, cc.rnorm);
       TQ_LAUNCH_CHECK();
     }
   }
@@ -796,7 +897,8 @@ tq_status launch_encode(const Derived &D, const void *x, int dtype, int64_t n, t
     set_error("tq_encode: workspace too small");
     return TQ_ERR_NO_MEMORY;
   }
-  if (D.p.mode == TQ_MODE_MSE && (n + kGVec - 1) / kGVec * (D.p.d / 128) > 0x7fffffffLL) {
+  if (D.p.mode == TQ_MODE_MSE &&
+      ((n + kGVec - 1) / kGVec * (D.p.d / 128) > 0x7fffffffLL || (n + 3) / 4 > 0x7fffffffLL)) {
     set_error("tq_encode: too many vectors for one launch");
     return TQ_ERR_UNSUPPORTED;
   }
