@@ -28,7 +28,8 @@
  *     the PolarQuant calls, one small table per device), built on the first
  *     call that needs them and freed by tq_release_cache().  The hot-path
  *     calls allocate nothing and record no memset (they can be captured in a
- *     HIP graph); scratch comes in through `workspace`.
+ *     HIP graph); scratch comes in through `workspace` (tq_attend_noalloc
+ *     uses the library's own device array instead, see there).
  *   - Sizes: d and m must be multiples of 128 in [128, 1024].  tq_encode,
  *     tq_score and tq_search take every such shape; tq_attend, tq_decode,
  *     tq_encode_slots and tq_attend_paged are built for d == 128 (and
@@ -172,6 +173,27 @@ tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
                     int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
                     tq_codes vcodes, int64_t seq, float scale, float *out,
                     void *workspace, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): tq_attend
+ * with the same arguments except the workspace, which is replaced by a
+ * file-scope device array of TQ_NOALLOC_SCRATCH_BYTES in the library (one per
+ * GPU, held until the process ends).  Calls no hipMalloc, hipFree or other
+ * allocating routine, records no memset, and needs nothing cleared.
+ *   - Sizes whose workspace (tq_attend_workspace_bytes) exceeds
+ *     TQ_NOALLOC_SCRATCH_BYTES return TQ_ERR_UNSUPPORTED (tq_last_error gives
+ *     the bytes needed); nothing is launched.
+ *   - The per-(parameters, device) cache of kp and vp must exist already on
+ *     the current device (TQ_ERR_INVALID_ARG otherwise): any earlier call with
+ *     the same parameters builds it, e.g. tq_encode of the keys and values.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one device (different streams, different host threads) race
+ *     and give wrong outputs.  Calls on one stream are ordered and safe.  */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+tq_status tq_attend_noalloc(const tq_params *kp, const tq_params *vp, const float *q,
+                            int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
+                            tq_codes vcodes, int64_t seq, float scale, float *out,
+                            void *stream);
 
 /* ---------------------------------------------------------------------------
  * Paged code cache for decoding.  The pages "TurboQuant压缩效果" (the kernel

@@ -495,6 +495,17 @@ typedef std::tuple<int, int, int, int, uint64_t, uint64_t, int> CacheKey;
 static std::mutex g_cache_mu;
 static std::map<CacheKey, Derived *> g_cache;
 
+const Derived *find_derived(const tq_params *p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  const int m = p->mode == TQ_MODE_PROD ? p->m : 0;
+  const uint64_t ss = p->mode == TQ_MODE_PROD ? p->seed_s : 0;
+  CacheKey key(p->d, p->b, m, p->mode, p->seed_pi, ss, dev);
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  auto it = g_cache.find(key);
+  return it == g_cache.end() ? nullptr : it->second;
+}
+
 tq_status get_derived(const tq_params *p, const Derived **out) {
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
@@ -1074,6 +1085,62 @@ tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
   if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)kp->d);
   return launch_attend(*K, *V, q, batch, n_kv, g, kcodes, vcodes, seq, scale, out,
                        workspace, (hipStream_t)stream);
+}
+
+tq_status tq_attend_noalloc(const tq_params *kp, const tq_params *vp, const float *q,
+                            int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
+                            tq_codes vcodes, int64_t seq, float scale, float *out, void *stream) {
+  tq_status st = check_params(kp);
+  if (st) return st;
+  if ((st = check_params(vp))) return st;
+  if (kp->mode != TQ_MODE_PROD || vp->mode != TQ_MODE_MSE || kp->d != vp->d) {
+    set_error("tq_attend_noalloc: keys must be prod mode, values mse mode, same d");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (batch < 0 || n_kv < 0 || g < 1 || seq < 0) {
+    set_error("tq_attend_noalloc: bad sizes");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (batch == 0 || n_kv == 0) return TQ_OK;
+  if (seq == 0) {
+    set_error("tq_attend_noalloc: softmax over an empty sequence");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (!q || !out) {
+    set_error("tq_attend_noalloc: NULL q/out");
+    return TQ_ERR_INVALID_ARG;
+  }
+  if ((st = check_codes(kp, kcodes)) || (st = check_codes(vp, vcodes))) return st;
+  if (!aligned16(q) || !aligned16(out)) {
+    set_error("tq_attend_noalloc: pointers must be 16-byte aligned");
+    return TQ_ERR_ALIGNMENT;
+  }
+  if (!is_d128(*kp) || !is_d128(*vp)) {
+    set_error("tq_attend_noalloc: device kernels are built for d = m = 128 only");
+    return TQ_ERR_UNSUPPORTED;
+  }
+  // scratch needed, against the fixed size of the device array
+  size_t need = 0;
+  if ((st = tq_attend_workspace_bytes(kp, vp, batch, n_kv, g, seq, &need))) return st;
+  if (need > kNoAllocScratchBytes) {
+    set_error("tq_attend_noalloc: these sizes need %zu bytes of scratch, more than the %zu bytes "
+              "of the no-allocation scratch array; use tq_attend with a caller workspace",
+              need, (size_t)kNoAllocScratchBytes);
+    return TQ_ERR_UNSUPPORTED;
+  }
+  // the parameter caches must exist already: building them allocates
+  const Derived *K = find_derived(kp), *V = find_derived(vp);
+  if (!K || !V) {
+    set_error("tq_attend_noalloc: the rotation/codebook cache of these parameters is not built on "
+              "this device; any earlier call with the same parameters (tq_encode of the keys and of "
+              "the values, tq_attend) builds it");
+    return TQ_ERR_INVALID_ARG;
+  }
+  void *ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)kp->d);
+  return launch_attend(*K, *V, q, batch, n_kv, g, kcodes, vcodes, seq, scale, out, ws,
+                       (hipStream_t)stream);
 }
 
 tq_status tq_encode_slots(const tq_params *p, const void *x, int32_t dtype, int64_t n,

@@ -77,6 +77,8 @@ inline bool is_d128(const tq_params &p) {
 
 // Returns the cache entry for (p, current device), building it on first use.
 tq_status get_derived(const tq_params *p, const Derived **out);
+// The cache entry if it exists already (allocates nothing), else nullptr.
+const Derived *find_derived(const tq_params *p);
 
 void set_error(const char *fmt, ...);
 
@@ -101,6 +103,12 @@ tq_status launch_attend(const Derived &K, const Derived &V, const float *q,
                         void *ws, hipStream_t stream, const int32_t *block_table = nullptr,
                         int64_t max_pages = 0, int64_t num_pages = 0,
                         const int32_t *seq_lens = nullptr);
+
+// Device address of this device's scratch array (tq_kernels.hip), looked up
+// once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = TQ_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+tq_status noalloc_scratch(void **ptr);
 
 tq_status launch_decode(const Derived &D, tq_codes codes, int64_t n, float *out,
                         hipStream_t stream);

@@ -33,6 +33,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "tq_internal.h"
@@ -2657,6 +2658,38 @@ tq_status launch_attend(const Derived &K, const Derived &V, const float *q, int6
       return TQ_ERR_UNSUPPORTED;
   }
   TQ_LAUNCH_CHECK();
+  return TQ_OK;
+}
+
+// ===========================================================================
+// Scratch of the no-allocation attention entry point: one file-scope device
+// array per GPU (the module's own copy on each device), used in place of a
+// caller workspace.  Host code never passes the array's name to a kernel: its
+// device address is looked up once per device with hipGetSymbolAddress (with
+// that device current) and kept here.  Nothing in it needs clearing: every
+// byte a call reads was written earlier in the same call.
+// ===========================================================================
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+tq_status noalloc_scratch(void **out) {
+  static std::mutex mu;
+  static void *ptr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("no usable HIP device for the scratch array");
+    return TQ_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_error("hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return TQ_ERR_HIP;
+    }
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
   return TQ_OK;
 }
 

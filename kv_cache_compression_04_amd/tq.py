@@ -63,7 +63,7 @@ class _Codes(ctypes.Structure):
 EXPORTS = ["tq_status_string", "tq_last_error", "tq_layout_version", "tq_make_codebook",
            "tq_codes_bytes", "tq_export_matrices", "tq_encode_workspace_bytes", "tq_encode",
            "tq_score_workspace_bytes",
-           "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_decode",
+           "tq_score", "tq_attend_workspace_bytes", "tq_attend", "tq_attend_noalloc", "tq_decode",
            "tq_search_workspace_bytes", "tq_search", "tq_encode_slots",
            "tq_attend_paged_workspace_bytes", "tq_attend_paged", "tq_polar_make_codebook", "tq_polar_encode",
            "tq_polar_score_workspace_bytes", "tq_polar_score", "tq_split_words", "tq_split_encode",
@@ -99,6 +99,7 @@ def lib():
             "tq_score": (ctypes.c_int, [P, vp, i64, i64, C, i64, vp, vp, sz, vp]),
             "tq_attend_workspace_bytes": (ctypes.c_int, [P, P, i64, i64, i64, i64, ctypes.POINTER(sz)]),
             "tq_attend": (ctypes.c_int, [P, P, vp, i64, i64, i64, C, C, i64, ctypes.c_float, vp, vp, sz, vp]),
+            "tq_attend_noalloc": (ctypes.c_int, [P, P, vp, i64, i64, i64, C, C, i64, ctypes.c_float, vp, vp]),
             "tq_decode": (ctypes.c_int, [P, C, i64, vp, vp]),
             "tq_search_workspace_bytes": (ctypes.c_int, [P, i64, i64, ctypes.c_int32, ctypes.POINTER(sz)]),
             "tq_search": (ctypes.c_int, [P, vp, i64, C, i64, ctypes.c_int32, vp, vp, vp, sz, vp]),
@@ -266,6 +267,19 @@ def attend(kp: Params, vp: Params, q, batch, n_kv, g, kcodes, vcodes, seq, out, 
                                         _codes(kcodes), _codes(vcodes), seq, scale, _ptr(out),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # TQ_NOALLOC_SCRATCH_BYTES
+
+
+def attend_noalloc(kp: Params, vp: Params, q, batch, n_kv, g, kcodes, vcodes, seq, out,
+                   scale: float = 0.0, stream=None):
+    """tq_attend without a workspace (the library's per-GPU scratch array):
+    q: [batch, n_kv*g, d] float32; out: [batch, n_kv*g, d] float32 (written)."""
+    assert q.is_contiguous() and out.is_contiguous()
+    _check("tq_attend_noalloc", lib().tq_attend_noalloc(ctypes.byref(kp.c()), ctypes.byref(vp.c()), _ptr(q),
+                                                        batch, n_kv, g, _codes(kcodes), _codes(vcodes), seq,
+                                                        scale, _ptr(out), _stream(stream)))
 
 
 def decode(p: Params, codes: dict, n: int, out, stream=None):
