@@ -162,13 +162,20 @@ tq_status tq_attend_workspace_bytes(const tq_params *kp, const tq_params *vp,
                                     int64_t batch, int64_t n_kv, int64_t g,
                                     int64_t seq, size_t *bytes);
 
-/* One decode step of attention over a compressed KV cache:
- *   p = softmax(scale * logits) over all seq positions (logits as tq_score),
+/* One decode step of attention over a compressed KV cache, the computation
+ * whose speed-up over 32-bit keys the yeyulingfeng.com explainer reports for
+ * 4-bit TurboQuant on H100 (section "TurboQuant：6倍压缩，零损失", and its
+ * caveat that the speed-up is for attention, not end-to-end inference): the
+ * logits are [P3] 非对称估计器 applied to the compressed keys (tq_score); the
+ * values are the MSE reconstructions of [P5] 第一阶段 (mse mode):
+ *   p = softmax(scale * logits) over all seq positions,
  *   out[b][h] = sum_n p_n * ||v_n|| * Pi_V^T c_V[idx_n].
+ * The softmax temperature is not on the pages: scale <= 0 selects the usual
+ * 1/sqrt(d).
  * kp: prod-mode parameters of the keys; vp: mse-mode parameters of the
  * values (same d).  q: device float [batch][n_kv*g][d]; kcodes / vcodes:
  * device, batch*n_kv*seq vectors each; out: device float [batch][n_kv*g][d].
- * scale <= 0 selects 1/sqrt(d).  workspace: device, >= the size above.     */
+ * workspace: device, >= the size above.                                  */
 tq_status tq_attend(const tq_params *kp, const tq_params *vp, const float *q,
                     int64_t batch, int64_t n_kv, int64_t g, tq_codes kcodes,
                     tq_codes vcodes, int64_t seq, float scale, float *out,
@@ -247,8 +254,10 @@ tq_status tq_decode(const tq_params *p, tq_codes codes, int64_t n, float *out,
 tq_status tq_search_workspace_bytes(const tq_params *p, int64_t nq, int64_t n,
                                     int32_t k, size_t *bytes);
 
-/* Top-k search over compressed vectors (vector search with the same
- * estimator as tq_score): for each of nq queries, the k database vectors of
+/* Top-k search over compressed vectors: the vector-search use the
+ * "TurboQuant压缩效果" transcript names beside the KV cache (compressing the
+ * memory of vector search engines), scored with the same estimator as
+ * tq_score ([P3] 非对称估计器): for each of nq queries, the k database vectors of
  * largest logit, in descending order, ties broken by the lower index.  The
  * logits are never materialised: workgroups keep running top-k lists over
  * segments of the database and a final pass merges them.

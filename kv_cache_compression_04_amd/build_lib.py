@@ -1,4 +1,6 @@
-"""Builds libtq.so (host C++ + gfx950 HIP kernels) in-tree with hipcc."""
+"""Builds libtq.so (host C++ + gfx950 HIP kernels) in-tree with hipcc, and a
+host-sanitizer build of the same library for the CPU tests."""
+import glob
 import os
 import shutil
 import subprocess
@@ -8,15 +10,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
-
-SOURCES = ["tq_host.cpp", "tq_kernels.hip"]
+KERNELS_OBJ = os.path.join(HERE, "tq_kernels.o")   # kept for the sanitizer build
+HOST_OBJ = os.path.join(HERE, "tq_host.o")
 
 # Device code is built for gfx950 only, without packed-fp32 instructions.
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for tq_host.cpp
+# (the host code only: every -fsanitize flag is behind -Xarch_host).
+SANITIZE = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def hipcc_path():
@@ -26,11 +32,7 @@ def hipcc_path():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [hipcc_path(), *FLAGS, "-I", os.path.join(ROOT, "include")]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd += ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,8 +43,43 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def _compile(src, obj, extra=(), verbose=False):
+    tmp = obj + ".tmp"
+    _run([hipcc_path(), *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src),
+          "-o", tmp], verbose)
+    os.replace(tmp, obj)
+
+
+def build(verbose: bool = False) -> str:
+    _compile("tq_kernels.hip", KERNELS_OBJ, verbose=verbose)
+    _compile("tq_host.cpp", HOST_OBJ, verbose=verbose)
+    tmp = LIB + ".tmp"
+    _run([hipcc_path(), *FLAGS, "-shared", HOST_OBJ, KERNELS_OBJ, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
+
+
+def sanitizer_runtime() -> str:
+    """The compiler's AddressSanitizer runtime, to preload into the process
+    that loads the sanitizer build."""
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/*/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+    return hits[-1]
+
+
+def build_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """libtq with tq_host.cpp built under ASan + UBSan (device code as in
+    build()), written to out_dir/libtq_asan.so."""
+    if not os.path.exists(KERNELS_OBJ):
+        _compile("tq_kernels.hip", KERNELS_OBJ, verbose=verbose)
+    host = os.path.join(out_dir, "tq_host_asan.o")
+    _compile("tq_host.cpp", host, extra=SANITIZE, verbose=verbose)
+    lib = os.path.join(out_dir, "libtq_asan.so")
+    _run([hipcc_path(), *FLAGS, *SANITIZE, "-shared", host, KERNELS_OBJ, "-o", lib], verbose)
+    return lib
 
 
 if __name__ == "__main__":

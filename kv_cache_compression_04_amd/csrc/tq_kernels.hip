@@ -90,6 +90,20 @@ __device__ __forceinline__ void split2h(float a, float b, uint32_t &hi, uint32_t
   lo = pk_f16(a - (float)h[0], b - (float)h[1]);
 }
 
+// Streaming accesses: packed codes that a call reads once and outputs it
+// writes once go through the non-temporal path, so they do not displace
+// reused data from the caches (measured: the 32-layer score call ~7% faster).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t nt_load(const uint32_t *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float nt_load(const float *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x2 nt_load2(const uint32_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+__device__ __forceinline__ u32x4 nt_load4(const uint32_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void nt_store(float *p, float v) { __builtin_nontemporal_store(v, p); }
+
 // Power-of-two scale of one encoded vector: with e the exponent of its norm
 // nu (nu = f 2^e, f in [0.5, 1)), the kernels feed x 2^(1-e) (norm in [1, 2))
 // to fp16 MFMAs against kEncScale times the matrices, so rotated coordinates
@@ -1007,134 +1021,203 @@ __device__ __forceinline__ int limb_of(int Q, int t) {
   return digit;
 }
 
-// Query preparation for the d = 128 kernels, one workgroup of 1024 threads
-// per (KV head, group of 4 queries):
-//   1. the rows of Pi (and S) are copied into LDS with coalesced loads;
-//   2. wave w takes query w % 4 and rows 64 (w / 4) .. + 63, one per lane,
-//      and forms qt = Pi q (rows < 128) or qs = S q (float32 partial sums of
-//      8 products, accumulated in float64); the query is wave-uniform, so it
-//      is read with scalar loads, and the row elements come from LDS with a
-//      padded stride (no bank conflicts);
-//   3. per query: the exponents that put the largest operand below 2^26, the
-//      per-query constants, and
-//   4. the int8 operands of the score MFMAs.  MFMA j (part j / 2, half j % 2;
+// Query preparation for the d = 128 kernels.  One workgroup of 4 waves takes
+// kQPGroups query groups of 4 queries (columns 4 group + query of an MFMA
+// tile; with one group per workgroup, the latency of a small call is that of
+// one group's work):
+//   1. each query is scaled by a power of two to norm [1, 2) and split into
+//      fp16 hi + lo (lane (column j, lane group g) holds coordinates
+//      32 kt + 8 g .. + 7 of query j, the encoder's operand layout);
+//   2. qt = Pi q on fp16 MFMAs against the encoder's fragments of 16 Pi (three
+//      passes: hi hi, lo hi, hi lo), wave w forming rotated rows 32 w .. + 31;
+//   3. qs = S q = S' qt (S' = S Pi^T) on the encoder's fragments of 16 S',
+//      the scaled qt coming back from LDS as the B operand, wave w forming
+//      rows 32 w .. + 31;
+//   4. per query: the exponents that put the largest operand below 2^26 and
+//      the per-query constants (float64 and float32);
+//   5. the int8 operands of the score MFMAs.  MFMA j (part j / 2, half j % 2;
 //      the sign part last) lane l = 16 kg + 4 jq + t holds limb t of query jq
 //      at the coordinates of lane group kg; one thread computes the 16 scaled
-//      values of (j, jq, kg) once and writes all four limbs.
-constexpr int kQprepThreads = 1024;
-constexpr int kQprepPad = 129;  // LDS row stride in floats: lane r reads bank (r + k) mod 64
+//      values of (group, j, jq, kg) once and writes all four limbs.
+// The projections carry ~2^-21 of ||q|| (fp16 hi + lo products, float32
+// accumulation), far below the operands' 26-bit quantisation step relative
+// to the logit scale.
+constexpr int kQPGroups = 1;  // query groups per workgroup (at most 4)
+constexpr int kQPThreads = 256;
 
 template <bool PROD>
-__global__ __launch_bounds__(kQprepThreads) void qprep128_kernel(
-    const float *__restrict__ q, int64_t g, int ngroups, const float *__restrict__ pi,
-    const float *__restrict__ s, Codebook cb, int m, i32x4 *__restrict__ aops,
-    QConst *__restrict__ qc) {
-  constexpr int NR = PROD ? 256 : 128;  // rows: Pi, then S
-  __shared__ float mat[NR][kQprepPad];
-  __shared__ double qvs[2][4][128];  // [0] = Pi q, [1] = S q
-  __shared__ int expo[4][2];
-  const int hg = blockIdx.x;
-  const int h = hg / ngroups, grp = hg % ngroups;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kQPThreads) void qprep128_kernel(
+    const float *__restrict__ q, int64_t g, int ngroups, int64_t nhg, const uint4 *__restrict__ pi_hi,
+    const uint4 *__restrict__ pi_lo, const uint4 *__restrict__ sp_hi, const uint4 *__restrict__ sp_lo,
+    Codebook cb, int m, i32x4 *__restrict__ aops, QConst *__restrict__ qc) {
+  __shared__ float qv[2][16][129];  // [0] = Pi q, [1] = S q, unscaled; column = 4 group + query
+  __shared__ float qts[16][129];    // Pi q scaled by 2^esh (the second product's operand)
+  __shared__ int expo[16][2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, lg = lane >> 4;
+  const int64_t hg0 = (int64_t)blockIdx.x * kQPGroups;
   {
-    constexpr int kPer = NR * 32 / kQprepThreads;  // float4 per thread
-    float4 buf[kPer];
+    const int64_t hg = hg0 + (col >> 2);
+    const int jq = col & 3;
+    const int64_t h = hg / ngroups, qh = (hg % ngroups) * 4 + jq;
+    const bool valid = (col >> 2) < kQPGroups && hg < nhg && qh < g;
+    const float *qrow = q + (h * g + (valid ? qh : 0)) * 128;
+    // the matrix fragments of this wave's rows, requested before anything else
+    uint4 fa[2][4][2], fs[2][4][2];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int f = tid + i * kQprepThreads;  // float4 index over the rows
-      const int r = f >> 5, c4 = f & 31;
-      buf[i] = reinterpret_cast<const float4 *>(r < 128 ? pi + r * 128 : s + (r - 128) * 128)[c4];
-    }
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int f = tid + i * kQprepThreads;
-      const int r = f >> 5, c4 = f & 31;
-      mat[r][4 * c4 + 0] = buf[i].x;
-      mat[r][4 * c4 + 1] = buf[i].y;
-      mat[r][4 * c4 + 2] = buf[i].z;
-      mat[r][4 * c4 + 3] = buf[i].w;
-    }
-  }
-  __syncthreads();
-  {
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int jq = wv & 3, r = (wv >> 2) * 64 + (tid & 63);
-    const int64_t qh = (int64_t)grp * 4 + jq;
-    if (r < NR && qh < g) {
-      // float32 partial sums of 8 products, added in float64: the error stays
-      // below 8 * 2^-24 of the sum of |products| (a few 1e-7 of |q|)
-      const float *qrow = q + ((int64_t)h * g + qh) * 128;  // wave-uniform
-      double acc = 0.0;
-#pragma unroll
-      for (int k0 = 0; k0 < 128; k0 += 8) {
-        float p = 0.f;
-#pragma unroll
-        for (int k = k0; k < k0 + 8; ++k) p = fmaf(mat[r][k], qrow[k], p);
-        acc += (double)p;
+      for (int kt = 0; kt < 4; ++kt) {
+        const int o = ((2 * wave + h2) * 4 + kt) * 64 + lane;
+        fa[h2][kt][0] = pi_hi[o];
+        fa[h2][kt][1] = pi_lo[o];
+        if (PROD) {
+          fs[h2][kt][0] = sp_hi[o];
+          fs[h2][kt][1] = sp_lo[o];
+        }
       }
-      qvs[r >> 7][jq][r & 127] = acc;
-    } else if (r < NR) {
-      qvs[r >> 7][jq][r & 127] = 0.0;
+    uint4 raw[4][2];
+    float ss = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(qrow + 32 * kt + 8 * lg);
+      raw[kt][0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
+      raw[kt][1] = valid ? p[1] : make_uint4(0, 0, 0, 0);
+      const uint32_t w[8] = {raw[kt][0].x, raw[kt][0].y, raw[kt][0].z, raw[kt][0].w,
+                             raw[kt][1].x, raw[kt][1].y, raw[kt][1].z, raw[kt][1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(__uint_as_float(w[i]), __uint_as_float(w[i]), ss);
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const int esh = enc_scale_exp(sqrtf(ss));  // rotated values come out times 2^esh
+    uint4 xh[4], xl[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) x_frag_f16<false>(raw[kt], esh - kEncScaleLog2, xh[kt], xl[kt]);
+    // 2. Pi q, rows 32 wave .. + 31
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int nt = 2 * wave + h2;
+      // three independent accumulation chains (one per pass), summed after
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const f16x8 ah = as_f16x8(fa[h2][kt][0]), al = as_f16x8(fa[h2][kt][1]);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xh[kt]), a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_f16x8(xh[kt]), a1, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xl[kt]), a2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * nt + 4 * lg + r;
+        const float v = a0[r] + (a1[r] + a2[r]);
+        qts[col][row] = v;
+        qv[0][col][row] = ldexpf(v, -esh);
+      }
+    }
+    if (PROD) {
+      __syncthreads();
+      // 3. S q = S' (Pi q): element e of lane group lg in block kt is rotated
+      // coordinate 32 kt + 16 (e / 4) + 4 lg + e % 4 (the S' fragments' order)
+      uint4 bh[4], bl[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = qts[col][32 * kt + 16 * (e >> 2) + 4 * lg + (e & 3)];
+        uint32_t hh[4], ll[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split2h(v[2 * i], v[2 * i + 1], hh[i], ll[i]);
+        bh[kt] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
+        bl[kt] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int nt = 2 * wave + h2;
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const f16x8 ah = as_f16x8(fs[h2][kt][0]), al = as_f16x8(fs[h2][kt][1]);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(bh[kt]), a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_f16x8(bh[kt]), a1, 0, 0, 0);
+          a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(bl[kt]), a2, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          qv[1][col][16 * nt + 4 * lg + r] = ldexpf(a0[r] + (a1[r] + a2[r]), -esh - kEncScaleLog2);
+      }
     }
   }
   __syncthreads();
   const int NP = cb.nparts;
-  if (tid < 256) {
-    // wave w reduces query w: max |qt|, max |qs|, sum qt, sum qs
-    const int jq = tid >> 6, lane = tid & 63;
-    double mq = fmax(fabs(qvs[0][jq][lane]), fabs(qvs[0][jq][lane + 64]));
-    double ms = PROD ? fmax(fabs(qvs[1][jq][lane]), fabs(qvs[1][jq][lane + 64])) : 0.0;
-    double sq = qvs[0][jq][lane] + qvs[0][jq][lane + 64];
-    double ss = PROD ? qvs[1][jq][lane] + qvs[1][jq][lane + 64] : 0.0;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      mq = fmax(mq, __shfl_xor(mq, off));
-      ms = fmax(ms, __shfl_xor(ms, off));
-      sq += __shfl_xor(sq, off);
-      ss += __shfl_xor(ss, off);
+  // 4. the waves reduce the 4 kQPGroups queries in turn (query c = 4 group +
+  // jq): max |qt|, max |qs|, sum qt, sum qs
+  {
+    double acoef = 0, amax = 0;
+    for (int p = 0; p < NP; ++p) {
+      acoef += cb.coef[p];
+      amax = fmax(amax, fabs(cb.coef[p]));
     }
-    if (lane == 0) {
-      double acoef = 0, amax = 0;
-      for (int p = 0; p < NP; ++p) {
-        acoef += cb.coef[p];
-        amax = fmax(amax, fabs(cb.coef[p]));
+#pragma unroll 1
+    for (int c = wave; c < 4 * kQPGroups; c += kQPThreads / 64) {
+      const int64_t hg = hg0 + (c >> 2);
+      const int jq = c & 3;
+      float mq = fmaxf(fabsf(qv[0][c][lane]), fabsf(qv[0][c][lane + 64]));
+      float ms = PROD ? fmaxf(fabsf(qv[1][c][lane]), fabsf(qv[1][c][lane + 64])) : 0.f;
+      double sq = (double)qv[0][c][lane] + (double)qv[0][c][lane + 64];
+      double sqs = PROD ? (double)qv[1][c][lane] + (double)qv[1][c][lane + 64] : 0.0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        mq = fmaxf(mq, __shfl_xor(mq, off));
+        ms = fmaxf(ms, __shfl_xor(ms, off));
+        sq += __shfl_xor(sq, off);
+        sqs += __shfl_xor(sqs, off);
       }
-      // scale the largest operand magnitude below 2^26
-      int e1 = 0, e2 = 0, k;
-      const double A1 = 2.0 * amax * mq, A2 = 2.0 * ms;
-      if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
-      if (A2 > 0) { frexp(A2, &k); e2 = 26 - k; }
-      expo[jq][0] = e1;
-      expo[jq][1] = e2;
-      const double cq = sqrt(M_PI / 2.0) / m;
-      QConst o;
-      o.idx_scale = ldexp(1.0, -e1);
-      o.idx_bias = acoef * sq;
-      o.sgn_scale = cq * ldexp(1.0, -e2);
-      o.sgn_bias = cq * ss;
-      o.f[0] = (float)o.idx_scale;
-      o.f[1] = (float)o.idx_bias;
-      o.f[2] = (float)o.sgn_scale;
-      o.f[3] = (float)o.sgn_bias;
-      qc[(int64_t)hg * 4 + jq] = o;
+      if (lane == 0) {
+        // scale the largest operand magnitude below 2^26
+        int e1 = 0, e2 = 0, k;
+        const double A1 = 2.0 * amax * (double)mq, A2 = 2.0 * (double)ms;
+        if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
+        if (A2 > 0) { frexp(A2, &k); e2 = 26 - k; }
+        expo[c][0] = e1;
+        expo[c][1] = e2;
+        if (hg < nhg) {
+          const double cq = sqrt(M_PI / 2.0) / m;
+          QConst o;
+          o.idx_scale = ldexp(1.0, -e1);
+          o.idx_bias = acoef * sq;
+          o.sgn_scale = cq * ldexp(1.0, -e2);
+          o.sgn_bias = cq * sqs;
+          o.f[0] = (float)o.idx_scale;
+          o.f[1] = (float)o.idx_bias;
+          o.f[2] = (float)o.sgn_scale;
+          o.f[3] = (float)o.sgn_bias;
+          qc[hg * 4 + jq] = o;
+        }
+      }
     }
   }
   __syncthreads();
+  // 5. operands: unit (group gi, j, jq, kg, w): word w of the four lanes 16 kg + 4 jq + t
   const int NMF = score_mfmas(NP, PROD);
   uint32_t *aw = reinterpret_cast<uint32_t *>(aops);
-  for (int i = tid; i < NMF * 64; i += kQprepThreads) {
-    // unit (j, jq, kg, w): word w of the four lanes 16 kg + 4 jq + t
-    const int j = i >> 6, jq = (i >> 4) & 3, kg = (i >> 2) & 3, w = i & 3;
+  for (int i = tid; i < kQPGroups * NMF * 64; i += kQPThreads) {
+    const int gi = i / (NMF * 64), u = i % (NMF * 64);
+    const int64_t hg = hg0 + gi;
+    if (hg >= nhg) continue;
+    const int j = u >> 6, jq = (u >> 4) & 3, kg = (u >> 2) & 3, w = u & 3;
     const bool sgnpart = j >= 2 * NP;
     const int sl = 4 * (j & 1) + w;
     const double coef = sgnpart ? 2.0 : 2.0 * cb.coef[j >> 1];
-    const int E = expo[jq][sgnpart ? 1 : 0];
-    const double *src = qvs[sgnpart ? 1 : 0][jq];
+    const int c = 4 * gi + jq;
+    const int E = expo[c][sgnpart ? 1 : 0];
+    const float *src = qv[sgnpart ? 1 : 0][c];
     uint32_t out[4] = {0u, 0u, 0u, 0u};  // limb t
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int c = 32 * e + 16 * (sl >> 2) + 4 * kg + (sl & 3);
-      int Q = (int)llrint(ldexp(coef * src[c], E - (sl & 3)));
+      const int cc = 32 * e + 16 * (sl >> 2) + 4 * kg + (sl & 3);
+      int Q = (int)llrint(ldexp(coef * (double)src[cc], E - (sl & 3)));
 #pragma unroll
       for (int t = 0; t < 4; ++t) {  // balanced base-128 digits, lowest first
         const int digit = ((Q + 64) & 127) - 64;
@@ -1143,15 +1226,17 @@ __global__ __launch_bounds__(kQprepThreads) void qprep128_kernel(
       }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) aw[(((int64_t)hg * NMF + j) * 64 + 16 * kg + 4 * jq + t) * 4 + w] = out[t];
+    for (int t = 0; t < 4; ++t) aw[((hg * NMF + j) * 64 + 16 * kg + 4 * jq + t) * 4 + w] = out[t];
   }
 }
 
 template <bool PROD>
 static void launch_qprep128(const Derived &D, const float *q, int64_t g, int ngroups, int64_t nhg,
                             i32x4 *aops, QConst *qc, hipStream_t s) {
-  qprep128_kernel<PROD><<<dim3((unsigned)nhg), dim3(kQprepThreads), 0, s>>>(q, g, ngroups, D.pi32, D.s32,
-                                                                       D.cb, D.p.m, aops, qc);
+  const unsigned grid = (unsigned)((nhg + kQPGroups - 1) / kQPGroups);
+  qprep128_kernel<PROD><<<dim3(grid), dim3(kQPThreads), 0, s>>>(
+      q, g, ngroups, nhg, (const uint4 *)D.pi16_hi, (const uint4 *)D.pi16_lo, (const uint4 *)D.sp16_hi,
+      (const uint4 *)D.sp16_lo, D.cb, D.p.m, aops, qc);
 }
 
 constexpr int kScoreU = 4;  // tiles per load batch (64 keys)
@@ -1180,22 +1265,22 @@ __device__ __forceinline__ void score_load_full(ScoreBatch<(B > 0 ? B : 1)> &b,
   for (int u = 0; u < kScoreU; ++u) {
     const uint32_t *ip = idx_t + (uint32_t)(u * 64 * BB) + off_idx;
     if constexpr (B == 1) {
-      b.pl[u][0] = ip[0];
+      b.pl[u][0] = nt_load(ip);
     } else if constexpr (B == 2) {
-      const uint2 t = *reinterpret_cast<const uint2 *>(ip);
+      const u32x2 t = nt_load2(ip);
       b.pl[u][0] = t.x; b.pl[u][1] = t.y;
     } else if constexpr (B == 3) {
-      b.pl[u][0] = ip[0]; b.pl[u][1] = ip[1]; b.pl[u][2] = ip[2];
+      b.pl[u][0] = nt_load(ip); b.pl[u][1] = nt_load(ip + 1); b.pl[u][2] = nt_load(ip + 2);
     } else if constexpr (B == 4) {
-      const uint4 t = *reinterpret_cast<const uint4 *>(ip);
+      const u32x4 t = nt_load4(ip);
       b.pl[u][0] = t.x; b.pl[u][1] = t.y; b.pl[u][2] = t.z; b.pl[u][3] = t.w;
     } else {
       b.pl[u][0] = 0u;
     }
-    b.sw[u] = PROD ? sgn_t[(uint32_t)(u * 64) + off_sgn] : 0u;
+    b.sw[u] = PROD ? nt_load(&sgn_t[(uint32_t)(u * 64) + off_sgn]) : 0u;
   }
-  b.kn = kn_t[lane];
-  b.rn = PROD ? rn_t[lane] : 0.f;
+  b.kn = nt_load(&kn_t[lane]);
+  b.rn = PROD ? nt_load(&rn_t[lane]) : 0.f;
 }
 
 template <int B, bool PROD, int NP>
@@ -1218,7 +1303,7 @@ __device__ __forceinline__ void score_store_full(const ScoreBatch<(B > 0 ? B : 1
   }
   if (qvalid) {
 #pragma unroll
-    for (int u = 0; u < kScoreU; ++u) out_t[u * 16] = l[u];
+    for (int u = 0; u < kScoreU; ++u) nt_store(&out_t[u * 16], l[u]);
   }
 }
 
@@ -2250,10 +2335,10 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
       for (int u = 0; u < kAttU; ++u) {
         const uint32_t vp = min((uint32_t)((t0 + u) * 16 + c16), last);
 #pragma unroll
-        for (int p = 0; p < BK; ++p) planes[u][p] = ki[(vp * 4u + kg) * BKK + p];
-        sw[u] = ks[vp * 4u + kg];
-        kv[u] = kn[vp];
-        rv[u] = rn[vp];
+        for (int p = 0; p < BK; ++p) planes[u][p] = nt_load(&ki[(vp * 4u + kg) * BKK + p]);
+        sw[u] = nt_load(&ks[vp * 4u + kg]);
+        kv[u] = nt_load(&kn[vp]);
+        rv[u] = nt_load(&rn[vp]);
       }
 #pragma unroll
       for (int u = 0; u < kAttU; ++u) {
@@ -2290,7 +2375,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
         const uint32_t pos = (uint32_t)pl;
         const float pe = pl < npos ? __expf(lvv[e] - m) : 0.f;
         lsum += pe;
-        wv[e] = pe * vn[min(pos, last)];
+        wv[e] = pe * nt_load(&vn[min(pos, last)]);
         wmax = fmaxf(wmax, wv[e]);
       }
       *reinterpret_cast<float4 *>(&lg[wave][kg][pl0]) = make_float4(wv[0], wv[1], wv[2], wv[3]);
@@ -2345,14 +2430,14 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
         const uint32_t *src =
             reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(vi) + (__umul24(pos, 16u * BV) + woff));
         if constexpr (BV == 2) {
-          const uint2 t2 = *reinterpret_cast<const uint2 *>(src);
+          const u32x2 t2 = nt_load2(src);
           x[gi][e][0] = t2.x; x[gi][e][1] = t2.y;
         } else if constexpr (BV == 4) {
-          const uint4 t4 = *reinterpret_cast<const uint4 *>(src);
+          const u32x4 t4 = nt_load4(src);
           x[gi][e][0] = t4.x; x[gi][e][1] = t4.y; x[gi][e][2] = t4.z; x[gi][e][3] = t4.w;
         } else {
 #pragma unroll
-          for (int p = 0; p < BV; ++p) x[gi][e][p] = src[p];
+          for (int p = 0; p < BV; ++p) x[gi][e][p] = nt_load(src + p);
         }
       }
     {

@@ -14,7 +14,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# TQ_LIBRARY names another build of the same library (the host-sanitizer
+# build of build_lib.build_sanitized); there is no fallback when it is missing.
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(_HERE, "libtq.so")
 
 MODE_PROD = 0
 MODE_MSE = 1

@@ -7,7 +7,10 @@ Checks that hold at any size, plus the oracle on sampled outputs:
   logits within the logit tolerance;
 * every returned vector of those queries is re-encoded by the oracle, and its
   oracle logit matches the returned value wherever the oracle encodes that
-  vector identically.
+  vector identically (at most 2 may encode differently, each difference
+  inside the parity window);
+* the oracle's own top-10 of those queries over the whole store, scored on
+  the stored codes, equals the returned set up to swaps within tolerance.
 """
 import math
 
@@ -57,6 +60,11 @@ def test_search_database_scale():
     torch.cuda.synchronize()
     kn = codes["knorm"]
     gi, gv = out_idx[qs], out_val[qs]
+    # pools for the oracle check below: each sampled query's 2000 best codes by
+    # the full logit row, and the row's 2000th logit
+    POOL = 2000
+    pool_top = torch.topk(logits, POOL, dim=1)
+    pool_idx, pool_floor = pool_top.indices.cpu().numpy(), pool_top.values[:, -1].cpu().numpy()
     for r in range(len(qs)):
         row, ids, vals = logits[r], gi[r], gv[r]
         assert int(torch.unique(ids).numel()) == K and int(ids.min()) >= 0 and int(ids.max()) < N
@@ -86,6 +94,17 @@ def test_search_database_scale():
     gcodes = {kk: v[torch.from_numpy(cand).to(DEV)] for kk, v in codes.items() if v is not None}
     gc = o.unpack(to_numpy_codes(gcodes), op)
     same = np.all(gc["idx"] == cref["idx"], axis=1) & np.all(gc["sign"] == cref["sign"], axis=1)
+    # returned vectors whose codes differ from the oracle's are few, and each
+    # of their differing decisions lies inside the parity window
+    assert int((~same).sum()) <= 2, f"{int((~same).sum())} of {len(cand)} returned vectors encode differently"
+    _, t32 = op.codebook
+    for i in np.nonzero(~same)[0]:
+        imis = gc["idx"][i] != cref["idx"][i]
+        dist = np.min(np.abs(cref["u"][i][:, None] - t32.astype(np.float64)[None, :]), axis=1)
+        assert np.all(dist[imis] < 1e-5), "index mismatch outside the window"
+        rs = o.residual_signs(xs[i:i + 1], gc["idx"][i:i + 1], op)
+        smis = gc["sign"][i] != rs["sign"][0]
+        assert np.all(np.abs(rs["z"][0][smis]) < 1e-5 * float(cref["knorm"][i])), "sign mismatch outside the window"
     pos = {int(v): i for i, v in enumerate(cand)}
     qn_all = q[qs].double().cpu().numpy()
     giv, gvv = gi.cpu().numpy(), gv.cpu().numpy()
@@ -100,3 +119,29 @@ def test_search_database_scale():
             assert abs(float(gvv[r, j]) - lref[i]) <= tol
     print(f"[parity] search over {N} vectors: top-{K} of {len(qs)} sampled queries consistent; "
           f"{int(same.sum())}/{len(cand)} returned vectors encode identically", flush=True)
+
+    # The oracle's top-k over the whole store, from the GPU's codes: the
+    # oracle scores (oracle.score on oracle.unpack of the stored codes) each
+    # query's pool of the 2000 codes of largest tq_score logit.  Every code
+    # outside the pool has a tq_score logit below the pool's 2000th, and
+    # tq_score agrees with the oracle's estimator to the logit tolerance, so
+    # the pool holds the oracle's whole top-k once its k-th oracle logit
+    # clears the pool floor by twice the tolerance (asserted).
+    kn_all = codes["knorm"]
+    for r in range(len(qs)):
+        pidx = torch.from_numpy(pool_idx[r]).to(DEV)
+        pc = o.unpack(to_numpy_codes({kk: v[pidx] for kk, v in codes.items() if v is not None}), op)
+        lo = o.score(qn_all[r][None], pc, op, 1, 1, POOL)[0]
+        qn = float(np.linalg.norm(qn_all[r]))
+        knp = kn_all[pidx].double().cpu().numpy()
+        tol = 1e-4 * np.maximum(np.abs(lo), qn * knp / math.sqrt(D))
+        order = np.argsort(-lo, kind="stable")
+        kth = lo[order[K - 1]]
+        assert kth > float(pool_floor[r]) + 2 * float(tol.max()), "pool too small to hold the oracle's top-k"
+        ret = set(int(v) for v in giv[r])
+        ok_pool = {int(pool_idx[r][j]) for j in range(POOL) if lo[j] >= kth - tol[j] - tol[order[K - 1]]}
+        must = {int(pool_idx[r][j]) for j in range(POOL) if lo[j] > kth + tol[j] + tol[order[K - 1]]}
+        assert must <= ret, f"query {int(qs[r])}: a clear oracle top-{K} code is missing"
+        assert ret <= ok_pool, f"query {int(qs[r])}: a returned code is not in the oracle's top-{K}"
+    print(f"[parity] search over {N} vectors: the oracle's top-{K} of {len(qs)} sampled queries (scored on the "
+          f"stored codes, pools of {POOL}) equals the returned sets up to swaps within tolerance", flush=True)
