@@ -1209,7 +1209,7 @@ __global__ __launch_bounds__(kQPThreads) void qprep128_kernel(
     const int j = u >> 6, jq = (u >> 4) & 3, kg = (u >> 2) & 3, w = u & 3;
     const bool sgnpart = j >= 2 * NP;
     const int sl = 4 * (j & 1) + w;
-    const double coef = sgnpart ? 2.0 : 2.0 * cb.coef[j >> 1];
+    const float coef = sgnpart ? 2.f : (float)(2.0 * cb.coef[j >> 1]);
     const int c = 4 * gi + jq;
     const int E = expo[c][sgnpart ? 1 : 0];
     const float *src = qv[sgnpart ? 1 : 0][c];
@@ -1217,7 +1217,9 @@ __global__ __launch_bounds__(kQPThreads) void qprep128_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int cc = 32 * e + 16 * (sl >> 2) + 4 * kg + (sl & 3);
-      int Q = (int)llrint(ldexp(coef * (double)src[cc], E - (sl & 3)));
+      // |Q| < 2^26, formed in float32: off by at most a few units of the
+      // 2^26 scale, a ~1e-7 relative error in the logit
+      int Q = (int)rintf(ldexpf(coef * src[cc], E - (sl & 3)));
 #pragma unroll
       for (int t = 0; t < 4; ++t) {  // balanced base-128 digits, lowest first
         const int digit = ((Q + 64) & 127) - 64;
@@ -3014,10 +3016,9 @@ __global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
   const int64_t pos = ((int64_t)blockIdx.x * kPolKPT + kr) * kPolScoreThreads + tid;
   if (pos >= seq) break;  // no barrier follows
   const int64_t v = (int64_t)h * seq + pos;
-  const uint4 *src = reinterpret_cast<const uint4 *>(pq + v * 12);
-  const uint4 u0 = src[0], u1 = src[1], u2 = src[2];
+  const u32x4 u0 = nt_load4(pq + v * 12), u1 = nt_load4(pq + v * 12 + 4), u2 = nt_load4(pq + v * 12 + 8);
   const uint32_t wd[12] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w, u2.x, u2.y, u2.z, u2.w};
-  const float R = radius[v];
+  const float R = nt_load(&radius[v]);
   // Blocks of 32 coordinates (t2) one loop iteration at a time, so that the
   // query and table reads of one block are not all hoisted and held together;
   // the level-5 and level-6 left siblings wait in p5, p6.
@@ -3083,7 +3084,7 @@ __global__ __launch_bounds__(kPolScoreThreads) void polar_score128_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t qh = (int64_t)grp * 4 + j;
-    if (qh < g) logits[((int64_t)h * g + qh) * seq + pos] = R * f7[j];
+    if (qh < g) nt_store(&logits[((int64_t)h * g + qh) * seq + pos], R * f7[j]);
   }
   }  // keys of this thread
 }
@@ -3398,8 +3399,10 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
   const int64_t v = (int64_t)h * seq + pos;
   uint32_t wd[W];
 #pragma unroll
-  for (int i = 0; i < W; ++i) wd[i] = words[v * W + i];
-  const float4 nr = *reinterpret_cast<const float4 *>(norms + v * 4);
+  for (int i = 0; i < W; ++i) wd[i] = nt_load(&words[v * W + i]);
+  const u32x4 nru = nt_load4(reinterpret_cast<const uint32_t *>(norms + v * 4));
+  const float4 nr = make_float4(__uint_as_float(nru.x), __uint_as_float(nru.y), __uint_as_float(nru.z),
+                                __uint_as_float(nru.w));
   float4 acc[2], accs[2];
 #pragma unroll
   for (int gg = 0; gg < 2; ++gg) {
@@ -3457,7 +3460,7 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
     if (qh < g) {
       const float l = nrm[0] * a0[j] + kq * nrm[1] * (2.f * s0[j] - t0[j]) + nrm[2] * a1[j] +
                       kq * nrm[3] * (2.f * s1[j] - t1[j]);
-      logits[((int64_t)h * g + qh) * seq + pos] = l;
+      nt_store(&logits[((int64_t)h * g + qh) * seq + pos], l);
     }
   }
   }  // keys of this thread
