@@ -103,3 +103,81 @@ def test_pack_roundtrip(b_out, b_rest):
     for g in range(2):
         for k in ("idx", "sign", "knorm", "rnorm"):
             assert np.array_equal(u[g][k], codes[g][k])
+
+
+# ---------------------------------------------------------------- outlier count
+@pytest.mark.parametrize("n_out,b_out,b_rest,bits,words", [
+    (32, 3, 2, 2.25, 3 * 1 + 2 * 3),      # a few outliers: 32 of 128 at 3 bits, 96 at 2
+    (96, 3, 2, 2.75, 3 * 3 + 2 * 1),
+    (32, 4, 3, 3.25, 4 * 1 + 3 * 3),
+    (64, 3, 2, 2.5, 2 * (2 + 1 + 1 + 1)),
+])
+def test_outlier_count_sets_the_average_and_the_record(n_out, b_out, b_rest, bits, words):
+    p = so.SplitParams(np.arange(128), b_out, b_rest, n_out=n_out)
+    assert p.dims == (n_out, 128 - n_out)
+    assert p.bits_per_coordinate == bits
+    assert so.words_per_vector(p) == words
+    assert p.groups[0].d == p.groups[0].m == n_out and p.groups[1].d == p.groups[1].m == 128 - n_out
+
+
+@pytest.mark.parametrize("dg", [32, 64, 96])
+def test_plane_layout_is_a_bijection_with_the_stated_positions(dg):
+    pos = [so._plane_pos(dg, c) for c in range(dg)]
+    assert sorted(pos) == list(range(dg))
+    # coordinate 16 t + 4 k + i sits at bit k dg / 4 + 4 t + i of the plane
+    t, k, i = dg // 16 - 1, 3, 3
+    assert so._plane_pos(dg, 16 * t + 4 * k + i) == dg - 1
+    assert so._plane_pos(dg, 16) == 4 and so._plane_pos(dg, 4) == dg // 4
+    if dg == 64:  # the two-word form: word k // 2, bit 16 (k % 2) + 4 t + i
+        for c in range(64):
+            tt, kk, ii = c // 16, (c // 4) % 4, c % 4
+            assert so._plane_pos(64, c) == 32 * (kk // 2) + 16 * (kk % 2) + 4 * tt + ii
+
+
+@pytest.mark.parametrize("n_out", [32, 96])
+def test_pack_round_trips_for_any_outlier_count(n_out):
+    x = _keys(40, seed=11)
+    p = so.SplitParams(so.outlier_channels(x, n_out), 3, 2, n_out=n_out)
+    codes = so.encode(x, p)
+    pk = so.pack(codes, p)
+    assert pk["words"].shape == (40, so.words_per_vector(p))
+    back = so.unpack(pk, p)
+    for g in range(2):
+        assert np.array_equal(back[g]["idx"], codes[g]["idx"])
+        assert np.array_equal(back[g]["sign"], codes[g]["sign"])
+    # a single set index bit lands in the word and bit the layout states
+    one = [{k: np.zeros_like(v) for k, v in c.items()} for c in codes]
+    dg = 128 - n_out
+    t = dg // 16 - 1                                     # group 1's last t, k = 1, i = 3
+    one[1]["idx"][0, 16 * t + 4 * 1 + 3] = 1
+    w = so.pack(one, p)["words"][0]
+    j = 1 * dg // 4 + 4 * t + 3
+    at = (p.groups[0].B + 1) * n_out // 32 + j // 32
+    assert w[at] == 1 << (j % 32) and np.count_nonzero(w) == 1
+
+
+def test_few_outliers_split_equals_group_zero_for_a_key_in_the_outlier_channels():
+    x = np.zeros((3, 128))
+    ch = np.concatenate([np.arange(0, 128, 4), np.setdiff1d(np.arange(128), np.arange(0, 128, 4))])
+    x[:, 0::4] = np.random.default_rng(12).standard_normal((3, 32))
+    q = np.random.default_rng(13).standard_normal((2, 128))
+    p = so.SplitParams(ch, 3, 2, n_out=32)
+    codes = so.encode(x, p)
+    assert np.all(codes[1]["knorm"] == 0)
+    got = so.score(q, codes, p, 1, 2, 3)
+    g0 = tqo.score(q[:, 0::4], tqo.encode(x[:, 0::4], p.groups[0]), p.groups[0], 1, 2, 3)
+    assert np.allclose(got, g0, rtol=0, atol=1e-12)
+
+
+def test_few_outliers_estimator_is_unbiased():
+    x = _keys(1, seed=14)
+    q = np.random.default_rng(15).standard_normal((1, 128))
+    ch = so.outlier_channels(_keys(300, seed=16), 32)
+    exact = float(q[0] @ x[0])
+    est = []
+    for s in range(300):
+        p = so.SplitParams(ch, 3, 2, seed_pi=2000 + 2 * s, seed_s=7000 + 2 * s, n_out=32)
+        est.append(so.score(q, so.encode(x, p), p, 1, 1, 1)[0, 0])
+    est = np.asarray(est)
+    sem = est.std(ddof=1) / math.sqrt(est.size)
+    assert abs(est.mean() - exact) <= 4.0 * sem
