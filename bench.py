@@ -479,9 +479,9 @@ def section_split(args, out, dev, stream):
     sq_ = synth.queries(nL * G, seed=6, device=dev)
     slg = torch.empty((nL * G, SEQ), device=dev)
     res = []
-    for b_rest, n_out in ((2, 64), (3, 64)):
+    for b_rest, n_out in ((2, 64), (3, 64), (2, 32), (3, 32)):
         chans = torch.cat([torch.sort(order[:n_out]).values, torch.sort(order[n_out:]).values]).tolist()
-        sp_ = tq.SplitParams(chans, b_rest + 1, b_rest, 2, 3)
+        sp_ = tq.SplitParams(chans, b_rest + 1, b_rest, 2, 3, n_out=n_out)
         sc1 = tq.alloc_split_codes(sp_, N_KV * SEQ, dev)
         sbig = tq.alloc_split_codes(sp_, nL * SEQ, dev)
         for layer in range(LAYERS):
@@ -516,7 +516,7 @@ def section_split(args, out, dev, stream):
                     "score_frac_hbm_peak": round(sbytes / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
         del sc1, sbig, sws
     out["split"] = {"workload": f"outlier-channel split of {N_KV} x {SEQ} bf16 Llama-shaped keys (outlier "
-                                f"group of 64 channels at one bit more); score {nL * G} query heads "
+                                f"group of 64 or 32 channels at one bit more); score {nL * G} query heads "
                                 f"over {LAYERS} layers", "rows": res}
 
 

@@ -275,33 +275,37 @@ tq_status tq_search(const tq_params *p, const float *q, int64_t nq, tq_codes cod
 tq_status tq_release_cache(void);
 
 /* ---------------------------------------------------------------------------
- * Outlier-channel mixed bit widths (2.5 and 3.5 bits per coordinate): the
- * channels of a head are split into outlier channels that get one bit more
- * and the ordinary ones ("TurboQuant压缩效果": 3 bits on the outlier
- * channels, 2 on the rest, over 128 channels).  An average of b_rest + 1/2
- * bits with b_out = b_rest + 1 puts half of the channels in each group.  The
- * split is made before the rotation; each group of 64 channels is its own
- * prod-mode TurboQuant instance of dimension 64 with m = 64 (rotation seed
- * seed_pi + g, JL seed seed_s + g; g = 0 outliers, 1 the rest), and the logit
- * is the sum of the two groups' estimators.
+ * Outlier-channel mixed bit widths: the channels of a head are split into a
+ * few outlier channels that get one bit more and the ordinary ones
+ * ("TurboQuant压缩效果": 3 bits on the outlier channels, 2 on the great
+ * majority, 2.5 and 3.5 bits per coordinate on average over 128 channels).
+ * With b_out = b_rest + 1 the average is b_rest + n_out / 128: n_out = 64
+ * gives the page's 2.5 / 3.5 bits, n_out = 32 a few outliers (2.25 / 3.25).
+ * The split is made before the rotation; group 0 (the n_out outlier
+ * channels) and group 1 (the other 128 - n_out) are each a prod-mode
+ * TurboQuant instance of their own dimension d_g with m = d_g (rotation seed
+ * seed_pi + g, JL seed seed_s + g), and the logit is the sum of the two
+ * groups' estimators.
  *
- * channels: a permutation of 0 .. 127 whose first 64 entries are the
+ * channels: a permutation of 0 .. 127 whose first n_out entries are the
  * outlier channels (chosen by the caller, e.g. the channels of largest mean
  * square in a prompt's keys).
  *
  * Packed record (d = 128): tq_split_words() uint32 words per vector, group 0
  * then group 1; a group with B = b - 1 Lloyd-Max bits holds its B index
- * planes and then its sign plane, two words each (rotated coordinate
- * c = 16 t + 4 k + i of the group at word k / 2, bit 16 (k % 2) + 4 t + i);
- * and float32 norms [n][4]:
- * ||x_0||, ||r_0||, ||x_1||, ||r_1||.  10 words + 16 bytes (56 bytes) at
- * 2.5 bits, 14 words + 16 bytes (72 bytes) at 3.5 bits.
+ * planes and then its sign plane, d_g / 32 words each.  Rotated coordinate
+ * c = 16 t + 4 k + i of the group (t < d_g / 16; k, i < 4) is bit
+ * k d_g / 4 + 4 t + i of the plane's bit string, bit j of which is bit
+ * j % 32 of the plane's word j / 32 (d_g = 64: word k / 2, bit
+ * 16 (k % 2) + 4 t + i).  Float32 norms [n][4]: ||x_0||, ||r_0||, ||x_1||,
+ * ||r_1||.  At n_out = 64: 10 words + 16 bytes (56 bytes) at 2.5 bits, 14
+ * words + 16 bytes (72 bytes) at 3.5 bits.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t d;             /* 128 */
   int32_t b_out;         /* bits of the outlier channels: b_rest + 1 */
-  int32_t b_rest;        /* 2 (2.5 bits) or 3 (3.5 bits) */
-  int32_t reserved;      /* 0 */
+  int32_t b_rest;        /* 2 or 3 */
+  int32_t n_out;         /* outlier channels: 32, 64 or 96 (0 selects 64) */
   uint64_t seed_pi;
   uint64_t seed_s;
   int32_t channels[128]; /* host copy of the channel order */

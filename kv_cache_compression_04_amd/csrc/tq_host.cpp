@@ -723,15 +723,22 @@ static tq_params polar_rotation_params(const tq_polar_params *p) {
 }
 
 // --------------------------------------------------------------------------
-// Mixed bit widths: two 64-channel TurboQuant groups of one head (d = 128).
+// Mixed bit widths: two TurboQuant groups of one head (d = 128), the n_out
+// outlier channels and the rest.
 // --------------------------------------------------------------------------
+static int split_n_out(const tq_split_params *p) { return p->n_out == 0 ? 64 : p->n_out; }
+
 static tq_status check_split(const tq_split_params *p, const char *fn) {
   if (!p) {
     set_error("%s: params is NULL", fn);
     return TQ_ERR_INVALID_ARG;
   }
-  if (p->reserved != 0 || p->b_out != p->b_rest + 1 || p->b_rest < 1 || p->b_rest > 4) {
-    set_error("%s: need b_out = b_rest + 1, 1 <= b_rest <= 4, reserved = 0", fn);
+  if (p->b_out != p->b_rest + 1 || p->b_rest < 1 || p->b_rest > 4) {
+    set_error("%s: need b_out = b_rest + 1, 1 <= b_rest <= 4", fn);
+    return TQ_ERR_INVALID_ARG;
+  }
+  if (p->n_out != 0 && (p->n_out <= 0 || p->n_out >= 128 || p->n_out % 32 != 0)) {
+    set_error("%s: n_out must be 32, 64 or 96 (0 selects 64)", fn);
     return TQ_ERR_INVALID_ARG;
   }
   if (p->d != 128) {
@@ -748,7 +755,7 @@ static tq_status check_split(const tq_split_params *p, const char *fn) {
     seen[c] = true;
   }
   if (p->b_rest != 2 && p->b_rest != 3) {
-    set_error("%s: device kernels are built for 2.5 and 3.5 bits (b_rest = 2 or 3)", fn);
+    set_error("%s: device kernels are built for b_rest = 2 or 3", fn);
     return TQ_ERR_UNSUPPORTED;
   }
   return TQ_OK;
@@ -757,51 +764,63 @@ static tq_status check_split(const tq_split_params *p, const char *fn) {
 static tq_status build_split(const tq_split_params *p, int dev, SplitDerived *D) {
   D->device = dev;
   const int b[2] = {p->b_out, p->b_rest};
-  std::vector<float> mat(4 * 64 * 64 + 32, 0.f), proj(256 * 128, 0.f);
+  D->DG[0] = split_n_out(p);
+  D->DG[1] = 128 - D->DG[0];
+  const size_t cb_off = split_codebook_offset(D->DG);
+  std::vector<float> mat(cb_off + 32, 0.f), proj(256 * 128, 0.f);
+  size_t moff[2][2];  // offsets of Pi_g and S'_g in mat
+  moff[0][0] = 0;
+  moff[0][1] = (size_t)D->DG[0] * D->DG[0];
+  moff[1][0] = 2 * moff[0][1];
+  moff[1][1] = moff[1][0] + (size_t)D->DG[1] * D->DG[1];
   for (int g = 0; g < 2; ++g) {
+    const int n = D->DG[g], coff = g ? D->DG[0] : 0;
     D->B[g] = b[g] - 1;  // prod mode: b - 1 Lloyd-Max bits + the QJL bit
     std::vector<double> gs, pi, sm;
-    seeded_gaussian(p->seed_pi + g, 64, 64, gs);
-    rotation_from_gaussian(64, gs, pi);
-    seeded_gaussian(p->seed_s + g, 64, 64, sm);
-    for (int r = 0; r < 64; ++r)
-      for (int k = 0; k < 64; ++k) {
-        mat[(2 * g) * 4096 + r * 64 + k] = (float)pi[r * 64 + k];
+    seeded_gaussian(p->seed_pi + g, n, n, gs);
+    rotation_from_gaussian(n, gs, pi);
+    seeded_gaussian(p->seed_s + g, n, n, sm);
+    for (int r = 0; r < n; ++r)
+      for (int k = 0; k < n; ++k) {
+        mat[moff[g][0] + (size_t)r * n + k] = (float)pi[(size_t)r * n + k];
         double sp = 0.0;  // S' = S Pi^T: S r = S' (Pi r)
-        for (int j = 0; j < 64; ++j) sp += sm[r * 64 + j] * pi[k * 64 + j];
-        mat[(2 * g + 1) * 4096 + r * 64 + k] = (float)sp;
-        const int ch = p->channels[64 * g + k];
-        proj[(64 * g + r) * 128 + ch] = (float)pi[r * 64 + k];
-        proj[(128 + 64 * g + r) * 128 + ch] = (float)sm[r * 64 + k];
+        for (int j = 0; j < n; ++j) sp += sm[(size_t)r * n + j] * pi[(size_t)k * n + j];
+        mat[moff[g][1] + (size_t)r * n + k] = (float)sp;
+        const int ch = p->channels[coff + k];
+        proj[(size_t)(coff + r) * 128 + ch] = (float)pi[(size_t)r * n + k];
+        proj[(size_t)(128 + coff + r) * 128 + ch] = (float)sm[(size_t)r * n + k];
       }
     Codebook cb;
-    build_codebook(64, D->B[g], cb);
-    for (int j = 0; j < (1 << D->B[g]); ++j) mat[4 * 4096 + 8 * g + j] = cb.c[j];
-    for (int j = 0; j + 1 < (1 << D->B[g]); ++j) mat[4 * 4096 + 16 + 8 * g + j] = cb.t[j];
+    build_codebook(n, D->B[g], cb);
+    for (int j = 0; j < (1 << D->B[g]); ++j) mat[cb_off + 8 * g + j] = cb.c[j];
+    for (int j = 0; j + 1 < (1 << D->B[g]); ++j) mat[cb_off + 16 + 8 * g + j] = cb.t[j];
   }
-  // bf16 hi / lo fragments of the 64 x 64 matrices for the encode MFMAs:
-  // [nt (4)][kt (2)][lane (64)][e (8)], element (lane, e) = M[16 nt + lane % 16]
-  // [col(kt, lane / 16, e)].  Pi: col = 32 kt + 8 g + e (the gathered keys);
-  // S': col = 32 kt + 16 (e / 4) + 4 g + e % 4 (the residual in the layout of
-  // the first product's output).
-  std::vector<uint16_t> frag(8 * 4096);
-  for (int g = 0; g < 2; ++g)
+  // bf16 hi / lo fragments of each group's matrices for the encode MFMAs:
+  // [nt (DG/16)][kt (DG/32)][lane (64)][e (8)], element (lane, e) =
+  // M[16 nt + lane % 16][col(kt, lane / 16, e)].  Pi: col = 32 kt + 8 g + e
+  // (the gathered keys); S': col = 32 kt + 16 (e / 4) + 4 g + e % 4 (the
+  // residual in the layout of the first product's output); g = lane / 16.
+  std::vector<uint16_t> frag;
+  for (int g = 0; g < 2; ++g) {
+    const int n = D->DG[g];
     for (int m = 0; m < 2; ++m) {
-      const float *src = &mat[(2 * g + m) * 4096];
-      uint16_t *hi = &frag[(4 * g + 2 * m) * 4096], *lo = hi + 4096;
-      size_t o = 0;
-      for (int nt = 0; nt < 4; ++nt)
-        for (int kt = 0; kt < 2; ++kt)
+      const float *src = &mat[moff[g][m]];
+      std::vector<uint16_t> hi, lo;
+      for (int nt = 0; nt < n / 16; ++nt)
+        for (int kt = 0; kt < n / 32; ++kt)
           for (int l = 0; l < 64; ++l)
-            for (int e = 0; e < 8; ++e, ++o) {
+            for (int e = 0; e < 8; ++e) {
               const int gg = l >> 4;
               const int col = m == 0 ? 32 * kt + 8 * gg + e : 32 * kt + 16 * (e / 4) + 4 * gg + e % 4;
-              const double v = src[(16 * nt + (l & 15)) * 64 + col];
+              const double v = src[(size_t)(16 * nt + (l & 15)) * n + col];
               const uint16_t h = bf16_bits((float)v);
-              hi[o] = h;
-              lo[o] = bf16_bits((float)(v - bf16_value(h)));
+              hi.push_back(h);
+              lo.push_back(bf16_bits((float)(v - bf16_value(h))));
             }
+      frag.insert(frag.end(), hi.begin(), hi.end());
+      frag.insert(frag.end(), lo.begin(), lo.end());
     }
+  }
   std::vector<int32_t> ch(p->channels, p->channels + 128);
   tq_status st;
   if ((st = upload(&D->mat, mat)) || (st = upload(&D->proj, proj)) || (st = upload(&D->chan, ch)) ||
@@ -1391,7 +1410,9 @@ tq_status tq_split_words(const tq_split_params *p, int32_t *words) {
     set_error("tq_split_words: words is NULL");
     return TQ_ERR_INVALID_ARG;
   }
-  *words = 2 * ((p->b_out - 1) + 1 + (p->b_rest - 1) + 1);
+  // b planes per group (b - 1 index planes and the sign plane), d_g / 32 words each
+  const int n_out = split_n_out(p);
+  *words = p->b_out * (n_out / 32) + p->b_rest * ((128 - n_out) / 32);
   return TQ_OK;
 }
 

@@ -142,17 +142,23 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
 struct SplitDerived {
   int device;
   int B[2];             // Lloyd-Max bits of the groups
-  // fp32 [4][64][64]: Pi_0, S'_0 = S_0 Pi_0^T, Pi_1, S'_1; then the codebooks:
-  // centroids [2][8], boundaries [2][8] (ascending, unused entries 0)
+  int DG[2];            // group dimensions: n_out, 128 - n_out
+  // fp32: Pi_0 [DG0][DG0], S'_0 = S_0 Pi_0^T, Pi_1 [DG1][DG1], S'_1; then,
+  // at split_codebook_offset(), the codebooks: centroids [2][8], boundaries
+  // [2][8] (ascending, unused entries 0)
   float *mat = nullptr;
-  // fp32 [256][128]: rows 0..127 the rotations and rows 128..255 the JL
-  // matrices of both groups on the original channels (the query projections)
+  // fp32 [256][128]: rows 0..127 the rotations of group 0 then group 1, rows
+  // 128..255 their JL matrices, on the original channels (the query
+  // projections)
   float *proj = nullptr;
   int32_t *chan = nullptr;  // [128] channel order
-  // bf16 MFMA fragments, uint4 [8][4 row tiles x 2 column blocks][64 lanes]:
-  // Pi_0 hi, lo, S'_0 hi, lo, Pi_1 hi, lo, S'_1 hi, lo (see build_split)
+  // bf16 MFMA fragments, per group Pi hi, Pi lo, S' hi, S' lo, each uint4
+  // [DG/16 row tiles][DG/32 column blocks][64 lanes] (see build_split)
   uint16_t *frag = nullptr;
 };
+inline size_t split_codebook_offset(const int DG[2]) {
+  return 2 * ((size_t)DG[0] * DG[0] + (size_t)DG[1] * DG[1]);
+}
 tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
                               tq_split_codes codes, hipStream_t stream);
 size_t split_score_workspace_bytes(int64_t nq);

@@ -3130,42 +3130,66 @@ tq_status launch_polar_score(const Derived &D, const PolarTables *T, const float
 }
 
 // ===========================================================================
-// Mixed bit widths: two 64-channel TurboQuant groups, d = 128
+// Mixed bit widths: two TurboQuant groups of one head, d = 128: the DG0
+// outlier channels and the other DG1 = 128 - DG0 (DG0 = 32, 64 or 96)
 // ===========================================================================
 // Encode: one wave per 16 vectors, the two channel groups in turn, as bf16
 // hi / lo MFMAs like the d = 128 encoder: Y_g = Pi_g X_g with X_g the keys'
 // channels of group g gathered into the B operand (lane (v, k) holds the
 // group's channels 32 kt + 8 k .. + 7 of vector v), so lane (v, k) receives
-// rotated coordinates 16 t + 4 k + i; bucketisation and the residual stay in
-// registers, Z_g = S'_g rho_g reads the residual in that layout (S'_g's
-// columns are arranged for it), and each lane packs the 16 bits of its
-// coordinates (16 t + 4 k + i -> word k / 2, bit 16 (k % 2) + 4 t + i), two
-// lane groups sharing a word.
-constexpr int kSplitMat = 64 * 64;
+// rotated coordinates 16 t + 4 k + i (t < DG / 16); bucketisation and the
+// residual stay in registers, Z_g = S'_g rho_g reads the residual in that
+// layout (S'_g's columns are arranged for it), and each lane holds the
+// DG / 4 bits of its coordinates (16 t + 4 k + i at bit 4 t + i), which lane
+// group 0 gathers into the plane's words (the field of lane group k starts at
+// bit k DG / 4 of the plane).
 constexpr int kSplitWaves = 16;
-constexpr int kSplitFragU4 = 4 * 2 * 64;  // uint4 per 64 x 64 fragment half
-constexpr int kSplitRowB = 272;           // LDS bytes per staged bfloat16 row (256 + 16)
+constexpr int kSplitRowB = 272;  // LDS bytes per staged bfloat16 row (256 + 16)
 
-// One channel group g with B Lloyd-Max bits for the wave's 16 vectors.
-template <bool XBF16, int B>
+__host__ __device__ constexpr int split_frag_u4(int DG) { return (DG / 16) * (DG / 32) * 64; }
+
+// The words of a plane from the four lane groups' fields of FB bits each
+// (field k at bit k FB of the plane's bit string).
+template <int FB, int NW>
+__device__ __forceinline__ void pack_fields(const uint32_t (&f)[4], uint32_t (&w)[NW]) {
+#pragma unroll
+  for (int j = 0; j < NW; ++j) w[j] = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int pos = k * FB, lo = 32 * j;
+      if (pos + FB <= lo || pos >= lo + 32) continue;
+      if (pos >= lo)
+        w[j] |= f[k] << (pos - lo);
+      else
+        w[j] |= f[k] >> (lo - pos);
+    }
+}
+
+// One channel group g of dimension DG with B Lloyd-Max bits for the wave's 16
+// vectors.  Fg: the group's fragments (Pi hi, Pi lo, S' hi, S' lo); goff: the
+// group's first entry in the channel order; off: its first word.
+template <bool XBF16, int B, int DG>
 __device__ __forceinline__ void split_encode_group(
-    const int g, const void *__restrict__ x, const uint16_t *xrow, const int64_t rr, const int64_t row,
-    const bool valid,
-    const int lane, const int kg, const uint4 (*F)[kSplitFragU4], const int *chs, const float (*cbc)[8],
-    const float (*cbt)[8], const int off, const int W, uint32_t *__restrict__ words,
-    float *__restrict__ norms) {
+    const int g, const int goff, const void *__restrict__ x, const uint16_t *xrow, const int64_t rr,
+    const int64_t row, const bool valid, const int lane, const int kg, const uint4 *Fg, const int *chs,
+    const float (*cbc)[8], const float (*cbt)[8], const int off, const int W,
+    uint32_t *__restrict__ words, float *__restrict__ norms) {
+  constexpr int NT = DG / 16, NK = DG / 32, NW = DG / 32, FB = DG / 4;
+  constexpr int FH = split_frag_u4(DG);
   constexpr int nbnd = (1 << B) - 1;
-  const uint4 *Ph = F[4 * g] + lane, *Pl = F[4 * g + 1] + lane;
-  const uint4 *Sh = F[4 * g + 2] + lane, *Sl = F[4 * g + 3] + lane;
+  const uint4 *Ph = Fg + lane, *Pl = Fg + FH + lane;
+  const uint4 *Sh = Fg + 2 * FH + lane, *Sl = Fg + 3 * FH + lane;
   // B operand: the group's channels 32 kt + 8 kg + e of vector rr
-  uint4 xh[2], xl[2];
+  uint4 xh[NK], xl[NK];
   float ss = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < NK; ++kt) {
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int c = chs[64 * g + 32 * kt + 8 * kg + e];
+      const int c = chs[goff + 32 * kt + 8 * kg + e];
       v[e] = XBF16 ? __uint_as_float((uint32_t)xrow[c] << 16) : reinterpret_cast<const float *>(x)[rr * 128 + c];
       ss = fmaf(v[e], v[e], ss);
     }
@@ -3178,13 +3202,13 @@ __device__ __forceinline__ void split_encode_group(
   ss += __shfl_xor(ss, 16);
   ss += __shfl_xor(ss, 32);
   const float nu = sqrtf(ss);
-  f32x4 acc[4];
+  f32x4 acc[NT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const bf16x8 ah = as_bf16x8(Ph[(nt * 2 + kt) * 64]), al = as_bf16x8(Pl[(nt * 2 + kt) * 64]);
+    for (int kt = 0; kt < NK; ++kt) {
+      const bf16x8 ah = as_bf16x8(Ph[(nt * NK + kt) * 64]), al = as_bf16x8(Pl[(nt * NK + kt) * 64]);
       const bf16x8 bh = as_bf16x8(xh[kt]);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[nt], 0, 0, 0);
@@ -3199,12 +3223,12 @@ __device__ __forceinline__ void split_encode_group(
   for (int j = 0; j < nbnd; ++j) tb[j] = nu > 0.f ? cbt[g][j] * nu : cbt[g][j];
 #pragma unroll
   for (int j = 0; j <= nbnd; ++j) cv[j] = cbc[g][j];
-  uint32_t pw[B];
+  uint32_t pf[B + 1];
 #pragma unroll
-  for (int p = 0; p < B; ++p) pw[p] = 0u;
-  float rho[4][4], rsq = 0.f;
+  for (int p = 0; p <= B; ++p) pf[p] = 0u;
+  float rho[NT][4], rsq = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float y = acc[nt][i];
@@ -3217,7 +3241,7 @@ __device__ __forceinline__ void split_encode_group(
         cm = ge ? cv[j + 1] : cm;
       }
 #pragma unroll
-      for (int p = 0; p < B; ++p) pw[p] |= (uint32_t)((idx >> p) & 1) << (4 * nt + i);
+      for (int p = 0; p < B; ++p) pf[p] |= (uint32_t)((idx >> p) & 1) << (4 * nt + i);
       const float r = fmaf(-cm, nu, y);
       rsq = fmaf(r, r, rsq);
       rho[nt][i] = r;
@@ -3225,9 +3249,9 @@ __device__ __forceinline__ void split_encode_group(
   rsq += __shfl_xor(rsq, 16);
   rsq += __shfl_xor(rsq, 32);
   // Z = S' rho: K block kt element e of lane group kg = coordinate 32 kt + 16 (e / 4) + 4 kg + e % 4
-  uint4 rh[2], rl[2];
+  uint4 rh[NK], rl[NK];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < NK; ++kt) {
     uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -3237,51 +3261,59 @@ __device__ __forceinline__ void split_encode_group(
     rh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
     rl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
   }
-  uint32_t sw = 0u;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const bf16x8 ah = as_bf16x8(Sh[(nt * 2 + kt) * 64]), al = as_bf16x8(Sl[(nt * 2 + kt) * 64]);
+    for (int kt = 0; kt < NK; ++kt) {
+      const bf16x8 ah = as_bf16x8(Sh[(nt * NK + kt) * 64]), al = as_bf16x8(Sl[(nt * NK + kt) * 64]);
       z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(rh[kt]), z, 0, 0, 0);
       z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(rl[kt]), z, 0, 0, 0);
       z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, as_bf16x8(rh[kt]), z, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sw |= (z[i] >= 0.f ? 1u : 0u) << (4 * nt + i);
+    for (int i = 0; i < 4; ++i) pf[B] |= (z[i] >= 0.f ? 1u : 0u) << (4 * nt + i);
   }
-  // two lane groups share a word: kg even takes the low half
-  uint32_t *dst = words + rr * W + off + (kg >> 1);
+  // lane group 0 gathers the four fields of each plane (index planes, then
+  // the sign plane) and writes the plane's words
+  const int kc = lane & 15;
+  uint32_t *dst = words + rr * W + off;
 #pragma unroll
-  for (int p = 0; p < B; ++p) {
-    const uint32_t o = __shfl_xor(pw[p], 16);
-    if (valid && !(kg & 1)) dst[2 * p] = pw[p] | o << 16;
+  for (int p = 0; p <= B; ++p) {
+    uint32_t f[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __shfl(pf[p], kc + 16 * k);
+    uint32_t wd[NW];
+    pack_fields<FB, NW>(f, wd);
+    if (valid && kg == 0) {
+#pragma unroll
+      for (int j = 0; j < NW; ++j) dst[p * NW + j] = wd[j];
+    }
   }
-  const uint32_t os = __shfl_xor(sw, 16);
-  if (valid && !(kg & 1)) dst[2 * B] = sw | os << 16;
   if (valid && kg == 0) {
     norms[row * 4 + 2 * g] = nu;
     norms[row * 4 + 2 * g + 1] = sqrtf(rsq);
   }
 }
 
-template <bool XBF16, int B0, int B1>
+template <bool XBF16, int B0, int B1, int DG0>
 __global__ __launch_bounds__(kSplitWaves * 64) void split_encode128_kernel(
-    const void *__restrict__ x, int64_t n, const uint4 *__restrict__ frag, const float *__restrict__ mat,
+    const void *__restrict__ x, int64_t n, const uint4 *__restrict__ frag, const float *__restrict__ cbk,
     const int32_t *__restrict__ chan, uint32_t *__restrict__ words, float *__restrict__ norms) {
-  constexpr int W = 2 * (B0 + 1 + B1 + 1);
-  __shared__ uint4 F[8][kSplitFragU4];  // Pi_0 hi, lo, S'_0 hi, lo, Pi_1 hi, lo, S'_1 hi, lo
+  constexpr int DG1 = 128 - DG0;
+  constexpr int FU0 = 4 * split_frag_u4(DG0), FU1 = 4 * split_frag_u4(DG1);
+  constexpr int W = (B0 + 1) * (DG0 / 32) + (B1 + 1) * (DG1 / 32);
+  __shared__ uint4 F[FU0 + FU1];  // group 0: Pi hi, lo, S' hi, lo; then group 1
   // bfloat16 keys: each wave's 16 rows, loaded whole (coalesced) and gathered
   // from here; rows padded to 272 bytes to spread the gathers over the banks
   __shared__ __attribute__((aligned(16))) unsigned char xs[XBF16 ? kSplitWaves : 1][16 * kSplitRowB];
   __shared__ int chs[128];
   __shared__ float cbc[2][8], cbt[2][8];
-  for (int i = threadIdx.x; i < 8 * kSplitFragU4; i += blockDim.x) F[i / kSplitFragU4][i % kSplitFragU4] = frag[i];
+  for (int i = threadIdx.x; i < FU0 + FU1; i += blockDim.x) F[i] = frag[i];
   if (threadIdx.x < 128) chs[threadIdx.x] = chan[threadIdx.x];
   if (threadIdx.x < 32) {
     const int t = threadIdx.x;
-    const float v = mat[4 * kSplitMat + t];
+    const float v = cbk[t];
     if (t < 16) cbc[t >> 3][t & 7] = v;
     else cbt[(t - 16) >> 3][(t - 16) & 7] = v;
   }
@@ -3312,10 +3344,11 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_encode128_kernel(
       __builtin_amdgcn_wave_barrier();
       xrow = reinterpret_cast<const uint16_t *>(&xs[wave][vcol * kSplitRowB]);
     }
-    split_encode_group<XBF16, B0>(0, x, xrow, rr, row, valid, lane, kg, F, chs, cbc, cbt, 0, W, words, norms);
+    split_encode_group<XBF16, B0, DG0>(0, 0, x, xrow, rr, row, valid, lane, kg, F, chs, cbc, cbt, 0, W,
+                                       words, norms);
     __builtin_amdgcn_sched_barrier(0);
-    split_encode_group<XBF16, B1>(1, x, xrow, rr, row, valid, lane, kg, F, chs, cbc, cbt, 2 * (B0 + 1), W,
-                                  words, norms);
+    split_encode_group<XBF16, B1, DG1>(1, DG0, x, xrow, rr, row, valid, lane, kg, F + FU0, chs, cbc, cbt,
+                                       (B0 + 1) * (DG0 / 32), W, words, norms);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -3332,18 +3365,19 @@ constexpr int kSplitKPT = 16;  // keys per thread (the tables amortised over 409
 
 __host__ __device__ constexpr int split_chunk(int B) { return B >= 2 ? 2 : 4; }
 
-template <int B0, int B1>
+template <int B0, int B1, int DG0>
 __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
-    const double *__restrict__ pq, const float *__restrict__ mat, const uint32_t *__restrict__ words,
-    const float *__restrict__ norms, int64_t seq, int64_t g, int ngroups, float kq,
+    const double *__restrict__ pq, const float *__restrict__ cbk, const uint32_t *__restrict__ words,
+    const float *__restrict__ norms, int64_t seq, int64_t g, int ngroups, float kq0, float kq1,
     float *__restrict__ logits) {
-  constexpr int W = 2 * (B0 + 1 + B1 + 1);
+  constexpr int DG1 = 128 - DG0;
+  constexpr int W = (B0 + 1) * (DG0 / 32) + (B1 + 1) * (DG1 / 32);
   constexpr int S0 = split_chunk(B0), S1 = split_chunk(B1);
   constexpr int C0 = 1 << (B0 * S0), C1 = 1 << (B1 * S1);  // codes per chunk
-  constexpr int N0 = 64 / S0, N1 = 64 / S1;                 // chunks per group
-  __shared__ float4 qs4[256];               // (Pi q)_c for c < 128, then (S q)_c
+  constexpr int N0 = DG0 / S0, N1 = DG1 / S1;               // chunks per group
+  __shared__ float4 qs4[256];  // (Pi q)_c for c < 128 (group 0, then group 1), then (S q)_c
   __shared__ float4 TI0[N0 * C0], TI1[N1 * C1];
-  __shared__ float4 TS[2][16][16];          // group, sign chunk, code
+  __shared__ float4 TS0[DG0 / 4][16], TS1[DG1 / 4][16];  // sign chunk, code
   __shared__ float4 SS[2];
   const int hg = blockIdx.y, h = hg / ngroups, grp = hg % ngroups;
   const int tid = threadIdx.x;
@@ -3366,26 +3400,29 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
     for (int j = 0; j < S; ++j) {
       int idx = 0;
       for (int p = 0; p < B; ++p) idx |= ((code >> (p * S + j)) & 1) << p;
-      const float cent = mat[4 * kSplitMat + (g1 ? 8 : 0) + idx];
-      const float4 q = qs4[64 * (g1 ? 1 : 0) + chunk * S + j];
+      const float cent = cbk[(g1 ? 8 : 0) + idx];
+      const float4 q = qs4[(g1 ? DG0 : 0) + chunk * S + j];
       a.x = fmaf(cent, q.x, a.x); a.y = fmaf(cent, q.y, a.y); a.z = fmaf(cent, q.z, a.z); a.w = fmaf(cent, q.w, a.w);
     }
     if (g1) TI1[ee] = a;
     else TI0[ee] = a;
   }
-  for (int e = tid; e < 2 * 16 * 16; e += kSplitScoreThreads) {
-    const int gg = e >> 8, chunk = (e >> 4) & 15, code = e & 15;
+  for (int e = tid; e < 32 * 16; e += kSplitScoreThreads) {
+    const int chunk = e >> 4, code = e & 15;  // chunk 0 .. 31 over both groups
+    const bool g1 = chunk >= DG0 / 4;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < 4; ++j)
       if ((code >> j) & 1) {
-        const float4 q = qs4[128 + 64 * gg + 4 * chunk + j];
+        const float4 q = qs4[128 + 4 * chunk + j];
         a.x += q.x; a.y += q.y; a.z += q.z; a.w += q.w;
       }
-    TS[gg][chunk][code] = a;
+    if (g1) TS1[chunk - DG0 / 4][code] = a;
+    else TS0[chunk][code] = a;
   }
   if (tid < 2) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c = 128 + 64 * tid; c < 128 + 64 * tid + 64; ++c) {
+    const int c0 = tid ? 128 + DG0 : 128, c1 = tid ? 256 : 128 + DG0;
+    for (int c = c0; c < c1; ++c) {
       a.x += qs4[c].x; a.y += qs4[c].y; a.z += qs4[c].z; a.w += qs4[c].w;
     }
     SS[tid] = a;
@@ -3409,42 +3446,46 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
     acc[gg] = make_float4(0.f, 0.f, 0.f, 0.f);
     accs[gg] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  // one group and one 32-coordinate half per loop iteration (the gathers of
-  // an iteration are not all hoisted together; words picked by uniform selects)
+  // one group at a time: plane word j holds bits 32 j .. 32 j + 31 of the
+  // plane; its 4-bit group at bit 4 bq is coordinate 16 t + 4 k + (0..3)
+  // with k = (32 j + 4 bq) / (DG / 4), t = ((32 j + 4 bq) % (DG / 4)) / 4.
+  // One word per loop iteration (the gathers of an iteration are not all
+  // hoisted together; words picked by wave-uniform selects).
   auto group = [&](auto gc) {
     constexpr int gg = decltype(gc)::value;
     constexpr int B = gg ? B1 : B0, S = gg ? S1 : S0, C = gg ? C1 : C0;
-    constexpr int off = gg ? 2 * (B0 + 1) : 0;
+    constexpr int DG = gg ? DG1 : DG0, NW = DG / 32, FB = DG / 4;
+    constexpr int off = gg ? (B0 + 1) * (DG0 / 32) : 0;
     const float4 *TI = gg ? TI1 : TI0;
+    const float4(*TS)[16] = gg ? TS1 : TS0;
+    auto pick = [&](int base, int j) -> uint32_t {  // an OR of masked words, not an indexed load
+      uint32_t w = 0u;
+#pragma unroll
+      for (int jj = 0; jj < NW; ++jj) w |= wd[base + jj] & (j == jj ? 0xFFFFFFFFu : 0u);
+      return w;
+    };
 #pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
+    for (int j = 0; j < NW; ++j) {
       uint32_t pl[3];
 #pragma unroll
-      for (int p = 0; p < 3; ++p) pl[p] = p < B ? (half ? wd[off + 2 * p + 1] : wd[off + 2 * p]) : 0u;
-      const uint32_t sw = half ? wd[off + 2 * B + 1] : wd[off + 2 * B];
-      // word `half` holds coordinates 16 t + 4 (2 half + kk) + i at bit 16 kk + 4 t + i
-      const float4 *TIh = TI + (8 * half / S) * C;
+      for (int p = 0; p < 3; ++p) pl[p] = p < B ? pick(off + p * NW, j) : 0u;
+      const uint32_t sw = pick(off + B * NW, j);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int bq = 0; bq < 8; ++bq) {
+        const int pos = 32 * j + 4 * bq;
+        const int c0 = 16 * ((pos % FB) / 4) + 4 * (pos / FB);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int i0 = 0; i0 < 4; i0 += S) {
+          uint32_t code = 0;
 #pragma unroll
-          for (int i0 = 0; i0 < 4; i0 += S) {
-            const int b0 = 16 * kk + 4 * t + i0;
-            uint32_t code = 0;
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-              if (p < B) code |= ((pl[p] >> b0) & ((1u << S) - 1u)) << (p * S);
-            const float4 tv = TIh[((16 * t + 4 * kk + i0) / S) * C + code];
-            acc[gg].x += tv.x; acc[gg].y += tv.y; acc[gg].z += tv.z; acc[gg].w += tv.w;
-          }
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const float4 tv = TS[gg][4 * t + kk + 2 * half][(sw >> (16 * kk + 4 * t)) & 15u];
-          accs[gg].x += tv.x; accs[gg].y += tv.y; accs[gg].z += tv.z; accs[gg].w += tv.w;
+          for (int p = 0; p < 3; ++p)
+            if (p < B) code |= ((pl[p] >> (4 * bq + i0)) & ((1u << S) - 1u)) << (p * S);
+          const float4 tv = TI[((c0 + i0) / S) * C + code];
+          acc[gg].x += tv.x; acc[gg].y += tv.y; acc[gg].z += tv.z; acc[gg].w += tv.w;
         }
+        const float4 tv = TS[c0 / 4][(sw >> (4 * bq)) & 15u];
+        accs[gg].x += tv.x; accs[gg].y += tv.y; accs[gg].z += tv.z; accs[gg].w += tv.w;
+      }
     }
   };
   group(std::integral_constant<int, 0>{});
@@ -3458,37 +3499,90 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
   for (int j = 0; j < 4; ++j) {
     const int64_t qh = (int64_t)grp * 4 + j;
     if (qh < g) {
-      const float l = nrm[0] * a0[j] + kq * nrm[1] * (2.f * s0[j] - t0[j]) + nrm[2] * a1[j] +
-                      kq * nrm[3] * (2.f * s1[j] - t1[j]);
+      const float l = nrm[0] * a0[j] + kq0 * nrm[1] * (2.f * s0[j] - t0[j]) + nrm[2] * a1[j] +
+                      kq1 * nrm[3] * (2.f * s1[j] - t1[j]);
       nt_store(&logits[((int64_t)h * g + qh) * seq + pos], l);
     }
   }
   }  // keys of this thread
 }
 
+template <int B0, int B1, int DG0>
+static void launch_split_encode_t(const SplitDerived &D, const void *x, bool bf, int64_t n, int grid,
+                                  tq_split_codes c, hipStream_t s) {
+  const uint4 *fr = reinterpret_cast<const uint4 *>(D.frag);
+  const float *cbk = D.mat + split_codebook_offset(D.DG);
+  if (bf)
+    split_encode128_kernel<true, B0, B1, DG0><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, cbk, D.chan, c.words,
+                                                                                 c.norms);
+  else
+    split_encode128_kernel<false, B0, B1, DG0><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, cbk, D.chan, c.words,
+                                                                                  c.norms);
+}
+
+template <int B0, int B1>
+static tq_status launch_split_encode_b(const SplitDerived &D, const void *x, bool bf, int64_t n, int grid,
+                                       tq_split_codes c, hipStream_t s) {
+  switch (D.DG[0]) {
+    case 32: launch_split_encode_t<B0, B1, 32>(D, x, bf, n, grid, c, s); break;
+    case 64: launch_split_encode_t<B0, B1, 64>(D, x, bf, n, grid, c, s); break;
+    case 96: launch_split_encode_t<B0, B1, 96>(D, x, bf, n, grid, c, s); break;
+    default:
+      set_error("tq_split_encode: no kernel for %d outlier channels", D.DG[0]);
+      return TQ_ERR_UNSUPPORTED;
+  }
+  return TQ_OK;
+}
+
 tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
                               tq_split_codes c, hipStream_t s) {
   const int64_t nbatch = (n + 15) / 16;
   const int64_t need = (nbatch + kSplitWaves - 1) / kSplitWaves;
-  // 64 KB of fragments per workgroup of 16 waves: two workgroups per CU
+  // 64 KB of fragments per workgroup of 16 waves at 64 outlier channels (two
+  // workgroups per CU), 80 KB otherwise (one)
   const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * 2);
-  const uint4 *fr = reinterpret_cast<const uint4 *>(D.frag);
   const bool bf = dtype == TQ_BF16;
-  if (D.B[0] == 2 && D.B[1] == 1) {
-    if (bf) split_encode128_kernel<true, 2, 1><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, c.words, c.norms);
-    else split_encode128_kernel<false, 2, 1><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, c.words, c.norms);
-  } else if (D.B[0] == 3 && D.B[1] == 2) {
-    if (bf) split_encode128_kernel<true, 3, 2><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, c.words, c.norms);
-    else split_encode128_kernel<false, 3, 2><<<grid, kSplitWaves * 64, 0, s>>>(x, n, fr, D.mat, D.chan, c.words, c.norms);
-  } else {
+  tq_status st;
+  if (D.B[0] == 2 && D.B[1] == 1)
+    st = launch_split_encode_b<2, 1>(D, x, bf, n, grid, c, s);
+  else if (D.B[0] == 3 && D.B[1] == 2)
+    st = launch_split_encode_b<3, 2>(D, x, bf, n, grid, c, s);
+  else {
     set_error("tq_split_encode: no kernel for Lloyd-Max bits (%d, %d)", D.B[0], D.B[1]);
     return TQ_ERR_UNSUPPORTED;
   }
+  if (st != TQ_OK) return st;
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
 
 size_t split_score_workspace_bytes(int64_t nq) { return (size_t)nq * 256 * sizeof(double); }
+
+template <int B0, int B1>
+static tq_status launch_split_score_b(const SplitDerived &D, const double *pq, tq_split_codes c, int64_t seq,
+                                      int64_t g, int ngroups, dim3 grid, float *logits, hipStream_t s) {
+  const float *cbk = D.mat + split_codebook_offset(D.DG);
+  // the QJL constant sqrt(pi/2)/m of each group (m = its dimension)
+  const float kq0 = (float)(std::sqrt(M_PI / 2.0) / D.DG[0]), kq1 = (float)(std::sqrt(M_PI / 2.0) / D.DG[1]);
+  switch (D.DG[0]) {
+    case 32:
+      split_score128_kernel<B0, B1, 32><<<grid, kSplitScoreThreads, 0, s>>>(pq, cbk, c.words, c.norms, seq, g,
+                                                                            ngroups, kq0, kq1, logits);
+      break;
+    case 64:
+      split_score128_kernel<B0, B1, 64><<<grid, kSplitScoreThreads, 0, s>>>(pq, cbk, c.words, c.norms, seq, g,
+                                                                            ngroups, kq0, kq1, logits);
+      break;
+    case 96:
+      split_score128_kernel<B0, B1, 96><<<grid, kSplitScoreThreads, 0, s>>>(pq, cbk, c.words, c.norms, seq, g,
+                                                                            ngroups, kq0, kq1, logits);
+      break;
+    default:
+      set_error("tq_split_score: no kernel for %d outlier channels", D.DG[0]);
+      return TQ_ERR_UNSUPPORTED;
+  }
+  return TQ_OK;
+}
 
 tq_status launch_split_score(const SplitDerived &D, const float *q, int64_t n_kv, int64_t g,
                              tq_split_codes c, int64_t seq, float *logits, void *ws, hipStream_t s) {
@@ -3503,19 +3597,19 @@ tq_status launch_split_score(const SplitDerived &D, const float *q, int64_t n_kv
   qproj_kernel<<<dim3(256 / kQJR, (unsigned)((n_kv * g + kQJQ - 1) / kQJQ)), dim3(256), 0, s>>>(
       q, n_kv * g, 128, 256, D.proj, D.proj + 128 * 128, pq);
   const dim3 grid((unsigned)nblk, (unsigned)nhg);
-  const float kq = (float)(std::sqrt(M_PI / 2.0) / 64.0);  // the QJL constant of a 64-row group
+  tq_status st;
   if (D.B[0] == 2 && D.B[1] == 1)
-    split_score128_kernel<2, 1><<<grid, kSplitScoreThreads, 0, s>>>(pq, D.mat, c.words, c.norms, seq, g, ngroups,
-                                                                    kq, logits);
+    st = launch_split_score_b<2, 1>(D, pq, c, seq, g, ngroups, grid, logits, s);
   else if (D.B[0] == 3 && D.B[1] == 2)
-    split_score128_kernel<3, 2><<<grid, kSplitScoreThreads, 0, s>>>(pq, D.mat, c.words, c.norms, seq, g, ngroups,
-                                                                    kq, logits);
+    st = launch_split_score_b<3, 2>(D, pq, c, seq, g, ngroups, grid, logits, s);
   else {
-    set_error("tq_split_score: built for 2.5 and 3.5 bits");
+    set_error("tq_split_score: built for b_rest = 2 or 3");
     return TQ_ERR_UNSUPPORTED;
   }
+  if (st != TQ_OK) return st;
   TQ_LAUNCH_CHECK();
   return TQ_OK;
 }
 
 }  // namespace tq
+

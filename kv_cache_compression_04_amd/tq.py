@@ -49,7 +49,7 @@ class _PolarCodes(ctypes.Structure):
 
 class _SplitParams(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("b_out", ctypes.c_int32), ("b_rest", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("seed_pi", ctypes.c_uint64), ("seed_s", ctypes.c_uint64),
+                ("n_out", ctypes.c_int32), ("seed_pi", ctypes.c_uint64), ("seed_s", ctypes.c_uint64),
                 ("channels", ctypes.c_int32 * 128)]
 
 
@@ -390,15 +390,18 @@ def polar_score(p: PolarParams, q, codes: dict, n_kv: int, g: int, seq: int, log
 # ----------------------------------------------------------------- mixed bit widths
 class SplitParams:
     """Outlier-channel split of a d = 128 head: channels (a permutation of
-    0..127, the first 64 are the outlier channels), b_out = b_rest + 1."""
+    0..127, the first n_out are the outlier channels; n_out = 32, 64 or 96),
+    b_out = b_rest + 1."""
 
-    def __init__(self, channels, b_out: int = 3, b_rest: int = 2, seed_pi: int = 2, seed_s: int = 3):
+    def __init__(self, channels, b_out: int = 3, b_rest: int = 2, seed_pi: int = 2, seed_s: int = 3,
+                 n_out: int = 64):
         ch = [int(c) for c in channels]
         assert len(ch) == 128
         self.channels, self.b_out, self.b_rest, self.seed_pi, self.seed_s = ch, b_out, b_rest, seed_pi, seed_s
+        self.n_out = n_out
 
     def c(self) -> _SplitParams:
-        return _SplitParams(128, self.b_out, self.b_rest, 0, self.seed_pi, self.seed_s,
+        return _SplitParams(128, self.b_out, self.b_rest, self.n_out, self.seed_pi, self.seed_s,
                             (ctypes.c_int32 * 128)(*self.channels))
 
 

@@ -147,9 +147,10 @@ def test_polar_and_split_guards():
     pl = gd.view((n_kv * g, n), torch.float32)
     tq.polar_score(pp, q, pc, n_kv, g, n, pl, gd.workspace(tq.polar_score_workspace_bytes(pp, n_kv, g)))
     gd.check("polar")
-    sp = tq.SplitParams(list(range(128)), 3, 2, 2, 3)
-    sc = {"words": gd.view((n, tq.split_words(sp)), torch.int32), "norms": gd.view((n, 4), torch.float32)}
-    tq.split_encode(sp, x, sc)
-    sl = gd.view((n_kv * g, n), torch.float32)
-    tq.split_score(sp, q, sc, n_kv, g, n, sl, gd.workspace(tq.split_score_workspace_bytes(sp, n_kv, g)))
-    gd.check("split")
+    for n_out in (64, 32, 96):
+        sp = tq.SplitParams(list(range(128)), 3, 2, 2, 3, n_out=n_out)
+        sc = {"words": gd.view((n, tq.split_words(sp)), torch.int32), "norms": gd.view((n, 4), torch.float32)}
+        tq.split_encode(sp, x, sc)
+        sl = gd.view((n_kv * g, n), torch.float32)
+        tq.split_score(sp, q, sc, n_kv, g, n, sl, gd.workspace(tq.split_score_workspace_bytes(sp, n_kv, g)))
+        gd.check(f"split n_out={n_out}")

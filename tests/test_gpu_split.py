@@ -1,5 +1,6 @@
-"""GPU parity of the outlier-channel mixed bit widths (2.5 and 3.5 bits)
-against the oracle: codes of both 64-channel groups, norms, and logits."""
+"""GPU parity of the outlier-channel mixed bit widths against the oracle:
+codes of both channel groups (n_out outlier channels and the rest; 64 + 64
+gives 2.5 and 3.5 bits, 32 + 96 a few outliers), norms, and logits."""
 import math
 
 import numpy as np
@@ -18,9 +19,10 @@ from kv_cache_compression_04_amd import synth, tq  # noqa: E402
 from tests.gpu_helpers import DEV  # noqa: E402
 from tests.parity import check_index_codes, check_sign_codes  # noqa: E402
 
-def _params(x, b_rest):
-    ch = so.outlier_channels(np.asarray(x, np.float64)[:2048], 64)
-    return tq.SplitParams(ch, b_rest + 1, b_rest, 2, 3), so.SplitParams(ch, b_rest + 1, b_rest, 2, 3)
+def _params(x, b_rest, n_out=64):
+    ch = so.outlier_channels(np.asarray(x, np.float64)[:2048], n_out)
+    return (tq.SplitParams(ch, b_rest + 1, b_rest, 2, 3, n_out=n_out),
+            so.SplitParams(ch, b_rest + 1, b_rest, 2, 3, n_out=n_out))
 
 
 def _gpu_unpacked(codes, op):
@@ -29,7 +31,7 @@ def _gpu_unpacked(codes, op):
 
 
 def check_group(xg, got, P, stats):
-    """One 64-channel group: the checks of the TurboQuant codes (same windows
+    """One channel group: the checks of the TurboQuant codes (same windows
     as the single-group encoder: raw-scale sign window, 1e-5 ||x||)."""
     ref = tqo.encode(xg, P)
     kn = ref["knorm"].astype(np.float64)
@@ -47,12 +49,14 @@ def check_group(xg, got, P, stats):
     stats.append((st["idx_mismatch"], st["sign_mismatch"], st["sign_window"]))
 
 
-@pytest.mark.parametrize("b_rest,dtype,n", [(2, torch.bfloat16, 3000), (3, torch.bfloat16, 1001),
-                                            (2, torch.float32, 777), (3, torch.float32, 1)])
-def test_split_encode_matches_oracle(b_rest, dtype, n):
+@pytest.mark.parametrize("b_rest,dtype,n,n_out", [(2, torch.bfloat16, 3000, 64), (3, torch.bfloat16, 1001, 64),
+                                                  (2, torch.float32, 777, 64), (3, torch.float32, 1, 64),
+                                                  (2, torch.bfloat16, 2049, 32), (3, torch.float32, 513, 32),
+                                                  (2, torch.float32, 300, 96), (3, torch.bfloat16, 1000, 96)])
+def test_split_encode_matches_oracle(b_rest, dtype, n, n_out):
     x = synth.llama_keys(heads=1, seq=n, seed=n + b_rest, dtype=dtype)
     xs = x.double().numpy()
-    p, op = _params(xs, b_rest)
+    p, op = _params(xs, b_rest, n_out)
     codes = tq.alloc_split_codes(p, n, DEV)
     tq.split_encode(p, x.to(DEV), codes)
     torch.cuda.synchronize()
@@ -60,8 +64,8 @@ def test_split_encode_matches_oracle(b_rest, dtype, n):
     stats = []
     for g in range(2):
         check_group(xs[:, op.group_channels(g)], got[g], op.groups[g], stats)
-    print(f"[parity] split encode b={b_rest + 0.5} {dtype} n={n}: (index, sign mismatches; sign window population) per group {stats}",
-          flush=True)
+    print(f"[parity] split encode b_rest={b_rest} n_out={n_out} {dtype} n={n}: (index, sign mismatches; sign "
+          f"window population) per group {stats}", flush=True)
 
 
 def test_split_encode_zero_vectors():
@@ -89,12 +93,13 @@ def _check_logits(got, ref, q, codes, n_kv, g, seq):
 
 
 # 9000 positions: two full workgroups of 4096 and a ragged third
-@pytest.mark.parametrize("b_rest,n_kv,g,seq", [(2, 2, 4, 1000), (3, 1, 5, 300), (2, 3, 1, 257), (3, 1, 4, 1),
-                                               (2, 1, 4, 9000)])
-def test_split_score_matches_oracle(b_rest, n_kv, g, seq):
+@pytest.mark.parametrize("b_rest,n_kv,g,seq,n_out", [(2, 2, 4, 1000, 64), (3, 1, 5, 300, 64), (2, 3, 1, 257, 64),
+                                                     (3, 1, 4, 1, 64), (2, 1, 4, 9000, 64), (2, 2, 4, 1000, 32),
+                                                     (3, 1, 5, 4500, 32), (2, 1, 3, 700, 96), (3, 2, 4, 257, 96)])
+def test_split_score_matches_oracle(b_rest, n_kv, g, seq, n_out):
     x = synth.llama_keys(heads=n_kv, seq=seq, seed=seq + g, dtype=torch.float32)
     xs = x.double().numpy()
-    p, op = _params(xs, b_rest)
+    p, op = _params(xs, b_rest, n_out)
     q = synth.queries(n_kv * g, seed=g).numpy().astype(np.float64)
     dq = torch.from_numpy(q.astype(np.float32)).to(DEV)
     ws = torch.empty(tq.split_score_workspace_bytes(p, n_kv, g), dtype=torch.uint8, device=DEV)
@@ -111,5 +116,5 @@ def test_split_score_matches_oracle(b_rest, n_kv, g, seq):
     torch.cuda.synchronize()
     gu = _gpu_unpacked(gcodes, op)
     w2 = _check_logits(logits.cpu().numpy(), so.score(q, gu, op, n_kv, g, seq), q, gu, n_kv, g, seq)
-    print(f"[parity] split score b={b_rest + 0.5} n_kv={n_kv} g={g} seq={seq}: worst/tol {w1:.4f} (oracle codes), "
-          f"{w2:.4f} (GPU codes)", flush=True)
+    print(f"[parity] split score b_rest={b_rest} n_out={n_out} n_kv={n_kv} g={g} seq={seq}: worst/tol {w1:.4f} "
+          f"(oracle codes), {w2:.4f} (GPU codes)", flush=True)

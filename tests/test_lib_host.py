@@ -235,6 +235,14 @@ def test_split_argument_checks():
     assert _status("tq_split_words", ctypes.byref(ok), ctypes.byref(w)) == 0 and w.value == 10
     assert _status("tq_split_words", ctypes.byref(tq.SplitParams(ch, 4, 3).c()), ctypes.byref(w)) == 0
     assert w.value == 14
+    # b planes of d_g / 32 words per group: 32 outliers at 3 bits + 96 at 2 = 3 + 6 words
+    assert _status("tq_split_words", ctypes.byref(tq.SplitParams(ch, 3, 2, n_out=32).c()), ctypes.byref(w)) == 0
+    assert w.value == 9
+    assert _status("tq_split_words", ctypes.byref(tq.SplitParams(ch, 4, 3, n_out=96).c()), ctypes.byref(w)) == 0
+    assert w.value == 4 * 3 + 3 * 1
+    zero = tq.SplitParams(ch, 3, 2).c()
+    zero.n_out = 0                                                      # 0 selects 64
+    assert _status("tq_split_words", ctypes.byref(zero), ctypes.byref(w)) == 0 and w.value == 10
     codes = tq._SplitCodes(a, a)
     enc = lambda pp, x=a, n=4, dt=0: _status("tq_split_encode", ctypes.byref(pp), x, dt, n, codes, None)
     assert enc(ok, n=0) == 0
@@ -242,7 +250,9 @@ def test_split_argument_checks():
     assert enc(ok, x=a + 4) == 3
     assert enc(tq.SplitParams(ch, 3, 3).c()) == 1                       # b_out must be b_rest + 1
     assert enc(tq.SplitParams([0] * 128, 3, 2).c()) == 1                 # not a permutation
-    assert enc(tq.SplitParams(ch, 5, 4).c()) == 2                        # kernels built for 2.5 / 3.5 bits
+    assert enc(tq.SplitParams(ch, 5, 4).c()) == 2                        # kernels built for b_rest = 2, 3
+    for bad in (16, 48, 128, -32):                                      # n_out: 32, 64 or 96
+        assert enc(tq.SplitParams(ch, 3, 2, n_out=bad).c()) == 1
     bad_d = tq.SplitParams(ch, 3, 2).c()
     bad_d.d = 64
     assert enc(bad_d) == 2
