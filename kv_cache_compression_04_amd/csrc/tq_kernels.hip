@@ -104,6 +104,44 @@ __device__ __forceinline__ u32x4 nt_load4(const uint32_t *p) {
 }
 __device__ __forceinline__ void nt_store(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
+// Raw buffer loads (non-temporal): a descriptor covers one region of `bytes`
+// bytes; the address is the descriptor's base + a per-lane offset + a
+// wave-uniform (scalar) offset, so a load whose offsets are loop constants
+// costs no vector instruction.  The range check covers the per-lane offset
+// only (a load whose per-lane offset lies past the region returns zeros); a
+// scalar offset is used only where every access is known to be in range.
+constexpr int kBufWord3 = 0x00020000;  // descriptor word 3 for raw dword loads
+typedef __amdgpu_buffer_rsrc_t bufrsrc;
+__device__ __forceinline__ bufrsrc buf_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ uint32_t buf_ld1(bufrsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 2);
+}
+// N consecutive dwords
+template <int N>
+__device__ __forceinline__ void buf_ldn(bufrsrc r, uint32_t voff, uint32_t soff, uint32_t *out) {
+  if constexpr (N == 1) {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 2);
+  } else if constexpr (N == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 2);
+    out[0] = v[0];
+    out[1] = v[1];
+  } else if constexpr (N == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)voff, (int)soff, 2);
+    out[0] = v[0];
+    out[1] = v[1];
+    out[2] = v[2];
+  } else {
+    static_assert(N == 4, "1 to 4 dwords");
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2);
+    out[0] = v[0];
+    out[1] = v[1];
+    out[2] = v[2];
+    out[3] = v[3];
+  }
+}
+
 // Power-of-two scale of one encoded vector: with e the exponent of its norm
 // nu (nu = f 2^e, f in [0.5, 1)), the kernels feed x 2^(1-e) (norm in [1, 2))
 // to fp16 MFMAs against kEncScale times the matrices, so rotated coordinates
@@ -2316,7 +2354,6 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   const int w = c16 >> 2, beta = c16 & 3;
   if (active) {
   const int npos = (int)(seq - p0 < kAttKPW ? seq - p0 : kAttKPW);
-  const uint32_t last = (uint32_t)(npos - 1);  // local index of the last position
 
   // ---------------- phase 1: logits of this wave's positions
   float m;
@@ -2325,33 +2362,52 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
 #pragma unroll
     for (int j = 0; j < NMF; ++j) A[j] = aops[((int64_t)hg * NMF + j) * 64 + lane];
     const QConst cst = qc[(int64_t)hg * 4 + kg];
-    const uint32_t *ki = kidx + vb * 4 * BKK;
-    const uint32_t *ks = ksgn + vb * 4;
-    const float *kn = knorm + vb;
-    const float *rn = rnorm + vb;
-    float mx = -INFINITY;
-    for (int t0 = 0; t0 < kAttKPW / 16; t0 += kAttU) {
-      uint32_t planes[kAttU][BKK], sw[kAttU];
-      float kv[kAttU], rv[kAttU];
+    // the wave's positions through buffer descriptors of exactly its npos
+    // codes (positions past them read zeros, and their logits are -inf):
+    // position 16 t + c16 at the lane's offset plus a per-tile scalar offset
+    const bufrsrc rki = buf_rsrc(kidx + vb * 4 * BKK, (uint32_t)npos * 16u * BKK);
+    const bufrsrc rks = buf_rsrc(ksgn + vb * 4, (uint32_t)npos * 16u);
+    const bufrsrc rkn = buf_rsrc(knorm + vb, (uint32_t)npos * 4u);
+    const bufrsrc rrn = buf_rsrc(rnorm + vb, (uint32_t)npos * 4u);
+    const uint32_t oki = (uint32_t)(4 * c16 + kg) * 4u * BKK, oks = (uint32_t)(4 * c16 + kg) * 4u;
+    const uint32_t okn = (uint32_t)c16 * 4u;
+    // a full split passes each tile's offset as the scalar offset (every
+    // access in range); the last split of a sequence adds it to the lane's
+    // offset, where the range check turns positions past npos into zeros
+    auto logits_of = [&](auto full_c) -> float {
+      constexpr bool FULL = decltype(full_c)::value;
+      auto ld = [&](auto n_c, bufrsrc r, uint32_t lane_off, uint32_t tile_off, uint32_t *out) {
+        constexpr int N = decltype(n_c)::value;
+        if constexpr (FULL)
+          buf_ldn<N>(r, lane_off, tile_off, out);
+        else
+          buf_ldn<N>(r, lane_off + tile_off, 0u, out);
+      };
+      float mx = -INFINITY;
+      for (int t0 = 0; t0 < kAttKPW / 16; t0 += kAttU) {
+        uint32_t planes[kAttU][BKK], sw[kAttU], kr[kAttU], rr[kAttU];
 #pragma unroll
-      for (int u = 0; u < kAttU; ++u) {
-        const uint32_t vp = min((uint32_t)((t0 + u) * 16 + c16), last);
+        for (int u = 0; u < kAttU; ++u) {
+          const uint32_t tile = (uint32_t)(t0 + u);
+          if constexpr (BK > 0) ld(std::integral_constant<int, BK>{}, rki, oki, tile * 256u * BKK, planes[u]);
+          ld(std::integral_constant<int, 1>{}, rks, oks, tile * 256u, &sw[u]);
+          ld(std::integral_constant<int, 1>{}, rkn, okn, tile * 64u, &kr[u]);
+          ld(std::integral_constant<int, 1>{}, rrn, okn, tile * 64u, &rr[u]);
+        }
 #pragma unroll
-        for (int p = 0; p < BK; ++p) planes[u][p] = nt_load(&ki[(vp * 4u + kg) * BKK + p]);
-        sw[u] = nt_load(&ks[vp * 4u + kg]);
-        kv[u] = nt_load(&kn[vp]);
-        rv[u] = nt_load(&rn[vp]);
+        for (int u = 0; u < kAttU; ++u) {
+          const int pl = (t0 + u) * 16 + c16;
+          const float lt = tile_logit_f32<BK, true, NPK>(A, planes[u], sw[u], __uint_as_float(kr[u]),
+                                                         __uint_as_float(rr[u]), cst.f[0], cst.f[1], cst.f[2],
+                                                         cst.f[3]);
+          const float logit = (FULL || pl < npos) ? lt * scale : -INFINITY;
+          lg[wave][kg][pl] = logit;
+          mx = fmaxf(mx, logit);
+        }
       }
-#pragma unroll
-      for (int u = 0; u < kAttU; ++u) {
-        const int pl = (t0 + u) * 16 + c16;
-        const float lt = tile_logit_f32<BK, true, NPK>(A, planes[u], sw[u], kv[u], rv[u], cst.f[0], cst.f[1],
-                                                       cst.f[2], cst.f[3]);
-        const float logit = pl < npos ? lt * scale : -INFINITY;
-        lg[wave][kg][pl] = logit;
-        mx = fmaxf(mx, logit);
-      }
-    }
+      return mx;
+    };
+    float mx = npos == kAttKPW ? logits_of(std::true_type{}) : logits_of(std::false_type{});
     // max over the 16 lanes of this query (lanes 16 kg .. 16 kg + 15)
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -2364,20 +2420,21 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   // lane (c16, kg): query kg, positions 4 c16 + 64 r + {0..3}
   float lsum = 0.f, wmax = 0.f;
   {
-    const float *vn = vnorm + vb;
+    const bufrsrc rvn = buf_rsrc(vnorm + vb, (uint32_t)npos * 4u);
 #pragma unroll
     for (int r = 0; r < kAttKPW / 64; ++r) {
       const int pl0 = 64 * r + 4 * c16;
       const float4 lv = *reinterpret_cast<const float4 *>(&lg[wave][kg][pl0]);
       const float lvv[4] = {lv.x, lv.y, lv.z, lv.w};
+      uint32_t vnr[4];
+      buf_ldn<4>(rvn, (uint32_t)c16 * 16u + (uint32_t)r * 256u, 0u, vnr);  // past npos: zeros
       float wv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pl = pl0 + e;
-        const uint32_t pos = (uint32_t)pl;
         const float pe = pl < npos ? __expf(lvv[e] - m) : 0.f;
         lsum += pe;
-        wv[e] = pe * nt_load(&vn[min(pos, last)]);
+        wv[e] = pe * __uint_as_float(vnr[e]);
         wmax = fmaxf(wmax, wv[e]);
       }
       *reinterpret_cast<float4 *>(&lg[wave][kg][pl0]) = make_float4(wv[0], wv[1], wv[2], wv[3]);
@@ -2417,31 +2474,28 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   double qsum = 0.0;
   const uint32_t *vi = vidx + vb * 4 * BV;
   const uint32_t woff = (uint32_t)w * (4u * BV);  // byte offset of index word w
-  // quantisation of one block: lane (c16, kg) takes query kg, positions
-  // 4 c16 .. 4 c16 + 3 of the block
+  // value index words through a descriptor of the wave's npos codes; lane
+  // (c16 = (w, beta), kg) reads word w of positions 16 kg + 4 gi + e of a
+  // block: the lane's offset plus a scalar offset per load.  Quantisation of
+  // one block: lane (c16, kg) takes query kg, positions 4 c16 .. 4 c16 + 3.
+  const bufrsrc rvi = buf_rsrc(vi, (uint32_t)npos * 16u * BV);
+  const uint32_t vlane = (uint32_t)(16 * kg) * (16u * BV) + woff;
   for (int blk = 0; blk < kAttKPW / 64; ++blk) {
     // V index words of this lane's 16 positions (issued first)
     uint32_t x[4][4][BV];
+    if (npos == kAttKPW) {  // every access in range: scalar offsets
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
+      for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pos = min((uint32_t)(blk * 64 + 16 * kg + 4 * gi + e), last);
-        // a 32-bit byte offset from the wave-uniform base (one scalar base,
-        // one offset register per load)
-        const uint32_t *src =
-            reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(vi) + (__umul24(pos, 16u * BV) + woff));
-        if constexpr (BV == 2) {
-          const u32x2 t2 = nt_load2(src);
-          x[gi][e][0] = t2.x; x[gi][e][1] = t2.y;
-        } else if constexpr (BV == 4) {
-          const u32x4 t4 = nt_load4(src);
-          x[gi][e][0] = t4.x; x[gi][e][1] = t4.y; x[gi][e][2] = t4.z; x[gi][e][3] = t4.w;
-        } else {
+        for (int e = 0; e < 4; ++e)
+          buf_ldn<BV>(rvi, vlane, (uint32_t)(blk * 64 + 4 * gi + e) * (16u * BV), x[gi][e]);
+    } else {  // range-checked lane offsets: positions past npos read zeros
 #pragma unroll
-          for (int p = 0; p < BV; ++p) x[gi][e][p] = nt_load(src + p);
-        }
-      }
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          buf_ldn<BV>(rvi, vlane + (uint32_t)(blk * 64 + 4 * gi + e) * (16u * BV), 0u, x[gi][e]);
+    }
     {
       const float4 wv4 = *reinterpret_cast<const float4 *>(&lg[wave][kg][blk * 64 + 4 * c16]);
       const float wv[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
