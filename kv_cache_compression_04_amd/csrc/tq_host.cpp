@@ -456,7 +456,30 @@ static tq_status build_derived(const tq_params *p, int dev, Derived *D) {
                          [](int kt, int g, int e) { return 32 * kt + 16 * (e / 4) + 4 * g + e % 4; }, hi,
                          lo);
       if ((st = upload(&D->sp16_hi, hi)) || (st = upload(&D->sp16_lo, lo))) return st;
+      // query preparation: S q from q itself, in Pi's fragment layout
+      make_fragments_f16(s, kEncScale, col1, hi, lo);
+      if ((st = upload(&D->s16_hi, hi)) || (st = upload(&D->s16_lo, lo))) return st;
     }
+    // column sums of Pi and S and the largest row norm of S
+    std::vector<float> qs(256, 0.f);
+    double smax = 0.0;
+    for (int c = 0; c < 128; ++c) {
+      double a = 0.0, b = 0.0;
+      for (int r = 0; r < 128; ++r) {
+        a += pi[(size_t)r * 128 + c];
+        if (prod) b += s[(size_t)r * 128 + c];
+      }
+      qs[c] = (float)a;
+      qs[128 + c] = (float)b;
+    }
+    if (prod)
+      for (int r = 0; r < 128; ++r) {
+        double n2 = 0.0;
+        for (int c = 0; c < 128; ++c) n2 += s[(size_t)r * 128 + c] * s[(size_t)r * 128 + c];
+        smax = std::max(smax, std::sqrt(n2));
+      }
+    D->smax = std::nextafter((float)smax, INFINITY);  // a bound: never below the true norm
+    if ((st = upload(&D->qsums, qs))) return st;
   } else {
     // same column maps, general shapes, K-block-major fragments
     std::vector<uint4> fr;
@@ -485,6 +508,9 @@ static void free_derived(Derived *D) {
   (void)hipFree(D->pi16_lo);
   (void)hipFree(D->sp16_hi);
   (void)hipFree(D->sp16_lo);
+  (void)hipFree(D->s16_hi);
+  (void)hipFree(D->s16_lo);
+  (void)hipFree(D->qsums);
   (void)hipFree(D->pi_frag);
   (void)hipFree(D->sp_frag);
   (void)hipSetDevice(cur);

@@ -1065,15 +1065,16 @@ __device__ __forceinline__ int limb_of(int Q, int t) {
 // one group's work):
 //   1. each query is scaled by a power of two to norm [1, 2) and split into
 //      fp16 hi + lo (lane (column j, lane group g) holds coordinates
-//      32 kt + 8 g .. + 7 of query j, the encoder's operand layout);
-//   2. qt = Pi q on fp16 MFMAs against the encoder's fragments of 16 Pi (three
-//      passes: hi hi, lo hi, hi lo), wave w forming rotated rows 32 w .. + 31;
-//   3. qs = S q = S' qt (S' = S Pi^T) on the encoder's fragments of 16 S',
-//      the scaled qt coming back from LDS as the B operand, wave w forming
-//      rows 32 w .. + 31;
-//   4. per query: the exponents that put the largest operand below 2^26 and
-//      the per-query constants (float64 and float32);
-//   5. the int8 operands of the score MFMAs.  MFMA j (part j / 2, half j % 2;
+//      32 kt + 8 g .. + 7 of query j, the encoder's operand layout); the same
+//      lanes form ||q||, u . q and v . q (u, v the column sums of Pi and S);
+//   2. qt = Pi q and qs = S q on fp16 MFMAs against the fragments of 16 Pi
+//      and 16 S (three passes each: hi hi, lo hi, hi lo), independent of each
+//      other; wave w forms rows 32 w .. + 31 of both;
+//   3. per query, from ||q|| alone: the exponents that put the largest
+//      operand below 2^26 (|qt_c| <= ||q||, |qs_r| <= smax ||q||, smax the
+//      largest row norm of S: one or two of the 26 bits spent on the bound),
+//      and the constants (sum_c qt_c = u . q, sum_r qs_r = v . q);
+//   4. the int8 operands of the score MFMAs.  MFMA j (part j / 2, half j % 2;
 //      the sign part last) lane l = 16 kg + 4 jq + t holds limb t of query jq
 //      at the coordinates of lane group kg; one thread computes the 16 scaled
 //      values of (group, j, jq, kg) once and writes all four limbs.
@@ -1086,15 +1087,16 @@ constexpr int kQPThreads = 256;
 template <bool PROD>
 __global__ __launch_bounds__(kQPThreads) void qprep128_kernel(
     const float *__restrict__ q, int64_t g, int ngroups, int64_t nhg, const uint4 *__restrict__ pi_hi,
-    const uint4 *__restrict__ pi_lo, const uint4 *__restrict__ sp_hi, const uint4 *__restrict__ sp_lo,
-    Codebook cb, int m, i32x4 *__restrict__ aops, QConst *__restrict__ qc) {
+    const uint4 *__restrict__ pi_lo, const uint4 *__restrict__ s_hi, const uint4 *__restrict__ s_lo,
+    const float *__restrict__ qsums, float smax, Codebook cb, int m, i32x4 *__restrict__ aops,
+    QConst *__restrict__ qc) {
   __shared__ float qv[2][16][129];  // [0] = Pi q, [1] = S q, unscaled; column = 4 group + query
-  __shared__ float qts[16][129];    // Pi q scaled by 2^esh (the second product's operand)
   __shared__ int expo[16][2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, lg = lane >> 4;
   const int64_t hg0 = (int64_t)blockIdx.x * kQPGroups;
+  const int NP = cb.nparts;
   {
     const int64_t hg = hg0 + (col >> 2);
     const int jq = col & 3;
@@ -1111,133 +1113,101 @@ __global__ __launch_bounds__(kQPThreads) void qprep128_kernel(
         fa[h2][kt][0] = pi_hi[o];
         fa[h2][kt][1] = pi_lo[o];
         if (PROD) {
-          fs[h2][kt][0] = sp_hi[o];
-          fs[h2][kt][1] = sp_lo[o];
+          fs[h2][kt][0] = s_hi[o];
+          fs[h2][kt][1] = s_lo[o];
         }
       }
     uint4 raw[4][2];
     float ss = 0.f;
+    double du = 0.0, dv = 0.0;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(qrow + 32 * kt + 8 * lg);
+      const int c0 = 32 * kt + 8 * lg;
+      const uint4 *p = reinterpret_cast<const uint4 *>(qrow + c0);
       raw[kt][0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
       raw[kt][1] = valid ? p[1] : make_uint4(0, 0, 0, 0);
       const uint32_t w[8] = {raw[kt][0].x, raw[kt][0].y, raw[kt][0].z, raw[kt][0].w,
                              raw[kt][1].x, raw[kt][1].y, raw[kt][1].z, raw[kt][1].w};
+      const float4 u0 = *reinterpret_cast<const float4 *>(qsums + c0);
+      const float4 u1 = *reinterpret_cast<const float4 *>(qsums + c0 + 4);
+      const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      float vv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (PROD) {
+        const float4 v0 = *reinterpret_cast<const float4 *>(qsums + 128 + c0);
+        const float4 v1 = *reinterpret_cast<const float4 *>(qsums + 128 + c0 + 4);
+        vv[0] = v0.x; vv[1] = v0.y; vv[2] = v0.z; vv[3] = v0.w;
+        vv[4] = v1.x; vv[5] = v1.y; vv[6] = v1.z; vv[7] = v1.w;
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss = fmaf(__uint_as_float(w[i]), __uint_as_float(w[i]), ss);
+      for (int i = 0; i < 8; ++i) {
+        const float x = __uint_as_float(w[i]);
+        ss = fmaf(x, x, ss);
+        du = fma((double)uu[i], (double)x, du);
+        if (PROD) dv = fma((double)vv[i], (double)x, dv);
+      }
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    const int esh = enc_scale_exp(sqrtf(ss));  // rotated values come out times 2^esh
+    du += __shfl_xor(du, 16);
+    du += __shfl_xor(du, 32);
+    if (PROD) {
+      dv += __shfl_xor(dv, 16);
+      dv += __shfl_xor(dv, 32);
+    }
+    const float qn = sqrtf(ss);
+    const int esh = enc_scale_exp(qn);  // projected values come out times 2^esh
+    // 3. exponents and constants of query col (lanes of lane group 0)
+    if (lg == 0 && wave == 0) {
+      double acoef = 0, amax = 0;
+      for (int p = 0; p < NP; ++p) {
+        acoef += cb.coef[p];
+        amax = fmax(amax, fabs(cb.coef[p]));
+      }
+      int e1 = 0, e2 = 0, k;
+      const double A1 = 2.0 * amax * (double)qn, A2 = 2.0 * (double)smax * (double)qn;
+      if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
+      if (PROD && A2 > 0) { frexp(A2, &k); e2 = 26 - k; }
+      expo[col][0] = e1;
+      expo[col][1] = e2;
+      if ((col >> 2) < kQPGroups && hg < nhg) {
+        const double cq = PROD ? sqrt(M_PI / 2.0) / m : 0.0;
+        QConst o;
+        o.idx_scale = ldexp(1.0, -e1);
+        o.idx_bias = acoef * du;
+        o.sgn_scale = cq * ldexp(1.0, -e2);
+        o.sgn_bias = cq * dv;
+        o.f[0] = (float)o.idx_scale;
+        o.f[1] = (float)o.idx_bias;
+        o.f[2] = (float)o.sgn_scale;
+        o.f[3] = (float)o.sgn_bias;
+        qc[hg * 4 + jq] = o;
+      }
+    }
     uint4 xh[4], xl[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) x_frag_f16<false>(raw[kt], esh - kEncScaleLog2, xh[kt], xl[kt]);
-    // 2. Pi q, rows 32 wave .. + 31
+    // 2. Pi q and S q, rows 32 wave .. + 31 of each
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int nt = 2 * wave + h2;
-      // three independent accumulation chains (one per pass), summed after
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const f16x8 ah = as_f16x8(fa[h2][kt][0]), al = as_f16x8(fa[h2][kt][1]);
-        a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xh[kt]), a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_f16x8(xh[kt]), a1, 0, 0, 0);
-        a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xl[kt]), a2, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * nt + 4 * lg + r;
-        const float v = a0[r] + (a1[r] + a2[r]);
-        qts[col][row] = v;
-        qv[0][col][row] = ldexpf(v, -esh);
-      }
-    }
-    if (PROD) {
-      __syncthreads();
-      // 3. S q = S' (Pi q): element e of lane group lg in block kt is rotated
-      // coordinate 32 kt + 16 (e / 4) + 4 lg + e % 4 (the S' fragments' order)
-      uint4 bh[4], bl[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = qts[col][32 * kt + 16 * (e >> 2) + 4 * lg + (e & 3)];
-        uint32_t hh[4], ll[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split2h(v[2 * i], v[2 * i + 1], hh[i], ll[i]);
-        bh[kt] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
-        bl[kt] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
-      }
+    for (int mat = 0; mat < (PROD ? 2 : 1); ++mat)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int nt = 2 * wave + h2;
+        // three independent accumulation chains (one per pass), summed after
         f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const f16x8 ah = as_f16x8(fs[h2][kt][0]), al = as_f16x8(fs[h2][kt][1]);
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(bh[kt]), a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_f16x8(bh[kt]), a1, 0, 0, 0);
-          a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(bl[kt]), a2, 0, 0, 0);
+          const uint4 *fr = mat ? fs[h2][kt] : fa[h2][kt];
+          const f16x8 ah = as_f16x8(fr[0]), al = as_f16x8(fr[1]);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xh[kt]), a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_f16x8(xh[kt]), a1, 0, 0, 0);
+          a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xl[kt]), a2, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          qv[1][col][16 * nt + 4 * lg + r] = ldexpf(a0[r] + (a1[r] + a2[r]), -esh - kEncScaleLog2);
+        for (int r = 0; r < 4; ++r) qv[mat][col][16 * nt + 4 * lg + r] = ldexpf(a0[r] + (a1[r] + a2[r]), -esh);
       }
-    }
   }
   __syncthreads();
-  const int NP = cb.nparts;
-  // 4. the waves reduce the 4 kQPGroups queries in turn (query c = 4 group +
-  // jq): max |qt|, max |qs|, sum qt, sum qs
-  {
-    double acoef = 0, amax = 0;
-    for (int p = 0; p < NP; ++p) {
-      acoef += cb.coef[p];
-      amax = fmax(amax, fabs(cb.coef[p]));
-    }
-#pragma unroll 1
-    for (int c = wave; c < 4 * kQPGroups; c += kQPThreads / 64) {
-      const int64_t hg = hg0 + (c >> 2);
-      const int jq = c & 3;
-      float mq = fmaxf(fabsf(qv[0][c][lane]), fabsf(qv[0][c][lane + 64]));
-      float ms = PROD ? fmaxf(fabsf(qv[1][c][lane]), fabsf(qv[1][c][lane + 64])) : 0.f;
-      double sq = (double)qv[0][c][lane] + (double)qv[0][c][lane + 64];
-      double sqs = PROD ? (double)qv[1][c][lane] + (double)qv[1][c][lane + 64] : 0.0;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        mq = fmaxf(mq, __shfl_xor(mq, off));
-        ms = fmaxf(ms, __shfl_xor(ms, off));
-        sq += __shfl_xor(sq, off);
-        sqs += __shfl_xor(sqs, off);
-      }
-      if (lane == 0) {
-        // scale the largest operand magnitude below 2^26
-        int e1 = 0, e2 = 0, k;
-        const double A1 = 2.0 * amax * (double)mq, A2 = 2.0 * (double)ms;
-        if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
-        if (A2 > 0) { frexp(A2, &k); e2 = 26 - k; }
-        expo[c][0] = e1;
-        expo[c][1] = e2;
-        if (hg < nhg) {
-          const double cq = sqrt(M_PI / 2.0) / m;
-          QConst o;
-          o.idx_scale = ldexp(1.0, -e1);
-          o.idx_bias = acoef * sq;
-          o.sgn_scale = cq * ldexp(1.0, -e2);
-          o.sgn_bias = cq * sqs;
-          o.f[0] = (float)o.idx_scale;
-          o.f[1] = (float)o.idx_bias;
-          o.f[2] = (float)o.sgn_scale;
-          o.f[3] = (float)o.sgn_bias;
-          qc[hg * 4 + jq] = o;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // 5. operands: unit (group gi, j, jq, kg, w): word w of the four lanes 16 kg + 4 jq + t
+  // 4. operands: unit (group gi, j, jq, kg, w): word w of the four lanes 16 kg + 4 jq + t
   const int NMF = score_mfmas(NP, PROD);
   uint32_t *aw = reinterpret_cast<uint32_t *>(aops);
   for (int i = tid; i < kQPGroups * NMF * 64; i += kQPThreads) {
@@ -1275,8 +1245,8 @@ static void launch_qprep128(const Derived &D, const float *q, int64_t g, int ngr
                             i32x4 *aops, QConst *qc, hipStream_t s) {
   const unsigned grid = (unsigned)((nhg + kQPGroups - 1) / kQPGroups);
   qprep128_kernel<PROD><<<dim3(grid), dim3(kQPThreads), 0, s>>>(
-      q, g, ngroups, nhg, (const uint4 *)D.pi16_hi, (const uint4 *)D.pi16_lo, (const uint4 *)D.sp16_hi,
-      (const uint4 *)D.sp16_lo, D.cb, D.p.m, aops, qc);
+      q, g, ngroups, nhg, (const uint4 *)D.pi16_hi, (const uint4 *)D.pi16_lo, (const uint4 *)D.s16_hi,
+      (const uint4 *)D.s16_lo, D.qsums, D.smax, D.cb, D.p.m, aops, qc);
 }
 
 constexpr int kScoreU = 4;  // tiles per load batch (64 keys)
