@@ -3532,8 +3532,17 @@ __global__ __launch_bounds__(kSplitScoreThreads) void split_score128_kernel(
 }
 
 template <int B0, int B1, int DG0>
-static void launch_split_encode_t(const SplitDerived &D, const void *x, bool bf, int64_t n, int grid,
-                                  tq_split_codes c, hipStream_t s) {
+static void launch_split_encode_t(const SplitDerived &D, const void *x, bool bf, int64_t n, tq_split_codes c,
+                                  hipStream_t s) {
+  // as many workgroups as fit in the CUs' LDS at once (the fragments, and for
+  // bfloat16 keys the staged rows): one per CU for bfloat16 keys, two for
+  // float32 keys with 64 outlier channels
+  constexpr size_t kLdsPerCU = 160 * 1024;
+  const size_t lds = 16 * (size_t)(4 * split_frag_u4(DG0) + 4 * split_frag_u4(128 - DG0)) +
+                     (bf ? (size_t)kSplitWaves * 16 * kSplitRowB : 0) + 1024;
+  const int64_t per_cu = std::max<int64_t>(1, (int64_t)(kLdsPerCU / lds));
+  const int64_t need = ((n + 15) / 16 + kSplitWaves - 1) / kSplitWaves;
+  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * per_cu);
   const uint4 *fr = reinterpret_cast<const uint4 *>(D.frag);
   const float *cbk = D.mat + split_codebook_offset(D.DG);
   if (bf)
@@ -3545,12 +3554,12 @@ static void launch_split_encode_t(const SplitDerived &D, const void *x, bool bf,
 }
 
 template <int B0, int B1>
-static tq_status launch_split_encode_b(const SplitDerived &D, const void *x, bool bf, int64_t n, int grid,
+static tq_status launch_split_encode_b(const SplitDerived &D, const void *x, bool bf, int64_t n,
                                        tq_split_codes c, hipStream_t s) {
   switch (D.DG[0]) {
-    case 32: launch_split_encode_t<B0, B1, 32>(D, x, bf, n, grid, c, s); break;
-    case 64: launch_split_encode_t<B0, B1, 64>(D, x, bf, n, grid, c, s); break;
-    case 96: launch_split_encode_t<B0, B1, 96>(D, x, bf, n, grid, c, s); break;
+    case 32: launch_split_encode_t<B0, B1, 32>(D, x, bf, n, c, s); break;
+    case 64: launch_split_encode_t<B0, B1, 64>(D, x, bf, n, c, s); break;
+    case 96: launch_split_encode_t<B0, B1, 96>(D, x, bf, n, c, s); break;
     default:
       set_error("tq_split_encode: no kernel for %d outlier channels", D.DG[0]);
       return TQ_ERR_UNSUPPORTED;
@@ -3560,17 +3569,12 @@ static tq_status launch_split_encode_b(const SplitDerived &D, const void *x, boo
 
 tq_status launch_split_encode(const SplitDerived &D, const void *x, int dtype, int64_t n,
                               tq_split_codes c, hipStream_t s) {
-  const int64_t nbatch = (n + 15) / 16;
-  const int64_t need = (nbatch + kSplitWaves - 1) / kSplitWaves;
-  // 64 KB of fragments per workgroup of 16 waves at 64 outlier channels (two
-  // workgroups per CU), 80 KB otherwise (one)
-  const int grid = (int)std::min<int64_t>(need, (int64_t)num_cus(D.device) * 2);
   const bool bf = dtype == TQ_BF16;
   tq_status st;
   if (D.B[0] == 2 && D.B[1] == 1)
-    st = launch_split_encode_b<2, 1>(D, x, bf, n, grid, c, s);
+    st = launch_split_encode_b<2, 1>(D, x, bf, n, c, s);
   else if (D.B[0] == 3 && D.B[1] == 2)
-    st = launch_split_encode_b<3, 2>(D, x, bf, n, grid, c, s);
+    st = launch_split_encode_b<3, 2>(D, x, bf, n, c, s);
   else {
     set_error("tq_split_encode: no kernel for Lloyd-Max bits (%d, %d)", D.B[0], D.B[1]);
     return TQ_ERR_UNSUPPORTED;
