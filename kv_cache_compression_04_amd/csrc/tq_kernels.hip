@@ -13,10 +13,12 @@
 //
 // Design notes for gfx950 (wave64, MFMA, 160 KB LDS):
 //   * encode: both projections are dense 128 x 128 contractions per vector and
-//     run on bf16 MFMA (v_mfma_f32_16x16x32_bf16).  Bucket decisions need the
-//     rotated coordinates to ~1e-7, so the matrices are split hi + lo in bf16
-//     (and float32 inputs / the residual too), giving float32-level products.
-//     The whole bf16 split of Pi and S' = S Pi^T lives in LDS (128 KB) for the
+//     run on 16-bit MFMAs.  Bucket decisions need the rotated coordinates to
+//     ~1e-7, so the matrices are split hi + lo (and float32 inputs and the
+//     residual too), giving float32-level products: bfloat16 keys against the
+//     bf16 split of Pi, float32 keys and the residual in fp16 hi + lo after a
+//     power-of-two scaling of each vector (fp16 keeps 11 bits per piece).
+//     The split matrices (Pi and S' = S Pi^T) live in LDS (128 KB) for the
 //     life of a persistent workgroup.  The first GEMM's output registers are
 //     already the second GEMM's operand layout, so the residual never leaves
 //     registers, and each lane packs its own 32-bit words of index planes and
@@ -90,6 +92,19 @@ __device__ __forceinline__ void split2h(float a, float b, uint32_t &hi, uint32_t
   lo = pk_f16(a - (float)h[0], b - (float)h[1]);
 }
 
+// The same split in three instructions: the remainders a - hi, b - hi are
+// formed and rounded to fp16 by one mixed-precision fma each (hi read as
+// fp16, a and b as float32), written straight into the halves of lo.
+__device__ __forceinline__ void split2h_mix(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pk_f16(a, b);
+  uint32_t l;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(l)
+      : "v"(hi), "v"(a), "v"(b));
+  lo = l;
+}
+
 // Streaming accesses: packed codes that a call reads once and outputs it
 // writes once go through the non-temporal path, so they do not displace
 // reused data from the caches (measured: the 32-layer score call ~7% faster).
@@ -149,6 +164,14 @@ __device__ __forceinline__ void buf_ldn(bufrsrc r, uint32_t voff, uint32_t soff,
 // that exponent (0 for a zero vector, whose inputs are all zero anyway).
 __device__ __forceinline__ int enc_scale_exp(float nu) {
   return nu > 0.f ? kEncScaleLog2 + 1 - __builtin_amdgcn_frexp_expf(nu) : 0;
+}
+
+// a * b - c in one v_fma_f32 with a negated third operand (left to itself the
+// compiler moves the negation into an integer XOR of c's sign)
+__device__ __forceinline__ float fma_negc(float a, float b, float c) {
+  float r;
+  asm("v_fma_f32 %0, %1, %2, -%3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // w = 2 w + (bit of this lane in mask): one v_addc with the lane mask as
@@ -271,7 +294,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
        batch += (int64_t)gridDim.x * kEncWaves) {
     const int64_t v0 = batch * kEncBatch;
     uint4 xh[kEncCT][4], xl[kEncCT][4];
-    float nu[kEncCT];
+    float nu[kEncCT], ysc[kEncCT];
     int esh[kEncCT];
     // the codebook is odd: magnitudes only, scaled by ||x|| 2^esh
     constexpr int kHalf = B > 0 ? 1 << (B - 1) : 1;
@@ -294,13 +317,24 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
       // a zero vector gets y' = 0 and a zero residual
       esh[ct] = enc_scale_exp(nu[ct]);
       const float nus = ldexpf(nu[ct], esh[ct]);
+      // bfloat16 keys enter a bf16 MFMA against the bf16 hi + lo split of Pi
+      // as they are, so y = Pi x comes out unscaled: the boundaries are
+      // scaled by ||x|| alone and the residual is brought to the fp16 scale
+      // of GEMM 2 by the factor 2^esh inside its fma
+      ysc[ct] = XBF16 ? ldexpf(1.f, esh[ct]) : 1.f;
+      const float nut = XBF16 ? nu[ct] : nus;
+      if (XBF16) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) x_frag_f16<XBF16>(raw[kt], esh[ct] - kEncScaleLog2, xh[ct][kt], xl[ct][kt]);
+        for (int kt = 0; kt < 4; ++kt) xh[ct][kt] = raw[kt][0];
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) x_frag_f16<XBF16>(raw[kt], esh[ct] - kEncScaleLog2, xh[ct][kt], xl[ct][kt]);
+      }
 #pragma unroll
       for (int j = 0; j < kHalf; ++j) cp[ct][j] = B > 0 ? cb.c[kHalf + j] * nus : 0.f;
       // (for a zero vector the unscaled boundaries reproduce the u = 0 decisions)
 #pragma unroll
-      for (int j = 0; j + 1 < kHalf; ++j) tp[ct][j] = nu[ct] > 0.f ? cb.t[kHalf + j] * nus : cb.t[kHalf + j];
+      for (int j = 0; j + 1 < kHalf; ++j) tp[ct][j] = nu[ct] > 0.f ? cb.t[kHalf + j] * nut : cb.t[kHalf + j];
     }
 
     // Coordinates are processed in 4 blocks of 32 (kt2).  For each block:
@@ -335,15 +369,20 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
         for (int kt = 0; kt < 4; ++kt) {                                                                                                    \
   _Pragma("unroll")                                                                                                                         \
           for (int h = 0; h < 2; ++h) {                                                                                                     \
-            const f16x8 ah = as_f16x8(Pk_[(h * 4 + kt) * 64]);                                                                              \
-            const f16x8 al = as_f16x8(Pk_[kFragU4 + (h * 4 + kt) * 64]);                                                                    \
+            const uint4 ah_ = Pk_[(h * 4 + kt) * 64];                                                                                      \
+            const uint4 al_ = Pk_[kFragU4 + (h * 4 + kt) * 64];                                                                            \
   _Pragma("unroll")                                                                                                                         \
             for (int ct = 0; ct < kEncCT; ++ct) {                                                                                           \
-              const f16x8 bh = as_f16x8(xh[ct][kt]);                                                                                        \
-              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[h][ct], 0, 0, 0);                                             \
-              acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[h][ct], 0, 0, 0);                                             \
-              if (!XBF16)                                                                                                                   \
+              if (XBF16) {                                                                                                                  \
+                const bf16x8 bh = as_bf16x8(xh[ct][kt]);                                                                                    \
+                acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah_), bh, acc[h][ct], 0, 0, 0);                              \
+                acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al_), bh, acc[h][ct], 0, 0, 0);                              \
+              } else {                                                                                                                      \
+                const f16x8 ah = as_f16x8(ah_), al = as_f16x8(al_), bh = as_f16x8(xh[ct][kt]);                                              \
+                acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[h][ct], 0, 0, 0);                                           \
+                acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[h][ct], 0, 0, 0);                                           \
                 acc[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xl[ct][kt]), acc[h][ct], 0, 0, 0);                         \
+              }                                                                                                                             \
             }                                                                                                                               \
           }                                                                                                                                 \
         }                                                                                                                                   \
@@ -356,7 +395,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
   _Pragma("unroll")                                                                                                                         \
             for (int i = 0; i < 4; ++i) {                                                                                                   \
               const float y = acc[h][ct][i];                                                                                                \
-              float r = y;                                                                                                                  \
+              float r = XBF16 ? y * ysc[ct] : y;                                                                                            \
               if (B > 0) {                                                                                                                  \
                 const float a = fabsf(y);                                                                                                   \
                 const uint64_t sm = __builtin_amdgcn_ballot_w64(y >= 0.f);                                                                  \
@@ -376,13 +415,13 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
                   planes[ct][p] = shift_in(planes[ct][p], ~(sm ^ mk));                                                                      \
                 }                                                                                                                           \
                 planes[ct][B - 1] = shift_in(planes[ct][B - 1], sm);                                                                        \
-                r = y - __builtin_copysignf(cm, y);                                                                                         \
+                r = XBF16 ? fma_negc(y, ysc[ct], __builtin_copysignf(cm, y)) : y - __builtin_copysignf(cm, y);                              \
               }                                                                                                                             \
               rsq[ct] = fmaf(r, r, rsq[ct]);                                                                                                \
               rho[i] = r;                                                                                                                   \
             }                                                                                                                               \
   _Pragma("unroll")                                                                                                                         \
-            for (int hh = 0; hh < 2; ++hh) split2h(rho[2 * hh], rho[2 * hh + 1], rh[ct][2 * h + hh], rl[ct][2 * h + hh]);                   \
+            for (int hh = 0; hh < 2; ++hh) split2h_mix(rho[2 * hh], rho[2 * hh + 1], rh[ct][2 * h + hh], rl[ct][2 * h + hh]);               \
           }                                                                                                                                 \
         }                                                                                                                                   \
         if (PROD) {                                                                                                                         \
@@ -459,8 +498,9 @@ static void launch_encode_t(const Derived &D, const void *x, int dtype, int64_t 
   const dim3 blk(kEncWaves * 64);
   const uint4 *ph = (const uint4 *)D.pi16_hi, *pl = (const uint4 *)D.pi16_lo;
   const uint4 *sh = (const uint4 *)D.sp16_hi, *sl = (const uint4 *)D.sp16_lo;
-  if (dtype == TQ_BF16)
-    encode128_kernel<B, PROD, true><<<grid, blk, 0, s>>>(x, n, ph, pl, sh, sl, D.cb, c.idx, c.sgn,
+  if (dtype == TQ_BF16)  // bfloat16 keys: GEMM 1 on bf16 MFMAs against the bf16 split of Pi
+    encode128_kernel<B, PROD, true><<<grid, blk, 0, s>>>(x, n, (const uint4 *)D.pi_hi, (const uint4 *)D.pi_lo,
+                                                         sh, sl, D.cb, c.idx, c.sgn,
                                                          c.knorm, c.rnorm, slots, capacity);
   else
     encode128_kernel<B, PROD, false><<<grid, blk, 0, s>>>(x, n, ph, pl, sh, sl, D.cb, c.idx, c.sgn,
