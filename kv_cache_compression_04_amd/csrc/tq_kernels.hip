@@ -446,7 +446,11 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
     for (int kt2 = 1; kt2 < 4; ++kt2) TQ_ENC_BLOCK(kt2, false);
 #undef TQ_ENC_BLOCK
     // sign bits: acc2[nt][ct][i] = z[row 16 nt + 4 g + i][vector 16 ct + vcol],
-    // shifted in from the highest row down so that row 4 nt + i lands at bit 4 nt + i
+    // shifted in from the highest row down so that row 4 nt + i lands at bit
+    // 4 nt + i.  One v_alignbit per bit shifts in the float's sign bit (1 for
+    // z < 0), and the word is complemented once at the end.  An exactly zero
+    // z comes out of the MFMA accumulation as +0 (its first product starts
+    // from +0), so it gets bit 1 as the z >= 0 rule says.
     uint32_t sbits[kEncCT];
 #pragma unroll
     for (int ct = 0; ct < kEncCT; ++ct) {
@@ -455,7 +459,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
 #pragma unroll
         for (int nt = 7; nt >= 0; --nt)
 #pragma unroll
-          for (int i = 3; i >= 0; --i) w = shift_in(w, __builtin_amdgcn_ballot_w64(acc2[nt][ct][i] >= 0.f));
+          for (int i = 3; i >= 0; --i) w = __builtin_amdgcn_alignbit(w, __float_as_uint(acc2[nt][ct][i]), 31);
+        w = ~w;
       }
       sbits[ct] = w;
     }
