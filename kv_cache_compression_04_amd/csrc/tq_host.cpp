@@ -456,9 +456,6 @@ static tq_status build_derived(const tq_params *p, int dev, Derived *D) {
                          [](int kt, int g, int e) { return 32 * kt + 16 * (e / 4) + 4 * g + e % 4; }, hi,
                          lo);
       if ((st = upload(&D->sp16_hi, hi)) || (st = upload(&D->sp16_lo, lo))) return st;
-      // query preparation: S q from q itself, in Pi's fragment layout
-      make_fragments_f16(s, kEncScale, col1, hi, lo);
-      if ((st = upload(&D->s16_hi, hi)) || (st = upload(&D->s16_lo, lo))) return st;
     }
     // column sums of Pi and S and the largest row norm of S
     std::vector<float> qs(256, 0.f);
@@ -480,6 +477,16 @@ static tq_status build_derived(const tq_params *p, int dev, Derived *D) {
       }
     D->smax = std::nextafter((float)smax, INFINITY);  // a bound: never below the true norm
     if ((st = upload(&D->qsums, qs))) return st;
+    // the query preparation's matrix, column-major: qmat[c][r] = Pi[r][c]
+    // for r < 128 and S[r - 128][c] for r >= 128 (zero in mse mode), so the
+    // threads of one column read one contiguous kilobyte
+    std::vector<float> qm((size_t)128 * 256, 0.f);
+    for (int c = 0; c < 128; ++c)
+      for (int r = 0; r < 128; ++r) {
+        qm[(size_t)c * 256 + r] = (float)pi[(size_t)r * 128 + c];
+        if (prod) qm[(size_t)c * 256 + 128 + r] = (float)s[(size_t)r * 128 + c];
+      }
+    if ((st = upload(&D->qmat, qm))) return st;
   } else {
     // same column maps, general shapes, K-block-major fragments
     std::vector<uint4> fr;
@@ -508,9 +515,8 @@ static void free_derived(Derived *D) {
   (void)hipFree(D->pi16_lo);
   (void)hipFree(D->sp16_hi);
   (void)hipFree(D->sp16_lo);
-  (void)hipFree(D->s16_hi);
-  (void)hipFree(D->s16_lo);
   (void)hipFree(D->qsums);
+  (void)hipFree(D->qmat);
   (void)hipFree(D->pi_frag);
   (void)hipFree(D->sp_frag);
   (void)hipSetDevice(cur);

@@ -63,14 +63,14 @@ struct Derived {
   uint16_t *pi16_lo = nullptr;
   uint16_t *sp16_hi = nullptr;
   uint16_t *sp16_lo = nullptr;
-  // query preparation (d = m = 128): fp16 fragments of kEncScale * S in the
-  // layout of Pi's (S q straight from q), the column sums of Pi and S
-  // (float [2][128]: sum_c (Pi q)_c = u . q, sum_r (S q)_r = v . q) and the
-  // largest row norm of S (|(S q)_r| <= smax ||q||)
-  uint16_t *s16_hi = nullptr;
-  uint16_t *s16_lo = nullptr;
+  // query preparation (d = m = 128): the column sums of Pi and S (float
+  // [2][128]: sum_c (Pi q)_c = u . q, sum_r (S q)_r = v . q) and the largest
+  // row norm of S (|(S q)_r| <= smax ||q||)
   float *qsums = nullptr;
   float smax = 0.f;
+  // float32 [128 columns][256 rows]: column c of Pi (rows 0..127) and of S
+  // (rows 128..255), for the query preparation's coalesced projections
+  float *qmat = nullptr;
   // General shapes (d, m multiples of 128 other than d = m = 128): GEMM
   // fragments [K/32 block kt][16-row tile nt][hi, lo][lane] of uint4 (8 fp16
   // of kEncScale * the matrix).

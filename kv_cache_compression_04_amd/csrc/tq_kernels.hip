@@ -1104,168 +1104,131 @@ __device__ __forceinline__ int limb_of(int Q, int t) {
   return digit;
 }
 
-// Query preparation for the d = 128 kernels.  One workgroup of 4 waves takes
-// kQPGroups query groups of 4 queries (columns 4 group + query of an MFMA
-// tile; with one group per workgroup, the latency of a small call is that of
-// one group's work):
-//   1. each query is scaled by a power of two to norm [1, 2) and split into
-//      fp16 hi + lo (lane (column j, lane group g) holds coordinates
-//      32 kt + 8 g .. + 7 of query j, the encoder's operand layout); the same
-//      lanes form ||q||, u . q and v . q (u, v the column sums of Pi and S);
-//   2. qt = Pi q and qs = S q on fp16 MFMAs against the fragments of 16 Pi
-//      and 16 S (three passes each: hi hi, lo hi, hi lo), independent of each
-//      other; wave w forms rows 32 w .. + 31 of both;
-//   3. per query, from ||q|| alone: the exponents that put the largest
+// Query preparation for the d = 128 kernels.  One workgroup of 1024 threads
+// takes one query group (4 queries of one KV head); the call is latency-bound
+// (a decode step has a few dozen groups), so the work of a group is spread
+// over as many threads as it has independent pieces:
+//   1. thread (quarter cq, row r) requests columns 32 cq .. 32 cq + 31 of row
+//      r of [Pi; S] first (column-major copy: each column is one contiguous
+//      kilobyte), then the group's queries land in LDS;
+//   2. the thread forms its partial dot products with the 4 queries with
+//      float64 accumulation; the four quarters are summed through LDS,
+//      giving qt = Pi q and qs = S q rounded once to float32 (~6e-8 of each
+//      value, below the operands' 26-bit quantisation step);
+//   3. per query (one wave each): ||q||, u . q and v . q (u, v the column
+//      sums of Pi and S) in float64; the exponents that put the largest
 //      operand below 2^26 (|qt_c| <= ||q||, |qs_r| <= smax ||q||, smax the
 //      largest row norm of S: one or two of the 26 bits spent on the bound),
 //      and the constants (sum_c qt_c = u . q, sum_r qs_r = v . q);
 //   4. the int8 operands of the score MFMAs.  MFMA j (part j / 2, half j % 2;
 //      the sign part last) lane l = 16 kg + 4 jq + t holds limb t of query jq
 //      at the coordinates of lane group kg; one thread computes the 16 scaled
-//      values of (group, j, jq, kg) once and writes all four limbs.
-// The projections carry ~2^-21 of ||q|| (fp16 hi + lo products, float32
-// accumulation), far below the operands' 26-bit quantisation step relative
-// to the logit scale.
-constexpr int kQPGroups = 1;  // query groups per workgroup (at most 4)
-constexpr int kQPThreads = 256;
+//      values of (j, jq, kg) once and writes all four limbs.
+constexpr int kQPThreads = 1024;
 
 template <bool PROD>
 __global__ __launch_bounds__(kQPThreads) void qprep128_kernel(
-    const float *__restrict__ q, int64_t g, int ngroups, int64_t nhg, const uint4 *__restrict__ pi_hi,
-    const uint4 *__restrict__ pi_lo, const uint4 *__restrict__ s_hi, const uint4 *__restrict__ s_lo,
+    const float *__restrict__ q, int64_t g, int ngroups, const float *__restrict__ qmat,
     const float *__restrict__ qsums, float smax, Codebook cb, int m, i32x4 *__restrict__ aops,
     QConst *__restrict__ qc) {
-  __shared__ float qv[2][16][129];  // [0] = Pi q, [1] = S q, unscaled; column = 4 group + query
-  __shared__ int expo[16][2];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, lg = lane >> 4;
-  const int64_t hg0 = (int64_t)blockIdx.x * kQPGroups;
-  const int NP = cb.nparts;
-  {
-    const int64_t hg = hg0 + (col >> 2);
-    const int jq = col & 3;
-    const int64_t h = hg / ngroups, qh = (hg % ngroups) * 4 + jq;
-    const bool valid = (col >> 2) < kQPGroups && hg < nhg && qh < g;
-    const float *qrow = q + (h * g + (valid ? qh : 0)) * 128;
-    // the matrix fragments of this wave's rows, requested before anything else
-    uint4 fa[2][4][2], fs[2][4][2];
+  constexpr int R = PROD ? 256 : 128;  // rows of [Pi; S] in use
+  __shared__ float qs[4][128];           // the group's queries (missing ones zero)
+  __shared__ double part[4][4][R];       // [quarter][query][row] partial projections
+  __shared__ float qv[4][R];             // [query][row]: rows < 128 Pi q, the rest S q
+  __shared__ int expo[4][2];
+  const int tid = threadIdx.x;
+  const int r = tid & 255, cq = tid >> 8;
+  const int64_t hg = blockIdx.x;
+  const int64_t h = hg / ngroups;
+  const int grp = (int)(hg % ngroups);
+  // 1. this thread's 32 matrix entries, then the queries
+  float mv[32];
+  if (r < R) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int k = 0; k < 32; ++k) mv[k] = qmat[(32 * cq + k) * 256 + r];
+  }
+  if (tid < 512) {
+    const int j = tid >> 7, c = tid & 127;
+    const int64_t qh = (int64_t)grp * 4 + j;
+    qs[j][c] = qh < g ? q[(h * g + qh) * 128 + c] : 0.f;
+  }
+  __syncthreads();
+  // 2. partial projections over this thread's quarter of the columns
+  if (r < R) {
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int o = ((2 * wave + h2) * 4 + kt) * 64 + lane;
-        fa[h2][kt][0] = pi_hi[o];
-        fa[h2][kt][1] = pi_lo[o];
-        if (PROD) {
-          fs[h2][kt][0] = s_hi[o];
-          fs[h2][kt][1] = s_lo[o];
-        }
+    for (int k = 0; k < 32; k += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 qq = *reinterpret_cast<const float4 *>(&qs[j][32 * cq + k]);
+        a[j] = fma((double)mv[k], (double)qq.x, a[j]);
+        a[j] = fma((double)mv[k + 1], (double)qq.y, a[j]);
+        a[j] = fma((double)mv[k + 2], (double)qq.z, a[j]);
+        a[j] = fma((double)mv[k + 3], (double)qq.w, a[j]);
       }
-    uint4 raw[4][2];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[cq][j][r] = a[j];
+  }
+  // 3. per query j (wave j): norm, column-sum dots, exponents, constants
+  if (tid < 256) {
+    const int j = tid >> 6, lane = tid & 63;
     float ss = 0.f;
     double du = 0.0, dv = 0.0;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int c0 = 32 * kt + 8 * lg;
-      const uint4 *p = reinterpret_cast<const uint4 *>(qrow + c0);
-      raw[kt][0] = valid ? p[0] : make_uint4(0, 0, 0, 0);
-      raw[kt][1] = valid ? p[1] : make_uint4(0, 0, 0, 0);
-      const uint32_t w[8] = {raw[kt][0].x, raw[kt][0].y, raw[kt][0].z, raw[kt][0].w,
-                             raw[kt][1].x, raw[kt][1].y, raw[kt][1].z, raw[kt][1].w};
-      const float4 u0 = *reinterpret_cast<const float4 *>(qsums + c0);
-      const float4 u1 = *reinterpret_cast<const float4 *>(qsums + c0 + 4);
-      const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-      float vv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (PROD) {
-        const float4 v0 = *reinterpret_cast<const float4 *>(qsums + 128 + c0);
-        const float4 v1 = *reinterpret_cast<const float4 *>(qsums + 128 + c0 + 4);
-        vv[0] = v0.x; vv[1] = v0.y; vv[2] = v0.z; vv[3] = v0.w;
-        vv[4] = v1.x; vv[5] = v1.y; vv[6] = v1.z; vv[7] = v1.w;
-      }
+    for (int e = 0; e < 2; ++e) {
+      const int c = lane + 64 * e;
+      const float x = qs[j][c];
+      ss = fmaf(x, x, ss);
+      du = fma((double)qsums[c], (double)x, du);
+      if (PROD) dv = fma((double)qsums[128 + c], (double)x, dv);
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = __uint_as_float(w[i]);
-        ss = fmaf(x, x, ss);
-        du = fma((double)uu[i], (double)x, du);
-        if (PROD) dv = fma((double)vv[i], (double)x, dv);
-      }
+    for (int off = 32; off >= 1; off >>= 1) {
+      ss += __shfl_xor(ss, off);
+      du += __shfl_xor(du, off);
+      if (PROD) dv += __shfl_xor(dv, off);
     }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    du += __shfl_xor(du, 16);
-    du += __shfl_xor(du, 32);
-    if (PROD) {
-      dv += __shfl_xor(dv, 16);
-      dv += __shfl_xor(dv, 32);
-    }
-    const float qn = sqrtf(ss);
-    const int esh = enc_scale_exp(qn);  // projected values come out times 2^esh
-    // 3. exponents and constants of query col (lanes of lane group 0)
-    if (lg == 0 && wave == 0) {
+    if (lane == 0) {
+      const float qn = sqrtf(ss);
       double acoef = 0, amax = 0;
-      for (int p = 0; p < NP; ++p) {
-        acoef += cb.coef[p];
-        amax = fmax(amax, fabs(cb.coef[p]));
+      for (int sp = 0; sp < cb.nparts; ++sp) {
+        acoef += cb.coef[sp];
+        amax = fmax(amax, fabs(cb.coef[sp]));
       }
       int e1 = 0, e2 = 0, k;
       const double A1 = 2.0 * amax * (double)qn, A2 = 2.0 * (double)smax * (double)qn;
       if (A1 > 0) { frexp(A1, &k); e1 = 26 - k; }
       if (PROD && A2 > 0) { frexp(A2, &k); e2 = 26 - k; }
-      expo[col][0] = e1;
-      expo[col][1] = e2;
-      if ((col >> 2) < kQPGroups && hg < nhg) {
-        const double cq = PROD ? sqrt(M_PI / 2.0) / m : 0.0;
-        QConst o;
-        o.idx_scale = ldexp(1.0, -e1);
-        o.idx_bias = acoef * du;
-        o.sgn_scale = cq * ldexp(1.0, -e2);
-        o.sgn_bias = cq * dv;
-        o.f[0] = (float)o.idx_scale;
-        o.f[1] = (float)o.idx_bias;
-        o.f[2] = (float)o.sgn_scale;
-        o.f[3] = (float)o.sgn_bias;
-        qc[hg * 4 + jq] = o;
-      }
+      expo[j][0] = e1;
+      expo[j][1] = e2;
+      const double cqj = PROD ? sqrt(M_PI / 2.0) / m : 0.0;
+      QConst o;
+      o.idx_scale = ldexp(1.0, -e1);
+      o.idx_bias = acoef * du;
+      o.sgn_scale = cqj * ldexp(1.0, -e2);
+      o.sgn_bias = cqj * dv;
+      o.f[0] = (float)o.idx_scale;
+      o.f[1] = (float)o.idx_bias;
+      o.f[2] = (float)o.sgn_scale;
+      o.f[3] = (float)o.sgn_bias;
+      qc[hg * 4 + j] = o;
     }
-    uint4 xh[4], xl[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) x_frag_f16<false>(raw[kt], esh - kEncScaleLog2, xh[kt], xl[kt]);
-    // 2. Pi q and S q, rows 32 wave .. + 31 of each
-#pragma unroll
-    for (int mat = 0; mat < (PROD ? 2 : 1); ++mat)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int nt = 2 * wave + h2;
-        // three independent accumulation chains (one per pass), summed after
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const uint4 *fr = mat ? fs[h2][kt] : fa[h2][kt];
-          const f16x8 ah = as_f16x8(fr[0]), al = as_f16x8(fr[1]);
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xh[kt]), a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_f16x8(xh[kt]), a1, 0, 0, 0);
-          a2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_f16x8(xl[kt]), a2, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) qv[mat][col][16 * nt + 4 * lg + r] = ldexpf(a0[r] + (a1[r] + a2[r]), -esh);
-      }
   }
   __syncthreads();
-  // 4. operands: unit (group gi, j, jq, kg, w): word w of the four lanes 16 kg + 4 jq + t
-  const int NMF = score_mfmas(NP, PROD);
+  if (r < R) qv[cq][r] = (float)(((part[0][cq][r] + part[1][cq][r]) + part[2][cq][r]) + part[3][cq][r]);
+  __syncthreads();
+  // 4. operands: unit (j, jq, kg, w): word w of the four lanes 16 kg + 4 jq + t
+  const int NMF = score_mfmas(cb.nparts, PROD);
+  const int NP = cb.nparts;
   uint32_t *aw = reinterpret_cast<uint32_t *>(aops);
-  for (int i = tid; i < kQPGroups * NMF * 64; i += kQPThreads) {
-    const int gi = i / (NMF * 64), u = i % (NMF * 64);
-    const int64_t hg = hg0 + gi;
-    if (hg >= nhg) continue;
-    const int j = u >> 6, jq = (u >> 4) & 3, kg = (u >> 2) & 3, w = u & 3;
+  for (int i = tid; i < NMF * 64; i += kQPThreads) {
+    const int j = i >> 6, jq = (i >> 4) & 3, kg = (i >> 2) & 3, w = i & 3;
     const bool sgnpart = j >= 2 * NP;
     const int sl = 4 * (j & 1) + w;
     const float coef = sgnpart ? 2.f : (float)(2.0 * cb.coef[j >> 1]);
-    const int c = 4 * gi + jq;
-    const int E = expo[c][sgnpart ? 1 : 0];
-    const float *src = qv[sgnpart ? 1 : 0][c];
+    const int E = expo[jq][sgnpart ? 1 : 0];
+    const float *src = &qv[jq][sgnpart ? 128 : 0];
     uint32_t out[4] = {0u, 0u, 0u, 0u};  // limb t
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1288,10 +1251,8 @@ __global__ __launch_bounds__(kQPThreads) void qprep128_kernel(
 template <bool PROD>
 static void launch_qprep128(const Derived &D, const float *q, int64_t g, int ngroups, int64_t nhg,
                             i32x4 *aops, QConst *qc, hipStream_t s) {
-  const unsigned grid = (unsigned)((nhg + kQPGroups - 1) / kQPGroups);
-  qprep128_kernel<PROD><<<dim3(grid), dim3(kQPThreads), 0, s>>>(
-      q, g, ngroups, nhg, (const uint4 *)D.pi16_hi, (const uint4 *)D.pi16_lo, (const uint4 *)D.s16_hi,
-      (const uint4 *)D.s16_lo, D.qsums, D.smax, D.cb, D.p.m, aops, qc);
+  qprep128_kernel<PROD><<<dim3((unsigned)nhg), dim3(kQPThreads), 0, s>>>(
+      q, g, ngroups, D.qmat, D.qsums, D.smax, D.cb, D.p.m, aops, qc);
 }
 
 constexpr int kScoreU = 4;  // tiles per load batch (64 keys)
