@@ -3216,18 +3216,32 @@ __device__ __forceinline__ void split_encode_group(
   float ss = 0.f;
 #pragma unroll
   for (int kt = 0; kt < NK; ++kt) {
-    float v[8];
+    if (XBF16) {  // bfloat16 channels are the operand as they are: pairs packed, squares by v_dot2
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      uint32_t h[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = chs[goff + 32 * kt + 8 * kg + e];
-      v[e] = XBF16 ? __uint_as_float((uint32_t)xrow[c] << 16) : reinterpret_cast<const float *>(x)[rr * 128 + c];
-      ss = fmaf(v[e], v[e], ss);
+      for (int i = 0; i < 4; ++i) {
+        const int c0 = chs[goff + 32 * kt + 8 * kg + 2 * i], c1 = chs[goff + 32 * kt + 8 * kg + 2 * i + 1];
+        h[i] = (uint32_t)xrow[c0] | (uint32_t)xrow[c1] << 16;
+        const bf16x2 hv = __builtin_bit_cast(bf16x2, h[i]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(hv, hv, ss, false);
+      }
+      xh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
+      xl[kt] = xh[kt];
+    } else {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = chs[goff + 32 * kt + 8 * kg + e];
+        v[e] = reinterpret_cast<const float *>(x)[rr * 128 + c];
+        ss = fmaf(v[e], v[e], ss);
+      }
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
+      xh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
+      xl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
     }
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split2(v[2 * i], v[2 * i + 1], h[i], l[i]);
-    xh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
-    xl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
   }
   ss += __shfl_xor(ss, 16);
   ss += __shfl_xor(ss, 32);
@@ -3253,25 +3267,35 @@ __device__ __forceinline__ void split_encode_group(
   for (int j = 0; j < nbnd; ++j) tb[j] = nu > 0.f ? cbt[g][j] * nu : cbt[g][j];
 #pragma unroll
   for (int j = 0; j <= nbnd; ++j) cv[j] = cbc[g][j];
+  // The compares form a thermometer code g_0 >= g_1 >= ... (the boundaries
+  // ascend), so bit p of the index k = #{j : g_j} is the parity of
+  // #{m >= 1 : k >= m 2^p}, i.e. the XOR of g_{m 2^p - 1}: one XOR of compare
+  // masks and one v_addc per plane bit, shifted in from the highest
+  // coordinate down so that coordinate 4 nt + i lands at bit 4 nt + i.
   uint32_t pf[B + 1];
 #pragma unroll
   for (int p = 0; p <= B; ++p) pf[p] = 0u;
   float rho[NT][4], rsq = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int nt = NT - 1; nt >= 0; --nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 3; i >= 0; --i) {
       const float y = acc[nt][i];
-      int idx = 0;
+      uint64_t gm[nbnd];
       float cm = cv[0];
 #pragma unroll
-      for (int j = 0; j < nbnd; ++j) {  // the boundaries ascend
+      for (int j = 0; j < nbnd; ++j) {
         const bool ge = y >= tb[j];
-        idx += ge ? 1 : 0;
+        gm[j] = __builtin_amdgcn_ballot_w64(ge);
         cm = ge ? cv[j + 1] : cm;
       }
 #pragma unroll
-      for (int p = 0; p < B; ++p) pf[p] |= (uint32_t)((idx >> p) & 1) << (4 * nt + i);
+      for (int p = 0; p < B; ++p) {
+        uint64_t mk = 0;
+#pragma unroll
+        for (int mm = 1; mm * (1 << p) <= nbnd; ++mm) mk ^= gm[mm * (1 << p) - 1];
+        pf[p] = shift_in(pf[p], mk);
+      }
       const float r = fmaf(-cm, nu, y);
       rsq = fmaf(r, r, rsq);
       rho[nt][i] = r;
@@ -3291,8 +3315,11 @@ __device__ __forceinline__ void split_encode_group(
     rh[kt] = make_uint4(h[0], h[1], h[2], h[3]);
     rl[kt] = make_uint4(l[0], l[1], l[2], l[3]);
   }
+  // sign bits from the highest row down, one v_alignbit each (the float's
+  // sign bit shifted in; an exactly zero z comes out of the accumulation as
+  // +0), complemented once within the field
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nt = NT - 1; nt >= 0; --nt) {
     f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
@@ -3302,8 +3329,9 @@ __device__ __forceinline__ void split_encode_group(
       z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, as_bf16x8(rh[kt]), z, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf[B] |= (z[i] >= 0.f ? 1u : 0u) << (4 * nt + i);
+    for (int i = 3; i >= 0; --i) pf[B] = __builtin_amdgcn_alignbit(pf[B], __float_as_uint(z[i]), 31);
   }
+  pf[B] = ~pf[B] & (4 * NT >= 32 ? 0xFFFFFFFFu : (1u << (4 * NT)) - 1u);
   // lane group 0 gathers the four fields of each plane (index planes, then
   // the sign plane) and writes the plane's words
   const int kc = lane & 15;
