@@ -17,7 +17,7 @@ Reported on one JSON line:
                rotating copies (Mvectors/s)
   encode_*     the encode kernel alone, rotating copies (HIP events around a
                graph of K encodes on the launch stream)
-  roofline     the dominant kernel (encode, an fp16 MFMA contraction)
+  roofline     the dominant kernel (encode, a bf16 + fp16 MFMA contraction)
   cpu_baseline the CPU oracle (numpy float64) on the same layer, one thread
 Further sections, each selectable with --only (comma list) or switched off
 with --no-<name>: score_hbm (32 layers' codes streamed by one score call),
@@ -264,8 +264,8 @@ def section_step(args, out, dev, stream):
                      "unit": "TFLOP/s", "frac": round(enc_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": profiled_traffic("step", f"tq::encode128_kernel<{args.b - 1}, true, true>"),
                      "kernel": "encode128_kernel",
-                     "algorithmic_per_launch": f"{enc_flops} flop ((2 d^2 + 2 d m) per key; the fp16 hi/lo "
-                                               "split executes 5 fp16 MFMA passes of the two products)"},
+                     "algorithmic_per_launch": f"{enc_flops} flop ((2 d^2 + 2 d m) per key; the hi/lo splits "
+                                               "execute 5 MFMA passes: 2 bf16 for Pi x, 3 fp16 for S' rho)"},
     })
 
 
@@ -698,7 +698,7 @@ def main():
         "value": None, "unit": "Mvectors/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp16 MFMA (hi/lo split, fp32 accumulate) + int8 MFMA (int32 accumulate)",
+        "dtype": "bf16 + fp16 MFMA (hi/lo splits, fp32 accumulate) + int8 MFMA (int32 accumulate)",
         "data": "synthetic (seeded Llama-3.1-8B-shaped keys: N(0,1) x per-channel log-normal, 2% outlier "
                 "channels x20)",
         "config": {"workload": "sections " + ",".join(args.sections)},
