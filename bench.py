@@ -121,21 +121,36 @@ def mse_distortion(x, xr):
 
 
 def cpu_baseline(b, heads):
-    """The oracle as it stands on `heads` KV heads of the same layer recipe:
-    encode + pack + score of one decode step, one thread (the canonical
-    figure), then all threads the BLAS pool offers."""
+    """The CPU oracles as they stand on `heads` KV heads of the same layer
+    recipe: encode + score of one decode step.  The canonical figure is the
+    plain C++ oracle on one thread; beside it the same oracle on every core
+    the process may use (std::thread over vectors and query heads), and the
+    numpy oracle (encode + pack + score) on one thread."""
     import numpy as np  # noqa: F401
-    from threadpoolctl import threadpool_info, threadpool_limits
+    from threadpoolctl import threadpool_limits
 
     from kv_cache_compression_04_amd import synth
+    from oracle import ref
     from oracle import tq_oracle as o
 
-    p = o.Params(D, b, M, o.MODE_PROD, 2, 3)
-    _ = p.pi, p.s, p.codebook          # set-up outside the timed region
     x = synth.llama_keys(heads=heads, seq=SEQ, seed=1).double().numpy()
     q = synth.queries(heads * G, seed=5).double().numpy()
+    n = heads * SEQ
+    cores = len(os.sched_getaffinity(0))
+    r = ref.Ref(D, b, M, 0, 2, 3)               # set-up outside the timed region
 
-    def run():
+    def run_ref(threads):
+        t0 = time.perf_counter()
+        codes = r.encode(x, threads=threads)
+        r.score(q, codes, heads, G, SEQ, threads=threads)
+        return time.perf_counter() - t0
+
+    dt1 = run_ref(1)
+    dtn = run_ref(cores)
+    p = o.Params(D, b, M, o.MODE_PROD, 2, 3)
+    _ = p.pi, p.s, p.codebook
+
+    def run_np():
         t0 = time.perf_counter()
         codes = o.encode(x, p)
         o.pack(codes, p)
@@ -143,15 +158,14 @@ def cpu_baseline(b, heads):
         return time.perf_counter() - t0
 
     with threadpool_limits(limits=1):
-        dt1 = run()
-    dtn = run()
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    n = heads * SEQ
+        dtp = run_np()
     return {"value": round(n / dt1 / 1e6, 4), "unit": "Mvectors/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} of {N_KV} KV heads x {SEQ} positions (encode + pack + score of "
-                      f"{heads * G} query heads), float64 numpy, one thread, {dt1:.1f} s",
-            "host_cores_available": len(os.sched_getaffinity(0)),
-            "all_threads": {"value": round(n / dtn / 1e6, 4), "threads": threads, "seconds": round(dtn, 2)}}
+            "sample": f"{heads} of {N_KV} KV heads x {SEQ} positions (encode + score of {heads * G} query "
+                      f"heads), C++ oracle (scalar loops, long double accumulation), one thread, {dt1:.1f} s",
+            "host_cores_available": cores,
+            "all_cores": {"value": round(n / dtn / 1e6, 4), "threads": cores, "seconds": round(dtn, 2)},
+            "numpy_oracle_one_thread": {"value": round(n / dtp / 1e6, 4), "seconds": round(dtp, 2),
+                                        "note": "float64 numpy with BLAS products, encode + pack + score"}}
 
 
 def _events(n=2):
