@@ -398,7 +398,6 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
               float r = XBF16 ? y * ysc[ct] : y;                                                                                            \
               if (B > 0) {                                                                                                                  \
                 const float a = fabsf(y);                                                                                                   \
-                const uint64_t sm = __builtin_amdgcn_ballot_w64(y >= 0.f);                                                                  \
                 uint64_t gm[kHalf > 1 ? kHalf - 1 : 1];                                                                                     \
                 float cm = cp[ct][0];                                                                                                       \
   _Pragma("unroll")                                                                                                                         \
@@ -412,9 +411,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
                   uint64_t mk = 0;                                                                                                          \
   _Pragma("unroll")                                                                                                                         \
                   for (int j = (1 << p) - 1; j < kHalf - 1; j += (1 << p)) mk ^= gm[j];                                                     \
-                  planes[ct][p] = shift_in(planes[ct][p], ~(sm ^ mk));                                                                      \
+                  planes[ct][p] = shift_in(planes[ct][p], mk);                                                                              \
                 }                                                                                                                           \
-                planes[ct][B - 1] = shift_in(planes[ct][B - 1], sm);                                                                        \
+                planes[ct][B - 1] = __builtin_amdgcn_alignbit(planes[ct][B - 1], __float_as_uint(y), 31);                                   \
                 r = XBF16 ? fma_negc(y, ysc[ct], __builtin_copysignf(cm, y)) : y - __builtin_copysignf(cm, y);                              \
               }                                                                                                                             \
               rsq[ct] = fmaf(r, r, rsq[ct]);                                                                                                \
@@ -464,11 +463,21 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode128_kernel(
       }
       sbits[ct] = w;
     }
-    // index planes were shifted in from the lowest coordinate up: reverse them
+    // index planes were shifted in from the lowest coordinate up: the top
+    // plane holds the sign bits of y (1 for y < 0) and plane p < B - 1 the
+    // XOR of its boundary masks, so plane p = (y >= 0) XNOR masks = sign XOR
+    // masks, and the top plane (y >= 0) = NOT sign; then reverse them
 #pragma unroll
-    for (int ct = 0; ct < kEncCT; ++ct)
+    for (int ct = 0; ct < kEncCT; ++ct) {
+      if (B > 0) {
+        const uint32_t sw = planes[ct][B > 0 ? B - 1 : 0];
+#pragma unroll
+        for (int p = 0; p + 1 < B; ++p) planes[ct][p] ^= sw;
+        planes[ct][B > 0 ? B - 1 : 0] = ~sw;
+      }
 #pragma unroll
       for (int p = 0; p < (B > 0 ? B : 1); ++p) planes[ct][p] = __builtin_bitreverse32(planes[ct][p]);
+    }
 
     // ---- store
 #pragma unroll
