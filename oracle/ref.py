@@ -37,6 +37,7 @@ def lib():
         L.tqref_matrices.argtypes = [P, P, P, P, P]
         L.tqref_encode.argtypes = [P, P, I64, P, P, P, P, P, I32]
         L.tqref_score.argtypes = [P, P, I64, I64, P, P, P, P, I64, P, I32]
+        L.tqref_attend.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P, P, P, D, P, I32]
         _lib = L
     return _lib
 
@@ -102,4 +103,20 @@ class Ref:
         out = np.empty((n_kv * g, seq))
         lib().tqref_score(self.h, _ptr(q), n_kv, g, _ptr(idx), _ptr(sign), _ptr(knorm), _ptr(rnorm), seq,
                           _ptr(out), threads)
+        return out
+
+    def attend(self, vref, q, kcodes, vcodes, batch, n_kv, g, seq, scale=None, threads=1):
+        """Attention of q [batch, n_kv g, d] over these K codes and the V codes
+        of the mse-mode context ``vref``; scale None selects 1 / sqrt(d)."""
+        q = np.ascontiguousarray(q, dtype=np.float64)
+        kidx = np.ascontiguousarray(kcodes["idx"], dtype=np.int32) if self.B > 0 else None
+        ksign = np.ascontiguousarray(kcodes["sign"], dtype=np.uint8) if self.mode == 0 else None
+        krn = np.ascontiguousarray(kcodes["rnorm"], dtype=np.float32) if self.mode == 0 else None
+        kn = np.ascontiguousarray(kcodes["knorm"], dtype=np.float32)
+        vidx = np.ascontiguousarray(vcodes["idx"], dtype=np.int32)
+        vn = np.ascontiguousarray(vcodes["knorm"], dtype=np.float32)
+        out = np.empty((batch, n_kv * g, vref.d))
+        lib().tqref_attend(self.h, vref.h, _ptr(q), batch, n_kv, g, seq, _ptr(kidx), _ptr(ksign), _ptr(kn),
+                           _ptr(krn), _ptr(vidx), _ptr(vn), -1.0 if scale is None else float(scale), _ptr(out),
+                           threads)
         return out

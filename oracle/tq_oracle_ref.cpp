@@ -18,6 +18,9 @@
 //     product from sign bits, sqrt(pi/2)/m * ||r|| * <S q, sign(S r)>; 零开销的
 //     秘密: norms stored as 32-bit floats) and 四 (三段论: rotation, then the
 //     signs of S times the residual).
+//   yeyulingfeng.com explainer, "TurboQuant：6倍压缩，零损失": attention over
+//     the compressed cache, here softmax over the logits of the keys' codes
+//     weighting the MSE reconstructions of the values.
 // Readings where the pages are silent (the same as the numpy oracle's):
 //   random numbers: SplitMix64 words, Gaussians by Box-Muller on word pairs
 //     (element (i, j) of an R x C matrix is counter i C + j; pair c / 2 takes
@@ -33,7 +36,9 @@
 //   index = #{j : fp32(u_i) >= t_j}; residual r = x - ||x|| Pi^T c[idx] in the
 //     original domain; sign bit = [fp32((S r)_j) >= 0]; norms float32; a zero
 //     vector has u = 0, r = 0;
-//   prod mode: b - 1 Lloyd-Max bits and m signs; mse mode: b bits.
+//   prod mode: b - 1 Lloyd-Max bits and m signs; mse mode: b bits;
+//   attention: softmax temperature 1 / sqrt(d) unless one is given, values
+//     in mse mode.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -356,6 +361,60 @@ void tqref_score(const void *ctx, const double *q, int64_t n_kv, int64_t g, cons
   std::vector<std::thread> pool;
   for (int t = 0; t < threads; ++t) pool.emplace_back(work, nq * t / threads, nq * (t + 1) / threads);
   for (auto &th : pool) th.join();
+}
+
+// Decode attention over compressed K and V, as the numpy oracle reads it:
+// for each batch entry bi and query head h (KV head h / g), logits from the
+// K codes (as tqref_score) times `scale` (<= 0 selects 1 / sqrt(d)), weights
+// softmax over all seq positions (the largest logit subtracted), output
+//   out[bi][h] = sum_p w_p v~_p,   v~_p = ||v_p|| Pi_V^T c_V[idx_p]
+// with each value reconstructed in the original domain first.  kctx is a
+// prod- or mse-mode context of dimension d, vctx an mse-mode context of
+// dimension dv; the codes of batch entry bi, KV head k, position p are row
+// (bi n_kv + k) seq + p.  q [batch][n_kv g][d], out [batch][n_kv g][dv].
+void tqref_attend(const void *kctx, const void *vctx, const double *q, int64_t batch, int64_t n_kv,
+                  int64_t g, int64_t seq, const int32_t *kidx, const uint8_t *ksign, const float *knorm,
+                  const float *krnorm, const int32_t *vidx, const float *vnorm, double scale, double *out,
+                  int threads) {
+  const Ctx &K = *static_cast<const Ctx *>(kctx);
+  const Ctx &V = *static_cast<const Ctx *>(vctx);
+  const int d = K.d, dv = V.d;
+  if (!(scale > 0)) scale = 1.0 / std::sqrt((double)d);
+  const int64_t nq = n_kv * g;
+  std::vector<double> logits((size_t)nq * seq);
+  for (int64_t bi = 0; bi < batch; ++bi) {
+    const int64_t k0 = bi * n_kv * seq;  // first key row of this batch entry
+    tqref_score(kctx, q + bi * nq * d, n_kv, g, K.B > 0 ? kidx + k0 * d : nullptr,
+                K.mode == 0 ? ksign + k0 * K.m : nullptr, knorm + k0, K.mode == 0 ? krnorm + k0 : nullptr,
+                seq, logits.data(), threads);
+    // the values of this batch entry, reconstructed one at a time
+    std::vector<double> vrec((size_t)n_kv * seq * dv);
+    for (int64_t r = 0; r < n_kv * seq; ++r) {
+      const int32_t *ix = vidx + (k0 + r) * dv;
+      for (int j = 0; j < dv; ++j) {
+        ld a = 0;
+        for (int i = 0; i < dv; ++i) a += (ld)V.pi[(size_t)i * dv + j] * (ld)V.c[ix[i]];
+        vrec[(size_t)r * dv + j] = (double)((ld)vnorm[k0 + r] * a);
+      }
+    }
+    for (int64_t h = 0; h < nq; ++h) {
+      const int64_t kv = h / g;
+      const double *lh = logits.data() + h * seq;
+      ld mx = -INFINITY;
+      for (int64_t p = 0; p < seq; ++p) mx = std::max<ld>(mx, (ld)lh[p] * scale);
+      std::vector<ld> w(seq);
+      ld wsum = 0;
+      for (int64_t p = 0; p < seq; ++p) {
+        w[p] = std::exp((ld)lh[p] * scale - mx);
+        wsum += w[p];
+      }
+      for (int j = 0; j < dv; ++j) {
+        ld a = 0;
+        for (int64_t p = 0; p < seq; ++p) a += w[p] * (ld)vrec[(size_t)(kv * seq + p) * dv + j];
+        out[(bi * nq + h) * dv + j] = (double)(a / wsum);
+      }
+    }
+  }
 }
 
 }  // extern "C"

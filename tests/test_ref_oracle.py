@@ -9,7 +9,9 @@ mathematics:
 * B = 1: the centroids are +-E[|u_1|] = +-G(d/2) / (sqrt(pi) G((d+1)/2));
 * d = 3: a coordinate of a rotated unit vector is uniform on [-1, 1], so the
   Lloyd-Max centroids are -1 + (2j + 1) / 2^B;
-* Pi is orthogonal and S has the seeded Gaussian entries.
+* Pi is orthogonal and S has the seeded Gaussian entries;
+* attention with a zero query weights every position equally, whatever the
+  temperature, so it returns the mean of the value reconstructions.
 """
 import math
 
@@ -101,3 +103,56 @@ def test_threads_give_the_same_codes_and_logits():
         assert np.array_equal(a1[k], a4[k])
     q = synth.queries(4, seed=5).double().numpy()
     assert np.array_equal(r.score(q, a1, 1, 4, 500, threads=1), r.score(q, a1, 1, 4, 500, threads=3))
+
+
+def _attend_case(seed=21, batch=2, n_kv=2, g=4, seq=300, d=128):
+    """Keys and values of Llama-like shape, queries, and both oracles' contexts."""
+    kx = synth.llama_keys(heads=n_kv, seq=seq, d=d, seed=seed, dtype=torch.float32, batch=batch)
+    vx = synth.llama_keys(heads=n_kv, seq=seq, d=d, seed=seed + 1, dtype=torch.float32, batch=batch)
+    q = synth.queries(batch * n_kv * g, d=d, seed=seed + 2).double().numpy().reshape(batch, n_kv * g, d)
+    return kx.double().numpy(), vx.double().numpy(), q
+
+
+@pytest.mark.parametrize("kb,vb,scale", [(3, 3, None), (3, 3, 0.37), (4, 2, None), (2, 4, 1.5)])
+def test_attend_matches_numpy_oracle(kb, vb, scale):
+    batch, n_kv, g, seq, d = 2, 2, 4, 300, 128
+    kx, vx, q = _attend_case(batch=batch, n_kv=n_kv, g=g, seq=seq, d=d)
+    kp, vp = o.Params(d, kb, d, o.MODE_PROD), o.Params(d, vb, d, o.MODE_MSE)
+    kr, vr = ref.Ref(d, kb, d, 0), ref.Ref(d, vb, d, 1)
+    # the same codes on both sides: the attention arithmetic alone is compared
+    kc, vc = o.encode(kx, kp), o.encode(vx, vp)
+    a = kr.attend(vr, q, kc, vc, batch, n_kv, g, seq, scale=scale)
+    e = o.attend(q, kc, vc, kp, vp, batch, n_kv, g, seq, scale=scale)
+    vscale = float(np.max(np.abs(o.dequantize(vc, vp))))
+    assert np.max(np.abs(a - e)) <= 1e-12 * vscale
+
+
+def test_attend_end_to_end_from_each_oracles_own_codes():
+    batch, n_kv, g, seq, d = 1, 2, 4, 257, 128
+    kx, vx, q = _attend_case(seed=31, batch=batch, n_kv=n_kv, g=g, seq=seq, d=d)
+    kp, vp = o.Params(d, 3, d, o.MODE_PROD), o.Params(d, 3, d, o.MODE_MSE)
+    kr, vr = ref.Ref(d, 3, d, 0), ref.Ref(d, 3, d, 1)
+    ka, va = kr.encode(kx), vr.encode(vx)
+    ke, ve = o.encode(kx, kp), o.encode(vx, vp)
+    # these inputs encode identically in both oracles (no decision on a boundary)
+    assert np.array_equal(ka["idx"], ke["idx"]) and np.array_equal(ka["sign"], ke["sign"])
+    assert np.array_equal(va["idx"], ve["idx"])
+    a = kr.attend(vr, q, ka, va, batch, n_kv, g, seq)
+    e = o.attend(q, ke, ve, kp, vp, batch, n_kv, g, seq)
+    assert np.max(np.abs(a - e)) <= 1e-12 * float(np.max(np.abs(o.dequantize(ve, vp))))
+
+
+@pytest.mark.parametrize("scale", [None, 0.01, 3.0])
+def test_attend_zero_query_is_the_mean_value(scale):
+    batch, n_kv, g, seq, d = 1, 1, 4, 129, 128
+    kx, vx, _ = _attend_case(seed=41, batch=batch, n_kv=n_kv, g=g, seq=seq, d=d)
+    kr, vr = ref.Ref(d, 3, d, 0), ref.Ref(d, 3, d, 1)
+    ka, va = kr.encode(kx), vr.encode(vx)
+    out = kr.attend(vr, np.zeros((batch, n_kv * g, d)), ka, va, batch, n_kv, g, seq, scale=scale)
+    # the mean of ||v|| Pi^T c[idx] over the positions, formed here from the
+    # C++ oracle's own matrices
+    pi, _, c, _ = vr.matrices()
+    vrec = (va["knorm"].astype(np.float64)[:, None] * c.astype(np.float64)[va["idx"]]) @ pi
+    want = vrec.mean(axis=0)
+    for h in range(g):
+        assert np.max(np.abs(out[0, h] - want)) <= 1e-13 * float(np.max(np.abs(vrec)))
