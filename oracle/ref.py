@@ -38,6 +38,7 @@ def lib():
         L.tqref_encode.argtypes = [P, P, I64, P, P, P, P, P, I32]
         L.tqref_score.argtypes = [P, P, I64, I64, P, P, P, P, I64, P, I32]
         L.tqref_attend.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P, P, P, D, P, I32]
+        L.tqref_search.argtypes = [P, P, I64, P, P, P, P, I64, I64, P, P, I32]
         _lib = L
     return _lib
 
@@ -120,3 +121,17 @@ class Ref:
                            _ptr(krn), _ptr(vidx), _ptr(vn), -1.0 if scale is None else float(scale), _ptr(out),
                            threads)
         return out
+
+    def search(self, q, codes, n, k, threads=1):
+        """Top-k (indices, logits) of each query over the n coded vectors."""
+        q = np.ascontiguousarray(q, dtype=np.float64)
+        nq = q.shape[0]
+        idx = np.ascontiguousarray(codes["idx"], dtype=np.int32) if self.B > 0 else None
+        sign = np.ascontiguousarray(codes["sign"], dtype=np.uint8) if self.mode == 0 else None
+        rnorm = np.ascontiguousarray(codes["rnorm"], dtype=np.float32) if self.mode == 0 else None
+        knorm = np.ascontiguousarray(codes["knorm"], dtype=np.float32)
+        oi = np.empty((nq, k), dtype=np.int64)
+        ov = np.empty((nq, k))
+        lib().tqref_search(self.h, _ptr(q), nq, _ptr(idx), _ptr(sign), _ptr(knorm), _ptr(rnorm), n, k, _ptr(oi),
+                           _ptr(ov), threads)
+        return oi, ov

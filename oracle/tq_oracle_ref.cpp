@@ -417,4 +417,39 @@ void tqref_attend(const void *kctx, const void *vctx, const double *q, int64_t b
   }
 }
 
+// Top-k search: for each of nq queries q [nq][d], the k of the n coded
+// vectors with the largest logit (as tqref_score, every query against the
+// same n vectors), in descending order of logit, ties to the lower index.
+// out_idx / out_val [nq][k]; k <= n.  A plain running list per query: each
+// logit is compared with the list's last entry and, if it beats it, inserted
+// in place.
+void tqref_search(const void *ctx, const double *q, int64_t nq, const int32_t *idx, const uint8_t *sign,
+                  const float *knorm, const float *rnorm, int64_t n, int64_t k, int64_t *out_idx,
+                  double *out_val, int threads) {
+  const Ctx &C = *static_cast<const Ctx *>(ctx);
+  for (int64_t i = 0; i < nq; ++i) {
+    std::vector<double> row(n);
+    tqref_score(ctx, q + i * C.d, 1, 1, idx, sign, knorm, rnorm, n, row.data(), threads);
+    std::vector<int64_t> li;
+    std::vector<double> lv;
+    for (int64_t v = 0; v < n; ++v) {
+      // strictly larger logits go first; an equal logit comes after (v is
+      // larger than every index already listed)
+      if ((int64_t)li.size() == k && !(row[v] > lv.back())) continue;
+      int64_t pos = (int64_t)li.size();
+      while (pos > 0 && row[v] > lv[pos - 1]) --pos;
+      li.insert(li.begin() + pos, v);
+      lv.insert(lv.begin() + pos, row[v]);
+      if ((int64_t)li.size() > k) {
+        li.pop_back();
+        lv.pop_back();
+      }
+    }
+    for (int64_t j = 0; j < k; ++j) {
+      out_idx[i * k + j] = li[j];
+      out_val[i * k + j] = lv[j];
+    }
+  }
+}
+
 }  // extern "C"

@@ -156,3 +156,28 @@ def test_attend_zero_query_is_the_mean_value(scale):
     want = vrec.mean(axis=0)
     for h in range(g):
         assert np.max(np.abs(out[0, h] - want)) <= 1e-13 * float(np.max(np.abs(vrec)))
+
+
+@pytest.mark.parametrize("b,mode,k", [(3, 0, 10), (2, 1, 1), (4, 0, 37)])
+def test_search_is_the_top_k_of_the_logits(b, mode, k):
+    d, n, nq = 128, 3000, 6
+    r, p = ref.Ref(d, b, d, mode), o.Params(d, b, d, mode)
+    x = synth.highdim_keys(n, d=d, seed=51).double().numpy()
+    x[5] *= 20.0                                   # a vector that leads query 0 ...
+    x[17] = x[5]                                   # ... tied exactly: the lower index first
+    c = o.encode(x, p)
+    q = synth.queries(nq, d=d, seed=52).double().numpy()
+    q[0] = x[5]                                    # both tied vectors lead this query
+    oi, ov = r.search(q, c, n, k)
+    own = r.score(q, c, 1, nq, n)                  # the C++ oracle's own logits
+    for i in range(nq):
+        order = np.argsort(-own[i], kind="stable")[:k]
+        assert np.array_equal(oi[i], order) and np.array_equal(ov[i], own[i][order])
+    assert oi[0][0] == 5 and (k == 1 or oi[0][1] == 17)
+    # against the numpy oracle's logits: the same sets wherever the k-th and
+    # (k+1)-th logits are apart by more than the two oracles' difference
+    le = o.score(q, c, p, 1, nq, n)
+    for i in range(nq):
+        srt = np.sort(le[i])[::-1]
+        if srt[k - 1] - srt[k] > 1e-9 * abs(srt[0]):
+            assert set(oi[i].tolist()) == set(np.argsort(-le[i], kind="stable")[:k].tolist())
