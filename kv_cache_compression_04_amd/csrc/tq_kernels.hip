@@ -2307,6 +2307,10 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   __shared__ __attribute__((aligned(16))) float lg[kAttWaves][4][kAttKPW];  // logits, then weights
   // one block of quantised weights: [set][query][limb][positions / 4]
   __shared__ __attribute__((aligned(16))) uint32_t limbs[kAttWaves][NQ][4][4][64 / 4];
+  // value index words of a 64-position block, copied into LDS by the
+  // memory unit (no registers) one block ahead of their use: two slots
+  constexpr bool VDMA = SHARED;
+  __shared__ __attribute__((aligned(16))) uint32_t vbuf[kAttWaves][2][VDMA ? 64 * 4 * BV : 4];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = blockIdx.y;  // (batch * n_kv + head) * ngroups + group
   const int hb = hg / ngroups;
@@ -2465,10 +2469,32 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
   // one block: lane (c16, kg) takes query kg, positions 4 c16 .. 4 c16 + 3.
   const bufrsrc rvi = buf_rsrc(vi, (uint32_t)npos * 16u * BV);
   const uint32_t vlane = (uint32_t)(16 * kg) * (16u * BV) + woff;
+  // block b's 64 * 16 BV bytes are contiguous: BV copies of 1 KB, lane l
+  // taking bytes 16 l .. 16 l + 15 of each; positions past npos read zeros
+  // (their weights are zero, so what a slot holds there never counts)
+  auto copy_block = [&](int b) {
+#pragma unroll
+    for (int k = 0; k < BV; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rvi, (__attribute__((address_space(3))) void *)&vbuf[wave][b & 1][256 * k], 16,
+          (int)((uint32_t)b * (1024u * BV) + 1024u * k + 16u * (uint32_t)lane), 0, 0, 2);
+  };
+  if constexpr (VDMA) copy_block(0);
   for (int blk = 0; blk < kAttKPW / 64; ++blk) {
     // V index words of this lane's 16 positions (issued first)
     uint32_t x[4][4][BV];
-    if (npos == kAttKPW) {  // every access in range: scalar offsets
+    if constexpr (VDMA) {
+      // the copy of this block is the wave's only vector-memory operation
+      // in flight here (the compiler does not track these copies itself)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const uint32_t *vb_ = &vbuf[wave][blk & 1][0];
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int p = 0; p < BV; ++p) x[gi][e][p] = vb_[(16 * kg + 4 * gi + e) * 4 * BV + w * BV + p];
+    } else if (npos == kAttKPW) {  // every access in range: scalar offsets
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
@@ -2525,6 +2551,14 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    i32x4 Aw0;
+    if constexpr (VDMA) {
+      // every LDS read of this block is done before the next block's copy
+      // is issued into the other slot
+      Aw0 = *reinterpret_cast<const i32x4 *>(&limbs[wave][0][c16 >> 2][c16 & 3][4 * kg]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (blk + 1 < kAttKPW / 64) copy_block(blk + 1);
+    }
     // transpose: D[S][gi] = parity part S of the byte-beta transposes
     uint32_t D[NPV][4];
 #pragma unroll
@@ -2548,8 +2582,11 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend128_kernel(
 #pragma unroll
     for (int sp = 0; sp < NPV; ++sp) {
       // A: rows (query c16 / 4, limb c16 % 4), positions 16 kg .. 16 kg + 15
-      const i32x4 Aw =
-          *reinterpret_cast<const i32x4 *>(&limbs[wave][SHARED ? 0 : sp][c16 >> 2][c16 & 3][4 * kg]);
+      i32x4 Aw;
+      if constexpr (VDMA)
+        Aw = Aw0;
+      else
+        Aw = *reinterpret_cast<const i32x4 *>(&limbs[wave][SHARED ? 0 : sp][c16 >> 2][c16 & 3][4 * kg]);
       i32x4 lo4[4], hi4[4];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
